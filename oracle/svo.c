@@ -1,0 +1,466 @@
+/* svo.c - reference oracle for batched lossless draft verification.
+ *
+ * TEST INFRASTRUCTURE ONLY: a plain, slow, single-threaded CPU statement of
+ * what the GPU library computes.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code with the HIP
+ * library.  All floating-point arithmetic is double precision; bf16 logits
+ * are widened exactly; the loops follow the method's steps in order with no
+ * blocking, fusion or reordering.
+ *
+ * Sources (the pages are cited by title and section):
+ *  [SD]  "投机解码" (Speculative decoding), rustineverything.app:
+ *        section "接受规则为什么不改变分布" (why the acceptance rule keeps the
+ *        distribution) with its sub-sections "贪心" (greedy), "采样：标准拒绝采样"
+ *        (standard rejection sampling), "默认路径：草稿当 one-hot" (one-hot
+ *        default), "SGLang 默认：只看目标概率，可以验证一棵树" (target-only tree);
+ *        section "对照：mistral.rs" (the q <= 0 rule).
+ *  [ZOO] "The speculative decoding zoo" (section 6.6), mlinterviewnotes.com:
+ *        "DFlash - the draft that borrows everything" (greedy prefix match).
+ *  [PHX] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ *        1, 2, 3", SC'11 (Philox4x32-10), which the pages do not fix.
+ *
+ * Readings where the pages leave a step open (all listed in the design notes):
+ *  - randomness is a counter-based Philox4x32-10 stream keyed by the request
+ *    seed; the coin for row r of request b is word 0 of counter (0, r, b, 0);
+ *    the race noise for vocab id y is word (y & 3) of counter (y>>2, r, b, 1);
+ *  - uniforms are (2*(w>>9)+1)/2^24, inside (0,1) and exact in fp32;
+ *  - the acceptance test is strict (u*q < p); q(x) <= 0 accepts iff p(x) > 0;
+ *  - the residual / bonus sample is an exponential race: argmax_y w(y)/E_y
+ *    with E_y = -ln U_y, ties to the smallest y; an all-zero residual falls
+ *    back to p;
+ *  - argmax ties go to the smallest index, on raw logits;
+ *  - T <= 0 means greedy, a non-finite T is rejected;
+ *  - draft id -1 ends the chain; NaN/+inf logits or an all -inf row are
+ *    rejected, -inf is a masked token.
+ */
+#include "svo.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 [PHX]: each round multiplies counter words 0 and 2 by the
+ * two round multipliers, and the new counter is
+ *   (hi(M1*c2) ^ c1 ^ k0,  lo(M1*c2),  hi(M0*c0) ^ c3 ^ k1,  lo(M0*c0));
+ * between rounds the key is bumped by the two Weyl constants. */
+#define SVO_PHILOX_M0 0xD2511F53u
+#define SVO_PHILOX_M1 0xCD9E8D57u
+#define SVO_PHILOX_W0 0x9E3779B9u
+#define SVO_PHILOX_W1 0xBB67AE85u
+
+void svo_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += SVO_PHILOX_W0;
+      k1 += SVO_PHILOX_W1;
+    }
+    uint64_t prod0 = (uint64_t)SVO_PHILOX_M0 * (uint64_t)c0;
+    uint64_t prod1 = (uint64_t)SVO_PHILOX_M1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+    uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+double svo_uniform(uint32_t w) {
+  uint32_t j = w >> 9; /* 23 bits */
+  return (double)(2u * j + 1u) / 16777216.0; /* 2^24 */
+}
+
+static void seed_key(uint64_t seed, uint32_t key[2]) {
+  key[0] = (uint32_t)(seed & 0xffffffffu);
+  key[1] = (uint32_t)(seed >> 32);
+}
+
+double svo_coin(uint64_t seed, int32_t b, int32_t r) {
+  uint32_t key[2], ctr[4] = {0u, (uint32_t)r, (uint32_t)b, 0u}, out[4];
+  seed_key(seed, key);
+  svo_philox4x32_10(ctr, key, out);
+  return svo_uniform(out[0]);
+}
+
+double svo_noise_uniform(uint64_t seed, int32_t b, int32_t r, int32_t y) {
+  uint32_t key[2], ctr[4] = {(uint32_t)y >> 2, (uint32_t)r, (uint32_t)b, 1u}, out[4];
+  seed_key(seed, key);
+  svo_philox4x32_10(ctr, key, out);
+  return svo_uniform(out[y & 3]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Logit rows. */
+
+static double logit_at(int32_t dtype, const void* base, int64_t idx) {
+  if (dtype == SVO_BF16) {
+    uint16_t h = ((const uint16_t*)base)[idx];
+    uint32_t bits = (uint32_t)h << 16; /* bf16 is the top half of an fp32 */
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)base)[idx];
+}
+
+/* One row's statistics: m = max, amax = smallest index attaining m, and for a
+ * stochastic row S = sum_y exp((l_y - m)/T), left to right.  The target
+ * distribution is p(y) = exp((l_y - m)/T)/S: the softmax of the tempered
+ * logits ([SD] "接受规则为什么不改变分布": p is taken after temperature). */
+typedef struct {
+  double m, S;
+  int32_t amax;
+  int32_t status;
+} row_stat;
+
+static row_stat scan_row(int32_t dtype, const void* logits, int64_t row_off, int32_t V, double T, int stochastic) {
+  row_stat st;
+  st.m = -INFINITY;
+  st.amax = 0;
+  st.S = NAN;
+  st.status = SVO_REQ_OK;
+  for (int32_t y = 0; y < V; ++y) {
+    double l = logit_at(dtype, logits, row_off + y);
+    if (isnan(l) || (isinf(l) && l > 0)) st.status = SVO_REQ_NONFINITE;
+    if (l > st.m) { /* strict: the first index of the max is kept */
+      st.m = l;
+      st.amax = y;
+    }
+  }
+  if (st.m == -INFINITY) st.status = SVO_REQ_NONFINITE; /* every token masked */
+  if (st.status != SVO_REQ_OK) return st;
+  if (stochastic) {
+    double S = 0.0;
+    for (int32_t y = 0; y < V; ++y) S += exp((logit_at(dtype, logits, row_off + y) - st.m) / T);
+    st.S = S;
+  }
+  return st;
+}
+
+static double p_of(int32_t dtype, const void* logits, int64_t row_off, const row_stat* st, double T, int32_t y) {
+  return exp((logit_at(dtype, logits, row_off + y) - st->m) / T) / st->S;
+}
+
+void svo_row_stats(int32_t rows, int32_t vocab, int32_t dtype, const void* logits, int64_t row_stride,
+                   const float* temperature, double* row_max, int32_t* row_argmax, double* row_sumexp,
+                   int32_t* row_status) {
+  for (int32_t i = 0; i < rows; ++i) {
+    double T = (double)temperature[i];
+    row_stat st = scan_row(dtype, logits, (int64_t)i * row_stride, vocab, T, T > 0.0);
+    if (row_max) row_max[i] = st.m;
+    if (row_argmax) row_argmax[i] = st.amax;
+    if (row_sumexp) row_sumexp[i] = st.S;
+    if (row_status) row_status[i] = st.status;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exponential race over non-negative weights w[0..V):
+ *   y* = argmax_y w(y) / E_y,  E_y = -ln U_y,
+ * with U_y from the race-noise stream of (seed, b, r).  Because E_y are
+ * independent Exp(1) variables, P(y* = y) = w(y) / sum w, so this samples
+ * the normalised weights exactly; the Gumbel-max trick of the vLLM resample
+ * step quoted in [SD] "采样：标准拒绝采样" is the same race in log space.
+ * Ties go to the smallest y.  Writes the relative gap between the two
+ * largest keys to *margin. */
+static int32_t race(const double* w, int32_t V, uint64_t seed, int32_t b, int32_t r, double* margin) {
+  int32_t best = -1;
+  double k1 = -1.0, k2 = -1.0;
+  for (int32_t y = 0; y < V; ++y) {
+    double E = -log(svo_noise_uniform(seed, b, r, y));
+    double key = w[y] / E;
+    if (key > k1) {
+      k2 = k1;
+      k1 = key;
+      best = y;
+    } else if (key > k2) {
+      k2 = key;
+    }
+  }
+  if (k2 < 0.0) k2 = 0.0;
+  *margin = (k1 > 0.0) ? (k1 - k2) / k1 : 0.0;
+  return best;
+}
+
+/* Sample from normalize(w); if every weight is zero, from p instead. */
+static int32_t emit_from(double* w, const double* p, int32_t V, uint64_t seed, int32_t b, int32_t r, double* margin) {
+  double total = 0.0;
+  for (int32_t y = 0; y < V; ++y) total += w[y];
+  if (!(total > 0.0)) memcpy(w, p, sizeof(double) * (size_t)V);
+  return race(w, V, seed, b, r, margin);
+}
+
+static double rel_gap(double a, double b) {
+  double hi = a > b ? a : b;
+  if (hi <= 0.0) return INFINITY;
+  return fabs(a - b) / hi;
+}
+
+static int is_finite_num(double x) { return !isnan(x) && !isinf(x); }
+
+/* ------------------------------------------------------------------------ */
+/* Chain verification of one request.
+ *
+ * [SD] "采样：标准拒绝采样": accept x_i with probability min(1, p(x_i)/q(x_i)),
+ * left to right; on the first rejection sample from max(0, p - q)/Z and drop
+ * the remaining drafts; when all k are accepted sample one more token from
+ * row k.  The ratio test is done as u*q(x) < p(x) (strict), as in the
+ * quoted engine kernels.  [SD] "对照：mistral.rs": q(x) <= 0 accepts iff
+ * p(x) > 0.  [SD] "默认路径：草稿当 one-hot": with a one-hot draft q(x) = 1, so
+ * the test is u < p(x) and the residual is p with x zeroed.  [SD] "贪心"
+ * and [ZOO] DFlash: with T = 0 a draft is accepted iff it equals the target
+ * argmax, a rejection emits the argmax, and the bonus is the argmax of the
+ * next row. */
+static void chain_one(const svo_chain_args* a, int32_t b, double* w, double* prow) {
+  const int32_t k = a->max_draft, V = a->vocab, R = k + 1;
+  int32_t* tok = a->tokens + (int64_t)b * R;
+  double* pd = a->p_draft ? a->p_draft + (int64_t)b * k : NULL;
+  double min_margin = INFINITY;
+  int32_t n_dec = 0;
+  int32_t status = SVO_REQ_OK;
+
+  for (int32_t i = 0; i < R; ++i) tok[i] = -1;
+  if (pd)
+    for (int32_t i = 0; i < k; ++i) pd[i] = NAN;
+  a->accept_len[b] = 0;
+
+  /* 1. validation */
+  double T = (double)a->temperature[b];
+  const int32_t* x = a->draft_ids + (int64_t)b * k;
+  int32_t kb = k;
+  for (int32_t i = 0; i < k; ++i)
+    if (x[i] == -1) {
+      kb = i;
+      break;
+    }
+  if (!is_finite_num(T)) status = SVO_REQ_BAD_TEMPERATURE;
+  for (int32_t i = 0; i < kb && status == SVO_REQ_OK; ++i)
+    if (x[i] < 0 || x[i] >= V) status = SVO_REQ_BAD_DRAFT_ID;
+  const int greedy = (T <= 0.0);
+
+  /* 2. row statistics of the rows that are read: 0..kb */
+  row_stat st[R > 0 ? R : 1];
+  if (status == SVO_REQ_OK) {
+    for (int32_t r = 0; r <= kb; ++r) {
+      st[r] = scan_row(a->logits_dtype, a->logits, ((int64_t)b * R + r) * a->logits_row_stride, V, T, !greedy);
+      if (st[r].status != SVO_REQ_OK) status = st[r].status;
+    }
+  }
+  if (status != SVO_REQ_OK) {
+    if (a->req_status) a->req_status[b] = status;
+    if (a->min_margin) a->min_margin[b] = INFINITY;
+    if (a->n_decisions) a->n_decisions[b] = 0;
+    return;
+  }
+
+  /* p_i(x_i) for every used draft slot */
+  double px[k > 0 ? k : 1];
+  for (int32_t i = 0; i < kb; ++i) {
+    int64_t off = ((int64_t)b * R + i) * a->logits_row_stride;
+    if (greedy)
+      px[i] = (x[i] == st[i].amax) ? 1.0 : 0.0; /* point mass at the argmax */
+    else
+      px[i] = p_of(a->logits_dtype, a->logits, off, &st[i], T, x[i]);
+    if (pd) pd[i] = px[i];
+  }
+
+  /* 3. left-to-right decisions, stopping at the first rejection */
+  int32_t acc = 0;
+  for (int32_t i = 0; i < kb; ++i) {
+    int accept;
+    ++n_dec;
+    if (greedy) {
+      accept = (x[i] == st[i].amax);
+    } else if (a->draft_kind == SVO_DRAFT_ONEHOT) {
+      double u = svo_coin(a->seed[b], b, i);
+      accept = (u < px[i]);
+      double g = rel_gap(u, px[i]);
+      if (g < min_margin) min_margin = g;
+    } else {
+      double q = (double)a->draft_probs[((int64_t)b * k + i) * a->q_row_stride + x[i]];
+      if (q <= 0.0) {
+        accept = (px[i] > 0.0);
+      } else {
+        double u = svo_coin(a->seed[b], b, i);
+        accept = (u * q < px[i]);
+        double g = rel_gap(u * q, px[i]);
+        if (g < min_margin) min_margin = g;
+      }
+    }
+    if (!accept) break;
+    tok[acc] = x[i];
+    ++acc;
+  }
+
+  /* 4. one token from row acc: the residual after a rejection, the bonus
+   *    after full acceptance */
+  int32_t emitted;
+  ++n_dec;
+  if (greedy) {
+    emitted = st[acc].amax;
+  } else {
+    int64_t off = ((int64_t)b * R + acc) * a->logits_row_stride;
+    for (int32_t y = 0; y < V; ++y) prow[y] = p_of(a->logits_dtype, a->logits, off, &st[acc], T, y);
+    if (acc < kb && a->draft_kind == SVO_DRAFT_PROBS) {
+      const float* qrow = a->draft_probs + ((int64_t)b * k + acc) * a->q_row_stride;
+      for (int32_t y = 0; y < V; ++y) {
+        double d = prow[y] - (double)qrow[y];
+        w[y] = d > 0.0 ? d : 0.0;
+      }
+    } else if (acc < kb) {
+      for (int32_t y = 0; y < V; ++y) w[y] = prow[y];
+      w[x[acc]] = 0.0;
+    } else {
+      for (int32_t y = 0; y < V; ++y) w[y] = prow[y];
+    }
+    double g;
+    emitted = emit_from(w, prow, V, a->seed[b], b, acc, &g);
+    if (g < min_margin) min_margin = g;
+  }
+  tok[acc] = emitted;
+  a->accept_len[b] = acc;
+  if (a->req_status) a->req_status[b] = SVO_REQ_OK;
+  if (a->min_margin) a->min_margin[b] = min_margin;
+  if (a->n_decisions) a->n_decisions[b] = n_dec;
+}
+
+void svo_verify_chain(const svo_chain_args* a) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(a->vocab > 0 ? a->vocab : 1));
+  double* prow = (double*)malloc(sizeof(double) * (size_t)(a->vocab > 0 ? a->vocab : 1));
+  for (int32_t b = 0; b < a->batch; ++b) chain_one(a, b, w, prow);
+  free(w);
+  free(prow);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Target-only tree verification of one request ([SD] "SGLang 默认：只看目标概率，
+ * 可以验证一棵树").  Node 0 is the root; row n is the target distribution after
+ * node n.  At each level one coin u is drawn; the children of the current
+ * node are tried in increasing node index, accumulating their target
+ * probabilities, and child j is accepted if p(tok_j) > 0 and u < acc_j.  If
+ * none is accepted, the tried children's probability is removed from p and
+ * the next token is drawn from what is left; at a leaf the bonus is drawn
+ * from p.  Greedy mode follows the argmax through the tree. */
+static void tree_one(const svo_tree_args* a, int32_t b, double* w, double* prow) {
+  const int32_t N = a->num_nodes, V = a->vocab;
+  int32_t* path = a->accept_path + (int64_t)b * N;
+  int32_t* tok = a->tokens + (int64_t)b * N;
+  const int32_t* ntok = a->node_tokens + (int64_t)b * N;
+  const int32_t* par = a->parent + (int64_t)b * N;
+  double min_margin = INFINITY;
+  int32_t n_dec = 0;
+  int32_t status = SVO_REQ_OK;
+
+  for (int32_t i = 0; i < N; ++i) {
+    path[i] = -1;
+    tok[i] = -1;
+  }
+  a->accept_len[b] = 0;
+
+  double T = (double)a->temperature[b];
+  if (!is_finite_num(T)) status = SVO_REQ_BAD_TEMPERATURE;
+  if (status == SVO_REQ_OK) {
+    if (par[0] != -1) status = SVO_REQ_BAD_TREE;
+    for (int32_t i = 1; i < N && status == SVO_REQ_OK; ++i) {
+      if (par[i] < 0 || par[i] >= i) status = SVO_REQ_BAD_TREE;
+      if (ntok[i] < 0 || ntok[i] >= V) status = SVO_REQ_BAD_TREE;
+    }
+    for (int32_t i = 1; i < N && status == SVO_REQ_OK; ++i)
+      for (int32_t j = i + 1; j < N; ++j)
+        if (par[i] == par[j] && ntok[i] == ntok[j]) status = SVO_REQ_BAD_TREE;
+  }
+  const int greedy = (T <= 0.0);
+  row_stat st[N > 0 ? N : 1];
+  if (status == SVO_REQ_OK) {
+    for (int32_t n = 0; n < N; ++n) {
+      st[n] = scan_row(a->logits_dtype, a->logits, ((int64_t)b * N + n) * a->logits_row_stride, V, T, !greedy);
+      if (st[n].status != SVO_REQ_OK) status = st[n].status;
+    }
+  }
+  if (status != SVO_REQ_OK) {
+    if (a->req_status) a->req_status[b] = status;
+    if (a->min_margin) a->min_margin[b] = INFINITY;
+    if (a->n_decisions) a->n_decisions[b] = 0;
+    return;
+  }
+
+  int32_t cur = 0, len = 0, emitted = -1;
+  for (;;) {
+    int64_t off = ((int64_t)b * N + cur) * a->logits_row_stride;
+    int32_t nchild = 0;
+    for (int32_t c = cur + 1; c < N; ++c)
+      if (par[c] == cur) ++nchild;
+    ++n_dec;
+    if (greedy) {
+      int32_t next = -1;
+      for (int32_t c = cur + 1; c < N; ++c)
+        if (par[c] == cur && ntok[c] == st[cur].amax) next = c;
+      if (next < 0) {
+        emitted = st[cur].amax;
+        break;
+      }
+      path[len] = next;
+      tok[len] = ntok[next];
+      ++len;
+      cur = next;
+      continue;
+    }
+    if (nchild == 0) { /* leaf: bonus token from p_cur */
+      for (int32_t y = 0; y < V; ++y) prow[y] = p_of(a->logits_dtype, a->logits, off, &st[cur], T, y);
+      for (int32_t y = 0; y < V; ++y) w[y] = prow[y];
+      double g;
+      emitted = emit_from(w, prow, V, a->seed[b], b, cur, &g);
+      if (g < min_margin) min_margin = g;
+      break;
+    }
+    double u = svo_coin(a->seed[b], b, cur);
+    double acc = 0.0;
+    int32_t next = -1;
+    for (int32_t c = cur + 1; c < N; ++c) {
+      if (par[c] != cur) continue;
+      double pc = p_of(a->logits_dtype, a->logits, off, &st[cur], T, ntok[c]);
+      acc += pc;
+      double g = rel_gap(u, acc);
+      if (g < min_margin) min_margin = g;
+      if (pc > 0.0 && (u < acc / a->threshold_acc || pc >= a->threshold_single)) {
+        next = c;
+        break;
+      }
+    }
+    if (next >= 0) {
+      path[len] = next;
+      tok[len] = ntok[next];
+      ++len;
+      cur = next;
+      continue;
+    }
+    /* no child accepted: p with every tried child's token removed */
+    for (int32_t y = 0; y < V; ++y) prow[y] = p_of(a->logits_dtype, a->logits, off, &st[cur], T, y);
+    for (int32_t y = 0; y < V; ++y) w[y] = prow[y];
+    for (int32_t c = cur + 1; c < N; ++c)
+      if (par[c] == cur) w[ntok[c]] = 0.0;
+    ++n_dec;
+    double g;
+    emitted = emit_from(w, prow, V, a->seed[b], b, cur, &g);
+    if (g < min_margin) min_margin = g;
+    break;
+  }
+  tok[len] = emitted;
+  a->accept_len[b] = len;
+  if (a->req_status) a->req_status[b] = SVO_REQ_OK;
+  if (a->min_margin) a->min_margin[b] = min_margin;
+  if (a->n_decisions) a->n_decisions[b] = n_dec;
+}
+
+void svo_verify_tree(const svo_tree_args* a) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(a->vocab > 0 ? a->vocab : 1));
+  double* prow = (double*)malloc(sizeof(double) * (size_t)(a->vocab > 0 ? a->vocab : 1));
+  for (int32_t b = 0; b < a->batch; ++b) tree_one(a, b, w, prow);
+  free(w);
+  free(prow);
+}

@@ -1,0 +1,102 @@
+/* svo.h - reference oracle for batched lossless draft verification.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This header and svo.c form a plain, slow,
+ * single-threaded CPU implementation of what the GPU library computes.  It
+ * exists so that tests, the smoke check and the benchmark's CPU-baseline leg
+ * can compare the HIP path against an independent implementation.  Nothing
+ * in the product path may include, link or call it.  It shares no code,
+ * header, table or constant with the HIP library.
+ *
+ * Every pointer is host memory.  Floating-point work is done in double;
+ * bf16 inputs are widened exactly.
+ */
+#ifndef SVO_H
+#define SVO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Per-request status codes (same numbering as the library's, defined here
+ * independently). */
+enum {
+  SVO_REQ_OK = 0,
+  SVO_REQ_BAD_DRAFT_ID = 1,
+  SVO_REQ_BAD_TREE = 2,
+  SVO_REQ_NONFINITE = 3,
+  SVO_REQ_BAD_TEMPERATURE = 4
+};
+
+enum { SVO_F32 = 0, SVO_BF16 = 1 };
+enum { SVO_DRAFT_PROBS = 0, SVO_DRAFT_ONEHOT = 1 };
+
+/* Philox4x32-10 block function: 10 rounds of the Philox-4x32 bijection keyed
+ * by key[0..1], applied to the 128-bit counter ctr[0..3]. */
+void svo_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+/* Uniform in the open interval (0,1) from one 32-bit word: (2*(w>>9)+1)/2^24. */
+double svo_uniform(uint32_t w);
+
+/* The coin for row r of request b, and the race noise word for vocab id y. */
+double svo_coin(uint64_t seed, int32_t b, int32_t r);
+double svo_noise_uniform(uint64_t seed, int32_t b, int32_t r, int32_t y);
+
+/* Row statistics of `rows` logit rows.  Row i starts at element i*row_stride.
+ * temperature[i] <= 0 means greedy (no sum is formed; sumexp = NaN).
+ * Outputs (any may be NULL): row_max, row_argmax (smallest index of the max,
+ * on raw logits), row_sumexp = sum_y exp((l_y - max)/T) summed left to right,
+ * row_status (SVO_REQ_OK or SVO_REQ_NONFINITE). */
+void svo_row_stats(int32_t rows, int32_t vocab, int32_t dtype, const void* logits, int64_t row_stride,
+                   const float* temperature, double* row_max, int32_t* row_argmax, double* row_sumexp,
+                   int32_t* row_status);
+
+typedef struct {
+  int32_t batch, max_draft, vocab;          /* bs, k, V */
+  int32_t logits_dtype;                     /* SVO_F32 or SVO_BF16 (raw uint16 bits) */
+  const void* logits;                       /* row (b*(k+1)+r) at element offset row*logits_row_stride */
+  int64_t logits_row_stride;
+  int32_t draft_kind;                       /* SVO_DRAFT_PROBS or SVO_DRAFT_ONEHOT */
+  const float* draft_probs;                 /* row (b*k+i) at offset row*q_row_stride; NULL for one-hot */
+  int64_t q_row_stride;
+  const int32_t* draft_ids;                 /* [bs][k]; -1 ends the chain */
+  const float* temperature;                 /* [bs]; <= 0 => greedy */
+  const uint64_t* seed;                     /* [bs] */
+  int32_t* accept_len;                      /* [bs] out */
+  int32_t* tokens;                          /* [bs][k+1] out */
+  int32_t* req_status;                      /* [bs] out, may be NULL */
+  double* p_draft;                          /* [bs][k] out: p_i(x_i), NaN where unused; may be NULL */
+  double* min_margin;                       /* [bs] out: smallest decision margin; may be NULL */
+  int32_t* n_decisions;                     /* [bs] out: decisions taken; may be NULL */
+} svo_chain_args;
+
+typedef struct {
+  int32_t batch, num_nodes, vocab;          /* bs, N (root included), V */
+  int32_t logits_dtype;
+  const void* logits;                       /* row (b*N+n): target distribution after node n */
+  int64_t logits_row_stride;
+  const int32_t* node_tokens;               /* [bs][N]; entry 0 ignored */
+  const int32_t* parent;                    /* [bs][N]; parent[0] = -1, 0 <= parent[i] < i */
+  const float* temperature;
+  const uint64_t* seed;
+  int32_t* accept_len;                      /* [bs] out: accepted nodes, root excluded */
+  int32_t* accept_path;                     /* [bs][N] out: accepted node ids, -1 padded */
+  int32_t* tokens;                          /* [bs][N] out: accepted tokens, then the emitted one */
+  int32_t* req_status;
+  double* min_margin;
+  int32_t* n_decisions;
+  /* Test-only relaxation knobs of the target-only tree rule.  1.0 is the
+   * exact rule; any other value makes the rule lossy and exists only so the
+   * statistical tests can show they detect a changed distribution. */
+  double threshold_acc, threshold_single;
+} svo_tree_args;
+
+void svo_verify_chain(const svo_chain_args* a);
+void svo_verify_tree(const svo_tree_args* a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
