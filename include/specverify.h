@@ -1,0 +1,182 @@
+/* specverify.h - C ABI of libspecverify: batched lossless verification of
+ * speculative-decoding drafts on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For each request the target model has produced one
+ * logit row per verified position.  The target distribution of a row is
+ * p = softmax(logits / T) (temperature T > 0), or the point mass on the
+ * argmax when T <= 0 (greedy).  Page "投机解码" (Speculative decoding,
+ * rustineverything.app), section "接受规则为什么不改变分布" (why the acceptance
+ * rule keeps the distribution), states the rule implemented here:
+ *   - chain drafts are accepted left to right, draft x with probability
+ *     min(1, p(x)/q(x)) (sub-section "采样：标准拒绝采样", standard rejection
+ *     sampling); at the first rejection one token is drawn from
+ *     max(0, p - q) normalised, the remaining drafts are dropped; if every
+ *     draft is accepted a bonus token is drawn from the next row's p;
+ *   - a one-hot ("target-only") draft has q(x) = 1, so x is accepted with
+ *     probability p(x) and the residual is p with x removed (sub-section
+ *     "默认路径：草稿当 one-hot");
+ *   - greedy rows accept x iff x is the target argmax and emit the argmax
+ *     (sub-section "贪心");
+ *   - a draft tree is walked from the root: one coin per level, the
+ *     children tried in increasing node index while their target
+ *     probabilities accumulate; if none is accepted the next token is drawn
+ *     from p with the tried children removed (sub-section "SGLang 默认：只看目标
+ *     概率，可以验证一棵树", with both relaxation thresholds at their exact value 1).
+ *   - q(x) <= 0 accepts iff p(x) > 0 (section "对照：mistral.rs").
+ *
+ * Randomness is a counter-based Philox4x32-10 stream (Salmon et al., SC'11)
+ * keyed by the request's 64-bit seed: the coin of row r of request b is
+ * word 0 of counter (0, r, b, 0); the sampling noise of vocabulary id y is
+ * word (y & 3) of counter (y >> 2, r, b, 1); a word w maps to the uniform
+ * (2*(w >> 9) + 1) / 2^24.  Every sample is an exponential race
+ * argmax_y w(y) / E_y, E_y = -ln U_y, ties to the smallest y, so a call is
+ * a pure function of its inputs: replaying it replays the result.
+ *
+ * Conventions.  Every data pointer is DEVICE memory unless marked [host].
+ * Logit rows are row-major: element y of row i is at logits + i*row_stride
+ * + y (in elements).  bf16 logits are widened exactly; all arithmetic that
+ * decides an outcome is fp32 with fp64 accumulation and fp64 re-evaluation
+ * of near-ties.  `stream` is a hipStream_t (NULL = the default stream).
+ * Calls only enqueue work: they never allocate, never synchronise, keep no
+ * state between calls and may be made from any host thread.  Results are
+ * valid once the stream reaches that point.
+ *
+ * Errors.  Problems visible on the host (NULL pointers, bad sizes, a
+ * workspace that is too small, unsupported values) return a non-zero
+ * sv_status and enqueue nothing.  Problems in the data set req_status[b]
+ * (an SV_REQ_* code); that request then reports accept_len 0 and tokens all
+ * -1, and every other request is unaffected.
+ *
+ * Workspace.  Each call needs a caller-owned device workspace of at least
+ * the size returned by the matching *_workspace_bytes function.  It holds
+ * scheduling counters and partial results; it must be zero-filled once
+ * before its first use (sv_workspace_init does that on a stream), and every
+ * completed call leaves it ready for the next one, whatever the shapes.
+ * Calls that share a workspace must not overlap in time (use one workspace
+ * per stream).  After a call reports SV_REQ_INTERNAL for any request,
+ * re-initialise the workspace.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+/* Limits of one call. */
+#define SV_MAX_BATCH 65536   /* requests per call */
+#define SV_MAX_DRAFT 63      /* chain drafts per request (k) */
+#define SV_MAX_NODES 64      /* tree nodes per request, root included (N) */
+#define SV_MAX_VOCAB (1 << 24)
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARGUMENT = 1,
+  SV_ERR_WORKSPACE_TOO_SMALL = 2,
+  SV_ERR_UNSUPPORTED = 3,
+  SV_ERR_LAUNCH = 4
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef enum {
+  SV_DRAFT_PROBS = 0,  /* q given as full fp32 rows: standard rejection sampling */
+  SV_DRAFT_ONEHOT = 1  /* q one-hot at the draft token ("target-only") */
+} sv_draft_kind;
+
+/* Per-request status codes written to req_status. */
+enum {
+  SV_REQ_OK = 0,
+  SV_REQ_BAD_DRAFT_ID = 1,     /* a used draft id outside [0, V), or below -1 */
+  SV_REQ_BAD_TREE = 2,         /* parent[0] != -1, parent[i] not in [0, i), node token outside [0, V),
+                                  or two children of one node with the same token */
+  SV_REQ_NONFINITE = 3,        /* a read row holds NaN or +inf, or is entirely -inf */
+  SV_REQ_BAD_TEMPERATURE = 4,  /* temperature is NaN or infinite */
+  SV_REQ_INTERNAL = 5          /* internal scheduling timeout; re-initialise the workspace */
+};
+
+/* Option bits for the `flags` fields. */
+#define SV_FLAG_PHASED 1u    /* run as three stream-ordered launches instead of one fused launch */
+#define SV_FLAG_FP64_RACE 2u /* evaluate every sampling race entirely in fp64 (slow; a test aid) */
+
+typedef struct {
+  int32_t batch;              /* bs, 1..SV_MAX_BATCH */
+  int32_t max_draft;          /* k, 0..SV_MAX_DRAFT; rows per request R = k + 1 */
+  int32_t vocab;              /* V, 1..SV_MAX_VOCAB */
+  sv_dtype logits_dtype;
+  const void* logits;         /* [bs][k+1] rows of V; row b*(k+1)+r is the target after r drafts */
+  int64_t logits_row_stride;  /* elements between rows, >= V */
+  sv_draft_kind draft_kind;
+  const float* draft_probs;   /* [bs][k] rows of V (SV_DRAFT_PROBS), row b*k+i is q_i; NULL for one-hot */
+  int64_t q_row_stride;       /* elements between q rows, >= V */
+  const int32_t* draft_ids;   /* [bs][k]; the first -1 ends a request's chain (later slots ignored) */
+  const float* temperature;   /* [bs]; <= 0 selects greedy */
+  const uint64_t* seed;       /* [bs]; Philox key of the request */
+  int32_t* accept_len;        /* [bs] out: drafts accepted (bonus excluded) */
+  int32_t* tokens;            /* [bs][k+1] out: accepted drafts, then the emitted token, -1 after */
+  int32_t* req_status;        /* [bs] out, may be NULL */
+  double* p_draft;            /* [bs][k] out, may be NULL: p_i(x_i) for used slots, NaN elsewhere
+                                 (greedy rows: 1 at the argmax, else 0) */
+  uint32_t flags;             /* SV_FLAG_* bits, 0 by default */
+} sv_chain_desc;
+
+typedef struct {
+  int32_t batch;              /* bs, 1..SV_MAX_BATCH */
+  int32_t num_nodes;          /* N, 1..SV_MAX_NODES, the root included */
+  int32_t vocab;
+  sv_dtype logits_dtype;
+  const void* logits;         /* [bs][N] rows of V; row b*N+n is the target after node n */
+  int64_t logits_row_stride;
+  const int32_t* node_tokens; /* [bs][N]; the token node n proposes (entry 0 ignored) */
+  const int32_t* parent;      /* [bs][N]; parent[0] = -1, 0 <= parent[i] < i */
+  const float* temperature;   /* [bs]; <= 0 selects greedy */
+  const uint64_t* seed;       /* [bs] */
+  int32_t* accept_len;        /* [bs] out: accepted nodes (root excluded) */
+  int32_t* accept_path;       /* [bs][N] out: accepted node ids from the root down, -1 after */
+  int32_t* tokens;            /* [bs][N] out: accepted nodes' tokens, then the emitted token, -1 after */
+  int32_t* req_status;        /* [bs] out, may be NULL */
+  uint32_t flags;
+} sv_tree_desc;
+
+/* Bytes of workspace a call of the given shape needs (0 if the shape is
+ * outside the limits). */
+size_t sv_chain_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab, sv_dtype logits_dtype);
+size_t sv_tree_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab, sv_dtype logits_dtype);
+size_t sv_row_stats_workspace_bytes(int32_t rows, int32_t vocab, sv_dtype logits_dtype);
+
+/* Zero-fill `bytes` of workspace on `stream` (a fill kernel, safe to
+ * capture in a graph). */
+sv_status sv_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Chain verification (standard, one-hot or greedy per request). */
+sv_status sv_verify_chain(const sv_chain_desc* desc /* [host] */, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Target-only tree verification (stochastic or greedy per request). */
+sv_status sv_verify_tree(const sv_tree_desc* desc /* [host] */, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Row statistics of `rows` logit rows (the streaming pass on its own):
+ * row_max = max_y l(y); row_argmax = the smallest y attaining it (raw
+ * logits); row_sumexp = sum_y exp((l(y) - row_max) / T_i) for T_i > 0 (NaN
+ * for greedy rows), so p(y) = exp((l(y) - row_max)/T_i) / row_sumexp;
+ * row_status = SV_REQ_OK or SV_REQ_NONFINITE.  temperature is per row.
+ * Outputs may be NULL individually. */
+sv_status sv_row_stats(int32_t rows, int32_t vocab, sv_dtype logits_dtype, const void* logits,
+                       int64_t logits_row_stride, const float* temperature, float* row_max,
+                       int32_t* row_argmax, double* row_sumexp, int32_t* row_status, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+const char* sv_status_string(sv_status status);
+int32_t sv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

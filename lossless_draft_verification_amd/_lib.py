@@ -1,0 +1,345 @@
+"""ctypes binding of libspecverify (include/specverify.h).
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+layout, their device pointers and the current HIP stream are passed to the C
+ABI, and every step of the verification runs in the library's HIP kernels.
+There is no fallback: if the library is not built or the call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+# sv_status
+OK, ERR_INVALID_ARGUMENT, ERR_WORKSPACE_TOO_SMALL, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3, 4
+# sv_dtype
+F32, BF16 = 0, 1
+# sv_draft_kind
+DRAFT_PROBS, DRAFT_ONEHOT = 0, 1
+# per-request status
+REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE, REQ_INTERNAL = 0, 1, 2, 3, 4, 5
+# flags
+FLAG_PHASED, FLAG_FP64_RACE = 1, 2
+
+MAX_BATCH, MAX_DRAFT, MAX_NODES, MAX_VOCAB = 65536, 63, 64, 1 << 24
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U32 = ctypes.c_uint32
+_SZ = ctypes.c_size_t
+
+
+class ChainDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("max_draft", _I32), ("vocab", _I32), ("logits_dtype", ctypes.c_int),
+                ("logits", _P), ("logits_row_stride", _I64), ("draft_kind", ctypes.c_int),
+                ("draft_probs", _P), ("q_row_stride", _I64), ("draft_ids", _P), ("temperature", _P),
+                ("seed", _P), ("accept_len", _P), ("tokens", _P), ("req_status", _P), ("p_draft", _P),
+                ("flags", _U32)]
+
+
+class TreeDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("num_nodes", _I32), ("vocab", _I32), ("logits_dtype", ctypes.c_int),
+                ("logits", _P), ("logits_row_stride", _I64), ("node_tokens", _P), ("parent", _P),
+                ("temperature", _P), ("seed", _P), ("accept_len", _P), ("accept_path", _P), ("tokens", _P),
+                ("req_status", _P), ("flags", _U32)]
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (sv_status {status})")
+        self.status = status
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """Load libspecverify.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+                L = ctypes.CDLL(LIB_PATH)
+                L.sv_abi_version.restype = _I32
+                L.sv_abi_version.argtypes = []
+                L.sv_status_string.restype = ctypes.c_char_p
+                L.sv_status_string.argtypes = [ctypes.c_int]
+                L.sv_chain_workspace_bytes.restype = _SZ
+                L.sv_chain_workspace_bytes.argtypes = [_I32, _I32, _I32, ctypes.c_int]
+                L.sv_tree_workspace_bytes.restype = _SZ
+                L.sv_tree_workspace_bytes.argtypes = [_I32, _I32, _I32, ctypes.c_int]
+                L.sv_row_stats_workspace_bytes.restype = _SZ
+                L.sv_row_stats_workspace_bytes.argtypes = [_I32, _I32, ctypes.c_int]
+                L.sv_workspace_init.restype = ctypes.c_int
+                L.sv_workspace_init.argtypes = [_P, _SZ, _P]
+                L.sv_verify_chain.restype = ctypes.c_int
+                L.sv_verify_chain.argtypes = [ctypes.POINTER(ChainDesc), _P, _SZ, _P]
+                L.sv_verify_tree.restype = ctypes.c_int
+                L.sv_verify_tree.argtypes = [ctypes.POINTER(TreeDesc), _P, _SZ, _P]
+                L.sv_row_stats.restype = ctypes.c_int
+                L.sv_row_stats.argtypes = [_I32, _I32, ctypes.c_int, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
+                _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sv_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().sv_abi_version())
+
+
+def chain_workspace_bytes(batch, max_draft, vocab, dtype) -> int:
+    return int(lib().sv_chain_workspace_bytes(batch, max_draft, vocab, dtype))
+
+
+def tree_workspace_bytes(batch, num_nodes, vocab, dtype) -> int:
+    return int(lib().sv_tree_workspace_bytes(batch, num_nodes, vocab, dtype))
+
+
+def row_stats_workspace_bytes(rows, vocab, dtype) -> int:
+    return int(lib().sv_row_stats_workspace_bytes(rows, vocab, dtype))
+
+
+# ------------------------------------------------------------------ workspace
+class Workspace:
+    """A device workspace (caller-owned memory for one stream at a time).
+
+    Zero-filled once by the library's fill kernel when allocated; the library
+    keeps it consistent from call to call.
+    """
+
+    def __init__(self, nbytes: int, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.nbytes = 0
+        self.buf = None
+        self.ensure(nbytes)
+
+    def ensure(self, nbytes: int):
+        if nbytes <= self.nbytes:
+            return
+        nbytes = max(int(nbytes), 1 << 20)
+        # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-buf.data_ptr()) % 256
+        self.buf = buf
+        self.base = buf.data_ptr() + off
+        self.nbytes = nbytes
+        st = lib().sv_workspace_init(ctypes.c_void_p(self.base), ctypes.c_size_t(nbytes), _stream(self.device))
+        if st != OK:
+            raise SpecVerifyError(st, "sv_workspace_init")
+
+    def reset(self):
+        st = lib().sv_workspace_init(ctypes.c_void_p(self.base), ctypes.c_size_t(self.nbytes), _stream(self.device))
+        if st != OK:
+            raise SpecVerifyError(st, "sv_workspace_init")
+
+
+_workspaces: dict = {}
+
+
+def default_workspace(device) -> Workspace:
+    device = torch.device(device)
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = Workspace(1 << 20, torch.device("cuda", key))
+        _workspaces[key] = ws
+    return ws
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ------------------------------------------------------------------ checks
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _rows_view(t: torch.Tensor, lead: int):
+    """Rows are indexed by the flattened first `lead` dims.  The library
+    needs a contiguous last dim and one common row stride (>= V); other
+    layouts are copied to a contiguous tensor.  Returns (tensor, row stride
+    in elements)."""
+    ok = t.stride(-1) == 1 and t.stride(lead - 1) >= t.shape[-1]
+    for d in range(lead - 1):
+        if t.shape[d] > 1 and t.stride(d) != t.stride(lead - 1) * _prod(t.shape[d + 1:lead]):
+            ok = False
+    if not ok:
+        t = t.contiguous()
+    return t, int(t.stride(lead - 1))
+
+
+def _prod(xs):
+    p = 1
+    for x in xs:
+        p *= int(x)
+    return p
+
+
+def _on(t: torch.Tensor, device, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.contiguous()
+
+
+def _seed_tensor(seeds, bs, device):
+    s = seeds
+    if not torch.is_tensor(s):
+        s = torch.as_tensor(s, dtype=torch.int64)
+    if s.dtype == torch.uint64:
+        s = s.view(torch.int64)
+    if s.dtype != torch.int64:
+        raise TypeError("seeds must be int64 (raw 64-bit keys) or uint64")
+    if s.numel() != bs:
+        raise ValueError("need one seed per request")
+    return s.to(device).contiguous()
+
+
+# ------------------------------------------------------------------ calls
+def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, *, flags=0,
+                 return_p_draft=False, workspace=None):
+    """Chain verification on the current stream (asynchronous).
+
+    logits [bs, k+1, V] float32/bfloat16; draft_ids [bs, k] int32 (-1 ends a
+    chain); temperature [bs] float32 (<= 0: greedy); seeds [bs] int64 (raw
+    64-bit Philox keys); draft_probs [bs, k, V] float32, or onehot=True.
+    Returns a dict of device tensors: accept_len [bs], tokens [bs, k+1],
+    status [bs] (int32), and p_draft [bs, k] float64 if requested.
+    """
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, k+1, vocab]")
+    device = logits.device
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    bs, R, V = (int(x) for x in logits.shape)
+    k = R - 1
+    code = _dtype_code(logits)
+    logits, lstride = _rows_view(logits, 2)
+    ids = _on(draft_ids.reshape(bs, k) if k > 0 else torch.empty(bs, 0, dtype=torch.int32, device=device),
+              device, torch.int32, "draft_ids")
+    temp = _on(temperature.reshape(bs), device, torch.float32, "temperature")
+    sd = _seed_tensor(seeds, bs, device)
+    q = None
+    qstride = 0
+    if not onehot:
+        if draft_probs is None:
+            if k > 0:
+                raise ValueError("draft_probs is required unless onehot=True")
+        else:
+            if tuple(draft_probs.shape) != (bs, k, V):
+                raise ValueError("draft_probs must be [batch, k, vocab]")
+            q = _on(draft_probs, device, torch.float32, "draft_probs")
+            q, qstride = _rows_view(q, 2)
+    out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=device),
+               tokens=torch.empty(bs, R, dtype=torch.int32, device=device),
+               status=torch.empty(bs, dtype=torch.int32, device=device))
+    if return_p_draft:
+        out["p_draft"] = torch.empty(bs, k, dtype=torch.float64, device=device)
+    need = chain_workspace_bytes(bs, k, V, code)
+    if need == 0:
+        raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_chain_workspace_bytes")
+    ws = workspace if workspace is not None else default_workspace(device)
+    ws.ensure(need)
+    d = ChainDesc(bs, k, V, code, logits.data_ptr(), lstride, DRAFT_ONEHOT if onehot else DRAFT_PROBS,
+                  q.data_ptr() if q is not None else None, qstride, ids.data_ptr() if k > 0 else None,
+                  temp.data_ptr(), sd.data_ptr(), out["accept_len"].data_ptr(), out["tokens"].data_ptr(),
+                  out["status"].data_ptr(), out["p_draft"].data_ptr() if return_p_draft else None, int(flags))
+    st = lib().sv_verify_chain(ctypes.byref(d), ctypes.c_void_p(ws.base), ctypes.c_size_t(ws.nbytes),
+                               _stream(device))
+    if st != OK:
+        raise SpecVerifyError(st, "sv_verify_chain")
+    return out
+
+
+def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, workspace=None):
+    """Target-only tree verification on the current stream (asynchronous).
+
+    logits [bs, N, V]; node_tokens, parent [bs, N] int32.  Returns
+    accept_len [bs], accept_path [bs, N], tokens [bs, N], status [bs].
+    """
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, nodes, vocab]")
+    device = logits.device
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    bs, N, V = (int(x) for x in logits.shape)
+    code = _dtype_code(logits)
+    logits, lstride = _rows_view(logits, 2)
+    nt = _on(node_tokens.reshape(bs, N), device, torch.int32, "node_tokens")
+    par = _on(parent.reshape(bs, N), device, torch.int32, "parent")
+    temp = _on(temperature.reshape(bs), device, torch.float32, "temperature")
+    sd = _seed_tensor(seeds, bs, device)
+    out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=device),
+               accept_path=torch.empty(bs, N, dtype=torch.int32, device=device),
+               tokens=torch.empty(bs, N, dtype=torch.int32, device=device),
+               status=torch.empty(bs, dtype=torch.int32, device=device))
+    need = tree_workspace_bytes(bs, N, V, code)
+    if need == 0:
+        raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_tree_workspace_bytes")
+    ws = workspace if workspace is not None else default_workspace(device)
+    ws.ensure(need)
+    d = TreeDesc(bs, N, V, code, logits.data_ptr(), lstride, nt.data_ptr(), par.data_ptr(), temp.data_ptr(),
+                 sd.data_ptr(), out["accept_len"].data_ptr(), out["accept_path"].data_ptr(),
+                 out["tokens"].data_ptr(), out["status"].data_ptr(), int(flags))
+    st = lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(ws.base), ctypes.c_size_t(ws.nbytes),
+                              _stream(device))
+    if st != OK:
+        raise SpecVerifyError(st, "sv_verify_tree")
+    return out
+
+
+def row_stats(logits, temperature, *, workspace=None):
+    """Row statistics of a [rows, V] tensor with per-row temperature [rows].
+
+    Returns row_max float32, row_argmax int32, row_sumexp float64 (NaN for
+    greedy rows), row_status int32.
+    """
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, vocab]")
+    device = logits.device
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    rows, V = (int(x) for x in logits.shape)
+    code = _dtype_code(logits)
+    logits, lstride = _rows_view(logits, 1)
+    temp = _on(temperature.reshape(rows), device, torch.float32, "temperature")
+    out = dict(row_max=torch.empty(rows, dtype=torch.float32, device=device),
+               row_argmax=torch.empty(rows, dtype=torch.int32, device=device),
+               row_sumexp=torch.empty(rows, dtype=torch.float64, device=device),
+               row_status=torch.empty(rows, dtype=torch.int32, device=device))
+    need = row_stats_workspace_bytes(rows, V, code)
+    if need == 0:
+        raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_row_stats_workspace_bytes")
+    ws = workspace if workspace is not None else default_workspace(device)
+    ws.ensure(need)
+    st = lib().sv_row_stats(rows, V, code, ctypes.c_void_p(logits.data_ptr()), lstride,
+                            ctypes.c_void_p(temp.data_ptr()), ctypes.c_void_p(out["row_max"].data_ptr()),
+                            ctypes.c_void_p(out["row_argmax"].data_ptr()),
+                            ctypes.c_void_p(out["row_sumexp"].data_ptr()),
+                            ctypes.c_void_p(out["row_status"].data_ptr()), ctypes.c_void_p(ws.base),
+                            ctypes.c_size_t(ws.nbytes), _stream(device))
+    if st != OK:
+        raise SpecVerifyError(st, "sv_row_stats")
+    return out

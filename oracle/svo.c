@@ -142,6 +142,8 @@ static row_stat scan_row(int32_t dtype, const void* logits, int64_t row_off, int
   return st;
 }
 
+static int is_finite_num(double x) { return !isnan(x) && !isinf(x); }
+
 static double p_of(int32_t dtype, const void* logits, int64_t row_off, const row_stat* st, double T, int32_t y) {
   return exp((logit_at(dtype, logits, row_off + y) - st->m) / T) / st->S;
 }
@@ -151,7 +153,7 @@ void svo_row_stats(int32_t rows, int32_t vocab, int32_t dtype, const void* logit
                    int32_t* row_status) {
   for (int32_t i = 0; i < rows; ++i) {
     double T = (double)temperature[i];
-    row_stat st = scan_row(dtype, logits, (int64_t)i * row_stride, vocab, T, T > 0.0);
+    row_stat st = scan_row(dtype, logits, (int64_t)i * row_stride, vocab, T, T > 0.0 && is_finite_num(T));
     if (row_max) row_max[i] = st.m;
     if (row_argmax) row_argmax[i] = st.amax;
     if (row_sumexp) row_sumexp[i] = st.S;
@@ -200,8 +202,6 @@ static double rel_gap(double a, double b) {
   if (hi <= 0.0) return INFINITY;
   return fabs(a - b) / hi;
 }
-
-static int is_finite_num(double x) { return !isnan(x) && !isinf(x); }
 
 /* ------------------------------------------------------------------------ */
 /* Chain verification of one request.

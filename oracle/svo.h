@@ -44,7 +44,7 @@ double svo_coin(uint64_t seed, int32_t b, int32_t r);
 double svo_noise_uniform(uint64_t seed, int32_t b, int32_t r, int32_t y);
 
 /* Row statistics of `rows` logit rows.  Row i starts at element i*row_stride.
- * temperature[i] <= 0 means greedy (no sum is formed; sumexp = NaN).
+ * temperature[i] <= 0 or non-finite means greedy (no sum is formed; sumexp = NaN).
  * Outputs (any may be NULL): row_max, row_argmax (smallest index of the max,
  * on raw logits), row_sumexp = sum_y exp((l_y - max)/T) summed left to right,
  * row_status (SVO_REQ_OK or SVO_REQ_NONFINITE). */

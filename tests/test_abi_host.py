@@ -1,0 +1,154 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/specverify.h declares, sizes workspaces, and rejects
+bad arguments before any HIP call (so no device is touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lossless_draft_verification_amd as sv
+from lossless_draft_verification_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(sv_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for expected in ("sv_verify_chain", "sv_verify_tree", "sv_row_stats", "sv_chain_workspace_bytes",
+                     "sv_tree_workspace_bytes", "sv_row_stats_workspace_bytes", "sv_workspace_init",
+                     "sv_status_string", "sv_abi_version"):
+        assert expected in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = sv.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+
+
+def test_version_and_status_strings():
+    assert sv.abi_version() == 1
+    assert sv.status_string(0) == "ok"
+    assert "workspace" in sv.status_string(2)
+    assert sv.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    a = sv.chain_workspace_bytes(64, 7, 128256, sv.BF16)
+    b = sv.chain_workspace_bytes(64, 7, 128256, sv.F32)
+    assert a > 0 and b > a  # fp32 rows need more chunk partials
+    assert sv.chain_workspace_bytes(0, 7, 100, sv.F32) == 0
+    assert sv.chain_workspace_bytes(1, 64, 100, sv.F32) == 0
+    assert sv.chain_workspace_bytes(1, 3, 0, sv.F32) == 0
+    assert sv.chain_workspace_bytes(1, 3, 100, 7) == 0
+    assert sv.chain_workspace_bytes(sv.MAX_BATCH + 1, 3, 100, sv.F32) == 0
+    assert sv.tree_workspace_bytes(48, 8, 128256, sv.F32) > 0
+    assert sv.tree_workspace_bytes(1, 65, 10, sv.F32) == 0
+    assert sv.row_stats_workspace_bytes(10, 1000, sv.BF16) > 0
+    # monotone in batch
+    assert sv.chain_workspace_bytes(128, 7, 128256, sv.BF16) > a
+
+
+def _chain_desc(**kw):
+    fake = 0x100000  # a host-side non-null stand-in; validation never dereferences it
+    d = dict(batch=2, max_draft=3, vocab=100, logits_dtype=sv.F32, logits=fake, logits_row_stride=100,
+             draft_kind=sv.DRAFT_PROBS, draft_probs=fake, q_row_stride=100, draft_ids=fake, temperature=fake,
+             seed=fake, accept_len=fake, tokens=fake, req_status=None, p_draft=None, flags=0)
+    d.update(kw)
+    return _lib.ChainDesc(**d)
+
+
+def _call_chain(desc, ws_bytes=1 << 30, ws=0x200000):
+    return sv.lib().sv_verify_chain(ctypes.byref(desc) if desc is not None else None, ctypes.c_void_p(ws),
+                                    ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 1), ("batch", sv.MAX_BATCH + 1, 1), ("max_draft", -1, 1), ("max_draft", 64, 1),
+    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3),
+    ("logits", None, 1), ("temperature", None, 1), ("seed", None, 1), ("accept_len", None, 1),
+    ("tokens", None, 1), ("draft_ids", None, 1), ("logits_row_stride", 99, 1), ("draft_probs", None, 1),
+    ("q_row_stride", 50, 1),
+])
+def test_chain_argument_validation(field, value, code):
+    assert _call_chain(_chain_desc(**{field: value})) == code
+
+
+def test_chain_null_descriptor_and_workspace_checks():
+    assert sv.lib().sv_verify_chain(None, ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 1
+    assert _call_chain(_chain_desc(), ws=0) == 1
+    need = sv.chain_workspace_bytes(2, 3, 100, sv.F32)
+    assert _call_chain(_chain_desc(), ws_bytes=need - 1) == 2
+    assert _call_chain(_chain_desc(), ws=0x200010) == 1  # workspace must be 256-byte aligned
+    # one-hot drafts need no q
+    assert _call_chain(_chain_desc(draft_kind=sv.DRAFT_ONEHOT, draft_probs=None), ws_bytes=need - 1) == 2
+    # k = 0 needs no draft ids
+    need0 = sv.chain_workspace_bytes(2, 0, 100, sv.F32)
+    assert _call_chain(_chain_desc(max_draft=0, draft_ids=None, draft_probs=None), ws_bytes=need0 - 1) == 2
+
+
+def _tree_desc(**kw):
+    fake = 0x100000
+    d = dict(batch=2, num_nodes=8, vocab=100, logits_dtype=sv.BF16, logits=fake, logits_row_stride=100,
+             node_tokens=fake, parent=fake, temperature=fake, seed=fake, accept_len=fake, accept_path=fake,
+             tokens=fake, req_status=None, flags=0)
+    d.update(kw)
+    return _lib.TreeDesc(**d)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_nodes", 0, 1), ("num_nodes", 65, 1), ("parent", None, 1), ("node_tokens", None, 1),
+    ("accept_path", None, 1), ("logits_dtype", 3, 3), ("logits_row_stride", 10, 1), ("flags", 64, 3),
+])
+def test_tree_argument_validation(field, value, code):
+    d = _tree_desc(**{field: value})
+    assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == code
+
+
+def test_tree_workspace_too_small():
+    d = _tree_desc()
+    need = sv.tree_workspace_bytes(2, 8, 100, sv.BF16)
+    assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(need - 1), None) == 2
+
+
+def test_row_stats_validation():
+    L = sv.lib()
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    assert L.sv_row_stats(0, 10, sv.F32, fake, 10, fake, None, None, None, None, ws, 1 << 30, None) == 1
+    assert L.sv_row_stats(4, 10, sv.F32, None, 10, fake, None, None, None, None, ws, 1 << 30, None) == 1
+    assert L.sv_row_stats(4, 10, sv.F32, fake, 9, fake, None, None, None, None, ws, 1 << 30, None) == 1
+    assert L.sv_row_stats(4, 10, 4, fake, 10, fake, None, None, None, None, ws, 1 << 30, None) == 3
+    need = sv.row_stats_workspace_bytes(4, 10, sv.F32)
+    assert L.sv_row_stats(4, 10, sv.F32, fake, 10, fake, None, None, None, None, ws, need - 1, None) == 2
+
+
+def test_workspace_init_validation():
+    L = sv.lib()
+    assert L.sv_workspace_init(None, 100, None) == 1
+    assert L.sv_workspace_init(ctypes.c_void_p(0x100000), 0, None) == 1
+    assert L.sv_workspace_init(ctypes.c_void_p(0x100004), 64, None) == 1
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package and the HIP sources never import, link or name the oracle."""
+    pkg = os.path.join(ROOT, "lossless_draft_verification_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "svo_" not in text and "oracle/" not in text, f
