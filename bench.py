@@ -1,0 +1,224 @@
+"""Benchmark: batched lossless draft verification on one MI355X.
+
+One step = one sv_verify_chain call (the whole hot path: streaming row
+statistics, per-request decisions, residual/bonus sampling) over one batch
+of the chain workload bs=64, k=7, V=128256, bf16 target logits, half the
+requests greedy and half at T=0.8 with fp32 draft probabilities.  Inputs
+are resident in HBM before the timed region; the timed steps rotate over
+several input sets whose total size exceeds the 256 MB Infinity Cache, so
+the stream really comes from HBM.
+
+Prints one JSON line: verified draft positions per second (value), plus the
+roofline of the verify kernel (algorithmic bytes per launch / measured
+launch duration, against the 8 TB/s HBM peak) and the oracle timed on the
+host as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = {
+    "chain_bf16_mixed": "chain verify bs=64 k=7 V=128256, bf16 target logits, half greedy, half T=0.8 with fp32 draft probs",
+    "chain_fp32": "chain verify bs=8 k=3 V=128256, fp32 target logits, T=1, fp32 draft probs",
+    "onehot_bf16": "one-hot (target-only) chain verify bs=256 k=3 V=151936, bf16 target logits, T=1",
+}
+KERNEL_SOURCE = os.path.join(ROOT, "lossless_draft_verification_amd", "csrc", "specverify.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(inp, accept_len) -> int:
+    """Bytes the method must move for one call, from the actual outcomes:
+    every read logit row (rows 0..k_b of each request) once, the gathers at
+    the draft ids (logit, id, q value), per-request scalars, the re-read of
+    the one sampled row per stochastic request (its logits, plus its q row
+    after a standard rejection), and the outputs."""
+    bs, R, V = inp.logits.shape
+    k = R - 1
+    bl = inp.logits.dtype.itemsize
+    ids = inp.draft_ids
+    kb = np.where((ids == -1).any(axis=1), np.argmax(ids == -1, axis=1), k) if k else np.zeros(bs, np.int64)
+    stoch = (inp.temperature > 0) & np.isfinite(inp.temperature)
+    total = 0
+    for b in range(bs):
+        total += (kb[b] + 1) * V * bl                                        # streamed rows
+        total += kb[b] * (bl + 4 + (0 if inp.onehot else 4))                 # gathers at the draft ids
+        total += 4 + 8 + 4 * k                                               # temperature, seed, ids
+        if stoch[b]:
+            reject = accept_len[b] < kb[b]
+            total += V * bl + (V * 4 if (reject and not inp.onehot) else 0)  # sampled row (+ q row)
+        total += 4 + 4 * R + 4                                               # accept_len, tokens, status
+    return int(total)
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch measured with rocprofv3 counters for this
+    kernel source (committed under profiles/), or None if the kernel changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs, seconds: float):
+    import oracle
+
+    inp = inputs[0]
+    positions = int((inp.draft_ids >= 0).cumprod(axis=1).sum()) if inp.max_draft else 0
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=inp.draft_probs,
+                            onehot=inp.onehot)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": positions * calls / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full calls of the same workload (input set 0), single-threaded C oracle, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="chain_bf16_mixed", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated over the timed steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
+                    help="library schedule (auto: the library's default for the shape)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the verification hot path runs on a single MI355X here; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lossless_draft_verification_amd as sv
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = getattr(workloads, args.workload)
+    print(f"[bench] generating {args.sets} input sets of {args.workload}", file=sys.stderr, flush=True)
+    inputs = [gen(s) for s in range(args.sets)]
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        if a.dtype == np.uint64:
+            return torch.from_numpy(a.view(np.int64)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    flags = {"auto": 0, "phased": sv.FLAG_PHASED, "fused": sv.FLAG_FUSED}[args.schedule]
+    ws = sv.Workspace(1 << 20, dev)
+    calls = []
+    for inp in inputs:
+        calls.append(sv.PreparedChain(to_dev(inp.logits), to_dev(inp.draft_ids), to_dev(inp.temperature),
+                                      to_dev(inp.seeds), draft_probs=to_dev(inp.draft_probs), onehot=inp.onehot,
+                                      flags=flags, workspace=ws))
+    resident = sum(c.logits.numel() * c.logits.element_size() + (c.q.numel() * 4 if c.q is not None else 0)
+                   for c in calls)
+    stream = torch.cuda.current_stream(dev)
+    # algorithmic bytes of each set, from its outcome
+    alg = []
+    for c, inp in zip(calls, inputs):
+        c.launch()
+        torch.cuda.synchronize()
+        if (c.out["status"] != 0).any():
+            raise RuntimeError("a request reported a non-OK status on the benchmark inputs")
+        alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy()))
+    positions = [int((inp.draft_ids >= 0).cumprod(axis=1).sum()) for inp in inputs]
+
+    for i in range(args.warmup):
+        calls[i % len(calls)].launch()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        calls[i % len(calls)].launch()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    pos_total = sum(positions[i % len(calls)] for i in range(K))
+    bytes_total = sum(alg[i % len(calls)] for i in range(K))
+    value = pos_total / (total_ms * 1e-3)
+    achieved = bytes_total / (launch_ms.sum() * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    line = {
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOADS[args.workload],
+            "batch": int(inputs[0].batch),
+            "k": int(inputs[0].max_draft),
+            "vocab": int(inputs[0].vocab),
+            "logits_dtype": "bf16" if inputs[0].logits.dtype == np.uint16 else "f32",
+            "positions_per_step": positions[0],
+            "input_sets": len(calls),
+            "resident_input_bytes": int(resident),
+            "schedule": args.schedule,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": float(np.mean(alg)),
+            "launch_us_mean": float(launch_ms.mean() * 1e3),
+            "launch_us_p50": float(np.median(launch_ms) * 1e3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

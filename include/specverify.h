@@ -100,9 +100,12 @@ enum {
   SV_REQ_INTERNAL = 5          /* internal scheduling timeout; re-initialise the workspace */
 };
 
-/* Option bits for the `flags` fields. */
-#define SV_FLAG_PHASED 1u    /* run as three stream-ordered launches instead of one fused launch */
+/* Option bits for the `flags` fields.  Without a schedule bit the library
+ * picks the faster schedule for the shape; all schedules give bit-identical
+ * results. */
+#define SV_FLAG_PHASED 1u    /* three stream-ordered launches: row statistics, decisions, sampling */
 #define SV_FLAG_FP64_RACE 2u /* evaluate every sampling race entirely in fp64 (slow; a test aid) */
+#define SV_FLAG_FUSED 4u     /* one launch, sampling work interleaved with the row-statistics stream */
 
 typedef struct {
   int32_t batch;              /* bs, 1..SV_MAX_BATCH */

@@ -26,7 +26,7 @@ DRAFT_PROBS, DRAFT_ONEHOT = 0, 1
 # per-request status
 REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE, REQ_INTERNAL = 0, 1, 2, 3, 4, 5
 # flags
-FLAG_PHASED, FLAG_FP64_RACE = 1, 2
+FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED = 1, 2, 4
 
 MAX_BATCH, MAX_DRAFT, MAX_NODES, MAX_VOCAB = 65536, 63, 64, 1 << 24
 
@@ -343,3 +343,44 @@ def row_stats(logits, temperature, *, workspace=None):
     if st != OK:
         raise SpecVerifyError(st, "sv_row_stats")
     return out
+
+
+class PreparedChain:
+    """A chain verification with its arguments checked and its descriptor
+    built once, for calling repeatedly on fixed device buffers (benchmarks,
+    serving loops).  launch() enqueues one sv_verify_chain on the current
+    stream; outputs are overwritten in place."""
+
+    def __init__(self, logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, *, flags=0,
+                 workspace=None):
+        device = logits.device
+        bs, R, V = (int(x) for x in logits.shape)
+        k = R - 1
+        code = _dtype_code(logits)
+        self.logits, lstride = _rows_view(logits, 2)
+        self.ids = _on(draft_ids.reshape(bs, k), device, torch.int32, "draft_ids")
+        self.temp = _on(temperature.reshape(bs), device, torch.float32, "temperature")
+        self.seeds = _seed_tensor(seeds, bs, device)
+        self.q, qstride = (None, 0)
+        if not onehot:
+            self.q, qstride = _rows_view(_on(draft_probs, device, torch.float32, "draft_probs"), 2)
+        self.out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=device),
+                        tokens=torch.empty(bs, R, dtype=torch.int32, device=device),
+                        status=torch.empty(bs, dtype=torch.int32, device=device))
+        self.ws = workspace if workspace is not None else default_workspace(device)
+        self.ws.ensure(chain_workspace_bytes(bs, k, V, code))
+        self.device = device
+        self.desc = ChainDesc(bs, k, V, code, self.logits.data_ptr(), lstride,
+                              DRAFT_ONEHOT if onehot else DRAFT_PROBS,
+                              self.q.data_ptr() if self.q is not None else None, qstride,
+                              self.ids.data_ptr() if k > 0 else None, self.temp.data_ptr(), self.seeds.data_ptr(),
+                              self.out["accept_len"].data_ptr(), self.out["tokens"].data_ptr(),
+                              self.out["status"].data_ptr(), None, int(flags))
+        self._fn = lib().sv_verify_chain
+        self._ref = ctypes.byref(self.desc)
+
+    def launch(self, stream=None):
+        s = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream)
+        st = self._fn(self._ref, ctypes.c_void_p(self.ws.base), ctypes.c_size_t(self.ws.nbytes), s)
+        if st != OK:
+            raise SpecVerifyError(st, "sv_verify_chain")

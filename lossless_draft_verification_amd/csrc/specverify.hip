@@ -23,15 +23,18 @@
 //       error bounds, and a short list of near-maximal candidates; the
 //       workgroup that finishes a request's last K3 chunk re-evaluates the
 //       candidates in fp64 and writes the emitted token.
-// The fused schedule runs everything in one persistent launch: workgroups
-// take tickets from a device counter; the ticket space interleaves K1 chunks
-// of request g with K3 chunks of request g - L, so the ALU-heavy races of
-// early requests overlap the HBM stream of later ones, and a launch gap is
-// paid once.  K3 items wait (bounded) for their request's K2; since tickets
-// are handed out in order of execution, every K1 item a waiter depends on is
-// already held by a running workgroup, so the schedule cannot deadlock.  The
-// phased schedule runs K1, K2 and K3 as three stream-ordered launches with no
-// waiting at all; both give bit-identical results.
+// The fused schedule runs everything in one launch with one work item per
+// workgroup.  Item order interleaves the K1 chunks of request g with the K3
+// chunks of request g - L, so the ALU-heavy races of early requests overlap
+// the HBM stream of later ones, and a launch is paid once.  A K3 item waits
+// (bounded, about a second, then SV_REQ_INTERNAL) for its request's K2.
+// Workgroups are dispatched in index order, so every K1 item a waiter
+// depends on (a smaller index) is already running or finished: the waits
+// always end.  There is no global counter: per-request counters and flags
+// are reset by their last user, so the workspace is ready for the next call
+// without any reset pass.  The phased schedule runs K1, K2 and K3 as three
+// stream-ordered launches with no waiting at all; both give bit-identical
+// results.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -61,22 +64,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- workspace
 struct Ctrl {
-  uint32_t epoch;     // calls completed on this workspace
-  uint32_t ticket;    // next ticket of the running fused launch
-  uint32_t wg_done;   // workgroups of the running fused launch that have exited
-  uint32_t aborted;   // a bounded wait expired in the running launch
-  uint32_t pad[60];
+  uint32_t aborted;   // a bounded wait expired (left set: the workspace must be re-initialised)
+  uint32_t pad[63];
 };
 struct Sync {
-  uint32_t k1_count;  // K1 chunks of the request finished in this call
-  uint32_t k3_count;  // K3 chunks of the request finished in this call
-  uint32_t ready;     // epoch + 1 once the request's job is published
+  uint32_t k1_count;  // K1 chunks of the request finished in this call (reset by the K2 runner)
+  uint32_t k3_count;  // K3 chunks of the request finished in this call (reset by the last one)
+  uint32_t ready;     // 1 once the request's job is published (reset by the last K3 chunk)
   uint32_t pad;
 };
+// Target logit (and draft probability) at a draft token, gathered by the K1
+// chunk that holds it: chain slot r = row r's draft, tree slot n = node n's
+// token in its parent's row.
+struct Gather {
+  uint32_t l;         // fp32 bits of the logit
+  uint32_t q;         // fp32 bits of q at the draft (chain, draft probabilities)
+};
 struct Partial {
-  double s;           // chunk sum of 2^((l - m_c) * log2(e)/T), or a NaN flag for greedy rows
-  float m;            // chunk max
-  int32_t amax;       // smallest index attaining the chunk max
+  uint64_t s;         // bits of the chunk sum of 2^((l - m_c) log2(e)/T) (fp64), or a NaN flag for greedy rows
+  uint64_t m_amax;    // bits of the chunk max (fp32, low half) and the smallest index attaining it (high half)
 };
 struct Job {
   int32_t kind, row, qrow, r, n_excl, out_slot;
@@ -120,6 +126,7 @@ struct Params {
   int32_t* rs_status;
   Ctrl* ctrl;
   Sync* sync;
+  Gather* gat;        // [bs][SV_MAX_NODES]
   Job* jobs;
   Partial* part;
   K3Rec* k3;
@@ -199,28 +206,50 @@ __device__ __forceinline__ uint32_t noise_word(uint64_t seed, int b, int r, int 
   return w == 0 ? o.x : w == 1 ? o.y : w == 2 ? o.z : o.w;
 }
 
-// Cross-workgroup synchronisation (agent scope).
-__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// Communication between workgroups.  Every word that another workgroup
+// reads is written and read with agent-scope atomic stores and loads, which
+// are coherent across the XCDs' separate L2 caches on their own; the writer
+// waits for its stores to complete (s_waitcnt) before it bumps the relaxed
+// counter or flag that announces them, and the reader loads the data only
+// after it has observed that counter or flag.  No release/acquire fence is
+// used: on gfx950 those write back and invalidate a whole L2 cache, which
+// thousands of workgroups per call cannot afford.
+__device__ __forceinline__ void cst32(void* p, uint32_t v) {
+  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void cst64(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t cld32(const void* p) {
+  return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cld64(const void* p) {
+  return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst_f32(float* p, float v) { cst32(p, __float_as_uint(v)); }
+__device__ __forceinline__ void cst_f64(double* p, double v) { cst64(p, (uint64_t)__double_as_longlong(v)); }
+__device__ __forceinline__ float cld_f32(const float* p) { return __uint_as_float(cld32(p)); }
+__device__ __forceinline__ double cld_f64(const double* p) { return __longlong_as_double((long long)cld64(p)); }
+__device__ __forceinline__ int32_t cld_i32(const int32_t* p) { return (int32_t)cld32(p); }
+__device__ __forceinline__ void cst_i32(int32_t* p, int32_t v) { cst32(p, (uint32_t)v); }
+// Wait until this wave's memory operations have completed.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_release(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // A value that is the same in every lane, made visibly uniform (an SGPR) so
 // that branches on it are scalar branches rather than divergent regions.
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
+// The scalar part of a published job, read once with coherent loads.
+struct JobView {
+  int kind, row, qrow, r, n_excl, out_slot;
+  float m, c_hi, c_lo, inv_s;
+  double s, t;
+  const int32_t* excl;  // read with coherent loads
+};
 
 // Shared memory of one workgroup (every role reuses it).
 struct Smem {
@@ -243,9 +272,11 @@ struct Smem {
   int path[SV_MAX_NODES];
   int a, kb, status, cur, len, emit;
   // race candidates
+  JobView job;
   int ncand;
   int cand_y[kMergeCandMax];
   double cand_key[kMergeCandMax];
+  float cand_h[kCandMax];
   int overflow;
 };
 
@@ -299,20 +330,18 @@ __device__ __forceinline__ int chain_kb(const Params& P, int b, int& xi) {
 // ===================================================================== K1
 // Streaming statistics of one chunk of one row.  The chunk is read with
 // 16-byte nontemporal loads (kVecPerThread per thread, consecutive lanes on
-// consecutive 16-byte pieces), reduced to its max m_c; greedy rows then find
-// the first index of m_c, stochastic rows form sum 2^((l - m_c) c) with
+// consecutive 16-byte pieces) that are issued before anything else the
+// workgroup needs; it is reduced to its max m_c; greedy rows then find the
+// first index of m_c, stochastic rows form sum 2^((l - m_c) c) with
 // c = log2(e)/T: fp32 pairwise sums over each 16-byte group, fp64 across
-// groups, lanes and waves, in a fixed order (bit-reproducible).  With
-// NEED_AMAX stochastic rows also report their first argmax (row statistics).
-template <bool BF16, bool NEED_AMAX>
-__device__ void k1_chunk_stats(const Params& P, int64_t row, int c, float T, Smem& sm) {
+// groups, lanes and waves, in a fixed order (bit-reproducible).
+template <bool BF16>
+__device__ __forceinline__ void k1_load(const Params& P, int64_t row, int c, float* v) {
   constexpr int EPV = BF16 ? 8 : 4;
-  constexpr int NE = kVecPerThread * EPV;
   const int tid = threadIdx.x;
   const int64_t start = (int64_t)c * P.CH;
   const int n = (int)min((int64_t)P.CH, (int64_t)P.V - start);
   const int64_t elem0 = row * P.lstride + start;
-  float v[NE];
 #pragma unroll
   for (int j = 0; j < kVecPerThread; ++j) {
     const int e0 = (j * kWG + tid) * EPV;
@@ -347,13 +376,19 @@ __device__ void k1_chunk_stats(const Params& P, int64_t row, int c, float T, Sme
       }
     }
   }
-  float tm = v[0];
-#pragma unroll
-  for (int i = 1; i < NE; ++i) tm = fmaxf(tm, v[i]);
-  const float mc = block_max(tm, sm);
+}
 
-  Partial out;
-  out.m = mc;
+// With NEED_AMAX stochastic rows also report their first argmax (row
+// statistics).  tm is this thread's max of v.
+template <bool BF16, bool NEED_AMAX>
+__device__ void k1_chunk_stats(const Params& P, int64_t row, int c, float T, const float* v, float tm, Smem& sm) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NE = kVecPerThread * EPV;
+  const int tid = threadIdx.x;
+  const int64_t start = (int64_t)c * P.CH;
+  const float mc = block_max(tm, sm);
+  double out_s = 0.0;
+  int32_t out_amax = (int32_t)start;
   const bool stoch = is_stochastic(T);
   if (!stoch || NEED_AMAX) {
     int first = INT32_MAX;
@@ -364,14 +399,14 @@ __device__ void k1_chunk_stats(const Params& P, int64_t row, int c, float T, Sme
         if (v[j * EPV + e] == mc) first = (j * kWG + tid) * EPV + e;
     }
     const int amax = block_min_i(first, sm);
-    out.amax = (int32_t)(start + (amax == INT32_MAX ? 0 : amax));
+    out_amax = (int32_t)(start + (amax == INT32_MAX ? 0 : amax));
   }
   if (!stoch) {
     bool nan_seen = false;
 #pragma unroll
     for (int i = 0; i < NE; ++i) nan_seen |= (v[i] != v[i]);
     const int any_nan = block_min_i(nan_seen ? 0 : 1, sm) == 0;
-    out.s = any_nan ? __builtin_nan("") : 0.0;
+    out_s = any_nan ? __builtin_nan("") : 0.0;
   } else {
     double acc = 0.0;
     if (mc != -INFINITY) {
@@ -391,10 +426,13 @@ __device__ void k1_chunk_stats(const Params& P, int64_t row, int c, float T, Sme
         acc += (double)g;
       }
     }
-    out.s = block_sum_d(acc, sm);
-    if (!NEED_AMAX) out.amax = (int32_t)start;
+    out_s = block_sum_d(acc, sm);
   }
-  if (tid == 0) P.part[row * P.CPR + c] = out;
+  if (tid == 0) {
+    Partial* dst = &P.part[row * P.CPR + c];
+    cst64(&dst->s, (uint64_t)__double_as_longlong(out_s));
+    cst64(&dst->m_amax, (uint64_t)__float_as_uint(mc) | ((uint64_t)(uint32_t)out_amax << 32));
+  }
 }
 
 // ===================================================================== K2
@@ -406,9 +444,11 @@ __device__ void combine_row(const Params& P, int64_t row, float T, float& m_out,
   float m = -INFINITY;
   int nanflag = 0;
   for (int c = lane; c < P.CPR; c += 64) {
-    const Partial pt = P.part[row * P.CPR + c];
-    m = fmaxf(m, pt.m);
-    if (pt.s != pt.s) nanflag = 1;
+    const Partial* pt = &P.part[row * P.CPR + c];
+    const float pm = __uint_as_float((uint32_t)cld64(&pt->m_amax));
+    const double ps = __longlong_as_double((long long)cld64(&pt->s));
+    m = fmaxf(m, pm);
+    if (ps != ps) nanflag = 1;
   }
   m = wave_max(m);
   int amax = INT32_MAX;
@@ -416,9 +456,12 @@ __device__ void combine_row(const Params& P, int64_t row, float T, float& m_out,
   const bool stoch = is_stochastic(T);
   const double cd = stoch ? 1.4426950408889634074 / (double)T : 0.0;
   for (int c = lane; c < P.CPR; c += 64) {
-    const Partial pt = P.part[row * P.CPR + c];
-    if (pt.m == m) amax = min(amax, (int)pt.amax);
-    if (stoch && pt.m != -INFINITY && m != -INFINITY) s += pt.s * exp2(((double)pt.m - (double)m) * cd);
+    const Partial* pt = &P.part[row * P.CPR + c];
+    const uint64_t ma = cld64(&pt->m_amax);
+    const float pm = __uint_as_float((uint32_t)ma);
+    const double ps = __longlong_as_double((long long)cld64(&pt->s));
+    if (pm == m) amax = min(amax, (int)(int32_t)(uint32_t)(ma >> 32));
+    if (stoch && pm != -INFINITY && m != -INFINITY) s += ps * exp2(((double)pm - (double)m) * cd);
   }
   amax = wave_min_i(amax);
   s = wave_sum_d(s);
@@ -432,20 +475,32 @@ __device__ void combine_row(const Params& P, int64_t row, float T, float& m_out,
 // p(y) of a stochastic row in fp64: exp((l - m)/T) / S.
 __device__ __forceinline__ double p_at(double l, float m, double T, double S) { return exp((l - (double)m) / T) / S; }
 
-__device__ void publish_job(const Params& P, int b, uint32_t epoch) {
-  // called by thread 0 after the job is written
-  store_release(&P.sync[b].ready, epoch + 1u);
+// Called by thread 0 of a stochastic request once its job is written: wait
+// for the job's stores, then raise the request's ready flag (the last of
+// the request's K3 chunks lowers it again).
+__device__ void publish_job(const Params& P, int b) {
+  wait_mem();
+  cst32(&P.sync[b].ready, 1u);
 }
 
-__device__ void fill_job_common(Job& J, float m, double S, double T) {
-  J.m = m;
-  J.s = S;
-  J.t = T;
+// Writes the sampling job of request b (thread 0 only).
+__device__ void write_job(const Params& P, int b, int kind, int row, int qrow, int r, int out_slot, float m,
+                          double S, double T) {
+  Job* J = &P.jobs[b];
+  cst_i32(&J->kind, kind);
+  if (kind == JOB_NONE) return;
+  cst_i32(&J->row, row);
+  cst_i32(&J->qrow, qrow);
+  cst_i32(&J->r, r);
+  cst_i32(&J->out_slot, out_slot);
+  cst_f32(&J->m, m);
+  cst_f64(&J->s, S);
+  cst_f64(&J->t, T);
   float hi, lo;
   scale_pair(T, hi, lo);
-  J.c_hi = hi;
-  J.c_lo = lo;
-  J.inv_s = (float)(1.0 / S);
+  cst_f32(&J->c_hi, hi);
+  cst_f32(&J->c_lo, lo);
+  cst_f32(&J->inv_s, (float)(1.0 / S));
 }
 
 __device__ __forceinline__ void k2_rows(const Params& P, int b, Smem& sm) {
@@ -467,12 +522,15 @@ __device__ __forceinline__ void k2_rows(const Params& P, int b, Smem& sm) {
 }
 
 template <bool BF16>
-__device__ __forceinline__ void k2_chain(const Params& P, int b, uint32_t epoch, Smem& sm) {
+__device__ __forceinline__ void k2_chain(const Params& P, int b, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = P.k, R = P.R, V = P.V;
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
+  // the gathered target logit and q at this lane's draft (K1 stored them)
+  uint64_t gl = 0;
+  if (wave == 0 && lane < k && !greedy) gl = cld64(&P.gat[(int64_t)b * SV_MAX_NODES + lane]);
   int xi;
   const int kb = chain_kb(P, b, xi);
   const bool bad_id = __ballot(lane < kb && (xi < 0 || xi >= V)) != 0;
@@ -498,12 +556,13 @@ __device__ __forceinline__ void k2_chain(const Params& P, int b, uint32_t epoch,
   if (status == SV_REQ_OK && wave == 0 && lane < kb) {
     const int64_t row = (int64_t)b * R + lane;
     double p;
+    (void)row;
     if (greedy) {
       p = (xi == sm.ramax[lane]) ? 1.0 : 0.0;
     } else {
-      p = p_at((double)load_logit<BF16>(P, row, xi), sm.rm[lane], T, sm.rs[lane]);
+      p = p_at((double)__uint_as_float((uint32_t)gl), sm.rm[lane], T, sm.rs[lane]);
       sm.u[lane] = coin(P.seed[b], b, lane);
-      if (P.draft_kind == SV_DRAFT_PROBS) sm.qx[lane] = (double)P.q[((int64_t)b * k + lane) * P.qstride + xi];
+      if (P.draft_kind == SV_DRAFT_PROBS) sm.qx[lane] = (double)__uint_as_float((uint32_t)(gl >> 32));
     }
     sm.px[lane] = p;
     sm.xs[lane] = xi;
@@ -528,17 +587,12 @@ __device__ __forceinline__ void k2_chain(const Params& P, int b, uint32_t epoch,
     P.accept_len[b] = a;
     if (P.status) P.status[b] = status;
     if (status == SV_REQ_OK && !greedy) {
-      Job& J = P.jobs[b];
-      J.kind = (a < kb) ? (P.draft_kind == SV_DRAFT_PROBS ? JOB_RESID : JOB_EXCL) : JOB_P;
-      J.row = b * R + a;
-      J.qrow = b * k + a;
-      J.r = a;
-      J.out_slot = b * R + a;
-      J.n_excl = (J.kind == JOB_EXCL) ? 1 : 0;
-      J.excl[0] = (J.kind == JOB_EXCL) ? sm.xs[a] : -1;
-      fill_job_common(J, sm.rm[a], sm.rs[a], T);
+      const int kind = (a < kb) ? (P.draft_kind == SV_DRAFT_PROBS ? JOB_RESID : JOB_EXCL) : JOB_P;
+      write_job(P, b, kind, b * R + a, b * k + a, a, b * R + a, sm.rm[a], sm.rs[a], T);
+      cst_i32(&P.jobs[b].n_excl, kind == JOB_EXCL ? 1 : 0);
+      if (kind == JOB_EXCL) cst_i32(&P.jobs[b].excl[0], sm.xs[a]);
     } else {
-      P.jobs[b].kind = JOB_NONE;
+      write_job(P, b, JOB_NONE, 0, 0, 0, 0, 0.f, 1.0, 1.0);
     }
   }
   __syncthreads();
@@ -556,16 +610,18 @@ __device__ __forceinline__ void k2_chain(const Params& P, int b, uint32_t epoch,
     for (int i = tid; i < k; i += kWG)
       P.p_draft[(int64_t)b * k + i] = (sm.status == SV_REQ_OK && i < kb) ? sm.px[i] : __builtin_nan("");
   __syncthreads();
-  if (tid == 0) publish_job(P, b, epoch);
+  if (tid == 0 && is_stochastic(Tf)) publish_job(P, b);
 }
 
 template <bool BF16>
-__device__ __forceinline__ void k2_tree(const Params& P, int b, uint32_t epoch, Smem& sm) {
+__device__ __forceinline__ void k2_tree(const Params& P, int b, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = P.R, V = P.V;
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
+  uint32_t gl = 0;  // node lane's token's logit in its parent's row (K1 stored it)
+  if (wave == 0 && lane >= 1 && lane < N && !greedy) gl = cld32(&P.gat[(int64_t)b * SV_MAX_NODES + lane].l);
   int par = -2, tok = -1;
   if (lane < N) {
     par = P.parent[(int64_t)b * N + lane];
@@ -609,7 +665,7 @@ __device__ __forceinline__ void k2_tree(const Params& P, int b, uint32_t epoch, 
     if (lane >= 1) {
       const int pn = sm.par[lane];
       if (greedy) sm.px[lane] = (tok == sm.ramax[pn]) ? 1.0 : 0.0;
-      else sm.px[lane] = p_at((double)load_logit<BF16>(P, (int64_t)b * N + pn, tok), sm.rm[pn], T, sm.rs[pn]);
+      else sm.px[lane] = p_at((double)__uint_as_float(gl), sm.rm[pn], T, sm.rs[pn]);
     }
     if (!greedy) sm.u[lane] = coin(P.seed[b], b, lane);
   }
@@ -656,20 +712,14 @@ __device__ __forceinline__ void k2_tree(const Params& P, int b, uint32_t epoch, 
     P.accept_len[b] = len;
     if (P.status) P.status[b] = status;
     if (kind != JOB_NONE) {
-      Job& J = P.jobs[b];
-      J.kind = kind;
-      J.row = b * N + cur;
-      J.qrow = 0;
-      J.r = cur;
-      J.out_slot = b * N + len;
+      write_job(P, b, kind, b * N + cur, 0, cur, b * N + len, sm.rm[cur], sm.rs[cur], T);
       int ne = 0;
       if (kind == JOB_EXCL)
         for (int c = cur + 1; c < N; ++c)
-          if (sm.par[c] == cur) J.excl[ne++] = sm.tok[c];
-      J.n_excl = ne;
-      fill_job_common(J, sm.rm[cur], sm.rs[cur], T);
+          if (sm.par[c] == cur) cst_i32(&P.jobs[b].excl[ne++], sm.tok[c]);
+      cst_i32(&P.jobs[b].n_excl, ne);
     } else {
-      P.jobs[b].kind = JOB_NONE;
+      write_job(P, b, JOB_NONE, 0, 0, 0, 0, 0.f, 1.0, 1.0);
     }
   }
   __syncthreads();
@@ -690,30 +740,50 @@ __device__ __forceinline__ void k2_tree(const Params& P, int b, uint32_t epoch, 
     if (!skip) P.tokens[(int64_t)b * N + i] = t;
   }
   __syncthreads();
-  if (tid == 0) publish_job(P, b, epoch);
+  if (tid == 0 && is_stochastic(Tf)) publish_job(P, b);
 }
 
 // ===================================================================== K3
+
+// Thread 0 reads the job (coherent loads) into shared memory; the caller
+// synchronises before the others read it.
+__device__ __forceinline__ void read_job(const Params& P, int b, JobView& v) {
+  const Job* src = &P.jobs[b];
+  v.kind = cld_i32(&src->kind);
+  v.row = cld_i32(&src->row);
+  v.qrow = cld_i32(&src->qrow);
+  v.r = cld_i32(&src->r);
+  v.n_excl = cld_i32(&src->n_excl);
+  v.out_slot = cld_i32(&src->out_slot);
+  v.m = cld_f32(&src->m);
+  v.c_hi = cld_f32(&src->c_hi);
+  v.c_lo = cld_f32(&src->c_lo);
+  v.inv_s = cld_f32(&src->inv_s);
+  v.s = cld_f64(&src->s);
+  v.t = cld_f64(&src->t);
+  v.excl = src->excl;
+}
+
 // Exact fp64 race key of vocabulary id y, the same formula as the
 // definition: w(y) / (-ln U_y).  With use_p the weight is p itself (the
 // fallback for an all-zero residual).
 template <bool BF16>
-__device__ double race_weight_f64(const Params& P, const Job* J, int y, bool use_p) {
-  const double p = p_at((double)load_logit<BF16>(P, J->row, y), J->m, J->t, J->s);
+__device__ double race_weight_f64(const Params& P, const JobView& J, int y, bool use_p) {
+  const double p = p_at((double)load_logit<BF16>(P, J.row, y), J.m, J.t, J.s);
   if (use_p) return p;
-  if (J->kind == JOB_RESID) {
-    const double d = p - (double)P.q[(int64_t)J->qrow * P.qstride + y];
+  if (J.kind == JOB_RESID) {
+    const double d = p - (double)P.q[(int64_t)J.qrow * P.qstride + y];
     return d > 0.0 ? d : 0.0;
   }
-  if (J->kind == JOB_EXCL)
-    for (int i = 0; i < J->n_excl; ++i)
-      if (J->excl[i] == y) return 0.0;
+  if (J.kind == JOB_EXCL)
+    for (int i = 0; i < J.n_excl; ++i)
+      if (cld_i32(&J.excl[i]) == y) return 0.0;
   return p;
 }
 template <bool BF16>
-__device__ double race_key_f64(const Params& P, const Job* J, int b, int y, bool use_p) {
+__device__ double race_key_f64(const Params& P, const JobView& J, int b, int y, bool use_p) {
   const double w = race_weight_f64<BF16>(P, J, y, use_p);
-  const double U = uniform_f64(noise_word(P.seed[b], b, J->r, y));
+  const double U = uniform_f64(noise_word(P.seed[b], b, J.r, y));
   return w / -log(U);
 }
 
@@ -725,7 +795,7 @@ __device__ __forceinline__ bool better(double ka, int ya, double kb_, int yb) {
 // Whole-row race in fp64 by one workgroup: used when the fp32 screen
 // cannot certify its candidate list, and on request.
 template <bool BF16>
-__device__ __forceinline__ int race_row_f64(const Params& P, const Job* J, int b, Smem& sm) {
+__device__ __forceinline__ int race_row_f64(const Params& P, const JobView& J, int b, Smem& sm) {
   // an all-zero weight vector falls back to p
   int any_pos = 0;
   for (int y = threadIdx.x; y < P.V; y += kWG)
@@ -771,13 +841,13 @@ __device__ __forceinline__ int race_row_f64(const Params& P, const Job* J, int b
 // drop qualifying entries with an upper bound >= L (then, or when L is too
 // small for fp32 to certify, the whole row is raced in fp64).
 template <bool BF16>
-__device__ __forceinline__ void k3_merge(const Params& P, int b, const Job* J, Smem& sm) {
+__device__ __forceinline__ void k3_merge(const Params& P, int b, const JobView& J, Smem& sm) {
   const int tid = threadIdx.x;
   float lo = -INFINITY, ovf = -INFINITY;
   for (int c = tid; c < P.C3; c += kWG) {
-    const K3Rec& rec = P.k3[(int64_t)b * P.C3 + c];
-    lo = fmaxf(lo, rec.lo);
-    ovf = fmaxf(ovf, rec.ovf_hi);
+    const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
+    lo = fmaxf(lo, cld_f32(&rec->lo));
+    ovf = fmaxf(ovf, cld_f32(&rec->ovf_hi));
   }
   const float L = block_max(lo, sm);
   const float OVF = block_max(ovf, sm);
@@ -789,11 +859,12 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, const Job* J, S
   bool fallback = (P.flags & SV_FLAG_FP64_RACE) || !(L >= 0x1p-70f) || OVF >= L;
   if (!fallback) {
     for (int c = tid; c < P.C3; c += kWG) {
-      const K3Rec& rec = P.k3[(int64_t)b * P.C3 + c];
-      for (int i = 0; i < rec.count; ++i) {
-        if (rec.hi[i] >= L) {
+      const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
+      const int cnt = cld_i32(&rec->count);
+      for (int i = 0; i < cnt; ++i) {
+        if (cld_f32(&rec->hi[i]) >= L) {
           const int slot = atomicAdd(&sm.ncand, 1);
-          if (slot < kMergeCandMax) sm.cand_y[slot] = rec.idx[i];
+          if (slot < kMergeCandMax) sm.cand_y[slot] = cld_i32(&rec->idx[i]);
           else sm.overflow = 1;
         }
       }
@@ -821,10 +892,7 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, const Job* J, S
     fallback = best_y < 0;
   }
   if (fallback) best_y = race_row_f64<BF16>(P, J, b, sm);
-  if (tid == 0) {
-    P.tokens[J->out_slot] = best_y;
-    store_relaxed(&P.sync[b].k3_count, 0u);
-  }
+  if (tid == 0) P.tokens[J.out_slot] = best_y;
 }
 
 // Per-element fp32 race keys with certified bounds, for the 4*kK3Groups ids
@@ -836,19 +904,19 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, const Job* J, S
 // of w / E.  hi[] gets each key's upper bound (-1 when the id does not
 // race); lo_max the largest lower bound.
 template <bool BF16, int KIND>
-__device__ void k3_chunk_keys(const Params& P, const Job* J, int b, int c3, float* hi, float& lo_max) {
+__device__ void k3_chunk_keys(const Params& P, const JobView& J, int b, int c3, float* hi, float& lo_max) {
   const int tid = threadIdx.x;
   const uint64_t seed = P.seed[b];
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  const float m = J->m, chi = J->c_hi, clo = J->c_lo, inv_s = J->inv_s;
-  const int jr = J->r;
-  const int64_t lrow = (int64_t)J->row * P.lstride;
-  const int64_t qrow = (int64_t)J->qrow * P.qstride;
+  const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
+  const int jr = J.r;
+  const int64_t lrow = (int64_t)J.row * P.lstride;
+  const int64_t qrow = (int64_t)J.qrow * P.qstride;
   uint32_t excl_mask = 0;  // bit g*4+i: this thread's id is a removed token
   if (KIND == JOB_EXCL) {
-    const int n_excl = J->n_excl;
+    const int n_excl = J.n_excl;
     for (int i = 0; i < n_excl; ++i) {
-      const int z = J->excl[i] - c3 * kK3Chunk;
+      const int z = cld_i32(&J.excl[i]) - c3 * kK3Chunk;
       if (z >= 0 && z < kK3Chunk) {
         const int gi = z >> 2;
         if ((gi % kWG) == tid) excl_mask |= 1u << ((gi / kWG) * 4 + (z & 3));
@@ -876,7 +944,7 @@ __device__ void k3_chunk_keys(const Params& P, const Job* J, int b, int c3, floa
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J->row, y0 + i) : -INFINITY;
+      for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
     if (KIND == JOB_RESID) {
       if (full && P.q_aligned) {
@@ -921,76 +989,103 @@ __device__ void k3_chunk_keys(const Params& P, const Job* J, int b, int c3, floa
 }
 
 template <bool BF16>
-__device__ void k3_chunk(const Params& P, int b, int c3, uint32_t epoch, Smem& sm) {
+__device__ void k3_chunk(const Params& P, int b, int c3, Smem& sm) {
   const int tid = threadIdx.x;
   if (!is_stochastic(temp_of(P, b))) return;  // greedy requests and bad temperatures race nothing
-  if (!P.phased) {
-    if (tid == 0) {
+  if (tid == 0) {
+    int ok = 1;
+    if (!P.phased) {
       uint32_t spins = 0;
-      int ok = 1;
-      while (load_relaxed(&P.sync[b].ready) != epoch + 1u) {
+      while (cld32(&P.sync[b].ready) == 0u) {
         __builtin_amdgcn_s_sleep(8);
-        if (++spins > kSpinLimit || load_relaxed(&P.ctrl->aborted)) {
+        if (++spins > kSpinLimit || cld32(&P.ctrl->aborted)) {
           ok = 0;
           break;
         }
       }
-      fence_acquire();
-      sm.flag = ok;
       if (!ok) {
-        store_relaxed(&P.ctrl->aborted, 1u);
+        cst32(&P.ctrl->aborted, 1u);
         if (P.status) P.status[b] = SV_REQ_INTERNAL;
       }
     }
-    __syncthreads();
-    if (!uniform_i(sm.flag)) return;
-  }
-  const Job* J = &P.jobs[b];
-  const int kind = uniform_i(J->kind);
-  if (kind == JOB_NONE) return;
-  float hi[kK3Groups * 4];
-  float lo_max = -INFINITY;
-  if (kind == JOB_RESID) k3_chunk_keys<BF16, JOB_RESID>(P, J, b, c3, hi, lo_max);
-  else if (kind == JOB_EXCL) k3_chunk_keys<BF16, JOB_EXCL>(P, J, b, c3, hi, lo_max);
-  else k3_chunk_keys<BF16, JOB_P>(P, J, b, c3, hi, lo_max);
-  const float L = block_max(lo_max, sm);
-  if (tid == 0) {
-    sm.ncand = 0;
-    sm.overflow = 0;
+    sm.flag = ok;
+    if (ok) read_job(P, b, sm.job);
   }
   __syncthreads();
-  K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c3];
-  float ovf_hi = -INFINITY;
+  if (!uniform_i(sm.flag)) return;
+  const JobView J = sm.job;
+  const int kind = uniform_i(J.kind);
+  float L = -INFINITY, ovf_hi = -INFINITY;
+  if (kind != JOB_NONE) {
+    float hi[kK3Groups * 4];
+    float lo_max = -INFINITY;
+    if (kind == JOB_RESID) k3_chunk_keys<BF16, JOB_RESID>(P, J, b, c3, hi, lo_max);
+    else if (kind == JOB_EXCL) k3_chunk_keys<BF16, JOB_EXCL>(P, J, b, c3, hi, lo_max);
+    else k3_chunk_keys<BF16, JOB_P>(P, J, b, c3, hi, lo_max);
+    L = block_max(lo_max, sm);
+    if (tid == 0) sm.ncand = 0;
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kK3Groups * 4; ++i) {
-    if (hi[i] >= L && hi[i] > 0.f) {
-      const int slot = atomicAdd(&sm.ncand, 1);
-      if (slot < kCandMax) {
-        rec->idx[slot] = c3 * kK3Chunk + 4 * ((i >> 2) * kWG + tid) + (i & 3);
-        rec->hi[slot] = hi[i];
+    for (int i = 0; i < kK3Groups * 4; ++i) {
+      if (hi[i] >= L && hi[i] > 0.f) {
+        const int slot = atomicAdd(&sm.ncand, 1);
+        if (slot < kCandMax) {
+          sm.cand_y[slot] = c3 * kK3Chunk + 4 * ((i >> 2) * kWG + tid) + (i & 3);
+          sm.cand_h[slot] = hi[i];
+        }
+        ovf_hi = fmaxf(ovf_hi, hi[i]);
       }
-      ovf_hi = fmaxf(ovf_hi, hi[i]);
+    }
+    ovf_hi = block_max(ovf_hi, sm);
+  }
+  // wave 0 publishes the chunk's record, then thread 0 counts the chunk; the
+  // last chunk of the request lowers the ready flag and merges
+  if (tid < 64) {
+    if (kind != JOB_NONE) {
+      K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c3];
+      const int n = sm.ncand;
+      const int cnt = min(n, kCandMax);
+      if (tid < cnt) {
+        cst_i32(&rec->idx[tid], sm.cand_y[tid]);
+        cst_f32(&rec->hi[tid], sm.cand_h[tid]);
+      }
+      if (tid == 0) {
+        cst_f32(&rec->lo, L);
+        cst_i32(&rec->count, cnt);
+        cst_f32(&rec->ovf_hi, n > kCandMax ? ovf_hi : -INFINITY);
+      }
+      wait_mem();
+    }
+    if (tid == 0) {
+      const uint32_t old = atomic_add_relaxed(&P.sync[b].k3_count, 1u);
+      const int last = (old == (uint32_t)P.C3 - 1u);
+      if (last) {
+        cst32(&P.sync[b].k3_count, 0u);
+        cst32(&P.sync[b].ready, 0u);
+      }
+      sm.flag = last && kind != JOB_NONE;
     }
   }
-  ovf_hi = block_max(ovf_hi, sm);
-  if (tid == 0) {
-    const int n = sm.ncand;
-    rec->lo = L;
-    rec->count = min(n, kCandMax);
-    rec->ovf_hi = n > kCandMax ? ovf_hi : -INFINITY;
-    const uint32_t old = atomic_add_acq_rel(&P.sync[b].k3_count, 1u);
-    sm.flag = (old == (uint32_t)P.C3 - 1u);
-  }
   __syncthreads();
-  if (uniform_i(sm.flag)) {
-    fence_acquire();
-    k3_merge<BF16>(P, b, J, sm);
-  }
+  if (uniform_i(sm.flag)) k3_merge<BF16>(P, b, J, sm);
 }
 
 // ===================================================================== driver
+// K1 work item (request b, row r, chunk c).  Its HBM loads are issued first;
+// then the request's temperature and drafts decide whether the row is needed
+// (rows after a chain's first -1 are not).  Wave 0 also gathers the target
+// logit (and q) at the draft tokens that fall in this chunk, so the decision
+// step needs no dependent loads.  The workgroup that completes the
+// request's last chunk runs its decision step.
 template <int MODE, bool BF16>
-__device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, uint32_t epoch, Smem& sm) {
+__device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, Smem& sm) {
+  constexpr int NE = kVecPerThread * (BF16 ? 8 : 4);
+  const int64_t row = (int64_t)b * P.R + r;
+  float v[NE];
+  k1_load<BF16>(P, row, c, v);
+  float tm = v[0];
+#pragma unroll
+  for (int i = 1; i < NE; ++i) tm = fmaxf(tm, v[i]);
   const float T = temp_of(P, b);
   bool need = true;
   if (MODE == MODE_CHAIN) {
@@ -1000,29 +1095,49 @@ __device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, uin
   } else if (MODE == MODE_TREE) {
     need = isfinite(T);
   }
-  const int64_t row = (int64_t)b * P.R + r;
-  if (need) k1_chunk_stats<BF16, MODE == MODE_ROWS>(P, row, c, T, sm);
+  if (need) {
+    k1_chunk_stats<BF16, MODE == MODE_ROWS>(P, row, c, T, v, tm, sm);
+    if (MODE != MODE_ROWS && threadIdx.x < 64 && is_stochastic(T)) {
+      const int lane = threadIdx.x;
+      const int64_t start = (int64_t)c * P.CH, stop = min(start + P.CH, (int64_t)P.V);
+      int tok = -1, slot = -1;
+      if (MODE == MODE_CHAIN) {
+        if (lane == 0 && r < P.k) {
+          tok = P.ids[(int64_t)b * P.k + r];
+          slot = r;
+        }
+      } else if (lane >= 1 && lane < P.R && P.parent[(int64_t)b * P.R + lane] == r) {
+        tok = P.node_tokens[(int64_t)b * P.R + lane];
+        slot = lane;
+      }
+      if (slot >= 0 && tok >= start && tok < stop) {
+        const float l = load_logit<BF16>(P, row, tok);
+        float q = 0.f;
+        if (MODE == MODE_CHAIN && P.draft_kind == SV_DRAFT_PROBS) q = P.q[((int64_t)b * P.k + r) * P.qstride + tok];
+        cst64(&P.gat[(int64_t)b * SV_MAX_NODES + slot], (uint64_t)__float_as_uint(l) | ((uint64_t)__float_as_uint(q) << 32));
+      }
+    }
+  }
   if (P.phased) return;
-  __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = atomic_add_acq_rel(&P.sync[b].k1_count, 1u);
+    wait_mem();  // this wave's partial and gathers are complete
+    const uint32_t old = atomic_add_relaxed(&P.sync[b].k1_count, 1u);
     sm.flag = (old == (uint32_t)P.n1r - 1u);
   }
   __syncthreads();
   if (uniform_i(sm.flag)) {
-    fence_acquire();
-    if (threadIdx.x == 0) store_relaxed(&P.sync[b].k1_count, 0u);
-    if (MODE == MODE_CHAIN) k2_chain<BF16>(P, b, epoch, sm);
-    else if (MODE == MODE_TREE) k2_tree<BF16>(P, b, epoch, sm);
+    if (threadIdx.x == 0) cst32(&P.sync[b].k1_count, 0u);
+    if (MODE == MODE_CHAIN) k2_chain<BF16>(P, b, sm);
+    else if (MODE == MODE_TREE) k2_tree<BF16>(P, b, sm);
     else k2_rows(P, b, sm);
   }
 }
 
-// Ticket t of the fused schedule -> work item.  Blocks g = 0 .. bs+L-1:
-// block g holds the K1 chunks of request g (if g < bs) followed by the K3
-// chunks of request g - L (if g >= L).
+// Work item t of the fused schedule.  Blocks g = 0 .. bs+L-1: block g holds
+// the K1 chunks of request g (if g < bs) followed by the K3 chunks of
+// request g - L (if g >= L).
 template <int MODE, bool BF16>
-__device__ __forceinline__ void run_ticket(const Params& P, uint32_t t, uint32_t epoch, Smem& sm) {
+__device__ __forceinline__ void run_item(const Params& P, uint32_t t, Smem& sm) {
   const uint32_t n1 = (uint32_t)P.n1r, n3 = (uint32_t)P.C3, L = (uint32_t)P.lag, bs = (uint32_t)P.bs;
   const uint32_t seg1 = L * n1;
   const uint32_t seg2 = (bs - L) * (n1 + n3);
@@ -1050,34 +1165,16 @@ __device__ __forceinline__ void run_ticket(const Params& P, uint32_t t, uint32_t
     kind1 = 0;
   }
   if (kind1) {
-    run_k1<MODE, BF16>(P, b, (int)(o / (uint32_t)P.CPR), (int)(o % (uint32_t)P.CPR), epoch, sm);
+    run_k1<MODE, BF16>(P, b, (int)(o / (uint32_t)P.CPR), (int)(o % (uint32_t)P.CPR), sm);
   } else if (MODE != MODE_ROWS) {
-    k3_chunk<BF16>(P, b, (int)o, epoch, sm);
+    k3_chunk<BF16>(P, b, (int)o, sm);
   }
 }
 
-// Fused schedule: one work item per workgroup.  A workgroup's item is the
-// ticket it draws when it starts (not its blockIdx), so items are handed out
-// in the order workgroups actually run; the last workgroup to finish resets
-// the schedule and advances the epoch for the next call.
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG) void fused_kernel(Params P) {
   __shared__ Smem sm;
-  const uint32_t epoch = P.ctrl->epoch;
-  if (threadIdx.x == 0) sm.ticket = atomic_add_relaxed(&P.ctrl->ticket, 1u);
-  __syncthreads();
-  const uint32_t t = uniform_u(sm.ticket);
-  if (t < (uint32_t)P.n_tickets) run_ticket<MODE, BF16>(P, t, epoch, sm);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomic_add_acq_rel(&P.ctrl->wg_done, 1u);
-    if (old == gridDim.x - 1u) {
-      store_relaxed(&P.ctrl->ticket, 0u);
-      store_relaxed(&P.ctrl->wg_done, 0u);
-      store_relaxed(&P.ctrl->aborted, 0u);
-      store_release(&P.ctrl->epoch, epoch + 1u);
-    }
-  }
+  run_item<MODE, BF16>(P, blockIdx.x, sm);
 }
 
 template <int MODE, bool BF16>
@@ -1086,15 +1183,15 @@ __global__ __launch_bounds__(kWG) void k1_kernel(Params P) {
   const uint32_t t = blockIdx.x;
   const int b = (int)(t / (uint32_t)P.n1r);
   const uint32_t o = t % (uint32_t)P.n1r;
-  run_k1<MODE, BF16>(P, b, (int)(o / (uint32_t)P.CPR), (int)(o % (uint32_t)P.CPR), 0u, sm);
+  run_k1<MODE, BF16>(P, b, (int)(o / (uint32_t)P.CPR), (int)(o % (uint32_t)P.CPR), sm);
 }
 
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG) void k2_kernel(Params P) {
   __shared__ Smem sm;
   const int b = blockIdx.x;
-  if (MODE == MODE_CHAIN) k2_chain<BF16>(P, b, 0u, sm);
-  else if (MODE == MODE_TREE) k2_tree<BF16>(P, b, 0u, sm);
+  if (MODE == MODE_CHAIN) k2_chain<BF16>(P, b, sm);
+  else if (MODE == MODE_TREE) k2_tree<BF16>(P, b, sm);
   else k2_rows(P, b, sm);
 }
 
@@ -1103,7 +1200,7 @@ __global__ __launch_bounds__(kWG) void k3_kernel(Params P) {
   __shared__ Smem sm;
   const int b = (int)(blockIdx.x / (uint32_t)P.C3);
   const int c3 = (int)(blockIdx.x % (uint32_t)P.C3);
-  k3_chunk<BF16>(P, b, c3, 0u, sm);
+  k3_chunk<BF16>(P, b, c3, sm);
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -1117,7 +1214,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 // ===================================================================== host
 struct Shape {
   int CH, CPR, C3;
-  size_t jobs_off, part_off, k3_off, total;
+  size_t gat_off, jobs_off, part_off, k3_off, total;
 };
 
 static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
@@ -1125,7 +1222,8 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   s.CH = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
   s.CPR = (int)((V + s.CH - 1) / s.CH);
   s.C3 = races ? (int)((V + kK3Chunk - 1) / kK3Chunk) : 0;
-  s.jobs_off = kDataOffset;
+  s.gat_off = kDataOffset;
+  s.jobs_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
   s.part_off = s.jobs_off + align256(sizeof(Job) * (size_t)bs);
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
   s.total = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
@@ -1194,6 +1292,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   uint8_t* base = (uint8_t*)ws;
   P.ctrl = (Ctrl*)base;
   P.sync = (Sync*)(base + kSyncOffset);
+  P.gat = (Gather*)(base + S.gat_off);
   P.jobs = (Job*)(base + S.jobs_off);
   P.part = (Partial*)(base + S.part_off);
   P.k3 = (K3Rec*)(base + S.k3_off);
@@ -1204,7 +1303,9 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   const int64_t n_tickets = (int64_t)P.bs * (P.n1r + P.C3);
   if (n_tickets <= 0 || n_tickets > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   P.n_tickets = (int32_t)n_tickets;
-  P.phased = (P.flags & SV_FLAG_PHASED) ? 1 : 0;
+  // Schedule: fused only on request for now; the phased schedule measures
+  // faster on the shapes benchmarked so far.
+  P.phased = (P.flags & SV_FLAG_FUSED) ? 0 : 1;
   KernelFn fused, k1, k2, k3;
   const bool bf16 = P.dtype == SV_BF16;
   select_kernels(P.mode, bf16, fused, k1, k2, k3);
@@ -1221,6 +1322,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
     // Lag between a request's K1 chunks and its K3 chunks, in requests:
     // about the number of requests the resident workgroups stream at once,
     // so that a K3 item rarely has to wait for its request's decision.
+    // (SV_LAG overrides it, for tuning.)
     int lag = env_int("SV_LAG", -1);
     if (lag < 0) lag = (int)((resident + P.n1r - 1) / P.n1r) + 1;
     if (P.C3 == 0) lag = 0;
@@ -1293,7 +1395,8 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
     return SV_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
   if (d->draft_kind != SV_DRAFT_PROBS && d->draft_kind != SV_DRAFT_ONEHOT) return SV_ERR_UNSUPPORTED;
-  if (d->flags & ~(SV_FLAG_PHASED | SV_FLAG_FP64_RACE)) return SV_ERR_UNSUPPORTED;
+  if (d->flags & ~(SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
+  if ((d->flags & SV_FLAG_PHASED) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_INVALID_ARGUMENT;
   if (d->logits == nullptr || d->temperature == nullptr || d->seed == nullptr || d->accept_len == nullptr ||
       d->tokens == nullptr)
     return SV_ERR_INVALID_ARGUMENT;
@@ -1336,7 +1439,8 @@ sv_status sv_verify_tree(const sv_tree_desc* d, void* ws, size_t ws_bytes, void*
       d->vocab < 1 || d->vocab > SV_MAX_VOCAB)
     return SV_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
-  if (d->flags & ~(SV_FLAG_PHASED | SV_FLAG_FP64_RACE)) return SV_ERR_UNSUPPORTED;
+  if (d->flags & ~(SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
+  if ((d->flags & SV_FLAG_PHASED) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_INVALID_ARGUMENT;
   if (d->logits == nullptr || d->node_tokens == nullptr || d->parent == nullptr || d->temperature == nullptr ||
       d->seed == nullptr || d->accept_len == nullptr || d->accept_path == nullptr || d->tokens == nullptr)
     return SV_ERR_INVALID_ARGUMENT;

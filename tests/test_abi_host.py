@@ -88,6 +88,10 @@ def test_chain_argument_validation(field, value, code):
     assert _call_chain(_chain_desc(**{field: value})) == code
 
 
+def test_schedule_flags_are_exclusive():
+    assert _call_chain(_chain_desc(flags=sv.FLAG_PHASED | sv.FLAG_FUSED)) == 1
+
+
 def test_chain_null_descriptor_and_workspace_checks():
     assert sv.lib().sv_verify_chain(None, ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 1
     assert _call_chain(_chain_desc(), ws=0) == 1

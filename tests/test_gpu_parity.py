@@ -142,13 +142,13 @@ def test_tree_workload(dev, greedy):
 # ------------------------------------------------- schedules and determinism
 def test_fused_and_phased_schedules_are_bit_identical(dev):
     inp = workloads.chain_bf16_mixed(1, bs=24)
-    _, a = run_chain(inp, dev)
+    _, a = run_chain(inp, dev, flags=sv.FLAG_FUSED)
     _, b = run_chain(inp, dev, flags=sv.FLAG_PHASED)
     for k in ("accept_len", "tokens", "status"):
         np.testing.assert_array_equal(a[k], b[k])
     np.testing.assert_array_equal(a["p_draft"].view(np.int64), b["p_draft"].view(np.int64))
     t = workloads.tree_fp32(1, bs=12)
-    _, c = run_tree(t, dev)
+    _, c = run_tree(t, dev, flags=sv.FLAG_FUSED)
     _, d = run_tree(t, dev, flags=sv.FLAG_PHASED)
     for k in ("accept_len", "tokens", "status", "accept_path"):
         np.testing.assert_array_equal(c[k], d[k])
@@ -311,8 +311,13 @@ def test_degenerate_distributions(dev):
 def _random_tree_inputs(seed, bs, N, V, dtype="f32", greedy_frac=0.3):
     rng = np.random.default_rng(seed)
     l = (rng.standard_normal((bs, N, V)) * 2.5).astype(np.float32)
-    parent = np.stack([workloads.random_tree(rng, N, max_depth=rng.integers(1, 6), max_children=4)
-                       for _ in range(bs)])
+    def topology():
+        depth = int(rng.integers(1, 6))
+        kids = 4
+        while sum(kids ** d for d in range(1, depth + 1)) < N - 1:  # room for every node
+            kids += 1
+        return workloads.random_tree(rng, N, max_depth=depth, max_children=kids)
+    parent = np.stack([topology() for _ in range(bs)])
     tok = np.full((bs, N), -1, np.int32)
     for b in range(bs):
         for n in range(N):
