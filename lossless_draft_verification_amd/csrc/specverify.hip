@@ -32,9 +32,10 @@
 // depends on (a smaller index) is already running or finished: the waits
 // always end.  There is no global counter: per-request counters and flags
 // are reset by their last user, so the workspace is ready for the next call
-// without any reset pass.  The phased schedule runs K1, K2 and K3 as three
-// stream-ordered launches with no waiting at all; both give bit-identical
-// results.
+// without any reset pass.  The split schedule is two stream-ordered
+// launches: K1 (each request's last workgroup running its K2, as above),
+// then K3 with nothing left to wait for.  The phased schedule runs K1, K2
+// and K3 as three launches.  All three give bit-identical results.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -49,7 +50,14 @@ namespace sv {
 
 constexpr int kWG = 256;
 constexpr int kWaves = kWG / 64;
-constexpr int kVecPerThread = 4;                // 16-byte loads per thread in a K1 chunk
+#ifndef SV_K1_VEC
+#define SV_K1_VEC 2
+#endif
+#ifndef SV_K1_SUBS
+#define SV_K1_SUBS 8
+#endif
+constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a K1 sub-chunk
+constexpr int kSubChunks = SV_K1_SUBS;          // sub-chunks per K1 work item (register double buffer)
 constexpr int kK3Groups = 4;                    // groups of 4 vocabulary ids per thread in a K3 chunk
 constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 4096 ids per K3 chunk
 constexpr int kCandMax = 8;                     // candidates kept per K3 chunk
@@ -58,6 +66,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second
 
 enum { MODE_CHAIN = 0, MODE_TREE = 1, MODE_ROWS = 2 };
 enum { JOB_NONE = 0, JOB_P = 1, JOB_RESID = 2, JOB_EXCL = 3 };
+enum { SCHED_FUSED = 0, SCHED_PHASED = 1, SCHED_SPLIT = 2 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -130,7 +139,7 @@ struct Params {
   Job* jobs;
   Partial* part;
   K3Rec* k3;
-  int32_t CH, CPR, n1r, C3, lag, n_tickets, phased;
+  int32_t CH, CPR, n1r, C3, lag, n_tickets, sched;
   uint32_t flags;
 };
 
@@ -328,107 +337,182 @@ __device__ __forceinline__ int chain_kb(const Params& P, int b, int& xi) {
 }
 
 // ===================================================================== K1
-// Streaming statistics of one chunk of one row.  The chunk is read with
-// 16-byte nontemporal loads (kVecPerThread per thread, consecutive lanes on
-// consecutive 16-byte pieces) that are issued before anything else the
-// workgroup needs; it is reduced to its max m_c; greedy rows then find the
-// first index of m_c, stochastic rows form sum 2^((l - m_c) c) with
-// c = log2(e)/T: fp32 pairwise sums over each 16-byte group, fp64 across
-// groups, lanes and waves, in a fixed order (bit-reproducible).
+// Streaming statistics of one work item: kSubChunks consecutive sub-chunks of
+// one row, each 256 threads x kVecPerThread nontemporal 16-byte loads
+// (consecutive lanes on consecutive 16-byte pieces).  The loads of sub-chunk
+// s+1 are in flight while sub-chunk s is reduced (a register double buffer).
+// Per sub-chunk a thread first takes the max of its entries.  Stochastic
+// rows then add 2^(l c - o) over the entries, with c = log2(e)/T rounded to
+// fp32 and o = fl(m c) the fp32 offset of the thread's running max m: one
+// fma and one exp2 per entry, the terms summed pairwise in fp32 and the
+// running sum kept in fp64, rescaled by 2^(o_old - o_new) when the max
+// grows.  At the end the rounding of o is undone exactly (m c is exact in
+// fp64) and the threads are combined with the fp64 scale, so a term
+// 2^((l - m) log2(e)/T) is evaluated with a relative exponent error of at
+// most 2^-24 from c plus the fma's rounding.  Greedy rows (and every row of
+// a row-statistics call) keep the first index of the running max and a NaN
+// flag.  One block reduction per item gives the item's (max, first argmax,
+// sum), in a fixed order (bit-reproducible).
 template <bool BF16>
-__device__ __forceinline__ void k1_load(const Params& P, int64_t row, int c, float* v) {
+__device__ __forceinline__ void k1_issue(const Params& P, int64_t elem0, int n, u32x4* raw) {
   constexpr int EPV = BF16 ? 8 : 4;
   const int tid = threadIdx.x;
-  const int64_t start = (int64_t)c * P.CH;
-  const int n = (int)min((int64_t)P.CH, (int64_t)P.V - start);
-  const int64_t elem0 = row * P.lstride + start;
 #pragma unroll
   for (int j = 0; j < kVecPerThread; ++j) {
     const int e0 = (j * kWG + tid) * EPV;
     if (P.aligned && e0 + EPV <= n) {
-      const u32x4 w = __builtin_nontemporal_load(
-          (const u32x4*)((const char*)P.logits + (elem0 + e0) * (BF16 ? 2 : 4)));
-      if (BF16) {
-        v[j * EPV + 0] = __uint_as_float(w.x << 16);
-        v[j * EPV + 1] = __uint_as_float(w.x & 0xffff0000u);
-        v[j * EPV + 2] = __uint_as_float(w.y << 16);
-        v[j * EPV + 3] = __uint_as_float(w.y & 0xffff0000u);
-        v[j * EPV + 4] = __uint_as_float(w.z << 16);
-        v[j * EPV + 5] = __uint_as_float(w.z & 0xffff0000u);
-        v[j * EPV + 6] = __uint_as_float(w.w << 16);
-        v[j * EPV + 7] = __uint_as_float(w.w & 0xffff0000u);
-      } else {
-        v[j * EPV + 0] = __uint_as_float(w.x);
-        v[j * EPV + 1] = __uint_as_float(w.y);
-        v[j * EPV + 2] = __uint_as_float(w.z);
-        v[j * EPV + 3] = __uint_as_float(w.w);
-      }
+      raw[j] = __builtin_nontemporal_load((const u32x4*)((const char*)P.logits + (elem0 + e0) * (BF16 ? 2 : 4)));
     } else {
+      // partial (or unaligned) group: scalar loads, -inf past the end
+      uint32_t w[4];
+      if (BF16) {
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int i = e0 + e;
-        float x = -INFINITY;
-        if (i < n) {
-          if (BF16) x = bf16_to_f32(((const uint16_t*)P.logits)[elem0 + i]);
-          else x = ((const float*)P.logits)[elem0 + i];
+        for (int h = 0; h < 4; ++h) {
+          const int i0 = e0 + 2 * h;
+          const uint32_t lo = (i0 < n) ? ((const uint16_t*)P.logits)[elem0 + i0] : 0xFF80u;
+          const uint32_t hi = (i0 + 1 < n) ? ((const uint16_t*)P.logits)[elem0 + i0 + 1] : 0xFF80u;
+          w[h] = lo | (hi << 16);
         }
-        v[j * EPV + e] = x;
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          w[h] = (e0 + h < n) ? ((const uint32_t*)P.logits)[elem0 + e0 + h] : 0xFF800000u;
       }
+      raw[j] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
 }
 
-// With NEED_AMAX stochastic rows also report their first argmax (row
-// statistics).  tm is this thread's max of v.
-template <bool BF16, bool NEED_AMAX>
-__device__ void k1_chunk_stats(const Params& P, int64_t row, int c, float T, const float* v, float tm, Smem& sm) {
-  constexpr int EPV = BF16 ? 8 : 4;
-  constexpr int NE = kVecPerThread * EPV;
-  const int tid = threadIdx.x;
-  const int64_t start = (int64_t)c * P.CH;
-  const float mc = block_max(tm, sm);
-  double out_s = 0.0;
-  int32_t out_amax = (int32_t)start;
-  const bool stoch = is_stochastic(T);
-  if (!stoch || NEED_AMAX) {
-    int first = INT32_MAX;
+// Running per-thread statistics of a K1 item.
+struct K1Run {
+  float m;       // running max
+  float off;     // fl(m c): the running sum is relative to 2^off (-inf while m = -inf)
+  int idx;       // first index (in the item) of the running max
+  double s;      // sum of 2^(l c - off) (stochastic rows)
+  bool nan;      // a NaN was seen (greedy rows; stochastic rows see it in s)
+};
+
+// The thread's entries of one sub-chunk, widened to fp32 (bf16 widening is
+// exact; as a conversion its results need no canonicalisation before max).
+template <bool BF16>
+__device__ __forceinline__ void k1_unpack(const u32x4* v, float* x) {
 #pragma unroll
-    for (int j = kVecPerThread - 1; j >= 0; --j) {
+  for (int j = 0; j < kVecPerThread; ++j) {
+    if (BF16) {
+      __bf16 h[8];
+      __builtin_memcpy(h, &v[j], 16);
 #pragma unroll
-      for (int e = EPV - 1; e >= 0; --e)
-        if (v[j * EPV + e] == mc) first = (j * kWG + tid) * EPV + e;
+      for (int i = 0; i < 8; ++i) x[j * 8 + i] = (float)h[i];
+    } else {
+      x[j * 4 + 0] = __uint_as_float(v[j].x);
+      x[j * 4 + 1] = __uint_as_float(v[j].y);
+      x[j * 4 + 2] = __uint_as_float(v[j].z);
+      x[j * 4 + 3] = __uint_as_float(v[j].w);
     }
-    const int amax = block_min_i(first, sm);
-    out_amax = (int32_t)(start + (amax == INT32_MAX ? 0 : amax));
   }
-  if (!stoch) {
+}
+
+// Folds the NV entries x of one sub-chunk into the running statistics.
+// Entry i sits at item offset base + (i / EPV) * kWG * EPV + i % EPV, so the
+// thread's order is the row order and the first hit is the smallest index.
+template <int NV, int EPV, bool STOCH, bool NEED_AMAX>
+__device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K1Run& st) {
+#pragma clang fp contract(off)
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) mx = fmaxf(mx, x[i]);
+  if (!STOCH || NEED_AMAX) {
+    if (mx > st.m) {  // strict: an earlier sub-chunk keeps a tie
+      int pos = 0;
+#pragma unroll
+      for (int i = NV - 1; i >= 0; --i)
+        if (x[i] == mx) pos = (i / EPV) * kWG * EPV + (i % EPV);
+      st.idx = base + pos;
+    }
+  }
+  if (!STOCH) {
     bool nan_seen = false;
 #pragma unroll
-    for (int i = 0; i < NE; ++i) nan_seen |= (v[i] != v[i]);
-    const int any_nan = block_min_i(nan_seen ? 0 : 1, sm) == 0;
+    for (int i = 0; i < NV; ++i) nan_seen |= (x[i] != x[i]);
+    st.nan |= nan_seen;
+    st.m = fmaxf(st.m, mx);
+  } else {
+    const float mn = fmaxf(st.m, mx);
+    const float off = (mn == -INFINITY) ? 0.f : mn * c;  // keeps l = -inf terms at 2^-inf = 0
+    // rescale factor: 0 until the first finite max (st.off = -inf; never
+    // inf * 0), exactly 1 while the max is unchanged, else at most 1
+    const float f = __builtin_amdgcn_exp2f(st.off - off);
+    float e[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -off));
+#pragma unroll
+    for (int w = 1; w < NV; w *= 2)
+#pragma unroll
+      for (int i = 0; i + w < NV; i += 2 * w) e[i] += e[i + w];
+    st.s = st.s * (double)f + (double)e[0];
+    st.m = mn;
+    st.off = (mn == -INFINITY) ? -INFINITY : off;
+  }
+}
+
+// Streams the item's sub-chunks from raw0 (the first sub-chunk, already in
+// flight) and writes the item's partial.
+template <bool BF16, bool STOCH, bool NEED_AMAX>
+__device__ __forceinline__ void k1_item_stats(const Params& P, int64_t row, int c, float T, u32x4* raw0, Smem& sm) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NV = kVecPerThread * EPV;  // entries per thread per sub-chunk
+  constexpr int SUB = NV * kWG;            // entries per sub-chunk
+  const int64_t start = (int64_t)c * P.CH;
+  const int n_item = (int)min((int64_t)P.CH, (int64_t)P.V - start);
+  const int64_t elem0 = row * P.lstride + start;
+  float cf = 0.f;
+  double cd = 0.0;
+  if (STOCH) {
+    cd = 1.4426950408889634074 / (double)T;
+    cf = (float)cd;
+  }
+  K1Run st;
+  st.m = -INFINITY;
+  st.off = -INFINITY;
+  st.idx = INT32_MAX;
+  st.s = 0.0;
+  st.nan = false;
+  u32x4 cur[kVecPerThread], nxt[kVecPerThread];
+#pragma unroll
+  for (int j = 0; j < kVecPerThread; ++j) cur[j] = raw0[j];
+#pragma unroll 1
+  for (int sub = 0; sub < kSubChunks; ++sub) {
+    if (sub + 1 < kSubChunks && (sub + 1) * SUB < n_item)
+      k1_issue<BF16>(P, elem0 + (int64_t)(sub + 1) * SUB, n_item - (sub + 1) * SUB, nxt);
+    if (sub * SUB < n_item) {
+      float x[NV];
+      k1_unpack<BF16>(cur, x);
+      k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
+    }
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j) cur[j] = nxt[j];
+  }
+  const float mc = block_max(st.m, sm);
+  double out_s = 0.0;
+  int32_t out_amax = (int32_t)start;
+  if (!STOCH || NEED_AMAX) {
+    const int amax = block_min_i(st.m == mc ? st.idx : INT32_MAX, sm);
+    out_amax = (int32_t)(start + (amax == INT32_MAX ? 0 : amax));
+  }
+  if (!STOCH) {
+    const int any_nan = block_min_i(st.nan ? 0 : 1, sm) == 0;
     out_s = any_nan ? __builtin_nan("") : 0.0;
   } else {
-    double acc = 0.0;
-    if (mc != -INFINITY) {
-      float chi, clo;
-      scale_pair((double)T, chi, clo);
-#pragma unroll
-      for (int j = 0; j < kVecPerThread; ++j) {
-        float e[EPV];
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-          const float d = v[j * EPV + i] - mc;
-          e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(d, chi, d * clo));
-        }
-        float g;
-        if (EPV == 8) g = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        else g = (e[0] + e[1]) + (e[2 % EPV] + e[3 % EPV]);
-        acc += (double)g;
-      }
-    }
-    out_s = block_sum_d(acc, sm);
+    // this thread's sum relative to 2^((mc) log2(e)/T): undo the offset's
+    // rounding (m cf is exact in fp64), then move from m to mc at the exact scale
+    double mine = 0.0;
+    if (st.m != -INFINITY && mc != -INFINITY)
+      mine = st.s * exp2((double)st.off - (double)st.m * (double)cf + ((double)st.m - (double)mc) * cd);
+    else if (st.s != st.s)
+      mine = st.s;
+    out_s = block_sum_d(mine, sm);
   }
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     Partial* dst = &P.part[row * P.CPR + c];
     cst64(&dst->s, (uint64_t)__double_as_longlong(out_s));
     cst64(&dst->m_amax, (uint64_t)__float_as_uint(mc) | ((uint64_t)(uint32_t)out_amax << 32));
@@ -994,7 +1078,7 @@ __device__ void k3_chunk(const Params& P, int b, int c3, Smem& sm) {
   if (!is_stochastic(temp_of(P, b))) return;  // greedy requests and bad temperatures race nothing
   if (tid == 0) {
     int ok = 1;
-    if (!P.phased) {
+    if (P.sched == SCHED_FUSED) {
       uint32_t spins = 0;
       while (cld32(&P.sync[b].ready) == 0u) {
         __builtin_amdgcn_s_sleep(8);
@@ -1079,13 +1163,10 @@ __device__ void k3_chunk(const Params& P, int b, int c3, Smem& sm) {
 // request's last chunk runs its decision step.
 template <int MODE, bool BF16>
 __device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, Smem& sm) {
-  constexpr int NE = kVecPerThread * (BF16 ? 8 : 4);
   const int64_t row = (int64_t)b * P.R + r;
-  float v[NE];
-  k1_load<BF16>(P, row, c, v);
-  float tm = v[0];
-#pragma unroll
-  for (int i = 1; i < NE; ++i) tm = fmaxf(tm, v[i]);
+  const int64_t start = (int64_t)c * P.CH;
+  u32x4 raw0[kVecPerThread];
+  k1_issue<BF16>(P, row * P.lstride + start, (int)min((int64_t)P.CH, (int64_t)P.V - start), raw0);
   const float T = temp_of(P, b);
   bool need = true;
   if (MODE == MODE_CHAIN) {
@@ -1095,11 +1176,13 @@ __device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, Sme
   } else if (MODE == MODE_TREE) {
     need = isfinite(T);
   }
-  if (need) {
-    k1_chunk_stats<BF16, MODE == MODE_ROWS>(P, row, c, T, v, tm, sm);
-    if (MODE != MODE_ROWS && threadIdx.x < 64 && is_stochastic(T)) {
+  const bool stoch = uniform_i(is_stochastic(T));
+  if (uniform_i(need)) {
+    if (stoch) k1_item_stats<BF16, true, MODE == MODE_ROWS>(P, row, c, T, raw0, sm);
+    else k1_item_stats<BF16, false, false>(P, row, c, T, raw0, sm);
+    if (MODE != MODE_ROWS && threadIdx.x < 64 && stoch) {
       const int lane = threadIdx.x;
-      const int64_t start = (int64_t)c * P.CH, stop = min(start + P.CH, (int64_t)P.V);
+      const int64_t stop = min(start + P.CH, (int64_t)P.V);
       int tok = -1, slot = -1;
       if (MODE == MODE_CHAIN) {
         if (lane == 0 && r < P.k) {
@@ -1118,7 +1201,7 @@ __device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, Sme
       }
     }
   }
-  if (P.phased) return;
+  if (P.sched == SCHED_PHASED) return;
   if (threadIdx.x == 0) {
     wait_mem();  // this wave's partial and gathers are complete
     const uint32_t old = atomic_add_relaxed(&P.sync[b].k1_count, 1u);
@@ -1177,6 +1260,7 @@ __global__ __launch_bounds__(kWG) void fused_kernel(Params P) {
   run_item<MODE, BF16>(P, blockIdx.x, sm);
 }
 
+// Phased schedule, K1: one item per workgroup.
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG) void k1_kernel(Params P) {
   __shared__ Smem sm;
@@ -1219,7 +1303,7 @@ struct Shape {
 
 static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   Shape s;
-  s.CH = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
+  s.CH = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG * kSubChunks;
   s.CPR = (int)((V + s.CH - 1) / s.CH);
   s.C3 = races ? (int)((V + kK3Chunk - 1) / kK3Chunk) : 0;
   s.gat_off = kDataOffset;
@@ -1234,7 +1318,7 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
 // workgroups per CU of each fused kernel (slot = mode * 2 + bf16).
 struct DeviceInfo {
   std::atomic<int> cu{0};
-  std::atomic<int> occ[6];
+  std::atomic<int> occ[12];  // fused kernels (slots 0..5), K1 kernels (slots 6..11)
 };
 static DeviceInfo g_dev[64];
 
@@ -1261,7 +1345,7 @@ static void select_kernels(int mode, bool bf16, KernelFn& fused, KernelFn& k1, K
   }
 }
 
-static sv_status device_info(KernelFn fused, int slot, int& cu, int& occ) {
+static sv_status device_info(KernelFn kernel, int slot, int& cu, int& occ) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_ERR_LAUNCH;
   cu = g_dev[dev].cu.load();
@@ -1269,7 +1353,7 @@ static sv_status device_info(KernelFn fused, int slot, int& cu, int& occ) {
   if (cu > 0 && occ > 0) return SV_OK;
   int c = 0, o = 0;
   if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SV_ERR_LAUNCH;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, (const void*)fused, kWG, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, (const void*)kernel, kWG, 0) != hipSuccess)
     return SV_ERR_LAUNCH;
   if (c <= 0 || o <= 0) return SV_ERR_LAUNCH;
   g_dev[dev].cu.store(c);
@@ -1303,16 +1387,16 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   const int64_t n_tickets = (int64_t)P.bs * (P.n1r + P.C3);
   if (n_tickets <= 0 || n_tickets > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   P.n_tickets = (int32_t)n_tickets;
-  // Schedule: fused only on request for now; the phased schedule measures
-  // faster on the shapes benchmarked so far.
-  P.phased = (P.flags & SV_FLAG_FUSED) ? 0 : 1;
+  // Schedule: split unless another one is asked for (it measures fastest on
+  // the shapes benchmarked so far).
+  P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : (P.flags & SV_FLAG_PHASED) ? SCHED_PHASED : SCHED_SPLIT;
   KernelFn fused, k1, k2, k3;
   const bool bf16 = P.dtype == SV_BF16;
   select_kernels(P.mode, bf16, fused, k1, k2, k3);
-  if (P.phased) {
+  if (P.sched != SCHED_FUSED) {
     P.lag = 0;
     hipLaunchKernelGGL(k1, dim3((unsigned)((int64_t)P.bs * P.n1r)), dim3(kWG), 0, stream, P);
-    hipLaunchKernelGGL(k2, dim3((unsigned)P.bs), dim3(kWG), 0, stream, P);
+    if (P.sched == SCHED_PHASED) hipLaunchKernelGGL(k2, dim3((unsigned)P.bs), dim3(kWG), 0, stream, P);
     if (P.C3 > 0) hipLaunchKernelGGL(k3, dim3((unsigned)(P.bs * P.C3)), dim3(kWG), 0, stream, P);
   } else {
     int cu = 0, occ = 0;
@@ -1359,6 +1443,13 @@ const char* sv_status_string(sv_status s) {
 
 static bool dtype_ok(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
 
+static const uint32_t kKnownFlags = SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_SPLIT;
+// At most one schedule bit.
+static bool one_schedule(uint32_t flags) {
+  const uint32_t s = flags & (SV_FLAG_PHASED | SV_FLAG_FUSED | SV_FLAG_SPLIT);
+  return (s & (s - 1)) == 0;
+}
+
 size_t sv_chain_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab, sv_dtype dt) {
   if (batch < 1 || batch > SV_MAX_BATCH || max_draft < 0 || max_draft > SV_MAX_DRAFT || vocab < 1 ||
       vocab > SV_MAX_VOCAB || !dtype_ok(dt))
@@ -1395,8 +1486,8 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
     return SV_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
   if (d->draft_kind != SV_DRAFT_PROBS && d->draft_kind != SV_DRAFT_ONEHOT) return SV_ERR_UNSUPPORTED;
-  if (d->flags & ~(SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
-  if ((d->flags & SV_FLAG_PHASED) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_INVALID_ARGUMENT;
+  if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
+  if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
   if (d->logits == nullptr || d->temperature == nullptr || d->seed == nullptr || d->accept_len == nullptr ||
       d->tokens == nullptr)
     return SV_ERR_INVALID_ARGUMENT;
@@ -1439,8 +1530,8 @@ sv_status sv_verify_tree(const sv_tree_desc* d, void* ws, size_t ws_bytes, void*
       d->vocab < 1 || d->vocab > SV_MAX_VOCAB)
     return SV_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
-  if (d->flags & ~(SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
-  if ((d->flags & SV_FLAG_PHASED) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_INVALID_ARGUMENT;
+  if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
+  if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
   if (d->logits == nullptr || d->node_tokens == nullptr || d->parent == nullptr || d->temperature == nullptr ||
       d->seed == nullptr || d->accept_len == nullptr || d->accept_path == nullptr || d->tokens == nullptr)
     return SV_ERR_INVALID_ARGUMENT;

@@ -89,7 +89,11 @@ def test_chain_argument_validation(field, value, code):
 
 
 def test_schedule_flags_are_exclusive():
-    assert _call_chain(_chain_desc(flags=sv.FLAG_PHASED | sv.FLAG_FUSED)) == 1
+    for f in (sv.FLAG_PHASED | sv.FLAG_FUSED, sv.FLAG_PHASED | sv.FLAG_SPLIT, sv.FLAG_FUSED | sv.FLAG_SPLIT,
+              sv.FLAG_PHASED | sv.FLAG_FUSED | sv.FLAG_SPLIT):
+        assert _call_chain(_chain_desc(flags=f)) == 1
+        d = _tree_desc(flags=f)
+        assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 1
 
 
 def test_chain_null_descriptor_and_workspace_checks():

@@ -140,18 +140,26 @@ def test_tree_workload(dev, greedy):
 
 
 # ------------------------------------------------- schedules and determinism
-def test_fused_and_phased_schedules_are_bit_identical(dev):
+def test_all_schedules_are_bit_identical(dev):
     inp = workloads.chain_bf16_mixed(1, bs=24)
-    _, a = run_chain(inp, dev, flags=sv.FLAG_FUSED)
-    _, b = run_chain(inp, dev, flags=sv.FLAG_PHASED)
-    for k in ("accept_len", "tokens", "status"):
-        np.testing.assert_array_equal(a[k], b[k])
-    np.testing.assert_array_equal(a["p_draft"].view(np.int64), b["p_draft"].view(np.int64))
+    ref = None
+    for flags in (sv.FLAG_PHASED, sv.FLAG_FUSED, sv.FLAG_SPLIT, 0):
+        _, out = run_chain(inp, dev, flags=flags)
+        if ref is None:
+            ref = out
+            continue
+        for k in ("accept_len", "tokens", "status"):
+            np.testing.assert_array_equal(out[k], ref[k])
+        np.testing.assert_array_equal(out["p_draft"].view(np.int64), ref["p_draft"].view(np.int64))
     t = workloads.tree_fp32(1, bs=12)
-    _, c = run_tree(t, dev, flags=sv.FLAG_FUSED)
-    _, d = run_tree(t, dev, flags=sv.FLAG_PHASED)
-    for k in ("accept_len", "tokens", "status", "accept_path"):
-        np.testing.assert_array_equal(c[k], d[k])
+    ref = None
+    for flags in (sv.FLAG_PHASED, sv.FLAG_FUSED, sv.FLAG_SPLIT):
+        _, out = run_tree(t, dev, flags=flags)
+        if ref is None:
+            ref = out
+            continue
+        for k in ("accept_len", "tokens", "status", "accept_path"):
+            np.testing.assert_array_equal(out[k], ref[k])
 
 
 def test_fp64_race_flag_gives_the_same_tokens(dev):
@@ -380,12 +388,21 @@ def test_row_stats_parity(dev, dtype):
     for V in (1, 7, 4096, 8192, 10000, 128256):
         rows = 12
         l = (rng.standard_normal((rows, V)) * 3).astype(np.float32)
+        temp = rng.choice([0.0, 0.3, 1.0, 4.0], size=rows).astype(np.float32)
         if V > 10:
             l[0, 5] = l[0].max() + 1
             l[0, V - 1] = l[0, 5]            # an exact tie: the first index wins
             l[1, ::3] = -np.inf
+            # far-negative and far-positive rows at small temperatures: large
+            # scaled offsets (2^(-l/T) overflows fp32) in both directions
+            l[2] -= 60.0
+            l[3] += 60.0
+            temp[2], temp[3] = 0.05, 0.01
+            # -inf everywhere but the last entry
+            l[4, :] = -np.inf
+            l[4, V - 1] = -3.0
+            temp[4] = 0.05
         logits = workloads.f32_to_bf16_bits(l) if dtype == "bf16" else l
-        temp = rng.choice([0.0, 0.3, 1.0, 4.0], size=rows).astype(np.float32)
         m, am, S, st = oracle.row_stats(logits, temp)
         out = _np(sv.row_stats(_t(logits, dev), _t(temp, dev)))
         torch.cuda.synchronize()
