@@ -107,7 +107,7 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated over the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", choices=["auto", "phased", "fused", "split"], default="auto",
+    ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
                     help="library schedule (auto: the library's default for the shape)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -135,7 +135,7 @@ def main():
             return torch.from_numpy(a.view(np.int64)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    flags = {"auto": 0, "phased": sv.FLAG_PHASED, "fused": sv.FLAG_FUSED, "split": sv.FLAG_SPLIT}[args.schedule]
+    flags = {"auto": 0, "phased": sv.FLAG_PHASED, "fused": sv.FLAG_FUSED}[args.schedule]
     ws = sv.Workspace(1 << 20, dev)
     calls = []
     for inp in inputs:

@@ -100,15 +100,12 @@ enum {
   SV_REQ_INTERNAL = 5          /* internal scheduling timeout; re-initialise the workspace */
 };
 
-/* Option bits for the `flags` fields.  At most one schedule bit (PHASED,
- * FUSED, SPLIT) may be set (else SV_ERR_INVALID_ARGUMENT); without one the
- * library picks the schedule it measures fastest.  All schedules give
- * bit-identical results. */
-#define SV_FLAG_PHASED 1u    /* three stream-ordered launches: row statistics, decisions, sampling */
+/* Option bits for the `flags` fields.  At most one schedule bit (PHASED or
+ * FUSED) may be set (else SV_ERR_INVALID_ARGUMENT); without one the library
+ * picks the schedule it measures fastest.  Both give bit-identical results. */
+#define SV_FLAG_PHASED 1u    /* two stream-ordered launches: row statistics, then decisions and sampling */
 #define SV_FLAG_FP64_RACE 2u /* evaluate every sampling race entirely in fp64 (slow; a test aid) */
-#define SV_FLAG_FUSED 4u     /* one launch, sampling work interleaved with the row-statistics stream */
-#define SV_FLAG_SPLIT 8u     /* two launches: row statistics, each request's decisions run by the workgroup
-                                that finishes its rows; then sampling */
+#define SV_FLAG_FUSED 4u     /* one launch: the decision/sampling workgroups wait for their rows' statistics */
 
 typedef struct {
   int32_t batch;              /* bs, 1..SV_MAX_BATCH */

@@ -8,34 +8,37 @@
 // the special cases of the same rule.  The public contract is in
 // include/specverify.h.
 //
-// Work decomposition.  One call is three kinds of work item:
-//   K1  a streaming chunk of one logit row: max, first argmax and
-//       sum exp((l - m)/T) of CH consecutive entries (16-byte nontemporal
+// Work decomposition.  One call is two kinds of work item:
+//   K1  a streaming segment of one logit row: max, first argmax and
+//       sum exp((l - m)/T) over a run of sub-chunks (16-byte nontemporal
 //       loads, wave shuffles, a cross-wave LDS reduction).  Almost all HBM
-//       bytes are read here, once.
-//   K2  the per-request decision step, run by the workgroup that finishes a
-//       request's last K1 chunk: combine the row partials in fp64, gather
-//       p (and q) at the draft ids, draw the Philox coins, find the first
-//       rejection (chain) or walk the tree, write the outputs, and publish
-//       the request's sampling job.
-//   K3  a chunk of one sampling race (residual, one-hot residual or bonus)
-//       over 4096 vocabulary ids: Philox noise, fp32 keys with rigorous
-//       error bounds, and a short list of near-maximal candidates; the
-//       workgroup that finishes a request's last K3 chunk re-evaluates the
-//       candidates in fp64 and writes the emitted token.
-// The fused schedule runs everything in one launch with one work item per
-// workgroup.  Item order interleaves the K1 chunks of request g with the K3
-// chunks of request g - L, so the ALU-heavy races of early requests overlap
-// the HBM stream of later ones, and a launch is paid once.  A K3 item waits
-// (bounded, about a second, then SV_REQ_INTERNAL) for its request's K2.
-// Workgroups are dispatched in index order, so every K1 item a waiter
-// depends on (a smaller index) is already running or finished: the waits
-// always end.  There is no global counter: per-request counters and flags
-// are reset by their last user, so the workspace is ready for the next call
-// without any reset pass.  The split schedule is two stream-ordered
-// launches: K1 (each request's last workgroup running its K2, as above),
-// then K3 with nothing left to wait for.  The phased schedule runs K1, K2
-// and K3 as three launches.  All three give bit-identical results.
+//       bytes are read here, once.  The rows' sub-chunks, flattened, are
+//       split evenly over a fixed number of workgroups that are all
+//       resident at once, so the stream ends in one round with no tail; a
+//       workgroup whose range crosses a row boundary writes one partial per
+//       row it touches.
+//   K23 one chunk of 2048 vocabulary ids of one request's sampling race.
+//       The workgroup first runs the request's decision step itself (K2):
+//       combine the row partials in fp64, take p (and q) at the draft ids
+//       that K1 gathered, draw the Philox coins, find the first rejection
+//       (chain) or walk the tree.  Every chunk of the request computes the
+//       same decision from the same few hundred bytes, so no workgroup
+//       waits for another's result; chunk 0 writes the request's outputs.
+//       Then (K3) it races its ids: one exp per id gives certified bounds
+//       on the id's weight; only ids whose weight could still beat a
+//       certified lower bound of some key (few, for any peaked
+//       distribution) are compacted in LDS and pay for Philox noise and the
+//       key; the chunk's near-maximal keys are re-evaluated in fp64 and its
+//       best (key, id) recorded.  The last chunk of the request to finish
+//       takes the best record and writes the emitted token.
+// The phased schedule is two stream-ordered launches (K1, then K23).  The
+// fused schedule is one launch: the K23 items come after every K1 item in
+// dispatch order and wait (bounded, about a second, then SV_REQ_INTERNAL)
+// until their request's K1 segments are counted; workgroups are dispatched
+// in index order, so the K1 items they wait for are running or done.
+// Per-request counters are reset by their last user, so the workspace is
+// ready for the next call without any reset pass.  Both schedules give
+// bit-identical results.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -53,20 +56,25 @@ constexpr int kWaves = kWG / 64;
 #ifndef SV_K1_VEC
 #define SV_K1_VEC 2
 #endif
-#ifndef SV_K1_SUBS
-#define SV_K1_SUBS 8
+#ifndef SV_K1_SLOTS
+#define SV_K1_SLOTS (256 * 7)
+#endif
+#ifndef SV_K1_ROUNDS
+#define SV_K1_ROUNDS 1
 #endif
 constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a K1 sub-chunk
-constexpr int kSubChunks = SV_K1_SUBS;          // sub-chunks per K1 work item (register double buffer)
-constexpr int kK3Groups = 4;                    // groups of 4 vocabulary ids per thread in a K3 chunk
-constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 4096 ids per K3 chunk
-constexpr int kCandMax = 8;                     // candidates kept per K3 chunk
-constexpr int kMergeCandMax = 256;              // candidates re-evaluated per race
+// K1 workgroups per call: an MI355X holds 256 CUs x 7 of them at once (71
+// VGPRs), so the stream is one round.
+constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
+constexpr int kK3Groups = 2;                    // groups of 4 vocabulary ids per thread in a sampling chunk
+constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 2048 ids per sampling chunk
+constexpr int kList = 512;                      // race entries a chunk compacts (more: every id is raced)
+constexpr int kCandMax = 64;                    // candidates a race's merge re-keys in fp64 (more: whole row)
 constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second)
 
 enum { MODE_CHAIN = 0, MODE_TREE = 1, MODE_ROWS = 2 };
 enum { JOB_NONE = 0, JOB_P = 1, JOB_RESID = 2, JOB_EXCL = 3 };
-enum { SCHED_FUSED = 0, SCHED_PHASED = 1, SCHED_SPLIT = 2 };
+enum { SCHED_FUSED = 0, SCHED_PHASED = 1 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -77,35 +85,36 @@ struct Ctrl {
   uint32_t pad[63];
 };
 struct Sync {
-  uint32_t k1_count;  // K1 chunks of the request finished in this call (reset by the K2 runner)
-  uint32_t k3_count;  // K3 chunks of the request finished in this call (reset by the last one)
-  uint32_t ready;     // 1 once the request's job is published (reset by the last K3 chunk)
-  uint32_t pad;
+  uint32_t k1_count;  // K1 segments of the request (row, in row-statistics calls) done in this call
+  uint32_t k3_count;  // sampling chunks of the request done in this call
+  uint32_t pad[2];    // both counters are reset to 0 by their last user
 };
 // Target logit (and draft probability) at a draft token, gathered by the K1
-// chunk that holds it: chain slot r = row r's draft, tree slot n = node n's
+// segment that holds it: chain slot r = row r's draft, tree slot n = node n's
 // token in its parent's row.
 struct Gather {
   uint32_t l;         // fp32 bits of the logit
   uint32_t q;         // fp32 bits of q at the draft (chain, draft probabilities)
 };
 struct Partial {
-  uint64_t s;         // bits of the chunk sum of 2^((l - m_c) log2(e)/T) (fp64), or a NaN flag for greedy rows
-  uint64_t m_amax;    // bits of the chunk max (fp32, low half) and the smallest index attaining it (high half)
+  uint64_t s;         // bits of the segment sum of 2^((l - m_c) log2(e)/T) (fp64), or a NaN flag for greedy rows
+  uint64_t m_amax;    // bits of the segment max (fp32, low half) and the smallest index attaining it (high half)
 };
-struct Job {
-  int32_t kind, row, qrow, r, n_excl, out_slot;
-  float m, c_hi, c_lo, inv_s;
-  double s, t;
-  int32_t excl[SV_MAX_NODES];
+// A sampling chunk's result: its largest certified key lower bound L_c and
+// its candidates, the ids whose key upper bound reaches L_c (with the
+// logit and q, so that the merge can key them exactly without loads).
+constexpr int kRecCand = 4;
+struct K3Cand {
+  int32_t y;
+  float hi;           // upper bound of the key
+  float l, q;         // target logit and draft probability at y
 };
 struct K3Rec {
-  float lo;           // max over the chunk of the keys' lower bounds
-  int32_t count;      // candidates listed
-  float ovf_hi;       // if more than kCandMax qualified: the largest upper bound among them, else -inf
+  float lo;           // L_c (-inf: no id of the chunk has positive weight)
+  float ovf;          // the largest upper bound among candidates left out (-inf: none)
+  int32_t count;      // candidates listed, <= kRecCand
   int32_t pad;
-  int32_t idx[kCandMax];
-  float hi[kCandMax];
+  K3Cand cand[kRecCand];
 };
 
 constexpr size_t kSyncOffset = 256;
@@ -136,10 +145,16 @@ struct Params {
   Ctrl* ctrl;
   Sync* sync;
   Gather* gat;        // [bs][SV_MAX_NODES]
-  Job* jobs;
-  Partial* part;
-  K3Rec* k3;
-  int32_t CH, CPR, n1r, C3, lag, n_tickets, sched;
+  Partial* part;      // [bs*R][CPR]
+  K3Rec* k3;          // [bs][C3]
+  int64_t F;          // sub-chunks of all rows, flattened
+  double Finv;        // 1 / F
+  int32_t SUB;        // entries per K1 sub-chunk
+  int32_t nsub;       // sub-chunks per row
+  int32_t G;          // K1 workgroups
+  int32_t CPR;        // partial slots per row
+  int32_t C3;         // sampling chunks per request
+  int32_t sched;
   uint32_t flags;
 };
 
@@ -240,6 +255,17 @@ __device__ __forceinline__ void cst_f64(double* p, double v) { cst64(p, (uint64_
 __device__ __forceinline__ float cld_f32(const float* p) { return __uint_as_float(cld32(p)); }
 __device__ __forceinline__ double cld_f64(const double* p) { return __longlong_as_double((long long)cld64(p)); }
 __device__ __forceinline__ int32_t cld_i32(const int32_t* p) { return (int32_t)cld32(p); }
+// Loads of data that an earlier launch wrote (COH = false: plain, cached
+// loads; a kernel boundary makes the writes visible) or that other
+// workgroups of the same launch wrote (COH = true).
+template <bool COH>
+__device__ __forceinline__ uint64_t ld64(const void* p) {
+  return COH ? cld64(p) : *(const uint64_t*)p;
+}
+template <bool COH>
+__device__ __forceinline__ uint32_t ld32(const void* p) {
+  return COH ? cld32(p) : *(const uint32_t*)p;
+}
 __device__ __forceinline__ void cst_i32(int32_t* p, int32_t v) { cst32(p, (uint32_t)v); }
 // Wait until this wave's memory operations have completed.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -252,12 +278,12 @@ __device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 
-// The scalar part of a published job, read once with coherent loads.
-struct JobView {
-  int kind, row, qrow, r, n_excl, out_slot;
-  float m, c_hi, c_lo, inv_s;
-  double s, t;
-  const int32_t* excl;  // read with coherent loads
+// A request's sampling job: the result of its decision step (in LDS).
+struct Job {
+  int kind, row, qrow, r, out_slot, n_excl;
+  float m, c_hi, c_lo, inv_s;  // row max; log2(e)/T as hi + lo; 1/S rounded
+  double s, t;                  // S = sum exp((l - m)/T); T
+  int excl[SV_MAX_NODES];       // ids removed from p (JOB_EXCL)
 };
 
 // Shared memory of one workgroup (every role reuses it).
@@ -265,8 +291,9 @@ struct Smem {
   float red_f[kWaves];
   int red_i[kWaves];
   double red_d[kWaves];
+  uint64_t red_u[kWaves];
   int flag;
-  uint32_t ticket;
+  float l0;
   // per-row results of the decision step
   float rm[SV_MAX_NODES];
   int ramax[SV_MAX_NODES];
@@ -279,14 +306,21 @@ struct Smem {
   int tok[SV_MAX_NODES];
   int xs[SV_MAX_NODES];
   int path[SV_MAX_NODES];
-  int a, kb, status, cur, len, emit;
-  // race candidates
-  JobView job;
+  int a, kb, status, len, emit;
+  Job job;
+  // sampling race of one chunk
+  int nlist;
+  int list_y[kList];
+  float list_whi[kList];  // weight upper bound, then key upper bound
+  float list_wlo[kList];
+  float list_l[kList];    // the id's logit and q, for the fp64 key
+  float list_q[kList];
   int ncand;
-  int cand_y[kMergeCandMax];
-  double cand_key[kMergeCandMax];
+  int cand_y[kCandMax];
+  float cand_l[kCandMax];
+  float cand_q[kCandMax];
   float cand_h[kCandMax];
-  int overflow;
+  double cand_key[kCandMax];
 };
 
 __device__ __forceinline__ float block_max(float v, Smem& sm) {
@@ -298,6 +332,20 @@ __device__ __forceinline__ float block_max(float v, Smem& sm) {
   float r = sm.red_f[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) r = fmaxf(r, sm.red_f[w]);
+  return r;
+}
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, Smem& sm) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sm.red_u[wave] = v;
+  __syncthreads();
+  uint64_t r = sm.red_u[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = sm.red_u[w] > r ? sm.red_u[w] : r;
   return r;
 }
 __device__ __forceinline__ int block_min_i(int v, Smem& sm) {
@@ -337,10 +385,10 @@ __device__ __forceinline__ int chain_kb(const Params& P, int b, int& xi) {
 }
 
 // ===================================================================== K1
-// Streaming statistics of one work item: kSubChunks consecutive sub-chunks of
-// one row, each 256 threads x kVecPerThread nontemporal 16-byte loads
-// (consecutive lanes on consecutive 16-byte pieces).  The loads of sub-chunk
-// s+1 are in flight while sub-chunk s is reduced (a register double buffer).
+// Streaming statistics of one segment: consecutive sub-chunks of one row,
+// each 256 threads x kVecPerThread nontemporal 16-byte loads (consecutive
+// lanes on consecutive 16-byte pieces).  The loads of sub-chunk s+1 are in
+// flight while sub-chunk s is reduced (a register double buffer).
 // Per sub-chunk a thread first takes the max of its entries.  Stochastic
 // rows then add 2^(l c - o) over the entries, with c = log2(e)/T rounded to
 // fp32 and o = fl(m c) the fp32 offset of the thread's running max m: one
@@ -351,7 +399,7 @@ __device__ __forceinline__ int chain_kb(const Params& P, int b, int& xi) {
 // 2^((l - m) log2(e)/T) is evaluated with a relative exponent error of at
 // most 2^-24 from c plus the fma's rounding.  Greedy rows (and every row of
 // a row-statistics call) keep the first index of the running max and a NaN
-// flag.  One block reduction per item gives the item's (max, first argmax,
+// flag.  One block reduction per segment gives its (max, first argmax,
 // sum), in a fixed order (bit-reproducible).
 template <bool BF16>
 __device__ __forceinline__ void k1_issue(const Params& P, int64_t elem0, int n, u32x4* raw) {
@@ -455,15 +503,17 @@ __device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K
   }
 }
 
-// Streams the item's sub-chunks from raw0 (the first sub-chunk, already in
-// flight) and writes the item's partial.
+// Streams sub-chunks [s0, s1) of row `row` (the first already in flight in
+// raw0) and writes the segment's partial to slot `slot` of the row.
 template <bool BF16, bool STOCH, bool NEED_AMAX>
-__device__ __forceinline__ void k1_item_stats(const Params& P, int64_t row, int c, float T, u32x4* raw0, Smem& sm) {
+__device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s0, int s1, int slot, float T,
+                                             u32x4* raw0, Smem& sm) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NV = kVecPerThread * EPV;  // entries per thread per sub-chunk
   constexpr int SUB = NV * kWG;            // entries per sub-chunk
-  const int64_t start = (int64_t)c * P.CH;
-  const int n_item = (int)min((int64_t)P.CH, (int64_t)P.V - start);
+  const int64_t start = (int64_t)s0 * SUB;
+  const int n_seg = (int)(min((int64_t)s1 * SUB, (int64_t)P.V) - start);
+  const int nsub = s1 - s0;
   const int64_t elem0 = row * P.lstride + start;
   float cf = 0.f;
   double cd = 0.0;
@@ -481,14 +531,11 @@ __device__ __forceinline__ void k1_item_stats(const Params& P, int64_t row, int 
 #pragma unroll
   for (int j = 0; j < kVecPerThread; ++j) cur[j] = raw0[j];
 #pragma unroll 1
-  for (int sub = 0; sub < kSubChunks; ++sub) {
-    if (sub + 1 < kSubChunks && (sub + 1) * SUB < n_item)
-      k1_issue<BF16>(P, elem0 + (int64_t)(sub + 1) * SUB, n_item - (sub + 1) * SUB, nxt);
-    if (sub * SUB < n_item) {
-      float x[NV];
-      k1_unpack<BF16>(cur, x);
-      k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
-    }
+  for (int sub = 0; sub < nsub; ++sub) {
+    if (sub + 1 < nsub) k1_issue<BF16>(P, elem0 + (int64_t)(sub + 1) * SUB, n_seg - (sub + 1) * SUB, nxt);
+    float x[NV];
+    k1_unpack<BF16>(cur, x);
+    k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) cur[j] = nxt[j];
   }
@@ -503,7 +550,7 @@ __device__ __forceinline__ void k1_item_stats(const Params& P, int64_t row, int 
     const int any_nan = block_min_i(st.nan ? 0 : 1, sm) == 0;
     out_s = any_nan ? __builtin_nan("") : 0.0;
   } else {
-    // this thread's sum relative to 2^((mc) log2(e)/T): undo the offset's
+    // this thread's sum relative to 2^(mc log2(e)/T): undo the offset's
     // rounding (m cf is exact in fp64), then move from m to mc at the exact scale
     double mine = 0.0;
     if (st.m != -INFINITY && mc != -INFINITY)
@@ -513,248 +560,270 @@ __device__ __forceinline__ void k1_item_stats(const Params& P, int64_t row, int 
     out_s = block_sum_d(mine, sm);
   }
   if (threadIdx.x == 0) {
-    Partial* dst = &P.part[row * P.CPR + c];
+    Partial* dst = &P.part[row * P.CPR + slot];
     cst64(&dst->s, (uint64_t)__double_as_longlong(out_s));
     cst64(&dst->m_amax, (uint64_t)__float_as_uint(mc) | ((uint64_t)(uint32_t)out_amax << 32));
   }
 }
 
-// ===================================================================== K2
-// Combine the chunk partials of one row (one wave): max, first argmax,
-// NaN/inf detection, and S = sum_c S_c 2^((m_c - m) log2(e)/T) in fp64.
-__device__ void combine_row(const Params& P, int64_t row, float T, float& m_out, int& amax_out, double& s_out,
-                            int& bad_out) {
-  const int lane = threadIdx.x & 63;
-  float m = -INFINITY;
-  int nanflag = 0;
-  for (int c = lane; c < P.CPR; c += 64) {
-    const Partial* pt = &P.part[row * P.CPR + c];
-    const float pm = __uint_as_float((uint32_t)cld64(&pt->m_amax));
-    const double ps = __longlong_as_double((long long)cld64(&pt->s));
-    m = fmaxf(m, pm);
-    if (ps != ps) nanflag = 1;
-  }
-  m = wave_max(m);
-  int amax = INT32_MAX;
-  double s = 0.0;
-  const bool stoch = is_stochastic(T);
-  const double cd = stoch ? 1.4426950408889634074 / (double)T : 0.0;
-  for (int c = lane; c < P.CPR; c += 64) {
-    const Partial* pt = &P.part[row * P.CPR + c];
-    const uint64_t ma = cld64(&pt->m_amax);
-    const float pm = __uint_as_float((uint32_t)ma);
-    const double ps = __longlong_as_double((long long)cld64(&pt->s));
-    if (pm == m) amax = min(amax, (int)(int32_t)(uint32_t)(ma >> 32));
-    if (stoch && pm != -INFINITY && m != -INFINITY) s += ps * exp2(((double)pm - (double)m) * cd);
-  }
-  amax = wave_min_i(amax);
-  s = wave_sum_d(s);
-  const int any_nan = wave_min_i(nanflag ? 0 : 1) == 0;
-  m_out = m;
-  amax_out = amax;
-  s_out = stoch ? s : __builtin_nan("");
-  bad_out = any_nan || m == INFINITY || m == -INFINITY || (stoch && !(s > 0.0));
+// Split of the flattened sub-chunks f = row * nsub + s over the G K1
+// workgroups: workgroup w takes [floor(w F / G), floor((w + 1) F / G)).
+__host__ __device__ __forceinline__ int64_t k1_range_begin(int64_t w, int64_t F, int64_t G) { return w * F / G; }
+// The workgroup whose range holds sub-chunk f.
+__host__ __device__ __forceinline__ int64_t k1_wg_of(int64_t f, int64_t F, int64_t G) { return ((f + 1) * G - 1) / F; }
+// The same on the device, without a 64-bit integer division: the quotient
+// x / F (x < 2^47) from fp64 with 1/F, then corrected to the exact floor.
+__device__ __forceinline__ int64_t k1_wg_of_dev(const Params& P, int64_t f) {
+  const int64_t x = (f + 1) * (int64_t)P.G - 1;
+  int64_t q = (int64_t)((double)x * P.Finv);
+  if (q * P.F > x) --q;
+  else if ((q + 1) * P.F <= x) ++q;
+  return q;
+}
+// The first workgroup of a row, and the number of segments (partials) the row has.
+__device__ __forceinline__ int64_t k1_first_wg(const Params& P, int64_t row) {
+  return k1_wg_of_dev(P, row * P.nsub);
+}
+__device__ __forceinline__ int k1_segments(const Params& P, int64_t row) {
+  return (int)(k1_wg_of_dev(P, row * P.nsub + P.nsub - 1) - k1_first_wg(P, row) + 1);
 }
 
+// ===================================================================== K2
 // p(y) of a stochastic row in fp64: exp((l - m)/T) / S.
 __device__ __forceinline__ double p_at(double l, float m, double T, double S) { return exp((l - (double)m) / T) / S; }
 
-// Called by thread 0 of a stochastic request once its job is written: wait
-// for the job's stores, then raise the request's ready flag (the last of
-// the request's K3 chunks lowers it again).
-__device__ void publish_job(const Params& P, int b) {
-  wait_mem();
-  cst32(&P.sync[b].ready, 1u);
+// 2^x for x <= 0 (rescale factors of partial sums), within about 2^-22
+// relative: 2^frac(x) by v_exp_f32, scaled by 2^floor(x) exactly.
+__device__ __forceinline__ double exp2_scale(double x) {
+  if (!(x > -1074.0)) return x != x ? x : 0.0;
+  const double n = floor(x);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(x - n)), (int)n);
 }
 
-// Writes the sampling job of request b (thread 0 only).
-__device__ void write_job(const Params& P, int b, int kind, int row, int qrow, int r, int out_slot, float m,
-                          double S, double T) {
-  Job* J = &P.jobs[b];
-  cst_i32(&J->kind, kind);
-  if (kind == JOB_NONE) return;
-  cst_i32(&J->row, row);
-  cst_i32(&J->qrow, qrow);
-  cst_i32(&J->r, r);
-  cst_i32(&J->out_slot, out_slot);
-  cst_f32(&J->m, m);
-  cst_f64(&J->s, S);
-  cst_f64(&J->t, T);
-  float hi, lo;
-  scale_pair(T, hi, lo);
-  cst_f32(&J->c_hi, hi);
-  cst_f32(&J->c_lo, lo);
-  cst_f32(&J->inv_s, (float)(1.0 / S));
-}
-
-__device__ __forceinline__ void k2_rows(const Params& P, int b, Smem& sm) {
-  // Row-statistics mode: the "request" is one row.
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const float T = temp_of(P, b);
-    float m;
-    int amax, bad;
-    double s;
-    combine_row(P, b, T, m, amax, s, bad);
-    if (tid == 0) {
-      if (P.rs_max) P.rs_max[b] = m;
-      if (P.rs_amax) P.rs_amax[b] = amax;
-      if (P.rs_sum) P.rs_sum[b] = s;
-      if (P.rs_status) P.rs_status[b] = bad ? SV_REQ_NONFINITE : SV_REQ_OK;
+// One row's results from its segments' partials, folded by one lane in
+// segment order: max, first argmax, a bad flag (NaN or +inf seen, the row
+// entirely -inf, or S not positive) and, for stochastic rows,
+// S = sum over segments of S_c 2^((m_c - m) log2(e)/T) in fp64.  The loads
+// of up to kRowLoads partials are issued together.
+constexpr int kRowLoads = 4;
+struct RowStats {
+  float m;
+  int amax;
+  double s;
+  bool bad;
+};
+template <bool COH>
+__device__ __forceinline__ RowStats fold_row(const Params& P, int64_t row, float T) {
+  const bool stoch = is_stochastic(T);
+  const double cd = stoch ? 1.4426950408889634074 / (double)T : 0.0;
+  const int cnt = k1_segments(P, row);
+  const Partial* pt = &P.part[row * P.CPR];
+  float m = -INFINITY;
+  int a = INT32_MAX;
+  double s = 0.0;
+  bool nan = false;
+  for (int c0 = 0; c0 < cnt; c0 += kRowLoads) {
+    uint64_t ma[kRowLoads], sb[kRowLoads];
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) {
+      ma[i] = 0xFF800000ull;
+      sb[i] = 0ull;
+      if (c0 + i < cnt) {
+        ma[i] = ld64<COH>(&pt[c0 + i].m_amax);
+        sb[i] = ld64<COH>(&pt[c0 + i].s);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) {
+      if (c0 + i >= cnt) break;
+      const float pm = __uint_as_float((uint32_t)ma[i]);
+      const int pa = (int)(uint32_t)(ma[i] >> 32);
+      const double ps = __longlong_as_double((long long)sb[i]);
+      if (ps != ps) nan = true;
+      if (pm > m) {
+        if (stoch) s = (m == -INFINITY ? 0.0 : s * exp2_scale(((double)m - (double)pm) * cd)) + ps;
+        m = pm;
+        a = pa;
+      } else {
+        if (pm == m) a = min(a, pa);
+        if (stoch && pm != -INFINITY) s += ps * exp2_scale(((double)pm - (double)m) * cd);
+      }
+    }
+  }
+  RowStats r;
+  r.m = m;
+  r.amax = a;
+  r.s = stoch ? s : __builtin_nan("");
+  r.bad = nan || m == INFINITY || m == -INFINITY || (stoch && !(s > 0.0));
+  return r;
+}
+
+// Row-statistics call: the "request" is one row.
+__device__ __forceinline__ void k2_rows(const Params& P, int b, Smem& sm) {
+  if (threadIdx.x == 0) {
+    const RowStats r = fold_row<true>(P, b, temp_of(P, b));
+    if (P.rs_max) P.rs_max[b] = r.m;
+    if (P.rs_amax) P.rs_amax[b] = r.amax;
+    if (P.rs_sum) P.rs_sum[b] = r.s;
+    if (P.rs_status) P.rs_status[b] = r.bad ? SV_REQ_NONFINITE : SV_REQ_OK;
   }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void k2_chain(const Params& P, int b, Smem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Decision step of chain request b, by wave 0 with lane r on row r (and on
+// draft r): every workgroup that samples for the request runs it (its
+// inputs are a few hundred bytes, in L2 after the first), so none waits for
+// another's result; `writer` also writes the request's outputs, except the
+// token that the request's race emits.  Leaves the status and the sampling
+// job (kind JOB_NONE: nothing to sample) in shared memory, behind a barrier.
+template <bool BF16, bool COH>
+__device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const int k = P.k, R = P.R, V = P.V;
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
-  // the gathered target logit and q at this lane's draft (K1 stored them)
-  uint64_t gl = 0;
-  if (wave == 0 && lane < k && !greedy) gl = cld64(&P.gat[(int64_t)b * SV_MAX_NODES + lane]);
-  int xi;
-  const int kb = chain_kb(P, b, xi);
-  const bool bad_id = __ballot(lane < kb && (xi < 0 || xi >= V)) != 0;
-  int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_id ? SV_REQ_BAD_DRAFT_ID : SV_REQ_OK;
-  if (status == SV_REQ_OK) {
-    for (int r = wave; r <= kb; r += kWaves) {
-      float m;
-      int amax, bad;
-      double s;
-      combine_row(P, (int64_t)b * R + r, Tf, m, amax, s, bad);
-      if (lane == 0) {
-        sm.rm[r] = m;
-        sm.ramax[r] = amax;
-        sm.rs[r] = s;
-        sm.rbad[r] = bad;
+  if (tid < 64) {
+    // every load first, none depending on another: the drafts, the gathered
+    // target logit and q at this lane's draft, every row's partials (rows
+    // after the chain's end hold stale values, ignored)
+    int xi;
+    const int kb = chain_kb(P, b, xi);
+    uint64_t gl = 0;
+    if (lane < k) gl = ld64<COH>(&P.gat[(int64_t)b * SV_MAX_NODES + lane]);
+    RowStats rs;
+    rs.m = -INFINITY;
+    rs.amax = 0;
+    rs.s = 1.0;
+    rs.bad = false;
+    if (lane < R) rs = fold_row<COH>(P, (int64_t)b * R + lane, Tf);
+    const bool bad_id = __ballot(lane < kb && (xi < 0 || xi >= V)) != 0;
+    int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_id ? SV_REQ_BAD_DRAFT_ID : SV_REQ_OK;
+    double u = 0.0;
+    if (status == SV_REQ_OK && !greedy && lane < kb) u = coin(P.seed[b], b, lane);
+    if (status == SV_REQ_OK && __ballot(lane <= kb && rs.bad)) status = SV_REQ_NONFINITE;
+    bool accept = false;
+    double p = 0.0;
+    if (status == SV_REQ_OK && lane < kb) {
+      if (greedy) {
+        accept = (xi == rs.amax);
+        p = accept ? 1.0 : 0.0;
+      } else {
+        p = p_at((double)__uint_as_float((uint32_t)gl), rs.m, T, rs.s);
+        if (P.draft_kind == SV_DRAFT_ONEHOT) {
+          accept = u < p;
+        } else {
+          const double q = (double)__uint_as_float((uint32_t)(gl >> 32));
+          accept = (q <= 0.0) ? p > 0.0 : u * q < p;
+        }
       }
     }
-  }
-  __syncthreads();
-  if (status == SV_REQ_OK)
-    for (int r = 0; r <= kb; ++r)
-      if (sm.rbad[r]) status = SV_REQ_NONFINITE;
-  if (status == SV_REQ_OK && wave == 0 && lane < kb) {
-    const int64_t row = (int64_t)b * R + lane;
-    double p;
-    (void)row;
-    if (greedy) {
-      p = (xi == sm.ramax[lane]) ? 1.0 : 0.0;
-    } else {
-      p = p_at((double)__uint_as_float((uint32_t)gl), sm.rm[lane], T, sm.rs[lane]);
-      sm.u[lane] = coin(P.seed[b], b, lane);
-      if (P.draft_kind == SV_DRAFT_PROBS) sm.qx[lane] = (double)__uint_as_float((uint32_t)(gl >> 32));
-    }
-    sm.px[lane] = p;
+    const uint64_t rejected = __ballot(status == SV_REQ_OK && lane < kb && !accept);
+    const int a = status != SV_REQ_OK ? 0 : rejected ? (int)__builtin_ctzll(rejected) : kb;
     sm.xs[lane] = xi;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    if (status == SV_REQ_OK) {
-      for (int i = 0; i < kb; ++i) {
-        bool accept;
-        if (greedy) accept = (sm.xs[i] == sm.ramax[i]);
-        else if (P.draft_kind == SV_DRAFT_ONEHOT) accept = sm.u[i] < sm.px[i];
-        else if (sm.qx[i] <= 0.0) accept = sm.px[i] > 0.0;
-        else accept = sm.u[i] * sm.qx[i] < sm.px[i];
-        if (!accept) break;
-        ++a;
+    sm.px[lane] = p;
+    sm.ramax[lane] = rs.amax;
+    // lane a holds the emitted row's statistics and the draft it rejected
+    if (lane == a) {
+      sm.a = a;
+      sm.kb = kb;
+      sm.status = status;
+      Job& J = sm.job;
+      J.kind = JOB_NONE;
+      if (status == SV_REQ_OK && !greedy) {
+        J.kind = (a < kb) ? (P.draft_kind == SV_DRAFT_PROBS ? JOB_RESID : JOB_EXCL) : JOB_P;
+        J.row = b * R + a;
+        J.qrow = b * k + a;
+        J.r = a;
+        J.out_slot = b * R + a;
+        J.m = rs.m;
+        J.s = rs.s;
+        J.t = T;
+        scale_pair(T, J.c_hi, J.c_lo);
+        J.inv_s = (float)(1.0 / rs.s);
+        J.n_excl = (J.kind == JOB_EXCL) ? 1 : 0;
+        J.excl[0] = xi;
       }
     }
-    sm.a = a;
-    sm.kb = kb;
-    sm.status = status;
-    P.accept_len[b] = a;
-    if (P.status) P.status[b] = status;
-    if (status == SV_REQ_OK && !greedy) {
-      const int kind = (a < kb) ? (P.draft_kind == SV_DRAFT_PROBS ? JOB_RESID : JOB_EXCL) : JOB_P;
-      write_job(P, b, kind, b * R + a, b * k + a, a, b * R + a, sm.rm[a], sm.rs[a], T);
-      cst_i32(&P.jobs[b].n_excl, kind == JOB_EXCL ? 1 : 0);
-      if (kind == JOB_EXCL) cst_i32(&P.jobs[b].excl[0], sm.xs[a]);
-    } else {
-      write_job(P, b, JOB_NONE, 0, 0, 0, 0, 0.f, 1.0, 1.0);
-    }
   }
   __syncthreads();
+  if (!writer) return;
   const int a = sm.a;
+  if (tid == 0) {
+    P.accept_len[b] = a;
+    if (P.status) P.status[b] = sm.status;
+  }
   for (int i = tid; i < R; i += kWG) {
     int t = -1;
     if (sm.status == SV_REQ_OK) {
       if (i < a) t = sm.xs[i];
       else if (i == a && greedy) t = sm.ramax[a];
-      else if (i == a) continue;  // written by the race merge
+      else if (i == a) continue;  // written by the race's merge
     }
     P.tokens[(int64_t)b * R + i] = t;
   }
   if (P.p_draft)
     for (int i = tid; i < k; i += kWG)
-      P.p_draft[(int64_t)b * k + i] = (sm.status == SV_REQ_OK && i < kb) ? sm.px[i] : __builtin_nan("");
-  __syncthreads();
-  if (tid == 0 && is_stochastic(Tf)) publish_job(P, b);
+      P.p_draft[(int64_t)b * k + i] = (sm.status == SV_REQ_OK && i < sm.kb) ? sm.px[i] : __builtin_nan("");
 }
 
-template <bool BF16>
-__device__ __forceinline__ void k2_tree(const Params& P, int b, Smem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Decision step of tree request b (same contract as decide_chain): lane n
+// on node n's row; p at node n uses its parent's row (by shuffle); thread 0
+// walks the tree.
+template <bool BF16, bool COH>
+__device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const int N = P.R, V = P.V;
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
-  uint32_t gl = 0;  // node lane's token's logit in its parent's row (K1 stored it)
-  if (wave == 0 && lane >= 1 && lane < N && !greedy) gl = cld32(&P.gat[(int64_t)b * SV_MAX_NODES + lane].l);
-  int par = -2, tok = -1;
-  if (lane < N) {
-    par = P.parent[(int64_t)b * N + lane];
-    tok = P.node_tokens[(int64_t)b * N + lane];
-  }
-  bool bad = false;
-  if (lane < N) {
-    if (lane == 0) bad = (par != -1);
-    else bad = (par < 0 || par >= lane || tok < 0 || tok >= V);
-  }
-  for (int j = 1; j < N; ++j) {
-    const int pj = __shfl(par, j, 64), tj = __shfl(tok, j, 64);
-    if (lane >= 1 && lane < N && j > lane && pj == par && tj == tok) bad = true;
-  }
-  const bool bad_tree = __ballot(bad) != 0;
-  int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_tree ? SV_REQ_BAD_TREE : SV_REQ_OK;
-  if (wave == 0 && lane < N) {
-    sm.par[lane] = par;
-    sm.tok[lane] = tok;
-  }
-  if (status == SV_REQ_OK) {
-    for (int r = wave; r < N; r += kWaves) {
-      float m;
-      int amax, badr;
-      double s;
-      combine_row(P, (int64_t)b * N + r, Tf, m, amax, s, badr);
-      if (lane == 0) {
-        sm.rm[r] = m;
-        sm.ramax[r] = amax;
-        sm.rs[r] = s;
-        sm.rbad[r] = badr;
-      }
+  if (tid < 64) {
+    uint32_t gl = 0;  // node lane's token's logit in its parent's row (K1 gathered it)
+    if (lane >= 1 && lane < N) gl = ld32<COH>(&P.gat[(int64_t)b * SV_MAX_NODES + lane].l);
+    int par = -2, tok = -1;
+    if (lane < N) {
+      par = P.parent[(int64_t)b * N + lane];
+      tok = P.node_tokens[(int64_t)b * N + lane];
     }
-  }
-  __syncthreads();
-  if (status == SV_REQ_OK)
-    for (int r = 0; r < N; ++r)
-      if (sm.rbad[r]) status = SV_REQ_NONFINITE;
-  // per-node values: p_parent(tok_n) and the coin drawn when node n is current
-  if (status == SV_REQ_OK && wave == 0 && lane < N) {
-    if (lane >= 1) {
-      const int pn = sm.par[lane];
-      if (greedy) sm.px[lane] = (tok == sm.ramax[pn]) ? 1.0 : 0.0;
-      else sm.px[lane] = p_at((double)__uint_as_float(gl), sm.rm[pn], T, sm.rs[pn]);
+    bool bad = false;
+    if (lane < N) {
+      if (lane == 0) bad = (par != -1);
+      else bad = (par < 0 || par >= lane || tok < 0 || tok >= V);
     }
-    if (!greedy) sm.u[lane] = coin(P.seed[b], b, lane);
+    for (int j = 1; j < N; ++j) {
+      const int pj = __shfl(par, j, 64), tj = __shfl(tok, j, 64);
+      if (lane >= 1 && lane < N && j > lane && pj == par && tj == tok) bad = true;
+    }
+    const bool bad_tree = __ballot(bad) != 0;
+    int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_tree ? SV_REQ_BAD_TREE : SV_REQ_OK;
+    RowStats rs;
+    rs.m = -INFINITY;
+    rs.amax = 0;
+    rs.s = 1.0;
+    rs.bad = false;
+    if (lane < N) rs = fold_row<COH>(P, (int64_t)b * N + lane, Tf);
+    double u = 0.0;
+    if (status == SV_REQ_OK && !greedy && lane < N) u = coin(P.seed[b], b, lane);
+    if (status == SV_REQ_OK && __ballot(lane < N && rs.bad)) status = SV_REQ_NONFINITE;
+    // p_parent(tok_n), from the parent lane's row statistics
+    const int src = (lane >= 1 && lane < N && status == SV_REQ_OK) ? par : 0;
+    const float pm = __shfl(rs.m, src, 64);
+    const double ps = __shfl(rs.s, src, 64);
+    const int pa = __shfl(rs.amax, src, 64);
+    if (lane < N) {
+      sm.par[lane] = par;
+      sm.tok[lane] = tok;
+      sm.ramax[lane] = rs.amax;
+      sm.rm[lane] = rs.m;
+      sm.rs[lane] = rs.s;
+      sm.u[lane] = u;
+      if (lane >= 1 && status == SV_REQ_OK)
+        sm.px[lane] = greedy ? (tok == pa ? 1.0 : 0.0) : p_at((double)__uint_as_float(gl), pm, T, ps);
+    }
+    if (lane == 0) sm.status = status;
   }
   __syncthreads();
   if (tid == 0) {
+    const int status = sm.status;
     int cur = 0, len = 0, emit = -1;
     int kind = JOB_NONE;
     if (status == SV_REQ_OK) {
@@ -768,14 +837,14 @@ __device__ __forceinline__ void k2_tree(const Params& P, int b, Smem& sm) {
             break;
           }
         } else {
-          const double u = sm.u[cur];
+          const double uc = sm.u[cur];
           double acc = 0.0;
           for (int c = cur + 1; c < N; ++c) {
             if (sm.par[c] != cur) continue;
             ++nchild;
             const double pc = sm.px[c];
             acc += pc;
-            if (pc > 0.0 && u < acc) {
+            if (pc > 0.0 && uc < acc) {
               next = c;
               break;
             }
@@ -789,25 +858,34 @@ __device__ __forceinline__ void k2_tree(const Params& P, int b, Smem& sm) {
         cur = next;
       }
     }
-    sm.cur = cur;
     sm.len = len;
     sm.emit = emit;
-    sm.status = status;
-    P.accept_len[b] = len;
-    if (P.status) P.status[b] = status;
+    Job& J = sm.job;
+    J.kind = kind;
     if (kind != JOB_NONE) {
-      write_job(P, b, kind, b * N + cur, 0, cur, b * N + len, sm.rm[cur], sm.rs[cur], T);
+      J.row = b * N + cur;
+      J.qrow = 0;
+      J.r = cur;
+      J.out_slot = b * N + len;
+      J.m = sm.rm[cur];
+      J.s = sm.rs[cur];
+      J.t = T;
+      scale_pair(T, J.c_hi, J.c_lo);
+      J.inv_s = (float)(1.0 / J.s);
       int ne = 0;
       if (kind == JOB_EXCL)
         for (int c = cur + 1; c < N; ++c)
-          if (sm.par[c] == cur) cst_i32(&P.jobs[b].excl[ne++], sm.tok[c]);
-      cst_i32(&P.jobs[b].n_excl, ne);
-    } else {
-      write_job(P, b, JOB_NONE, 0, 0, 0, 0, 0.f, 1.0, 1.0);
+          if (sm.par[c] == cur) J.excl[ne++] = sm.tok[c];
+      J.n_excl = ne;
     }
   }
   __syncthreads();
+  if (!writer) return;
   const int len = sm.len;
+  if (tid == 0) {
+    P.accept_len[b] = len;
+    if (P.status) P.status[b] = sm.status;
+  }
   for (int i = tid; i < N; i += kWG) {
     int node = -1, t = -1;
     bool skip = false;
@@ -817,201 +895,165 @@ __device__ __forceinline__ void k2_tree(const Params& P, int b, Smem& sm) {
         t = sm.tok[node];
       } else if (i == len) {
         if (greedy) t = sm.emit;
-        else skip = true;  // written by the race merge
+        else skip = true;  // written by the race's merge
       }
     }
     P.accept_path[(int64_t)b * N + i] = node;
     if (!skip) P.tokens[(int64_t)b * N + i] = t;
   }
-  __syncthreads();
-  if (tid == 0 && is_stochastic(Tf)) publish_job(P, b);
 }
 
 // ===================================================================== K3
-
-// Thread 0 reads the job (coherent loads) into shared memory; the caller
-// synchronises before the others read it.
-__device__ __forceinline__ void read_job(const Params& P, int b, JobView& v) {
-  const Job* src = &P.jobs[b];
-  v.kind = cld_i32(&src->kind);
-  v.row = cld_i32(&src->row);
-  v.qrow = cld_i32(&src->qrow);
-  v.r = cld_i32(&src->r);
-  v.n_excl = cld_i32(&src->n_excl);
-  v.out_slot = cld_i32(&src->out_slot);
-  v.m = cld_f32(&src->m);
-  v.c_hi = cld_f32(&src->c_hi);
-  v.c_lo = cld_f32(&src->c_lo);
-  v.inv_s = cld_f32(&src->inv_s);
-  v.s = cld_f64(&src->s);
-  v.t = cld_f64(&src->t);
-  v.excl = src->excl;
-}
-
 // Exact fp64 race key of vocabulary id y, the same formula as the
 // definition: w(y) / (-ln U_y).  With use_p the weight is p itself (the
-// fallback for an all-zero residual).
-template <bool BF16>
-__device__ double race_weight_f64(const Params& P, const JobView& J, int y, bool use_p) {
-  const double p = p_at((double)load_logit<BF16>(P, J.row, y), J.m, J.t, J.s);
-  if (use_p) return p;
-  if (J.kind == JOB_RESID) {
-    const double d = p - (double)P.q[(int64_t)J.qrow * P.qstride + y];
-    return d > 0.0 ? d : 0.0;
-  }
-  if (J.kind == JOB_EXCL)
-    for (int i = 0; i < J.n_excl; ++i)
-      if (cld_i32(&J.excl[i]) == y) return 0.0;
-  return p;
+// fallback for an all-zero residual).  l and q are the id's target logit
+// and draft probability (fp32 values, exact in fp64).
+__device__ __forceinline__ bool is_excluded(const Job& J, int y) {
+  for (int i = 0; i < J.n_excl; ++i)
+    if (J.excl[i] == y) return true;
+  return false;
 }
-template <bool BF16>
-__device__ double race_key_f64(const Params& P, const JobView& J, int b, int y, bool use_p) {
-  const double w = race_weight_f64<BF16>(P, J, y, use_p);
-  const double U = uniform_f64(noise_word(P.seed[b], b, J.r, y));
+__device__ __forceinline__ double race_key_from(const Job& J, uint64_t seed, int b, int y, double l, double q,
+                                                bool use_p) {
+  const double p = p_at(l, J.m, J.t, J.s);
+  double w = p;
+  if (!use_p) {
+    if (J.kind == JOB_RESID) w = (p - q > 0.0) ? p - q : 0.0;
+    else if (J.kind == JOB_EXCL && is_excluded(J, y)) w = 0.0;
+  }
+  const double U = uniform_f64(noise_word(seed, b, J.r, y));
   return w / -log(U);
 }
-
 // Pick the larger key, ties to the smaller id.
 __device__ __forceinline__ bool better(double ka, int ya, double kb_, int yb) {
   return ka > kb_ || (ka == kb_ && ya < yb);
 }
 
-// Whole-row race in fp64 by one workgroup: used when the fp32 screen
-// cannot certify its candidate list, and on request.
-template <bool BF16>
-__device__ __forceinline__ int race_row_f64(const Params& P, const JobView& J, int b, Smem& sm) {
-  // an all-zero weight vector falls back to p
-  int any_pos = 0;
-  for (int y = threadIdx.x; y < P.V; y += kWG)
-    if (race_weight_f64<BF16>(P, J, y, false) > 0.0) any_pos = 1;
-  const bool use_p = block_min_i(any_pos ? 0 : 1, sm) == 1;
-  double best_k = -1.0;
-  int best_y = INT32_MAX;
-  for (int y = threadIdx.x; y < P.V; y += kWG) {
-    const double key = race_key_f64<BF16>(P, J, b, y, use_p);
-    if (better(key, y, best_k, best_y)) {
-      best_k = key;
-      best_y = y;
-    }
-  }
+// Block-wide best (key, id) pair.
+__device__ __forceinline__ void block_best(double& k, int& y, Smem& sm) {
   for (int o = 32; o > 0; o >>= 1) {
-    const double ok = __shfl_xor(best_k, o, 64);
-    const int oy = __shfl_xor(best_y, o, 64);
-    if (better(ok, oy, best_k, best_y)) {
-      best_k = ok;
-      best_y = oy;
+    const double ok = __shfl_xor(k, o, 64);
+    const int oy = __shfl_xor(y, o, 64);
+    if (better(ok, oy, k, y)) {
+      k = ok;
+      y = oy;
     }
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) {
-    sm.red_d[wave] = best_k;
-    sm.red_i[wave] = best_y;
+    sm.red_d[wave] = k;
+    sm.red_i[wave] = y;
   }
   __syncthreads();
-  best_k = sm.red_d[0];
-  best_y = sm.red_i[0];
+  k = sm.red_d[0];
+  y = sm.red_i[0];
   for (int w = 1; w < kWaves; ++w)
-    if (better(sm.red_d[w], sm.red_i[w], best_k, best_y)) {
-      best_k = sm.red_d[w];
-      best_y = sm.red_i[w];
+    if (better(sm.red_d[w], sm.red_i[w], k, y)) {
+      k = sm.red_d[w];
+      y = sm.red_i[w];
     }
+}
+
+// Exact fp64 key of one id, kept out of line for the whole-row fallback
+// below: inlined into that loop, its fp64 constants would be held in
+// registers for the whole kernel.
+__device__ __attribute__((noinline)) double race_key_cold(double l, double q, double m, double T, double S,
+                                                          int resid, int use_p, uint64_t seed, int b, int r, int y) {
+  const double p = exp((l - m) / T) / S;
+  double w = p;
+  if (!use_p && resid) w = (p - q > 0.0) ? p - q : 0.0;
+  const double U = uniform_f64(noise_word(seed, b, r, y));
+  return w / -log(U);
+}
+
+// Whole-row race in fp64 by one workgroup: used when the fp32 screen
+// cannot certify its result, and on request.
+template <bool BF16>
+__device__ __forceinline__ int race_row_f64(const Params& P, const Job& J, int b, Smem& sm) {
+  const int64_t row_off = (int64_t)J.row * P.lstride;
+  const float* qrow = J.kind == JOB_RESID ? P.q + (int64_t)J.qrow * P.qstride : nullptr;
+  const uint64_t seed = P.seed[b];
+  // an all-zero weight vector falls back to p
+  int any_pos = 0;
+#pragma unroll 1
+  for (int y = threadIdx.x; y < P.V; y += kWG) {
+    const double l = (double)load_logit<BF16>(P, J.row, y);
+    const double q = qrow ? (double)qrow[y] : 0.0;
+    if (!(J.kind == JOB_EXCL && is_excluded(J, y)) &&
+        race_key_cold(l, q, J.m, J.t, J.s, J.kind == JOB_RESID, 0, seed, b, J.r, y) > 0.0)
+      any_pos = 1;
+  }
+  const int use_p = block_min_i(any_pos ? 0 : 1, sm) == 1;
+  double best_k = -1.0;
+  int best_y = INT32_MAX;
+#pragma unroll 1
+  for (int y = threadIdx.x; y < P.V; y += kWG) {
+    const double l = (double)load_logit<BF16>(P, J.row, y);
+    const double q = qrow ? (double)qrow[y] : 0.0;
+    const bool zero = !use_p && J.kind == JOB_EXCL && is_excluded(J, y);
+    const double key = zero ? 0.0 : race_key_cold(l, q, J.m, J.t, J.s, J.kind == JOB_RESID, use_p, seed, b, J.r, y);
+    if (better(key, y, best_k, best_y)) {
+      best_k = key;
+      best_y = y;
+    }
+  }
+  (void)row_off;
+  block_best(best_k, best_y, sm);
   return best_y;
 }
 
-// Merge of one race: L = the largest certified lower bound over all chunks;
-// the true winner's upper bound reaches L, so re-evaluating in fp64 every
-// listed candidate with upper bound >= L finds it, unless some chunk had to
-// drop qualifying entries with an upper bound >= L (then, or when L is too
-// small for fp32 to certify, the whole row is raced in fp64).
-template <bool BF16>
-__device__ __forceinline__ void k3_merge(const Params& P, int b, const JobView& J, Smem& sm) {
-  const int tid = threadIdx.x;
-  float lo = -INFINITY, ovf = -INFINITY;
-  for (int c = tid; c < P.C3; c += kWG) {
-    const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
-    lo = fmaxf(lo, cld_f32(&rec->lo));
-    ovf = fmaxf(ovf, cld_f32(&rec->ovf_hi));
-  }
-  const float L = block_max(lo, sm);
-  const float OVF = block_max(ovf, sm);
-  if (tid == 0) {
-    sm.ncand = 0;
-    sm.overflow = 0;
-  }
-  __syncthreads();
-  bool fallback = (P.flags & SV_FLAG_FP64_RACE) || !(L >= 0x1p-70f) || OVF >= L;
-  if (!fallback) {
-    for (int c = tid; c < P.C3; c += kWG) {
-      const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
-      const int cnt = cld_i32(&rec->count);
-      for (int i = 0; i < cnt; ++i) {
-        if (cld_f32(&rec->hi[i]) >= L) {
-          const int slot = atomicAdd(&sm.ncand, 1);
-          if (slot < kMergeCandMax) sm.cand_y[slot] = cld_i32(&rec->idx[i]);
-          else sm.overflow = 1;
-        }
-      }
-    }
-    __syncthreads();
-    fallback = sm.overflow != 0;
-  }
-  int best_y = -1;
-  if (!fallback) {
-    const int nc = sm.ncand;
-    for (int i = tid; i < nc; i += kWG) sm.cand_key[i] = race_key_f64<BF16>(P, J, b, sm.cand_y[i], false);
-    __syncthreads();
-    if (tid == 0) {
-      double bk = -1.0;
-      int by = INT32_MAX;
-      for (int i = 0; i < nc; ++i)
-        if (better(sm.cand_key[i], sm.cand_y[i], bk, by)) {
-          bk = sm.cand_key[i];
-          by = sm.cand_y[i];
-        }
-      sm.flag = (bk > 0.0) ? by : -1;  // a zero best key means an all-zero residual
-    }
-    __syncthreads();
-    best_y = sm.flag;
-    fallback = best_y < 0;
-  }
-  if (fallback) best_y = race_row_f64<BF16>(P, J, b, sm);
-  if (tid == 0) P.tokens[J.out_slot] = best_y;
-}
-
-// Per-element fp32 race keys with certified bounds, for the 4*kK3Groups ids
-// this thread owns in chunk c3.  e = 2^t approximates exp((l - m)/T) with
-// relative error at most eta = (|t| 2^-21 + 2^-17) (argument rounding plus
+// Sampling chunk c3 of request b (job in shared memory).  Screening in fp32
+// with certified bounds: e = 2^t approximates exp((l - m)/T) with relative
+// error at most eta = (|t| 2^-21 + 2^-17) (argument rounding plus
 // v_exp_f32, far above the measured 2^-23.5); E2 = -log2(U) and its
 // reciprocal are each within 2^-22 (v_log_f32 measured at 2^-23 over every
 // possible U, v_rcp_f32 at 2^-23.4).  The key w / E2 is a constant multiple
-// of w / E.  hi[] gets each key's upper bound (-1 when the id does not
-// race); lo_max the largest lower bound.
+// of w / E.  For a residual w = max(p - q, 0) with p = e/S; otherwise w = e
+// (the constant 1/S does not change the argmax).
+//   1. Each thread bounds the weights of its 8 ids: whi >= w >= wlo (a
+//      residual's whi is exactly 0 where p cannot exceed q).
+//   2. One thread keys the chunk's id of largest wlo (Philox, log, rcp):
+//      its lower bound L0 is a certified lower bound of the chunk's best
+//      key.  Since U <= 1 - 2^-24, E2 > 2^-24 and no key exceeds whi 2^25:
+//      an id with whi 2^25 < L0 cannot be the chunk's best, nor a
+//      candidate below, nor raise L.
+//   3. The other ids are compacted in LDS (with l and q) and keyed by one
+//      lane each; past kList entries every id of the chunk is keyed in
+//      place instead.
+//   4. L = the largest lower bound; the ids whose upper bound reaches L
+//      (the candidates) are re-keyed exactly in fp64 and the chunk records
+//      L, its best fp64 key and id, and, if more than kCandMax candidates
+//      qualified, the largest upper bound among those left out.
 template <bool BF16, int KIND>
-__device__ void k3_chunk_keys(const Params& P, const JobView& J, int b, int c3, float* hi, float& lo_max) {
+__device__ __forceinline__ void k3_sample(const Params& P, const Job& J, int b, int c3, Smem& sm) {
+  constexpr int NI = 4 * kK3Groups;  // ids per thread
   const int tid = threadIdx.x;
   const uint64_t seed = P.seed[b];
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
   const int jr = J.r;
+  const int y_base = c3 * kK3Chunk;
   const int64_t lrow = (int64_t)J.row * P.lstride;
   const int64_t qrow = (int64_t)J.qrow * P.qstride;
   uint32_t excl_mask = 0;  // bit g*4+i: this thread's id is a removed token
   if (KIND == JOB_EXCL) {
-    const int n_excl = J.n_excl;
-    for (int i = 0; i < n_excl; ++i) {
-      const int z = cld_i32(&J.excl[i]) - c3 * kK3Chunk;
+    for (int i = 0; i < J.n_excl; ++i) {
+      const int z = J.excl[i] - y_base;
       if (z >= 0 && z < kK3Chunk) {
         const int gi = z >> 2;
         if ((gi % kWG) == tid) excl_mask |= 1u << ((gi / kWG) * 4 + (z & 3));
       }
     }
   }
+  // 1. weight bounds
+  float whi[NI], wlo[NI], lv[NI], qv[NI];
 #pragma unroll
   for (int g = 0; g < kK3Groups; ++g) {
-    const int y0 = c3 * kK3Chunk + 4 * (g * kWG + tid);
-    float l[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
+    const int y0 = y_base + 4 * (g * kWG + tid);
     const bool full = y0 + 4 <= P.V;
+    float* l = &lv[g * 4];
+    float* q = &qv[g * 4];
     if (full && P.aligned) {
       if (BF16) {
         const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
@@ -1030,143 +1072,249 @@ __device__ void k3_chunk_keys(const Params& P, const JobView& J, int b, int c3, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = 0.f;
     if (KIND == JOB_RESID) {
       if (full && P.q_aligned) {
         const u32x4 w = __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
-        qv[0] = __uint_as_float(w.x);
-        qv[1] = __uint_as_float(w.y);
-        qv[2] = __uint_as_float(w.z);
-        qv[3] = __uint_as_float(w.w);
+        q[0] = __uint_as_float(w.x);
+        q[1] = __uint_as_float(w.y);
+        q[2] = __uint_as_float(w.z);
+        q[3] = __uint_as_float(w.w);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv[i] = (y0 + i < P.V) ? P.q[qrow + y0 + i] : 0.f;
+        for (int i = 0; i < 4; ++i) q[i] = (y0 + i < P.V) ? P.q[qrow + y0 + i] : 0.f;
       }
     }
-    const u32x4 ctr = {(uint32_t)y0 >> 2, (uint32_t)jr, (uint32_t)b, 1u};
-    const u32x4 rnd = philox10(ctr, k0, k1);
-    const uint32_t words[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float d = l[i] - m;
       const float t = __builtin_fmaf(d, chi, d * clo);
       const float e = __builtin_amdgcn_exp2f(t);
-      const float e2 = -__builtin_amdgcn_logf(uniform_f32(words[i]));  // -log2 U > 0
-      const float rE = __builtin_amdgcn_rcpf(e2);
       const float eta = __builtin_fmaf(fminf(fabsf(t), 256.f), 0x1p-21f, 0x1p-17f);
       float h, lw;
       if (KIND == JOB_RESID) {
         const float p = e * inv_s;
-        const float w = fmaxf(p - qv[i], 0.f);
-        const float err = __builtin_fmaf(eta, p, 0x1p-22f * w);
-        h = (w + err) * rE * (1.f + 0x1p-20f);
-        lw = (w - err) * rE * (1.f - 0x1p-20f);
+        h = fmaxf(__builtin_fmaf(p, eta, p) - q[i], 0.f) * (1.f + 0x1p-22f);
+        lw = fmaxf(__builtin_fmaf(-p, eta, p) - q[i], 0.f) * (1.f - 0x1p-22f);
       } else {
-        const float key = e * rE;
-        h = __builtin_fmaf(key, eta + 0x1p-20f, key);
-        lw = __builtin_fmaf(-key, eta + 0x1p-20f, key);
+        h = __builtin_fmaf(e, eta, e);
+        lw = __builtin_fmaf(-e, eta, e);
       }
       const bool out = !(y0 + i < P.V) || (KIND == JOB_EXCL && ((excl_mask >> (g * 4 + i)) & 1u));
-      hi[g * 4 + i] = out ? -1.f : h;
-      if (!out) lo_max = fmaxf(lo_max, lw);
+      whi[g * 4 + i] = out ? -1.f : h;
+      wlo[g * 4 + i] = out ? -1.f : lw;
+    }
+  }
+  // 2. every key is at least wlo/32 (E2 <= 24): the chunk's largest wlo
+  // over 32 is a certified lower bound L0 of its best key
+  float wmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) wmax = fmaxf(wmax, wlo[i]);
+  const float L0 = block_max(wmax, sm) * 0x1p-5f;
+  // 3. count the ids that can still matter (ballots), then either compact
+  // them in LDS (one lane keys each) or, past kList, key every id in place
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t qmask = 0;  // bit i: this thread's id i qualifies
+  int wcount = 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bool qi = whi[i] > 0.f && whi[i] * 0x1p25f >= L0;
+    qmask |= (qi ? 1u : 0u) << i;
+    wcount += __popcll(__ballot(qi));
+  }
+  __syncthreads();
+  if (lane == 0) sm.red_i[wave] = wcount;
+  __syncthreads();
+  int n = 0, base = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    base += (w < wave) ? sm.red_i[w] : 0;
+    n += sm.red_i[w];
+  }
+  const bool dense = n > kList;
+  float lo_max = -INFINITY;
+  if (!dense) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint64_t mask = __ballot((qmask >> i) & 1u);
+      if ((qmask >> i) & 1u) {
+        const int slot = base + __popcll(mask & lt);
+        sm.list_y[slot] = y_base + 4 * ((i >> 2) * kWG + tid) + (i & 3);
+        sm.list_whi[slot] = whi[i];
+        sm.list_wlo[slot] = wlo[i];
+        sm.list_l[slot] = lv[i];
+        sm.list_q[slot] = qv[i];
+      }
+      base += __popcll(mask);
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kWG) {
+      const float rE = __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uniform_f32(noise_word(seed, b, jr, sm.list_y[i]))));
+      sm.list_whi[i] = sm.list_whi[i] * rE * (1.f + 0x1p-20f);
+      lo_max = fmaxf(lo_max, sm.list_wlo[i] * rE * (1.f - 0x1p-20f));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kK3Groups; ++g) {
+      const int y0 = y_base + 4 * (g * kWG + tid);
+      const u32x4 ctr = {(uint32_t)y0 >> 2, (uint32_t)jr, (uint32_t)b, 1u};
+      const u32x4 rnd = philox10(ctr, k0, k1);
+      const uint32_t words[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float rE = __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uniform_f32(words[i])));
+        const int j = g * 4 + i;
+        if (whi[j] > 0.f) {
+          lo_max = fmaxf(lo_max, wlo[j] * rE * (1.f - 0x1p-20f));
+          whi[j] = whi[j] * rE * (1.f + 0x1p-20f);
+        }
+      }
+    }
+  }
+  if (tid == 0) sm.ncand = 0;
+  const float L = block_max(lo_max, sm);
+  // 4. the candidates (upper bound >= L), recorded for the merge
+  float ovf = -INFINITY;
+  if (!dense) {
+    for (int i = tid; i < n; i += kWG) {
+      const float h = sm.list_whi[i];
+      if (h >= L) {
+        const int slot = atomicAdd(&sm.ncand, 1);
+        if (slot < kRecCand) {
+          sm.cand_y[slot] = sm.list_y[i];
+          sm.cand_h[slot] = h;
+          sm.cand_l[slot] = sm.list_l[i];
+          sm.cand_q[slot] = sm.list_q[i];
+        } else {
+          ovf = fmaxf(ovf, h);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (whi[i] > 0.f && whi[i] >= L) {
+        const int slot = atomicAdd(&sm.ncand, 1);
+        if (slot < kRecCand) {
+          sm.cand_y[slot] = y_base + 4 * ((i >> 2) * kWG + tid) + (i & 3);
+          sm.cand_h[slot] = whi[i];
+          sm.cand_l[slot] = lv[i];
+          sm.cand_q[slot] = qv[i];
+        } else {
+          ovf = fmaxf(ovf, whi[i]);
+        }
+      }
+    }
+  }
+  ovf = block_max(ovf, sm);
+  if (tid < 64) {
+    K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c3];
+    const int nc = min(sm.ncand, kRecCand);
+    if (tid < nc) {
+      cst_i32(&rec->cand[tid].y, sm.cand_y[tid]);
+      cst_f32(&rec->cand[tid].hi, sm.cand_h[tid]);
+      cst_f32(&rec->cand[tid].l, sm.cand_l[tid]);
+      cst_f32(&rec->cand[tid].q, sm.cand_q[tid]);
+    }
+    if (tid == 0) {
+      cst_f32(&rec->lo, L);
+      cst_f32(&rec->ovf, ovf);
+      cst_i32(&rec->count, nc);
     }
   }
 }
 
 template <bool BF16>
-__device__ void k3_chunk(const Params& P, int b, int c3, Smem& sm) {
+__device__ __forceinline__ void sample_chunk(const Params& P, int b, int c3, Smem& sm) {
+  const int kind = uniform_i(sm.job.kind);
+  if (kind == JOB_RESID) k3_sample<BF16, JOB_RESID>(P, sm.job, b, c3, sm);
+  else if (kind == JOB_EXCL) k3_sample<BF16, JOB_EXCL>(P, sm.job, b, c3, sm);
+  else k3_sample<BF16, JOB_P>(P, sm.job, b, c3, sm);
+}
+
+// Merge of one race by the request's last chunk: L = the largest certified
+// lower bound over all chunks.  The winner's upper bound reaches L, so it
+// is among the listed candidates whose upper bound reaches L, unless a
+// chunk had to leave out such a candidate (then, or when L is too small for
+// fp32 to certify, the whole row is raced in fp64).  A single such
+// candidate is the winner; several are re-keyed exactly in fp64.
+template <bool BF16>
+__device__ __forceinline__ void k3_merge(const Params& P, int b, Smem& sm) {
+  const Job& J = sm.job;
   const int tid = threadIdx.x;
-  if (!is_stochastic(temp_of(P, b))) return;  // greedy requests and bad temperatures race nothing
-  if (tid == 0) {
-    int ok = 1;
-    if (P.sched == SCHED_FUSED) {
-      uint32_t spins = 0;
-      while (cld32(&P.sync[b].ready) == 0u) {
-        __builtin_amdgcn_s_sleep(8);
-        if (++spins > kSpinLimit || cld32(&P.ctrl->aborted)) {
-          ok = 0;
-          break;
+  float lo = -INFINITY, ov = -INFINITY;
+  for (int c = tid; c < P.C3; c += kWG) {
+    const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
+    lo = fmaxf(lo, cld_f32(&rec->lo));
+    ov = fmaxf(ov, cld_f32(&rec->ovf));
+  }
+  if (tid == 0) sm.ncand = 0;
+  const float L = block_max(lo, sm);
+  const float OVF = block_max(ov, sm);
+  bool fallback = (P.flags & SV_FLAG_FP64_RACE) || !(L >= 0x1p-70f) || OVF >= L;
+  if (!fallback) {
+    for (int c = tid; c < P.C3; c += kWG) {
+      const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
+      const int cnt = cld_i32(&rec->count);
+      for (int i = 0; i < cnt; ++i) {
+        const float h = cld_f32(&rec->cand[i].hi);
+        if (h >= L) {
+          const int slot = atomicAdd(&sm.ncand, 1);
+          if (slot < kCandMax) {
+            sm.cand_y[slot] = cld_i32(&rec->cand[i].y);
+            sm.cand_l[slot] = cld_f32(&rec->cand[i].l);
+            sm.cand_q[slot] = cld_f32(&rec->cand[i].q);
+          }
         }
       }
-      if (!ok) {
-        cst32(&P.ctrl->aborted, 1u);
-        if (P.status) P.status[b] = SV_REQ_INTERNAL;
-      }
     }
-    sm.flag = ok;
-    if (ok) read_job(P, b, sm.job);
-  }
-  __syncthreads();
-  if (!uniform_i(sm.flag)) return;
-  const JobView J = sm.job;
-  const int kind = uniform_i(J.kind);
-  float L = -INFINITY, ovf_hi = -INFINITY;
-  if (kind != JOB_NONE) {
-    float hi[kK3Groups * 4];
-    float lo_max = -INFINITY;
-    if (kind == JOB_RESID) k3_chunk_keys<BF16, JOB_RESID>(P, J, b, c3, hi, lo_max);
-    else if (kind == JOB_EXCL) k3_chunk_keys<BF16, JOB_EXCL>(P, J, b, c3, hi, lo_max);
-    else k3_chunk_keys<BF16, JOB_P>(P, J, b, c3, hi, lo_max);
-    L = block_max(lo_max, sm);
-    if (tid == 0) sm.ncand = 0;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kK3Groups * 4; ++i) {
-      if (hi[i] >= L && hi[i] > 0.f) {
-        const int slot = atomicAdd(&sm.ncand, 1);
-        if (slot < kCandMax) {
-          sm.cand_y[slot] = c3 * kK3Chunk + 4 * ((i >> 2) * kWG + tid) + (i & 3);
-          sm.cand_h[slot] = hi[i];
+    fallback = sm.ncand < 1 || sm.ncand > kCandMax;
+  }
+  int by = -1;
+  if (!fallback) {
+    const int nc = sm.ncand;
+    if (nc == 1) {
+      by = sm.cand_y[0];
+    } else {
+      if (tid < nc)
+        sm.cand_key[tid] =
+            race_key_from(J, P.seed[b], b, sm.cand_y[tid], (double)sm.cand_l[tid], (double)sm.cand_q[tid], false);
+      __syncthreads();
+      double bk = -1.0;
+      int byy = INT32_MAX;
+      for (int i = 0; i < nc; ++i)
+        if (better(sm.cand_key[i], sm.cand_y[i], bk, byy)) {
+          bk = sm.cand_key[i];
+          byy = sm.cand_y[i];
         }
-        ovf_hi = fmaxf(ovf_hi, hi[i]);
-      }
-    }
-    ovf_hi = block_max(ovf_hi, sm);
-  }
-  // wave 0 publishes the chunk's record, then thread 0 counts the chunk; the
-  // last chunk of the request lowers the ready flag and merges
-  if (tid < 64) {
-    if (kind != JOB_NONE) {
-      K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c3];
-      const int n = sm.ncand;
-      const int cnt = min(n, kCandMax);
-      if (tid < cnt) {
-        cst_i32(&rec->idx[tid], sm.cand_y[tid]);
-        cst_f32(&rec->hi[tid], sm.cand_h[tid]);
-      }
-      if (tid == 0) {
-        cst_f32(&rec->lo, L);
-        cst_i32(&rec->count, cnt);
-        cst_f32(&rec->ovf_hi, n > kCandMax ? ovf_hi : -INFINITY);
-      }
-      wait_mem();
-    }
-    if (tid == 0) {
-      const uint32_t old = atomic_add_relaxed(&P.sync[b].k3_count, 1u);
-      const int last = (old == (uint32_t)P.C3 - 1u);
-      if (last) {
-        cst32(&P.sync[b].k3_count, 0u);
-        cst32(&P.sync[b].ready, 0u);
-      }
-      sm.flag = last && kind != JOB_NONE;
+      by = byy;
+      fallback = !(bk > 0.0);
     }
   }
-  __syncthreads();
-  if (uniform_i(sm.flag)) k3_merge<BF16>(P, b, J, sm);
+  if (fallback) by = race_row_f64<BF16>(P, J, b, sm);
+  if (tid == 0) P.tokens[J.out_slot] = by;
 }
 
 // ===================================================================== driver
-// K1 work item (request b, row r, chunk c).  Its HBM loads are issued first;
-// then the request's temperature and drafts decide whether the row is needed
-// (rows after a chain's first -1 are not).  Wave 0 also gathers the target
-// logit (and q) at the draft tokens that fall in this chunk, so the decision
-// step needs no dependent loads.  The workgroup that completes the
-// request's last chunk runs its decision step.
+// K1 segment: sub-chunks [s0, s1) of row r of request b, written to the
+// row's partial slot `slot`.  Its first HBM loads are issued before
+// anything else; then the request's temperature and drafts decide whether
+// the row is needed (rows after a chain's first -1 are not).  Wave 0 also
+// gathers the target logit (and q) at the draft tokens that fall in the
+// segment, so the decision step needs no dependent loads.  Row-statistics
+// calls count each row's segments; the workgroup that completes a row
+// combines it.  The fused schedule counts each request's segments for its
+// sampling chunks to wait on.
 template <int MODE, bool BF16>
-__device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, Smem& sm) {
+__device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0, int s1, int slot, Smem& sm) {
   const int64_t row = (int64_t)b * P.R + r;
-  const int64_t start = (int64_t)c * P.CH;
+  const int64_t start = (int64_t)s0 * P.SUB;
+  const int n_seg = (int)(min((int64_t)s1 * P.SUB, (int64_t)P.V) - start);
   u32x4 raw0[kVecPerThread];
-  k1_issue<BF16>(P, row * P.lstride + start, (int)min((int64_t)P.CH, (int64_t)P.V - start), raw0);
+  k1_issue<BF16>(P, row * P.lstride + start, n_seg, raw0);
   const float T = temp_of(P, b);
   bool need = true;
   if (MODE == MODE_CHAIN) {
@@ -1178,113 +1326,154 @@ __device__ __forceinline__ void run_k1(const Params& P, int b, int r, int c, Sme
   }
   const bool stoch = uniform_i(is_stochastic(T));
   if (uniform_i(need)) {
-    if (stoch) k1_item_stats<BF16, true, MODE == MODE_ROWS>(P, row, c, T, raw0, sm);
-    else k1_item_stats<BF16, false, false>(P, row, c, T, raw0, sm);
+    if (stoch) k1_seg_stats<BF16, true, MODE == MODE_ROWS>(P, row, s0, s1, slot, T, raw0, sm);
+    else k1_seg_stats<BF16, false, false>(P, row, s0, s1, slot, T, raw0, sm);
     if (MODE != MODE_ROWS && threadIdx.x < 64 && stoch) {
       const int lane = threadIdx.x;
-      const int64_t stop = min(start + P.CH, (int64_t)P.V);
-      int tok = -1, slot = -1;
+      const int64_t stop = start + n_seg;
+      int tok = -1, gslot = -1;
       if (MODE == MODE_CHAIN) {
         if (lane == 0 && r < P.k) {
           tok = P.ids[(int64_t)b * P.k + r];
-          slot = r;
+          gslot = r;
         }
       } else if (lane >= 1 && lane < P.R && P.parent[(int64_t)b * P.R + lane] == r) {
         tok = P.node_tokens[(int64_t)b * P.R + lane];
-        slot = lane;
+        gslot = lane;
       }
-      if (slot >= 0 && tok >= start && tok < stop) {
+      if (gslot >= 0 && tok >= start && tok < stop) {
         const float l = load_logit<BF16>(P, row, tok);
         float q = 0.f;
         if (MODE == MODE_CHAIN && P.draft_kind == SV_DRAFT_PROBS) q = P.q[((int64_t)b * P.k + r) * P.qstride + tok];
-        cst64(&P.gat[(int64_t)b * SV_MAX_NODES + slot], (uint64_t)__float_as_uint(l) | ((uint64_t)__float_as_uint(q) << 32));
+        cst64(&P.gat[(int64_t)b * SV_MAX_NODES + gslot],
+              (uint64_t)__float_as_uint(l) | ((uint64_t)__float_as_uint(q) << 32));
       }
     }
   }
-  if (P.sched == SCHED_PHASED) return;
+  if (MODE != MODE_ROWS && P.sched != SCHED_FUSED) return;
   if (threadIdx.x == 0) {
     wait_mem();  // this wave's partial and gathers are complete
     const uint32_t old = atomic_add_relaxed(&P.sync[b].k1_count, 1u);
-    sm.flag = (old == (uint32_t)P.n1r - 1u);
+    sm.flag = (MODE == MODE_ROWS) && old == (uint32_t)k1_segments(P, row) - 1u;
+  }
+  if (MODE == MODE_ROWS) {
+    __syncthreads();
+    if (uniform_i(sm.flag)) {
+      if (threadIdx.x == 0) cst32(&P.sync[b].k1_count, 0u);
+      k2_rows(P, b, sm);
+    }
+  }
+}
+
+// K1 workgroup w: its range of flattened sub-chunks, one segment per row it
+// touches.  A range is never longer than a row, so it touches at most two.
+template <int MODE, bool BF16>
+__device__ __forceinline__ void run_k1_range(const Params& P, int64_t w, Smem& sm) {
+  const int64_t f0 = k1_range_begin(w, P.F, P.G);
+  int rem = (int)(k1_range_begin(w + 1, P.F, P.G) - f0);
+  int row = (int)(f0 / P.nsub);
+  int s = (int)(f0 - (int64_t)row * P.nsub);
+  int slot = (int)(w - k1_first_wg(P, row));
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    if (rem > 0) {
+      const int len = min(rem, P.nsub - s);
+      const int b = row / P.R;
+      run_k1_seg<MODE, BF16>(P, b, row - b * P.R, s, s + len, slot, sm);
+      rem -= len;
+      ++row;
+      s = 0;
+      slot = 0;  // a range that goes on into the next row starts it
+      __syncthreads();
+    }
+  }
+}
+
+// Sampling chunk c3 of request b, after its own run of the decision step.
+// Greedy requests (and bad temperatures) sample nothing: only their chunk 0
+// works, to decide and write the outputs.  The last chunk of a sampling
+// request to finish merges the chunks' results and resets the request's
+// counters.
+template <int MODE, bool BF16, bool COH>
+__device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm) {
+  const int tid = threadIdx.x;
+  const bool writer = (c3 == 0);
+  const bool stoch = uniform_i(is_stochastic(temp_of(P, b)));
+  const bool work = stoch || writer;
+  int ok = 1;
+  if (P.sched == SCHED_FUSED && work) {
+    if (tid == 0) {
+      uint32_t expect = 0;
+      for (int r = 0; r < P.R; ++r) expect += (uint32_t)k1_segments(P, (int64_t)b * P.R + r);
+      uint32_t spins = 0;
+      while (cld32(&P.sync[b].k1_count) < expect) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++spins > kSpinLimit || cld32(&P.ctrl->aborted)) {
+          ok = 0;
+          break;
+        }
+      }
+      if (!ok) {
+        cst32(&P.ctrl->aborted, 1u);
+        if (P.status) P.status[b] = SV_REQ_INTERNAL;
+      }
+      sm.flag = ok;
+    }
+    __syncthreads();
+    ok = uniform_i(sm.flag);
+  }
+  bool sampled = false;
+  if (work && ok) {
+    if (MODE == MODE_CHAIN) decide_chain<BF16, COH>(P, b, writer, sm);
+    else decide_tree<BF16, COH>(P, b, writer, sm);
+    if (uniform_i(sm.job.kind) != JOB_NONE) {
+      sample_chunk<BF16>(P, b, c3, sm);
+      sampled = true;
+    }
+  }
+  if (!stoch && P.sched != SCHED_FUSED) return;  // nothing to count
+  __syncthreads();
+  if (tid == 0) {
+    wait_mem();  // this wave wrote the chunk's record
+    const uint32_t old = atomic_add_relaxed(&P.sync[b].k3_count, 1u);
+    const int last = (old == (uint32_t)P.C3 - 1u);
+    if (last) {
+      cst32(&P.sync[b].k3_count, 0u);
+      cst32(&P.sync[b].k1_count, 0u);
+    }
+    sm.flag = last && sampled && !cld32(&P.ctrl->aborted);
   }
   __syncthreads();
-  if (uniform_i(sm.flag)) {
-    if (threadIdx.x == 0) cst32(&P.sync[b].k1_count, 0u);
-    if (MODE == MODE_CHAIN) k2_chain<BF16>(P, b, sm);
-    else if (MODE == MODE_TREE) k2_tree<BF16>(P, b, sm);
-    else k2_rows(P, b, sm);
+  if (uniform_i(sm.flag)) k3_merge<BF16>(P, b, sm);
+}
+
+template <int MODE, bool BF16>
+__global__ __launch_bounds__(kWG, 7) void k1_kernel(Params P) {
+  __shared__ Smem sm;
+  run_k1_range<MODE, BF16>(P, blockIdx.x, sm);
+}
+
+template <int MODE, bool BF16>
+__global__ __launch_bounds__(kWG, 8) void k23_kernel(Params P) {
+  __shared__ Smem sm;
+  if constexpr (MODE != MODE_ROWS) {
+    const int b = (int)(blockIdx.x / (uint32_t)P.C3);
+    run_k23<MODE, BF16, false>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.C3), sm);
   }
 }
 
-// Work item t of the fused schedule.  Blocks g = 0 .. bs+L-1: block g holds
-// the K1 chunks of request g (if g < bs) followed by the K3 chunks of
-// request g - L (if g >= L).
+// One launch: workgroups [0, G) stream K1 ranges, the rest are sampling
+// chunks (request-major), dispatched after every K1 workgroup.
 template <int MODE, bool BF16>
-__device__ __forceinline__ void run_item(const Params& P, uint32_t t, Smem& sm) {
-  const uint32_t n1 = (uint32_t)P.n1r, n3 = (uint32_t)P.C3, L = (uint32_t)P.lag, bs = (uint32_t)P.bs;
-  const uint32_t seg1 = L * n1;
-  const uint32_t seg2 = (bs - L) * (n1 + n3);
-  int b = 0, kind1 = 1;
-  uint32_t o = 0;
-  if (t < seg1) {
-    b = (int)(t / n1);
-    o = t % n1;
-  } else if (t < seg1 + seg2) {
-    const uint32_t u = t - seg1;
-    const uint32_t g = L + u / (n1 + n3);
-    const uint32_t oo = u % (n1 + n3);
-    if (oo < n1) {
-      b = (int)g;
-      o = oo;
-    } else {
-      b = (int)(g - L);
-      o = oo - n1;
-      kind1 = 0;
-    }
-  } else {
-    const uint32_t u = t - seg1 - seg2;
-    b = (int)(bs - L + u / n3);
-    o = u % n3;
-    kind1 = 0;
+__global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
+  __shared__ Smem sm;
+  if (blockIdx.x < (uint32_t)P.G) {
+    run_k1_range<MODE, BF16>(P, blockIdx.x, sm);
+  } else if constexpr (MODE != MODE_ROWS) {
+    const uint32_t t = blockIdx.x - (uint32_t)P.G;
+    const int b = (int)(t / (uint32_t)P.C3);
+    run_k23<MODE, BF16, true>(P, b, (int)(t - (uint32_t)b * (uint32_t)P.C3), sm);
   }
-  if (kind1) {
-    run_k1<MODE, BF16>(P, b, (int)(o / (uint32_t)P.CPR), (int)(o % (uint32_t)P.CPR), sm);
-  } else if (MODE != MODE_ROWS) {
-    k3_chunk<BF16>(P, b, (int)o, sm);
-  }
-}
-
-template <int MODE, bool BF16>
-__global__ __launch_bounds__(kWG) void fused_kernel(Params P) {
-  __shared__ Smem sm;
-  run_item<MODE, BF16>(P, blockIdx.x, sm);
-}
-
-// Phased schedule, K1: one item per workgroup.
-template <int MODE, bool BF16>
-__global__ __launch_bounds__(kWG) void k1_kernel(Params P) {
-  __shared__ Smem sm;
-  const uint32_t t = blockIdx.x;
-  const int b = (int)(t / (uint32_t)P.n1r);
-  const uint32_t o = t % (uint32_t)P.n1r;
-  run_k1<MODE, BF16>(P, b, (int)(o / (uint32_t)P.CPR), (int)(o % (uint32_t)P.CPR), sm);
-}
-
-template <int MODE, bool BF16>
-__global__ __launch_bounds__(kWG) void k2_kernel(Params P) {
-  __shared__ Smem sm;
-  const int b = blockIdx.x;
-  if (MODE == MODE_CHAIN) k2_chain<BF16>(P, b, sm);
-  else if (MODE == MODE_TREE) k2_tree<BF16>(P, b, sm);
-  else k2_rows(P, b, sm);
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(kWG) void k3_kernel(Params P) {
-  __shared__ Smem sm;
-  const int b = (int)(blockIdx.x / (uint32_t)P.C3);
-  const int c3 = (int)(blockIdx.x % (uint32_t)P.C3);
-  k3_chunk<BF16>(P, b, c3, sm);
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -1297,76 +1486,60 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 
 // ===================================================================== host
 struct Shape {
-  int CH, CPR, C3;
-  size_t gat_off, jobs_off, part_off, k3_off, total;
+  int SUB, nsub, G, CPR, C3;
+  int64_t F;
+  size_t gat_off, part_off, k3_off, total;
 };
 
+// Work split of a call (a function of the shape alone, so results never
+// depend on the device or the schedule).
 static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   Shape s;
-  s.CH = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG * kSubChunks;
-  s.CPR = (int)((V + s.CH - 1) / s.CH);
+  s.SUB = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
+  s.nsub = (int)((V + s.SUB - 1) / s.SUB);
+  s.F = bs * R * s.nsub;
+  // G workgroups, each with a range of floor(F/G) or ceil(F/G) sub-chunks:
+  // no more than fit on the device at once, a range no longer than a row
+  // (so it touches at most two rows), and no row split into more than 64
+  // segments (a range of >= fmin sub-chunks; a row then spans at most
+  // ceil((nsub - 1) / fmin) + 1 ranges).
+  int64_t G = s.F < kK1Workgroups ? s.F : kK1Workgroups;
+  const int64_t g_row = (s.F + s.nsub - 1) / s.nsub;  // ranges of ceil(F/G) <= nsub
+  if (G < g_row) G = g_row;
+  const int64_t need = s.nsub > 1 ? (s.nsub - 1 + 62) / 63 : 1;  // fmin giving <= 64 spans
+  if (G > s.F / need) G = s.F / need;
+  s.G = (int)G;
+  const int64_t fmin = s.F / s.G;
+  const int64_t spans = (s.nsub - 1 + fmin - 1) / fmin + 1;
+  s.CPR = (int)(spans < s.nsub ? spans : s.nsub);
   s.C3 = races ? (int)((V + kK3Chunk - 1) / kK3Chunk) : 0;
   s.gat_off = kDataOffset;
-  s.jobs_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
-  s.part_off = s.jobs_off + align256(sizeof(Job) * (size_t)bs);
+  s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
   s.total = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
   return s;
 }
 
-// Read-only cache of device properties: compute-unit count and the resident
-// workgroups per CU of each fused kernel (slot = mode * 2 + bf16).
-struct DeviceInfo {
-  std::atomic<int> cu{0};
-  std::atomic<int> occ[12];  // fused kernels (slots 0..5), K1 kernels (slots 6..11)
-};
-static DeviceInfo g_dev[64];
-
 typedef void (*KernelFn)(Params);
 
 template <int MODE, bool BF16>
-static void kernels_for(KernelFn& fused, KernelFn& k1, KernelFn& k2, KernelFn& k3) {
-  fused = fused_kernel<MODE, BF16>;
+static void kernels_for(KernelFn& k1, KernelFn& k23, KernelFn& fused) {
   k1 = k1_kernel<MODE, BF16>;
-  k2 = k2_kernel<MODE, BF16>;
-  k3 = k3_kernel<BF16>;
+  k23 = k23_kernel<MODE, BF16>;
+  fused = fused_kernel<MODE, BF16>;
 }
 
-static void select_kernels(int mode, bool bf16, KernelFn& fused, KernelFn& k1, KernelFn& k2, KernelFn& k3) {
+static void select_kernels(int mode, bool bf16, KernelFn& k1, KernelFn& k23, KernelFn& fused) {
   if (mode == MODE_CHAIN) {
-    if (bf16) kernels_for<MODE_CHAIN, true>(fused, k1, k2, k3);
-    else kernels_for<MODE_CHAIN, false>(fused, k1, k2, k3);
+    if (bf16) kernels_for<MODE_CHAIN, true>(k1, k23, fused);
+    else kernels_for<MODE_CHAIN, false>(k1, k23, fused);
   } else if (mode == MODE_TREE) {
-    if (bf16) kernels_for<MODE_TREE, true>(fused, k1, k2, k3);
-    else kernels_for<MODE_TREE, false>(fused, k1, k2, k3);
+    if (bf16) kernels_for<MODE_TREE, true>(k1, k23, fused);
+    else kernels_for<MODE_TREE, false>(k1, k23, fused);
   } else {
-    if (bf16) kernels_for<MODE_ROWS, true>(fused, k1, k2, k3);
-    else kernels_for<MODE_ROWS, false>(fused, k1, k2, k3);
+    if (bf16) kernels_for<MODE_ROWS, true>(k1, k23, fused);
+    else kernels_for<MODE_ROWS, false>(k1, k23, fused);
   }
-}
-
-static sv_status device_info(KernelFn kernel, int slot, int& cu, int& occ) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_ERR_LAUNCH;
-  cu = g_dev[dev].cu.load();
-  occ = g_dev[dev].occ[slot].load();
-  if (cu > 0 && occ > 0) return SV_OK;
-  int c = 0, o = 0;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SV_ERR_LAUNCH;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, (const void*)kernel, kWG, 0) != hipSuccess)
-    return SV_ERR_LAUNCH;
-  if (c <= 0 || o <= 0) return SV_ERR_LAUNCH;
-  g_dev[dev].cu.store(c);
-  g_dev[dev].occ[slot].store(o);
-  cu = c;
-  occ = o;
-  return SV_OK;
-}
-
-static int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
 }
 
 static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -1377,42 +1550,29 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.ctrl = (Ctrl*)base;
   P.sync = (Sync*)(base + kSyncOffset);
   P.gat = (Gather*)(base + S.gat_off);
-  P.jobs = (Job*)(base + S.jobs_off);
   P.part = (Partial*)(base + S.part_off);
   P.k3 = (K3Rec*)(base + S.k3_off);
-  P.CH = S.CH;
+  P.SUB = S.SUB;
+  P.nsub = S.nsub;
+  P.F = S.F;
+  P.Finv = 1.0 / (double)S.F;
+  P.G = S.G;
   P.CPR = S.CPR;
   P.C3 = S.C3;
-  P.n1r = P.R * S.CPR;
-  const int64_t n_tickets = (int64_t)P.bs * (P.n1r + P.C3);
-  if (n_tickets <= 0 || n_tickets > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
-  P.n_tickets = (int32_t)n_tickets;
-  // Schedule: split unless another one is asked for (it measures fastest on
+  const int64_t grid23 = (int64_t)P.bs * P.C3;
+  if (grid23 + P.G > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
+  // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).
-  P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : (P.flags & SV_FLAG_PHASED) ? SCHED_PHASED : SCHED_SPLIT;
-  KernelFn fused, k1, k2, k3;
-  const bool bf16 = P.dtype == SV_BF16;
-  select_kernels(P.mode, bf16, fused, k1, k2, k3);
-  if (P.sched != SCHED_FUSED) {
-    P.lag = 0;
-    hipLaunchKernelGGL(k1, dim3((unsigned)((int64_t)P.bs * P.n1r)), dim3(kWG), 0, stream, P);
-    if (P.sched == SCHED_PHASED) hipLaunchKernelGGL(k2, dim3((unsigned)P.bs), dim3(kWG), 0, stream, P);
-    if (P.C3 > 0) hipLaunchKernelGGL(k3, dim3((unsigned)(P.bs * P.C3)), dim3(kWG), 0, stream, P);
+  P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : SCHED_PHASED;
+  KernelFn k1, k23, fused;
+  select_kernels(P.mode, P.dtype == SV_BF16, k1, k23, fused);
+  if (P.mode == MODE_ROWS) {
+    hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+  } else if (P.sched == SCHED_PHASED) {
+    hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+    hipLaunchKernelGGL(k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
   } else {
-    int cu = 0, occ = 0;
-    sv_status st = device_info(fused, P.mode * 2 + (bf16 ? 1 : 0), cu, occ);
-    if (st != SV_OK) return st;
-    const int64_t resident = (int64_t)cu * occ;
-    // Lag between a request's K1 chunks and its K3 chunks, in requests:
-    // about the number of requests the resident workgroups stream at once,
-    // so that a K3 item rarely has to wait for its request's decision.
-    // (SV_LAG overrides it, for tuning.)
-    int lag = env_int("SV_LAG", -1);
-    if (lag < 0) lag = (int)((resident + P.n1r - 1) / P.n1r) + 1;
-    if (P.C3 == 0) lag = 0;
-    P.lag = lag > P.bs ? P.bs : lag;
-    const int64_t grid = n_tickets;
-    hipLaunchKernelGGL(fused, dim3((unsigned)grid), dim3(kWG), 0, stream, P);
+    hipLaunchKernelGGL(fused, dim3((unsigned)(P.G + grid23)), dim3(kWG), 0, stream, P);
   }
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   return SV_OK;
@@ -1443,11 +1603,10 @@ const char* sv_status_string(sv_status s) {
 
 static bool dtype_ok(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
 
-static const uint32_t kKnownFlags = SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_SPLIT;
+static const uint32_t kKnownFlags = SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED;
 // At most one schedule bit.
 static bool one_schedule(uint32_t flags) {
-  const uint32_t s = flags & (SV_FLAG_PHASED | SV_FLAG_FUSED | SV_FLAG_SPLIT);
-  return (s & (s - 1)) == 0;
+  return (flags & (SV_FLAG_PHASED | SV_FLAG_FUSED)) != (SV_FLAG_PHASED | SV_FLAG_FUSED);
 }
 
 size_t sv_chain_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab, sv_dtype dt) {

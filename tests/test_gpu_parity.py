@@ -143,7 +143,7 @@ def test_tree_workload(dev, greedy):
 def test_all_schedules_are_bit_identical(dev):
     inp = workloads.chain_bf16_mixed(1, bs=24)
     ref = None
-    for flags in (sv.FLAG_PHASED, sv.FLAG_FUSED, sv.FLAG_SPLIT, 0):
+    for flags in (sv.FLAG_PHASED, sv.FLAG_FUSED, 0):
         _, out = run_chain(inp, dev, flags=flags)
         if ref is None:
             ref = out
@@ -153,7 +153,7 @@ def test_all_schedules_are_bit_identical(dev):
         np.testing.assert_array_equal(out["p_draft"].view(np.int64), ref["p_draft"].view(np.int64))
     t = workloads.tree_fp32(1, bs=12)
     ref = None
-    for flags in (sv.FLAG_PHASED, sv.FLAG_FUSED, sv.FLAG_SPLIT):
+    for flags in (sv.FLAG_PHASED, sv.FLAG_FUSED):
         _, out = run_tree(t, dev, flags=flags)
         if ref is None:
             ref = out
