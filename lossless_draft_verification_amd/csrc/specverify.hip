@@ -62,7 +62,14 @@ constexpr int kWaves = kWG / 64;
 #ifndef SV_K1_ROUNDS
 #define SV_K1_ROUNDS 1
 #endif
+#ifndef SV_K1_DEPTH
+#define SV_K1_DEPTH 1
+#endif
+#ifndef SV_K1_OCC
+#define SV_K1_OCC 7
+#endif
 constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a K1 sub-chunk
+constexpr int kK1Depth = SV_K1_DEPTH;           // K1 sub-chunks in flight ahead of the one being folded
 // K1 workgroups per call: an MI355X holds 256 CUs x 7 of them at once (71
 // VGPRs), so the stream is one round.
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
@@ -152,6 +159,7 @@ struct Params {
   int32_t SUB;        // entries per K1 sub-chunk
   int32_t nsub;       // sub-chunks per row
   int32_t G;          // K1 workgroups
+  int32_t Q;          // > 0: every row is split into Q segments, one per workgroup; 0: flattened ranges
   int32_t CPR;        // partial slots per row
   int32_t C3;         // sampling chunks per request
   int32_t sched;
@@ -527,6 +535,33 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
   st.idx = INT32_MAX;
   st.s = 0.0;
   st.nan = false;
+#if SV_K1_DEPTH > 1
+  // a ring of kK1Depth + 1 register buffers: kK1Depth sub-chunks are in
+  // flight ahead of the one being folded (the ring is unrolled, so every
+  // buffer index is static)
+  u32x4 buf[kK1Depth + 1][kVecPerThread];
+#pragma unroll
+  for (int j = 0; j < kVecPerThread; ++j) buf[0][j] = raw0[j];
+#pragma unroll
+  for (int d = 1; d <= kK1Depth; ++d)
+    if (d < nsub) k1_issue<BF16>(P, elem0 + (int64_t)d * SUB, n_seg - d * SUB, buf[d]);
+#pragma unroll 1
+  for (int sub0 = 0; sub0 < nsub; sub0 += kK1Depth + 1) {
+#pragma unroll
+    for (int d = 0; d <= kK1Depth; ++d) {
+      const int sub = sub0 + d;
+      if (sub < nsub) {
+        float x[NV];
+        k1_unpack<BF16>(buf[d], x);
+        if (sub + kK1Depth < nsub)
+          k1_issue<BF16>(P, elem0 + (int64_t)(sub + kK1Depth) * SUB, n_seg - (sub + kK1Depth) * SUB,
+                         buf[(d + kK1Depth) % (kK1Depth + 1)]);
+        k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
+      }
+    }
+  }
+#else
+  // two register buffers: the next sub-chunk is in flight while one is folded
   u32x4 cur[kVecPerThread], nxt[kVecPerThread];
 #pragma unroll
   for (int j = 0; j < kVecPerThread; ++j) cur[j] = raw0[j];
@@ -539,6 +574,7 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) cur[j] = nxt[j];
   }
+#endif
   const float mc = block_max(st.m, sm);
   double out_s = 0.0;
   int32_t out_amax = (int32_t)start;
@@ -585,6 +621,7 @@ __device__ __forceinline__ int64_t k1_first_wg(const Params& P, int64_t row) {
   return k1_wg_of_dev(P, row * P.nsub);
 }
 __device__ __forceinline__ int k1_segments(const Params& P, int64_t row) {
+  if (P.Q > 0) return P.Q;
   return (int)(k1_wg_of_dev(P, row * P.nsub + P.nsub - 1) - k1_first_wg(P, row) + 1);
 }
 
@@ -1365,10 +1402,21 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
   }
 }
 
-// K1 workgroup w: its range of flattened sub-chunks, one segment per row it
-// touches.  A range is never longer than a row, so it touches at most two.
+// K1 workgroup w: with Q > 0 (no more rows than K1 workgroups), segment
+// w % Q of row w / Q; else its range of flattened sub-chunks, one segment
+// per row it touches (a range is never longer than a row, so it touches at
+// most two).
 template <int MODE, bool BF16>
 __device__ __forceinline__ void run_k1_range(const Params& P, int64_t w, Smem& sm) {
+  if (P.Q > 0) {
+    // row-aligned: segment c of row w / Q, sub-chunks [c nsub / Q, (c + 1) nsub / Q)
+    const int q = P.Q;
+    const int row = (int)(w / q), c = (int)(w - (int64_t)row * q);
+    const int b = row / P.R;
+    run_k1_seg<MODE, BF16>(P, b, row - b * P.R, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c,
+                           sm);
+    return;
+  }
   const int64_t f0 = k1_range_begin(w, P.F, P.G);
   int rem = (int)(k1_range_begin(w + 1, P.F, P.G) - f0);
   int row = (int)(f0 / P.nsub);
@@ -1448,7 +1496,7 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
 }
 
 template <int MODE, bool BF16>
-__global__ __launch_bounds__(kWG, 7) void k1_kernel(Params P) {
+__global__ __launch_bounds__(kWG, SV_K1_OCC) void k1_kernel(Params P) {
   __shared__ Smem sm;
   run_k1_range<MODE, BF16>(P, blockIdx.x, sm);
 }
@@ -1486,7 +1534,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 
 // ===================================================================== host
 struct Shape {
-  int SUB, nsub, G, CPR, C3;
+  int SUB, nsub, G, Q, CPR, C3;
   int64_t F;
   size_t gat_off, part_off, k3_off, total;
 };
@@ -1498,20 +1546,33 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   s.SUB = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
   s.nsub = (int)((V + s.SUB - 1) / s.SUB);
   s.F = bs * R * s.nsub;
-  // G workgroups, each with a range of floor(F/G) or ceil(F/G) sub-chunks:
-  // no more than fit on the device at once, a range no longer than a row
-  // (so it touches at most two rows), and no row split into more than 64
-  // segments (a range of >= fmin sub-chunks; a row then spans at most
-  // ceil((nsub - 1) / fmin) + 1 ranges).
-  int64_t G = s.F < kK1Workgroups ? s.F : kK1Workgroups;
-  const int64_t g_row = (s.F + s.nsub - 1) / s.nsub;  // ranges of ceil(F/G) <= nsub
-  if (G < g_row) G = g_row;
-  const int64_t need = s.nsub > 1 ? (s.nsub - 1 + 62) / 63 : 1;  // fmin giving <= 64 spans
-  if (G > s.F / need) G = s.F / need;
-  s.G = (int)G;
-  const int64_t fmin = s.F / s.G;
-  const int64_t spans = (s.nsub - 1 + fmin - 1) / fmin + 1;
-  s.CPR = (int)(spans < s.nsub ? spans : s.nsub);
+  const int64_t rows = bs * R;
+  if (rows <= kK1Workgroups) {
+    // every row split evenly into Q segments, one per workgroup: no
+    // workgroup crosses a row
+    int64_t q = kK1Workgroups / rows;
+    if (q > s.nsub) q = s.nsub;
+    if (q > 64) q = 64;
+    s.Q = (int)q;
+    s.G = (int)(rows * q);
+    s.CPR = s.Q;
+  } else {
+    // G workgroups, each with a range of floor(F/G) or ceil(F/G)
+    // sub-chunks: no more than fit on the device at once, a range no longer
+    // than a row (so it touches at most two rows), and no row split into
+    // more than 64 segments (a range of >= fmin sub-chunks; a row then
+    // spans at most ceil((nsub - 1) / fmin) + 1 ranges).
+    s.Q = 0;
+    int64_t G = s.F < kK1Workgroups ? s.F : kK1Workgroups;
+    const int64_t g_row = (s.F + s.nsub - 1) / s.nsub;  // ranges of ceil(F/G) <= nsub
+    if (G < g_row) G = g_row;
+    const int64_t need = s.nsub > 1 ? (s.nsub - 1 + 62) / 63 : 1;  // fmin giving <= 64 spans
+    if (G > s.F / need) G = s.F / need;
+    s.G = (int)G;
+    const int64_t fmin = s.F / s.G;
+    const int64_t spans = (s.nsub - 1 + fmin - 1) / fmin + 1;
+    s.CPR = (int)(spans < s.nsub ? spans : s.nsub);
+  }
   s.C3 = races ? (int)((V + kK3Chunk - 1) / kK3Chunk) : 0;
   s.gat_off = kDataOffset;
   s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
@@ -1557,6 +1618,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.F = S.F;
   P.Finv = 1.0 / (double)S.F;
   P.G = S.G;
+  P.Q = S.Q;
   P.CPR = S.CPR;
   P.C3 = S.C3;
   const int64_t grid23 = (int64_t)P.bs * P.C3;
