@@ -92,9 +92,9 @@ struct Ctrl {
   uint32_t pad[63];
 };
 struct Sync {
-  uint32_t k1_count;  // K1 segments of the request (row, in row-statistics calls) done in this call
-  uint32_t k3_count;  // sampling chunks of the request done in this call
-  uint32_t pad[2];    // both counters are reset to 0 by their last user
+  uint32_t k1_count;  // K1 segments of the request (row, in row-statistics calls) done in this call,
+                      // reset to 0 by its last user
+  uint32_t pad[3];
 };
 // Target logit (and draft probability) at a draft token, gathered by the K1
 // segment that holds it: chain slot r = row r's draft, tree slot n = node n's
@@ -119,7 +119,8 @@ struct K3Cand {
 struct K3Rec {
   float lo;           // L_c (-inf: no id of the chunk has positive weight)
   float ovf;          // the largest upper bound among candidates left out (-inf: none)
-  int32_t count;      // candidates listed, <= kRecCand
+  int32_t count;      // 0 until the record is complete, then 1 + the candidates listed (<= kRecCand);
+                      // cleared by the request's first K1 segment of each call
   int32_t pad;
   K3Cand cand[kRecCand];
 };
@@ -1258,7 +1259,8 @@ __device__ __forceinline__ void k3_sample(const Params& P, const Job& J, int b, 
     if (tid == 0) {
       cst_f32(&rec->lo, L);
       cst_f32(&rec->ovf, ovf);
-      cst_i32(&rec->count, nc);
+      wait_mem();  // this wave's record stores are complete
+      cst_i32(&rec->count, nc + 1);
     }
   }
 }
@@ -1271,7 +1273,8 @@ __device__ __forceinline__ void sample_chunk(const Params& P, int b, int c3, Sme
   else k3_sample<BF16, JOB_P>(P, sm.job, b, c3, sm);
 }
 
-// Merge of one race by the request's last chunk: L = the largest certified
+// Merge of one race by the request's last chunk, once every chunk's record
+// is complete: L = the largest certified
 // lower bound over all chunks.  The winner's upper bound reaches L, so it
 // is among the listed candidates whose upper bound reaches L, unless a
 // chunk had to leave out such a candidate (then, or when L is too small for
@@ -1294,7 +1297,7 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, Smem& sm) {
   if (!fallback) {
     for (int c = tid; c < P.C3; c += kWG) {
       const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
-      const int cnt = cld_i32(&rec->count);
+      const int cnt = min(max(cld_i32(&rec->count) - 1, 0), kRecCand);
       for (int i = 0; i < cnt; ++i) {
         const float h = cld_f32(&rec->cand[i].hi);
         if (h >= L) {
@@ -1352,6 +1355,13 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
   const int n_seg = (int)(min((int64_t)s1 * P.SUB, (int64_t)P.V) - start);
   u32x4 raw0[kVecPerThread];
   k1_issue<BF16>(P, row * P.lstride + start, n_seg, raw0);
+  // The workspace region of the sampling records depends on the call's
+  // shape, so it may hold anything: the segment that starts the request's
+  // first row clears the request's completion markers (wave 0, whose
+  // stores the count below waits for; a kernel boundary orders them for
+  // the phased schedule).
+  if (MODE != MODE_ROWS && r == 0 && s0 == 0 && threadIdx.x < 64)
+    for (int c = threadIdx.x; c < P.C3; c += 64) cst_i32(&P.k3[(int64_t)b * P.C3 + c].count, 0);
   const float T = temp_of(P, b);
   bool need = true;
   if (MODE == MODE_CHAIN) {
@@ -1477,22 +1487,39 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
     if (uniform_i(sm.job.kind) != JOB_NONE) {
       sample_chunk<BF16>(P, b, c3, sm);
       sampled = true;
+    } else if (stoch && tid == 0) {
+      cst_i32(&P.k3[(int64_t)b * P.C3 + c3].count, 1);  // complete, nothing raced
     }
   }
-  if (!stoch && P.sched != SCHED_FUSED) return;  // nothing to count
-  __syncthreads();
-  if (tid == 0) {
-    wait_mem();  // this wave wrote the chunk's record
-    const uint32_t old = atomic_add_relaxed(&P.sync[b].k3_count, 1u);
-    const int last = (old == (uint32_t)P.C3 - 1u);
-    if (last) {
-      cst32(&P.sync[b].k3_count, 0u);
-      cst32(&P.sync[b].k1_count, 0u);
-    }
-    sm.flag = last && sampled && !cld32(&P.ctrl->aborted);
+  if (!stoch) {
+    // only chunk 0 worked; in the fused schedule it was the counter's last user
+    if (P.sched == SCHED_FUSED && work && ok && tid == 0) cst32(&P.sync[b].k1_count, 0u);
+    return;
   }
-  __syncthreads();
-  if (uniform_i(sm.flag)) k3_merge<BF16>(P, b, sm);
+  if (c3 != P.C3 - 1) return;
+  // The request's last chunk (dispatched after all its others, so none of
+  // them waits on it) merges once every chunk's record is complete (bounded
+  // wait), then resets the request's counter.
+  int done = ok;
+  if (ok) {
+    for (int c = tid; c < P.C3; c += kWG) {
+      uint32_t spins = 0;
+      while (cld_i32(&P.k3[(int64_t)b * P.C3 + c].count) == 0) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit || cld32(&P.ctrl->aborted)) {
+          done = 0;
+          break;
+        }
+      }
+    }
+  }
+  done = block_min_i(done, sm);
+  if (!done && ok && tid == 0) {
+    cst32(&P.ctrl->aborted, 1u);
+    if (P.status) P.status[b] = SV_REQ_INTERNAL;
+  }
+  if (done && sampled) k3_merge<BF16>(P, b, sm);
+  if (tid == 0 && P.sched == SCHED_FUSED) cst32(&P.sync[b].k1_count, 0u);
 }
 
 template <int MODE, bool BF16>

@@ -196,6 +196,28 @@ def test_workspace_reuse_across_shapes(dev):
         _compare(ref, _np(out), f"reuse {bs}x{k}x{V}")
 
 
+@pytest.mark.parametrize("flags", [sv.FLAG_PHASED, sv.FLAG_FUSED])
+def test_workspace_reuse_chain_then_tree(dev, flags):
+    """Calls of different kinds and shapes on one workspace: each call's
+    sampling records sit where the previous call kept other data, so a call
+    must not trust that region's contents (a tree call after a chain call
+    once read stale completion markers)."""
+    ws = sv.Workspace(1 << 20, dev)
+    for i in range(2):
+        inp = workloads.chain_bf16_mixed(20 + i, bs=24, V=50000)
+        ref = oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=inp.draft_probs)
+        out = sv.verify_chain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev),
+                              _t(inp.seeds, dev), draft_probs=_t(inp.draft_probs, dev), flags=flags, workspace=ws)
+        torch.cuda.synchronize()
+        _compare(ref, _np(out), f"reuse chain {i}")
+        t = workloads.tree_fp32(30 + i, bs=12, V=40000)
+        ref = oracle.verify_tree(t.logits, t.node_tokens, t.parent, t.temperature, t.seeds)
+        out = sv.verify_tree(_t(t.logits, dev), _t(t.node_tokens, dev), _t(t.parent, dev), _t(t.temperature, dev),
+                             _t(t.seeds, dev), flags=flags, workspace=ws)
+        torch.cuda.synchronize()
+        _compare(ref, _np(out), f"reuse tree {i}", extra=("accept_path",))
+
+
 # ---------------------------------------------------- random small shapes
 def _random_chain(seed, bs, k, V, dtype, kind, greedy_frac=0.3, pad_frac=0.3, scale=3.0):
     rng = np.random.default_rng(seed)
