@@ -155,14 +155,14 @@ struct Params {
   Gather* gat;        // [bs][SV_MAX_NODES]
   Partial* part;      // [bs*R][CPR]
   K3Rec* k3;          // [bs][C3]
-  int64_t F;          // sub-chunks of all rows, flattened
-  double Finv;        // 1 / F
   int32_t SUB;        // entries per K1 sub-chunk
   int32_t nsub;       // sub-chunks per row
-  int32_t G;          // K1 workgroups
-  int32_t Q;          // > 0: every row is split into Q segments, one per workgroup; 0: flattened ranges
-  int32_t CPR;        // partial slots per row
+  int32_t Q;          // segments (K1 items, partials) per row, <= 64
+  int32_t Qp;         // the power of two >= Q
+  int32_t G;          // K1 items: rows * Q
+  int32_t CPR;        // partial slots per row (= Q)
   int32_t C3;         // sampling chunks per request
+  int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
   uint32_t flags;
 };
@@ -603,28 +603,10 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
   }
 }
 
-// Split of the flattened sub-chunks f = row * nsub + s over the G K1
-// workgroups: workgroup w takes [floor(w F / G), floor((w + 1) F / G)).
-__host__ __device__ __forceinline__ int64_t k1_range_begin(int64_t w, int64_t F, int64_t G) { return w * F / G; }
-// The workgroup whose range holds sub-chunk f.
-__host__ __device__ __forceinline__ int64_t k1_wg_of(int64_t f, int64_t F, int64_t G) { return ((f + 1) * G - 1) / F; }
-// The same on the device, without a 64-bit integer division: the quotient
-// x / F (x < 2^47) from fp64 with 1/F, then corrected to the exact floor.
-__device__ __forceinline__ int64_t k1_wg_of_dev(const Params& P, int64_t f) {
-  const int64_t x = (f + 1) * (int64_t)P.G - 1;
-  int64_t q = (int64_t)((double)x * P.Finv);
-  if (q * P.F > x) --q;
-  else if ((q + 1) * P.F <= x) ++q;
-  return q;
-}
-// The first workgroup of a row, and the number of segments (partials) the row has.
-__device__ __forceinline__ int64_t k1_first_wg(const Params& P, int64_t row) {
-  return k1_wg_of_dev(P, row * P.nsub);
-}
-__device__ __forceinline__ int k1_segments(const Params& P, int64_t row) {
-  if (P.Q > 0) return P.Q;
-  return (int)(k1_wg_of_dev(P, row * P.nsub + P.nsub - 1) - k1_first_wg(P, row) + 1);
-}
+// Every row is split into Q segments of (almost) equal length, one K1
+// work item each: segment c of a row covers sub-chunks [c nsub / Q,
+// (c + 1) nsub / Q) and writes the row's partial c.
+__device__ __forceinline__ int k1_segments(const Params& P, int64_t row) { return P.Q; }
 
 // ===================================================================== K2
 // p(y) of a stochastic row in fp64: exp((l - m)/T) / S.
@@ -638,72 +620,78 @@ __device__ __forceinline__ double exp2_scale(double x) {
   return ldexp((double)__builtin_amdgcn_exp2f((float)(x - n)), (int)n);
 }
 
-// One row's results from its segments' partials, folded by one lane in
-// segment order: max, first argmax, a bad flag (NaN or +inf seen, the row
-// entirely -inf, or S not positive) and, for stochastic rows,
-// S = sum over segments of S_c 2^((m_c - m) log2(e)/T) in fp64.  The loads
-// of up to kRowLoads partials are issued together.
-constexpr int kRowLoads = 4;
+// Per-row results from the rows' segment partials, into shared memory
+// (rm, ramax, rs, rbad): max, first argmax, a bad flag (NaN or +inf seen,
+// the row entirely -inf, or S not positive) and, for stochastic rows,
+// S = sum over segments of S_c 2^((m_c - m) log2(e)/T) in fp64.  One thread
+// per partial: the Q partials of a row sit in a group of Qp adjacent lanes
+// (Qp the power of two >= Q, so the groups never straddle a wave) and are
+// reduced with butterflies in a fixed order; all loads of a pass are issued
+// together.  Every thread of the workgroup calls it; it ends with a barrier.
+template <bool COH>
+__device__ __forceinline__ void fold_rows(const Params& P, int64_t row0, int nrows, float T, Smem& sm) {
+  const int q = P.Q, qp = P.Qp;
+  const bool stoch = is_stochastic(T);
+  const double cd = stoch ? 1.4426950408889634074 / (double)T : 0.0;
+  for (int e0 = 0; e0 < nrows * qp; e0 += kWG) {
+    const int e = e0 + (int)threadIdx.x;
+    const int r = e / qp, c = e - r * qp;
+    uint64_t ma = 0xFF800000ull, sb = 0ull;  // max -inf, argmax 0, sum 0
+    if (r < nrows && c < q) {
+      const Partial* pt = &P.part[(row0 + r) * P.CPR + c];
+      ma = ld64<COH>(&pt->m_amax);
+      sb = ld64<COH>(&pt->s);
+    }
+    const float pm = __uint_as_float((uint32_t)ma);
+    const int pa = (int)(uint32_t)(ma >> 32);
+    const double ps = __longlong_as_double((long long)sb);
+    int nan = (ps != ps);
+    float m = pm;
+    for (int o = 1; o < qp; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    int a = (pm == m) ? pa : INT32_MAX;
+    double s = 0.0;
+    if (stoch) {
+      if (pm != -INFINITY && m != -INFINITY) s = ps * exp2_scale(((double)pm - (double)m) * cd);
+      else if (ps != ps) s = ps;
+    }
+    for (int o = 1; o < qp; o <<= 1) {
+      a = min(a, __shfl_xor(a, o, 64));
+      s += __shfl_xor(s, o, 64);
+      nan |= __shfl_xor(nan, o, 64);
+    }
+    if (r < nrows && c == 0) {
+      sm.rm[r] = m;
+      sm.ramax[r] = a;
+      sm.rs[r] = stoch ? s : __builtin_nan("");
+      sm.rbad[r] = nan || m == INFINITY || m == -INFINITY || (stoch && !(s > 0.0));
+    }
+  }
+  __syncthreads();
+}
+
 struct RowStats {
   float m;
   int amax;
   double s;
   bool bad;
 };
-template <bool COH>
-__device__ __forceinline__ RowStats fold_row(const Params& P, int64_t row, float T) {
-  const bool stoch = is_stochastic(T);
-  const double cd = stoch ? 1.4426950408889634074 / (double)T : 0.0;
-  const int cnt = k1_segments(P, row);
-  const Partial* pt = &P.part[row * P.CPR];
-  float m = -INFINITY;
-  int a = INT32_MAX;
-  double s = 0.0;
-  bool nan = false;
-  for (int c0 = 0; c0 < cnt; c0 += kRowLoads) {
-    uint64_t ma[kRowLoads], sb[kRowLoads];
-#pragma unroll
-    for (int i = 0; i < kRowLoads; ++i) {
-      ma[i] = 0xFF800000ull;
-      sb[i] = 0ull;
-      if (c0 + i < cnt) {
-        ma[i] = ld64<COH>(&pt[c0 + i].m_amax);
-        sb[i] = ld64<COH>(&pt[c0 + i].s);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kRowLoads; ++i) {
-      if (c0 + i >= cnt) break;
-      const float pm = __uint_as_float((uint32_t)ma[i]);
-      const int pa = (int)(uint32_t)(ma[i] >> 32);
-      const double ps = __longlong_as_double((long long)sb[i]);
-      if (ps != ps) nan = true;
-      if (pm > m) {
-        if (stoch) s = (m == -INFINITY ? 0.0 : s * exp2_scale(((double)m - (double)pm) * cd)) + ps;
-        m = pm;
-        a = pa;
-      } else {
-        if (pm == m) a = min(a, pa);
-        if (stoch && pm != -INFINITY) s += ps * exp2_scale(((double)pm - (double)m) * cd);
-      }
-    }
-  }
-  RowStats r;
-  r.m = m;
-  r.amax = a;
-  r.s = stoch ? s : __builtin_nan("");
-  r.bad = nan || m == INFINITY || m == -INFINITY || (stoch && !(s > 0.0));
-  return r;
+__device__ __forceinline__ RowStats row_stats_of(const Smem& sm, int r) {
+  RowStats x;
+  x.m = sm.rm[r];
+  x.amax = sm.ramax[r];
+  x.s = sm.rs[r];
+  x.bad = sm.rbad[r] != 0;
+  return x;
 }
 
 // Row-statistics call: the "request" is one row.
 __device__ __forceinline__ void k2_rows(const Params& P, int b, Smem& sm) {
+  fold_rows<true>(P, b, 1, temp_of(P, b), sm);
   if (threadIdx.x == 0) {
-    const RowStats r = fold_row<true>(P, b, temp_of(P, b));
-    if (P.rs_max) P.rs_max[b] = r.m;
-    if (P.rs_amax) P.rs_amax[b] = r.amax;
-    if (P.rs_sum) P.rs_sum[b] = r.s;
-    if (P.rs_status) P.rs_status[b] = r.bad ? SV_REQ_NONFINITE : SV_REQ_OK;
+    if (P.rs_max) P.rs_max[b] = sm.rm[0];
+    if (P.rs_amax) P.rs_amax[b] = sm.ramax[0];
+    if (P.rs_sum) P.rs_sum[b] = sm.rs[0];
+    if (P.rs_status) P.rs_status[b] = sm.rbad[0] ? SV_REQ_NONFINITE : SV_REQ_OK;
   }
 }
 
@@ -720,20 +708,23 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
+  // the loads first, none depending on another: the drafts and the gathered
+  // target logit and q at each draft (wave 0), every row's partials (rows
+  // after the chain's end hold stale values, ignored)
+  int xi = -1, kb = 0;
+  uint64_t gl = 0;
   if (tid < 64) {
-    // every load first, none depending on another: the drafts, the gathered
-    // target logit and q at this lane's draft, every row's partials (rows
-    // after the chain's end hold stale values, ignored)
-    int xi;
-    const int kb = chain_kb(P, b, xi);
-    uint64_t gl = 0;
+    kb = chain_kb(P, b, xi);
     if (lane < k) gl = ld64<COH>(&P.gat[(int64_t)b * SV_MAX_NODES + lane]);
+  }
+  fold_rows<COH>(P, (int64_t)b * R, R, Tf, sm);
+  if (tid < 64) {
     RowStats rs;
     rs.m = -INFINITY;
     rs.amax = 0;
     rs.s = 1.0;
     rs.bad = false;
-    if (lane < R) rs = fold_row<COH>(P, (int64_t)b * R + lane, Tf);
+    if (lane < R) rs = row_stats_of(sm, lane);
     const bool bad_id = __ballot(lane < kb && (xi < 0 || xi >= V)) != 0;
     int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_id ? SV_REQ_BAD_DRAFT_ID : SV_REQ_OK;
     double u = 0.0;
@@ -814,14 +805,17 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
+  uint32_t gl = 0;  // node lane's token's logit in its parent's row (K1 gathered it)
+  int par = -2, tok = -1;
   if (tid < 64) {
-    uint32_t gl = 0;  // node lane's token's logit in its parent's row (K1 gathered it)
     if (lane >= 1 && lane < N) gl = ld32<COH>(&P.gat[(int64_t)b * SV_MAX_NODES + lane].l);
-    int par = -2, tok = -1;
     if (lane < N) {
       par = P.parent[(int64_t)b * N + lane];
       tok = P.node_tokens[(int64_t)b * N + lane];
     }
+  }
+  fold_rows<COH>(P, (int64_t)b * N, N, Tf, sm);
+  if (tid < 64) {
     bool bad = false;
     if (lane < N) {
       if (lane == 0) bad = (par != -1);
@@ -838,7 +832,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
     rs.amax = 0;
     rs.s = 1.0;
     rs.bad = false;
-    if (lane < N) rs = fold_row<COH>(P, (int64_t)b * N + lane, Tf);
+    if (lane < N) rs = row_stats_of(sm, lane);
     double u = 0.0;
     if (status == SV_REQ_OK && !greedy && lane < N) u = coin(P.seed[b], b, lane);
     if (status == SV_REQ_OK && __ballot(lane < N && rs.bad)) status = SV_REQ_NONFINITE;
@@ -1412,39 +1406,29 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
   }
 }
 
-// K1 workgroup w: with Q > 0 (no more rows than K1 workgroups), segment
-// w % Q of row w / Q; else its range of flattened sub-chunks, one segment
-// per row it touches (a range is never longer than a row, so it touches at
-// most two).
+// K1 item o of request b: segment o % Q of row o / Q.
 template <int MODE, bool BF16>
-__device__ __forceinline__ void run_k1_range(const Params& P, int64_t w, Smem& sm) {
-  if (P.Q > 0) {
-    // row-aligned: segment c of row w / Q, sub-chunks [c nsub / Q, (c + 1) nsub / Q)
-    const int q = P.Q;
-    const int row = (int)(w / q), c = (int)(w - (int64_t)row * q);
-    const int b = row / P.R;
-    run_k1_seg<MODE, BF16>(P, b, row - b * P.R, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c,
-                           sm);
-    return;
-  }
-  const int64_t f0 = k1_range_begin(w, P.F, P.G);
-  int rem = (int)(k1_range_begin(w + 1, P.F, P.G) - f0);
-  int row = (int)(f0 / P.nsub);
-  int s = (int)(f0 - (int64_t)row * P.nsub);
-  int slot = (int)(w - k1_first_wg(P, row));
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    if (rem > 0) {
-      const int len = min(rem, P.nsub - s);
-      const int b = row / P.R;
-      run_k1_seg<MODE, BF16>(P, b, row - b * P.R, s, s + len, slot, sm);
-      rem -= len;
-      ++row;
-      s = 0;
-      slot = 0;  // a range that goes on into the next row starts it
-      __syncthreads();
-    }
-  }
+__device__ __forceinline__ void run_k1_item(const Params& P, int b, int o, Smem& sm) {
+  const int q = P.Q;
+  const int r = o / q, c = o - r * q;
+  run_k1_seg<MODE, BF16>(P, b, r, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c, sm);
+}
+
+// Request order of the fused schedule: for batches of at most 64 requests
+// the sampling requests go first (then the others, each group in index
+// order), so that the requests whose decision steps end the launch are
+// the ones with no race to run; larger batches keep index order.
+__device__ __forceinline__ int request_at(const Params& P, int g) {
+  if (P.bs > 64) return g;
+  const int lane = threadIdx.x & 63;
+  const uint64_t st = __ballot(lane < P.bs && is_stochastic(P.temp[lane]));
+  const int ns = __popcll(st);
+  const uint64_t want = g < ns ? st : (~st & (P.bs == 64 ? ~0ull : ((1ull << P.bs) - 1ull)));
+  const int k = g < ns ? g : g - ns;
+  // the position of the k-th set bit of `want`
+  const uint64_t below = (lane == 0) ? 0ull : (want & ((1ull << lane) - 1ull));
+  const uint64_t hit = __ballot(((want >> lane) & 1ull) && __popcll(below) == k);
+  return (int)__builtin_ctzll(hit);
 }
 
 // Sampling chunk c3 of request b, after its own run of the decision step.
@@ -1525,7 +1509,9 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, SV_K1_OCC) void k1_kernel(Params P) {
   __shared__ Smem sm;
-  run_k1_range<MODE, BF16>(P, blockIdx.x, sm);
+  const int n1 = P.R * P.Q;
+  const int b = (int)(blockIdx.x / (uint32_t)n1);
+  run_k1_item<MODE, BF16>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)n1), sm);
 }
 
 template <int MODE, bool BF16>
@@ -1537,17 +1523,42 @@ __global__ __launch_bounds__(kWG, 8) void k23_kernel(Params P) {
   }
 }
 
-// One launch: workgroups [0, G) stream K1 ranges, the rest are sampling
-// chunks (request-major), dispatched after every K1 workgroup.
+// One launch.  Work item order: for g = 0 .. bs + lag - 1, the K1 items of
+// request g (if g < bs), then the sampling chunks of request g - lag (if
+// g >= lag), requests in request_at order.  A sampling chunk waits only for
+// K1 items of its own request and the merge only for chunks of its own
+// request, all earlier in dispatch order.
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
   __shared__ Smem sm;
-  if (blockIdx.x < (uint32_t)P.G) {
-    run_k1_range<MODE, BF16>(P, blockIdx.x, sm);
-  } else if constexpr (MODE != MODE_ROWS) {
-    const uint32_t t = blockIdx.x - (uint32_t)P.G;
-    const int b = (int)(t / (uint32_t)P.C3);
-    run_k23<MODE, BF16, true>(P, b, (int)(t - (uint32_t)b * (uint32_t)P.C3), sm);
+  if constexpr (MODE != MODE_ROWS) {
+    const uint32_t n1 = (uint32_t)(P.R * P.Q), n3 = (uint32_t)P.C3, L = (uint32_t)P.lag, bs = (uint32_t)P.bs;
+    const uint32_t seg1 = L * n1, seg2 = (bs - L) * (n1 + n3);
+    const uint32_t t = blockIdx.x;
+    uint32_t g, o;
+    bool k1;
+    if (t < seg1) {
+      g = t / n1;
+      o = t - g * n1;
+      k1 = true;
+    } else if (t < seg1 + seg2) {
+      const uint32_t u = t - seg1, blk = u / (n1 + n3), oo = u - blk * (n1 + n3);
+      k1 = oo < n1;
+      g = k1 ? L + blk : blk;
+      o = k1 ? oo : oo - n1;
+    } else {
+      const uint32_t u = t - seg1 - seg2;
+      g = bs - L + u / n3;
+      o = u - (g - (bs - L)) * n3;
+      k1 = false;
+    }
+    const int b = uniform_i(request_at(P, (int)g));
+    if (k1) run_k1_item<MODE, BF16>(P, b, (int)o, sm);
+    else run_k23<MODE, BF16, true>(P, b, (int)o, sm);
+  } else {
+    const int n1 = P.R * P.Q;
+    const int b = (int)(blockIdx.x / (uint32_t)n1);
+    run_k1_item<MODE, BF16>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)n1), sm);
   }
 }
 
@@ -1561,45 +1572,27 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 
 // ===================================================================== host
 struct Shape {
-  int SUB, nsub, G, Q, CPR, C3;
-  int64_t F;
+  int SUB, nsub, Q, Qp, G, CPR, C3;
   size_t gat_off, part_off, k3_off, total;
 };
 
 // Work split of a call (a function of the shape alone, so results never
-// depend on the device or the schedule).
+// depend on the device or the schedule): every row in Q segments, as many
+// as the K1 workgroups that are resident at once allow (at most 64 and at
+// most one per sub-chunk; one when there are more rows than that).
 static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   Shape s;
   s.SUB = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
   s.nsub = (int)((V + s.SUB - 1) / s.SUB);
-  s.F = bs * R * s.nsub;
-  const int64_t rows = bs * R;
-  if (rows <= kK1Workgroups) {
-    // every row split evenly into Q segments, one per workgroup: no
-    // workgroup crosses a row
-    int64_t q = kK1Workgroups / rows;
-    if (q > s.nsub) q = s.nsub;
-    if (q > 64) q = 64;
-    s.Q = (int)q;
-    s.G = (int)(rows * q);
-    s.CPR = s.Q;
-  } else {
-    // G workgroups, each with a range of floor(F/G) or ceil(F/G)
-    // sub-chunks: no more than fit on the device at once, a range no longer
-    // than a row (so it touches at most two rows), and no row split into
-    // more than 64 segments (a range of >= fmin sub-chunks; a row then
-    // spans at most ceil((nsub - 1) / fmin) + 1 ranges).
-    s.Q = 0;
-    int64_t G = s.F < kK1Workgroups ? s.F : kK1Workgroups;
-    const int64_t g_row = (s.F + s.nsub - 1) / s.nsub;  // ranges of ceil(F/G) <= nsub
-    if (G < g_row) G = g_row;
-    const int64_t need = s.nsub > 1 ? (s.nsub - 1 + 62) / 63 : 1;  // fmin giving <= 64 spans
-    if (G > s.F / need) G = s.F / need;
-    s.G = (int)G;
-    const int64_t fmin = s.F / s.G;
-    const int64_t spans = (s.nsub - 1 + fmin - 1) / fmin + 1;
-    s.CPR = (int)(spans < s.nsub ? spans : s.nsub);
-  }
+  int64_t q = kK1Workgroups / (bs * R);
+  if (q > s.nsub) q = s.nsub;
+  if (q > 64) q = 64;
+  if (q < 1) q = 1;
+  s.Q = (int)q;
+  s.Qp = 1;
+  while (s.Qp < s.Q) s.Qp *= 2;
+  s.G = (int)(bs * R * q);
+  s.CPR = q;
   s.C3 = races ? (int)((V + kK3Chunk - 1) / kK3Chunk) : 0;
   s.gat_off = kDataOffset;
   s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
@@ -1630,6 +1623,26 @@ static void select_kernels(int mode, bool bf16, KernelFn& k1, KernelFn& k23, Ker
   }
 }
 
+// Workgroups of fused kernel `slot` (mode * 2 + bf16) resident on the
+// current device at once, queried once per device and kernel.
+static std::atomic<int> g_resident[64][6];
+static sv_status resident_workgroups(const void* kernel, int slot, int& out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || slot < 0 || slot >= 6) return SV_ERR_LAUNCH;
+  const int cached = g_resident[dev][slot].load();
+  if (cached > 0) {
+    out = cached;
+    return SV_OK;
+  }
+  int cu = 0, occ = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return SV_ERR_LAUNCH;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kWG, 0) != hipSuccess) return SV_ERR_LAUNCH;
+  if (cu <= 0 || occ <= 0) return SV_ERR_LAUNCH;
+  out = cu * occ;
+  g_resident[dev][slot].store(out);
+  return SV_OK;
+}
+
 static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (ws == nullptr) return SV_ERR_INVALID_ARGUMENT;
   if (ws_bytes < S.total) return SV_ERR_WORKSPACE_TOO_SMALL;
@@ -1642,10 +1655,9 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.k3 = (K3Rec*)(base + S.k3_off);
   P.SUB = S.SUB;
   P.nsub = S.nsub;
-  P.F = S.F;
-  P.Finv = 1.0 / (double)S.F;
-  P.G = S.G;
   P.Q = S.Q;
+  P.Qp = S.Qp;
+  P.G = S.G;
   P.CPR = S.CPR;
   P.C3 = S.C3;
   const int64_t grid23 = (int64_t)P.bs * P.C3;
@@ -1655,6 +1667,16 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : SCHED_PHASED;
   KernelFn k1, k23, fused;
   select_kernels(P.mode, P.dtype == SV_BF16, k1, k23, fused);
+  // fused: every K1 item first, then the sampling chunks (a lag of the
+  // whole batch; smaller lags interleave them, SV_FUSED_LAG, for tuning)
+  P.lag = P.bs;
+  if (P.sched == SCHED_FUSED && P.mode != MODE_ROWS) {
+    const char* e = getenv("SV_FUSED_LAG");
+    if (e && *e) {
+      const int l = atoi(e);
+      if (l >= 0 && l < P.bs) P.lag = l;
+    }
+  }
   if (P.mode == MODE_ROWS) {
     hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
   } else if (P.sched == SCHED_PHASED) {
