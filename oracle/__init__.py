@@ -75,6 +75,10 @@ def lib():
         L.svo_coin.restype = _D
         L.svo_noise_uniform.argtypes = [ctypes.c_uint64, _I32, _I32, _I32]
         L.svo_noise_uniform.restype = _D
+        L.svo_chunk_uniform.argtypes = [ctypes.c_uint64, _I32, _I32, _I32]
+        L.svo_chunk_uniform.restype = _D
+        L.svo_race.argtypes = [_P, _I32, _I32, ctypes.c_uint64, _I32, _I32, _P]
+        L.svo_race.restype = _I32
         L.svo_row_stats.argtypes = [_I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P]
         L.svo_row_stats.restype = None
         L.svo_verify_chain.argtypes = [ctypes.POINTER(_ChainArgs)]
@@ -119,6 +123,21 @@ def coin(seed: int, b: int, r: int) -> float:
 
 def noise_uniform(seed: int, b: int, r: int, y: int) -> float:
     return lib().svo_noise_uniform(int(seed), int(b), int(r), int(y))
+
+
+def chunk_uniform(seed: int, b: int, r: int, c: int) -> float:
+    return lib().svo_chunk_uniform(int(seed), int(b), int(r), int(c))
+
+
+RACE_CHUNK = 2048
+
+
+def race(w, seed: int, b: int, r: int, chunk: int = RACE_CHUNK):
+    """The two-level exponential race over the weights w (fp64): (id, margin)."""
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float64))
+    m = np.zeros(1, np.float64)
+    y = lib().svo_race(_ptr(w), int(w.size), int(chunk), int(seed), int(b), int(r), _ptr(m))
+    return int(y), float(m[0])
 
 
 def row_stats(logits, temperature):

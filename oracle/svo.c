@@ -23,11 +23,14 @@
  *  - randomness is a counter-based Philox4x32-10 stream keyed by the request
  *    seed; the coin for row r of request b is word 0 of counter (0, r, b, 0);
  *    the race noise for vocab id y is word (y & 3) of counter (y>>2, r, b, 1);
+ *    the chunk noise for chunk c is word 0 of counter (c, r, b, 2);
  *  - uniforms are (2*(w>>9)+1)/2^24, inside (0,1) and exact in fp32;
  *  - the acceptance test is strict (u*q < p); q(x) <= 0 accepts iff p(x) > 0;
- *  - the residual / bonus sample is an exponential race: argmax_y w(y)/E_y
- *    with E_y = -ln U_y, ties to the smallest y; an all-zero residual falls
- *    back to p;
+ *  - the residual / bonus sample is a two-level exponential race: the ids
+ *    are cut into chunks of SVO_RACE_CHUNK; the chunk c maximising
+ *    W_c / E_c (W_c its weight sum, E_c = -ln U_c) is chosen, then the id y
+ *    of that chunk maximising w(y) / E_y, ties to the smaller index at both
+ *    levels; an all-zero residual falls back to p;
  *  - argmax ties go to the smallest index, on raw logits;
  *  - T <= 0 means greedy, a non-finite T is rejected;
  *  - draft id -1 ends the chain; NaN/+inf logits or an all -inf row are
@@ -82,6 +85,13 @@ static void seed_key(uint64_t seed, uint32_t key[2]) {
 
 double svo_coin(uint64_t seed, int32_t b, int32_t r) {
   uint32_t key[2], ctr[4] = {0u, (uint32_t)r, (uint32_t)b, 0u}, out[4];
+  seed_key(seed, key);
+  svo_philox4x32_10(ctr, key, out);
+  return svo_uniform(out[0]);
+}
+
+double svo_chunk_uniform(uint64_t seed, int32_t b, int32_t r, int32_t c) {
+  uint32_t key[2], ctr[4] = {(uint32_t)c, (uint32_t)r, (uint32_t)b, 2u}, out[4];
   seed_key(seed, key);
   svo_philox4x32_10(ctr, key, out);
   return svo_uniform(out[0]);
@@ -162,20 +172,53 @@ void svo_row_stats(int32_t rows, int32_t vocab, int32_t dtype, const void* logit
 }
 
 /* ------------------------------------------------------------------------ */
-/* Exponential race over non-negative weights w[0..V):
- *   y* = argmax_y w(y) / E_y,  E_y = -ln U_y,
- * with U_y from the race-noise stream of (seed, b, r).  Because E_y are
- * independent Exp(1) variables, P(y* = y) = w(y) / sum w, so this samples
- * the normalised weights exactly; the Gumbel-max trick of the vLLM resample
- * step quoted in [SD] "采样：标准拒绝采样" is the same race in log space.
- * Ties go to the smallest y.  Writes the relative gap between the two
- * largest keys to *margin. */
-static int32_t race(const double* w, int32_t V, uint64_t seed, int32_t b, int32_t r, double* margin) {
-  int32_t best = -1;
+/* Exponential race over non-negative weights, two levels.
+ *
+ * One level: y* = argmax_y w(y) / E_y with E_y = -ln U_y independent Exp(1)
+ * variables gives P(y* = y) = w(y) / sum w, an exact sample of the
+ * normalised weights (the Gumbel-max trick of the vLLM resample step quoted
+ * in [SD] "采样：标准拒绝采样" is the same race in log space).
+ *
+ * Two levels: the ids are cut into consecutive chunks of `chunk` ids; first
+ * the chunks race with their weight sums W_c and the chunk noise, then the
+ * ids of the winning chunk race with their own weights and the id noise.
+ * The chunk wins with probability W_c / sum W and, given the chunk, the id
+ * with probability w(y) / W_c (the two noise streams are independent), so
+ * the sample is still exact; a single chunk is the one-level race.
+ *
+ * Ties go to the smaller chunk and the smaller id.  Writes the smaller of
+ * the two levels' relative gaps between their two largest keys to *margin
+ * (the gap is 1 for a level with a single positive key). */
+static double top_gap(double k1, double k2) {
+  if (k2 < 0.0) k2 = 0.0;
+  return (k1 > 0.0) ? (k1 - k2) / k1 : 0.0;
+}
+
+int32_t svo_race(const double* w, int32_t V, int32_t chunk, uint64_t seed, int32_t b, int32_t r,
+                 double* margin) {
+  const int32_t nchunk = (V + chunk - 1) / chunk;
+  int32_t cbest = -1;
   double k1 = -1.0, k2 = -1.0;
-  for (int32_t y = 0; y < V; ++y) {
-    double E = -log(svo_noise_uniform(seed, b, r, y));
-    double key = w[y] / E;
+  for (int32_t c = 0; c < nchunk; ++c) {
+    const int32_t y1 = (c + 1) * chunk < V ? (c + 1) * chunk : V;
+    double W = 0.0;
+    for (int32_t y = c * chunk; y < y1; ++y) W += w[y];
+    const double key = W / -log(svo_chunk_uniform(seed, b, r, c));
+    if (key > k1) {
+      k2 = k1;
+      k1 = key;
+      cbest = c;
+    } else if (key > k2) {
+      k2 = key;
+    }
+  }
+  const double gap_chunk = top_gap(k1, k2);
+  int32_t best = -1;
+  k1 = -1.0;
+  k2 = -1.0;
+  const int32_t y0 = cbest * chunk, y1 = (cbest + 1) * chunk < V ? (cbest + 1) * chunk : V;
+  for (int32_t y = y0; y < y1; ++y) {
+    const double key = w[y] / -log(svo_noise_uniform(seed, b, r, y));
     if (key > k1) {
       k2 = k1;
       k1 = key;
@@ -184,9 +227,13 @@ static int32_t race(const double* w, int32_t V, uint64_t seed, int32_t b, int32_
       k2 = key;
     }
   }
-  if (k2 < 0.0) k2 = 0.0;
-  *margin = (k1 > 0.0) ? (k1 - k2) / k1 : 0.0;
+  const double gap_id = top_gap(k1, k2);
+  if (margin) *margin = gap_chunk < gap_id ? gap_chunk : gap_id;
   return best;
+}
+
+static int32_t race(const double* w, int32_t V, uint64_t seed, int32_t b, int32_t r, double* margin) {
+  return svo_race(w, V, SVO_RACE_CHUNK, seed, b, r, margin);
 }
 
 /* Sample from normalize(w); if every weight is zero, from p instead. */

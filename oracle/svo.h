@@ -42,6 +42,16 @@ double svo_uniform(uint32_t w);
 /* The coin for row r of request b, and the race noise word for vocab id y. */
 double svo_coin(uint64_t seed, int32_t b, int32_t r);
 double svo_noise_uniform(uint64_t seed, int32_t b, int32_t r, int32_t y);
+/* Chunk noise of the two-level race: word 0 of counter (c, r, b, 2). */
+double svo_chunk_uniform(uint64_t seed, int32_t b, int32_t r, int32_t c);
+
+/* Ids per chunk of the sampling race. */
+#define SVO_RACE_CHUNK 2048
+
+/* The two-level exponential race over w[0..V) with `chunk` ids per chunk
+ * (the verifiers use SVO_RACE_CHUNK); *margin (may be NULL) receives the
+ * smaller relative top-two key gap of the two levels. */
+int32_t svo_race(const double* w, int32_t V, int32_t chunk, uint64_t seed, int32_t b, int32_t r, double* margin);
 
 /* Row statistics of `rows` logit rows.  Row i starts at element i*row_stride.
  * temperature[i] <= 0 or non-finite means greedy (no sum is formed; sumexp = NaN).

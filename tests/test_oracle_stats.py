@@ -342,3 +342,73 @@ def test_markov_chain_sequences_match_exact_joint():
     exact = np.einsum("a,ab,bc->abc", Pw[s0], Pw, Pw).reshape(-1)
     chi2, pv, dof = chi2_pvalue(np.bincount(idx, minlength=64), exact)
     assert pv > P_PASS, (chi2, dof, pv)
+
+
+# ------------------------------------------------ the two-level sampling race
+def test_single_chunk_race_is_the_one_level_race():
+    """With one chunk the race is argmax_y w(y) / -ln U_y over the id noise
+    alone (the textbook exponential race / Gumbel-max), ties to the
+    smaller id."""
+    rng = np.random.default_rng(77)
+    for trial in range(20):
+        V = int(rng.integers(1, 300))
+        w = rng.random(V) * (rng.random(V) < 0.7)
+        if not w.any():
+            w[0] = 1.0
+        seed, b, r = int(rng.integers(0, 2**63)), int(rng.integers(0, 64)), int(rng.integers(0, 8))
+        E = -np.log([oracle.noise_uniform(seed, b, r, y) for y in range(V)])
+        want = int(np.argmax(w / E))
+        assert oracle.race(w, seed, b, r, chunk=V)[0] == want
+        assert oracle.race(w, seed, b, r, chunk=V + 5)[0] == want
+
+
+def test_two_level_race_samples_the_weights_small_chunks():
+    """Chunks of 4 ids over V = 10 (the last chunk partial, one chunk all
+    zero): the two-level race still samples w / sum w exactly."""
+    w = np.array([0.5, 0.0, 1.5, 0.25, 0.0, 0.0, 0.0, 0.0, 2.0, 0.75])
+    n = 300_000
+    L = oracle.lib()
+    wc = np.ascontiguousarray(w)
+    ptr = wc.ctypes.data_as(__import__("ctypes").c_void_p)
+    seed = 0x5EED5EED1234
+    out = np.array([L.svo_race(ptr, 10, 4, seed, b % 4096, b // 4096, None) for b in range(n)])
+    chi2, pv, dof = chi2_pvalue(np.bincount(out, minlength=10), w / w.sum())
+    assert pv > P_PASS, (chi2, dof, pv)
+
+
+def test_two_level_race_samples_the_weights_at_the_verifier_chunk():
+    """The verifiers' chunk (2048 ids) over V = 2*2048 + 300: the chunk
+    frequencies follow the chunk weight sums, and the ids inside a chunk
+    follow their weights (coarse bins)."""
+    rng = np.random.default_rng(5)
+    V, C = 2 * 2048 + 300, oracle.RACE_CHUNK
+    w = rng.random(V) ** 3
+    w[100:2048] = 0.0            # chunk 0 is light: ids 0..99 only
+    w[2048 + 7] = 40.0           # one heavy id in chunk 1
+    n = 24_000
+    L = oracle.lib()
+    wc = np.ascontiguousarray(w)
+    ptr = wc.ctypes.data_as(__import__("ctypes").c_void_p)
+    out = np.array([L.svo_race(ptr, V, C, 99, b % 64, b // 64, None) for b in range(n)])
+    assert (w[out] > 0).all()
+    chunk = out // C
+    sums = np.array([w[:C].sum(), w[C:2 * C].sum(), w[2 * C:].sum()])
+    chi2, pv, dof = chi2_pvalue(np.bincount(chunk, minlength=3), sums / sums.sum())
+    assert pv > P_PASS, (chi2, dof, pv)
+    # inside chunk 1: the heavy id against 8 bins of the rest
+    sel = out[chunk == 1] - C
+    bins = np.where(sel == 7, 8, np.minimum(sel * 8 // C, 7))
+    wb = np.array([w[C + i * C // 8: C + (i + 1) * C // 8].sum() for i in range(8)])
+    wb[0] -= w[C + 7]
+    probs = np.append(wb, w[C + 7]) / w[C:2 * C].sum()
+    chi2, pv, dof = chi2_pvalue(np.bincount(bins, minlength=9), probs)
+    assert pv > P_PASS, (chi2, dof, pv)
+
+
+def test_chunk_noise_is_its_own_stream():
+    """Chunk noise of chunk c is word 0 of Philox counter (c, r, b, 2)."""
+    seed = 0x0123456789ABCDEF
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for c in (0, 1, 62, 1000):
+        out = oracle.philox4x32_10([c, 3, 11, 2], key)
+        assert oracle.chunk_uniform(seed, 11, 3, c) == oracle.uniform(int(out[0]))
