@@ -8,10 +8,20 @@ are resident in HBM before the timed region; the timed steps rotate over
 several input sets whose total size exceeds the 256 MB Infinity Cache, so
 the stream really comes from HBM.
 
-Prints one JSON line: verified draft positions per second (value), plus the
-roofline of the verify kernel (algorithmic bytes per launch / measured
-launch duration, against the 8 TB/s HBM peak) and the oracle timed on the
-host as a CPU baseline.
+The call is two stream-ordered kernels: the row-statistics pass (streams
+every logit row once; the dominant kernel) and the decision/sampling pass.
+Two timed passes over the same K steps:
+  1. throughput: K plain calls between two events -> value, ms_per_step;
+  2. kernels: the same K calls, split into their two phases
+     (FLAG_STATS_ONLY, FLAG_DECIDE_ONLY) and grouped by input set: the
+     row-statistics launches of all sets between one event pair, then their
+     decision launches between the next (each set has its own workspace)
+     -> each kernel's mean launch duration, and the roofline of the
+     row-statistics kernel (its algorithmic bytes / that duration, against
+     the 8 TB/s HBM peak).
+The fused schedule is one launch; there the roofline covers the whole call.
+
+Prints one JSON line, with the oracle timed on the host as a CPU baseline.
 """
 from __future__ import annotations
 
@@ -41,34 +51,37 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(inp, accept_len) -> int:
-    """Bytes the method must move for one call, from the actual outcomes:
-    every read logit row (rows 0..k_b of each request) once, the gathers at
-    the draft ids (logit, id, q value), per-request scalars, the re-read of
-    the one sampled row per stochastic request (its logits, plus its q row
-    after a standard rejection), and the outputs."""
+def algorithmic_bytes(inp, accept_len):
+    """Bytes the method must move for one call, from the actual outcomes,
+    split by phase.  Row statistics: every read logit row (rows 0..k_b of
+    each request) once, the gathers at the draft ids (logit, id, q value)
+    and the temperature.  Decision/sampling: per-request scalars, the
+    re-read of the one sampled row per stochastic request (its logits, plus
+    its q row after a standard rejection), and the outputs.  Returns
+    (stats_bytes, decide_bytes)."""
     bs, R, V = inp.logits.shape
     k = R - 1
     bl = inp.logits.dtype.itemsize
     ids = inp.draft_ids
     kb = np.where((ids == -1).any(axis=1), np.argmax(ids == -1, axis=1), k) if k else np.zeros(bs, np.int64)
     stoch = (inp.temperature > 0) & np.isfinite(inp.temperature)
-    total = 0
+    stats = decide = 0
     for b in range(bs):
-        total += (kb[b] + 1) * V * bl                                        # streamed rows
-        total += kb[b] * (bl + 4 + (0 if inp.onehot else 4))                 # gathers at the draft ids
-        total += 4 + 8 + 4 * k                                               # temperature, seed, ids
+        stats += (kb[b] + 1) * V * bl                                         # streamed rows
+        stats += kb[b] * (bl + 4 + (0 if inp.onehot else 4))                  # gathers at the draft ids
+        stats += 4                                                            # temperature
+        decide += 4 + 8 + 4 * k                                               # temperature, seed, ids
         if stoch[b]:
             reject = accept_len[b] < kb[b]
-            total += V * bl + (V * 4 if (reject and not inp.onehot) else 0)  # sampled row (+ q row)
-        total += 4 + 4 * R + 4                                               # accept_len, tokens, status
-    return int(total)
+            decide += V * bl + (V * 4 if (reject and not inp.onehot) else 0)  # sampled row (+ q row)
+        decide += 4 + 4 * R + 4                                               # accept_len, tokens, status
+    return int(stats), int(decide)
 
 
-def load_traffic(workload: str):
-    """HBM traffic per launch measured with rocprofv3 counters for this
-    kernel source (committed under profiles/), or None if the kernel changed
-    since the counters were taken."""
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters for
+    this kernel source (committed under profiles/), or None if there is no
+    record or the kernel changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -76,7 +89,7 @@ def load_traffic(workload: str):
         rec = json.load(f)
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
 def cpu_baseline(inputs, seconds: float):
@@ -109,6 +122,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
                     help="library schedule (auto: the library's default for the shape)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB a few times (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification hot path runs on a single MI355X here; "
@@ -116,6 +132,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration_mib:
+        dev = torch.device("cuda", 0)
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.zeros_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     import lossless_draft_verification_amd as sv
     import workloads
@@ -136,12 +163,11 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     flags = {"auto": 0, "phased": sv.FLAG_PHASED, "fused": sv.FLAG_FUSED}[args.schedule]
-    ws = sv.Workspace(1 << 20, dev)
     calls = []
     for inp in inputs:
         calls.append(sv.PreparedChain(to_dev(inp.logits), to_dev(inp.draft_ids), to_dev(inp.temperature),
                                       to_dev(inp.seeds), draft_probs=to_dev(inp.draft_probs), onehot=inp.onehot,
-                                      flags=flags, workspace=ws))
+                                      flags=flags, workspace=sv.Workspace(1 << 20, dev)))
     resident = sum(c.logits.numel() * c.logits.element_size() + (c.q.numel() * 4 if c.q is not None else 0)
                    for c in calls)
     stream = torch.cuda.current_stream(dev)
@@ -153,6 +179,16 @@ def main():
         if (c.out["status"] != 0).any():
             raise RuntimeError("a request reported a non-OK status on the benchmark inputs")
         alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy()))
+        if args.schedule != "fused":
+            # the split phases must reproduce the plain call
+            ref = {n: t.clone() for n, t in c.out.items()}
+            for t in c.out.values():
+                t.fill_(-7)
+            c.launch(phase_flag=sv.FLAG_STATS_ONLY)
+            c.launch(phase_flag=sv.FLAG_DECIDE_ONLY)
+            torch.cuda.synchronize()
+            if any(not torch.equal(ref[n], c.out[n]) for n in ref):
+                raise RuntimeError("split-phase call differs from the plain call")
     positions = [int((inp.draft_ids >= 0).cumprod(axis=1).sum()) for inp in inputs]
 
     for i in range(args.warmup):
@@ -160,24 +196,52 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # pass 1: throughput of plain calls
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         calls[i % len(calls)].launch()
-        ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     pos_total = sum(positions[i % len(calls)] for i in range(K))
-    bytes_total = sum(alg[i % len(calls)] for i in range(K))
     value = pos_total / (total_ms * 1e-3)
-    achieved = bytes_total / (launch_ms.sum() * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+
+    # pass 2: per-kernel durations; events on the launch stream around each
+    # group of one phase's launches over all input sets
+    split = args.schedule != "fused"
+    S = len(calls)
+    groups = max(1, K // S)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(groups)]
+    torch.cuda.synchronize()
+    for g in range(groups):
+        ev[g][0].record(stream)
+        if split:
+            for c in calls:
+                c.launch(phase_flag=sv.FLAG_STATS_ONLY)
+            ev[g][1].record(stream)
+            for c in calls:
+                c.launch(phase_flag=sv.FLAG_DECIDE_ONLY)
+        else:
+            for c in calls:
+                c.launch()
+            ev[g][1].record(stream)
+        ev[g][2].record(stream)
+    torch.cuda.synchronize()
+    first_ms = np.array([e[0].elapsed_time(e[1]) for e in ev]) / S
+    second_ms = np.array([e[1].elapsed_time(e[2]) for e in ev]) / S if split else None
+    stats_bytes = np.array([a[0] for a in alg] * groups, dtype=np.float64)
+    decide_bytes = np.array([a[1] for a in alg] * groups, dtype=np.float64)
+    if split:
+        kernel = "row statistics (k1_kernel)"
+        kbytes = stats_bytes
+    else:
+        kernel = "fused verify (fused_kernel)"
+        kbytes = stats_bytes + decide_bytes
+    achieved = kbytes.sum() / (first_ms.sum() * S * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, "k1_kernel" if split else "fused_kernel")
     line = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
         "value": value,
@@ -209,11 +273,19 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": float(np.mean(alg)),
-            "launch_us_mean": float(launch_ms.mean() * 1e3),
-            "launch_us_p50": float(np.median(launch_ms) * 1e3),
+            "kernel": kernel,
+            "algorithmic_bytes_per_launch": float(kbytes.mean()),
+            "launch_us_mean": float(first_ms.mean() * 1e3),
+            "launch_us_p50": float(np.median(first_ms) * 1e3),
         },
     }
+    if split:
+        line["roofline"]["other_kernel"] = {
+            "kernel": "decisions and sampling (k23_kernel)",
+            "algorithmic_bytes_per_launch": float(decide_bytes.mean()),
+            "launch_us_mean": float(second_ms.mean() * 1e3),
+            "achieved": float(decide_bytes.sum() / (second_ms.sum() * S * 1e-3) / 1e9),
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)

@@ -106,6 +106,14 @@ enum {
 #define SV_FLAG_PHASED 1u    /* two stream-ordered launches: row statistics, then decisions and sampling */
 #define SV_FLAG_FP64_RACE 2u /* evaluate every sampling race entirely in fp64 (slow; a test aid) */
 #define SV_FLAG_FUSED 4u     /* one launch: the decision/sampling workgroups wait for their rows' statistics */
+/* Split-phase use of the phased schedule: a call with STATS_ONLY runs only
+ * the row-statistics pass (outputs untouched); a following call with
+ * DECIDE_ONLY, the same descriptor and workspace, on the same stream, runs
+ * the decisions and sampling and writes the outputs.  Together they equal
+ * one plain call; other work may be queued between them.  Neither may be
+ * combined with SV_FLAG_FUSED or with each other. */
+#define SV_FLAG_STATS_ONLY 8u
+#define SV_FLAG_DECIDE_ONLY 16u
 
 typedef struct {
   int32_t batch;              /* bs, 1..SV_MAX_BATCH */

@@ -26,7 +26,7 @@ DRAFT_PROBS, DRAFT_ONEHOT = 0, 1
 # per-request status
 REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE, REQ_INTERNAL = 0, 1, 2, 3, 4, 5
 # flags
-FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED = 1, 2, 4
+FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED, FLAG_STATS_ONLY, FLAG_DECIDE_ONLY = 1, 2, 4, 8, 16
 
 MAX_BATCH, MAX_DRAFT, MAX_NODES, MAX_VOCAB = 65536, 63, 64, 1 << 24
 
@@ -378,9 +378,21 @@ class PreparedChain:
                               self.out["status"].data_ptr(), None, int(flags))
         self._fn = lib().sv_verify_chain
         self._ref = ctypes.byref(self.desc)
+        self._phase_descs, self._phase_refs = [], {}
 
-    def launch(self, stream=None):
+    def launch(self, stream=None, phase_flag=0):
+        """Enqueue the call; phase_flag FLAG_STATS_ONLY or FLAG_DECIDE_ONLY
+        enqueues only that phase (the two, in that order on one stream,
+        equal a plain launch)."""
         s = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream)
-        st = self._fn(self._ref, ctypes.c_void_p(self.ws.base), ctypes.c_size_t(self.ws.nbytes), s)
+        ref = self._ref
+        if phase_flag:
+            ref = self._phase_refs.get(phase_flag)
+            if ref is None:
+                d = ChainDesc.from_buffer_copy(self.desc)
+                d.flags = int(self.desc.flags) | int(phase_flag)
+                self._phase_descs.append(d)
+                ref = self._phase_refs[phase_flag] = ctypes.byref(d)
+        st = self._fn(ref, ctypes.c_void_p(self.ws.base), ctypes.c_size_t(self.ws.nbytes), s)
         if st != OK:
             raise SpecVerifyError(st, "sv_verify_chain")

@@ -1680,8 +1680,8 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   if (P.mode == MODE_ROWS) {
     hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
   } else if (P.sched == SCHED_PHASED) {
-    hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
-    hipLaunchKernelGGL(k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
+    if (!(P.flags & SV_FLAG_DECIDE_ONLY)) hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+    if (!(P.flags & SV_FLAG_STATS_ONLY)) hipLaunchKernelGGL(k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
   } else {
     hipLaunchKernelGGL(fused, dim3((unsigned)(P.G + grid23)), dim3(kWG), 0, stream, P);
   }
@@ -1714,10 +1714,15 @@ const char* sv_status_string(sv_status s) {
 
 static bool dtype_ok(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
 
-static const uint32_t kKnownFlags = SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED;
-// At most one schedule bit.
+static const uint32_t kKnownFlags =
+    SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY;
+// At most one of PHASED, FUSED, STATS_ONLY, DECIDE_ONLY, except PHASED with
+// one of the split-phase bits.
 static bool one_schedule(uint32_t flags) {
-  return (flags & (SV_FLAG_PHASED | SV_FLAG_FUSED)) != (SV_FLAG_PHASED | SV_FLAG_FUSED);
+  const uint32_t split = flags & (SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY);
+  if (split == (SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY)) return false;
+  if ((flags & SV_FLAG_FUSED) && (split || (flags & SV_FLAG_PHASED))) return false;
+  return true;
 }
 
 size_t sv_chain_workspace_bytes(int32_t batch, int32_t max_draft, int32_t vocab, sv_dtype dt) {

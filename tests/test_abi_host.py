@@ -79,7 +79,7 @@ def _call_chain(desc, ws_bytes=1 << 30, ws=0x200000):
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, 1), ("batch", sv.MAX_BATCH + 1, 1), ("max_draft", -1, 1), ("max_draft", 64, 1),
-    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3), ("flags", 8, 3),
+    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3), ("flags", 32, 3),
     ("logits", None, 1), ("temperature", None, 1), ("seed", None, 1), ("accept_len", None, 1),
     ("tokens", None, 1), ("draft_ids", None, 1), ("logits_row_stride", 99, 1), ("draft_probs", None, 1),
     ("q_row_stride", 50, 1),
@@ -89,7 +89,9 @@ def test_chain_argument_validation(field, value, code):
 
 
 def test_schedule_flags_are_exclusive():
-    for f in (sv.FLAG_PHASED | sv.FLAG_FUSED, sv.FLAG_PHASED | sv.FLAG_FUSED | sv.FLAG_FP64_RACE):
+    for f in (sv.FLAG_PHASED | sv.FLAG_FUSED, sv.FLAG_PHASED | sv.FLAG_FUSED | sv.FLAG_FP64_RACE,
+              sv.FLAG_STATS_ONLY | sv.FLAG_DECIDE_ONLY, sv.FLAG_FUSED | sv.FLAG_STATS_ONLY,
+              sv.FLAG_FUSED | sv.FLAG_DECIDE_ONLY):
         assert _call_chain(_chain_desc(flags=f)) == 1
         d = _tree_desc(flags=f)
         assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 1

@@ -162,6 +162,49 @@ def test_all_schedules_are_bit_identical(dev):
             np.testing.assert_array_equal(out[k], ref[k])
 
 
+@pytest.mark.parametrize("name", ["chain_bf16_mixed", "onehot_bf16"])
+def test_split_phases_equal_the_plain_call(dev, name):
+    """STATS_ONLY leaves the outputs alone; STATS_ONLY then DECIDE_ONLY on
+    one stream gives the plain call's outputs, also with other calls on the
+    same workspace queued before."""
+    inp = getattr(workloads, name)(4, bs=20, V=30000)
+    other = workloads.chain_fp32(5, bs=6, V=20000)
+
+    ws = sv.Workspace(1 << 20, dev)
+
+    def prep(x):
+        return sv.PreparedChain(_t(x.logits, dev), _t(x.draft_ids, dev), _t(x.temperature, dev),
+                                _t(x.seeds, dev), draft_probs=_t(x.draft_probs, dev), onehot=x.onehot,
+                                workspace=ws)
+
+    c, o = prep(inp), prep(other)
+    c.launch()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in c.out.items()}
+    for t in c.out.values():
+        t.fill_(-5)
+    c.launch(phase_flag=sv.FLAG_STATS_ONLY)
+    torch.cuda.synchronize()
+    for t in c.out.values():
+        assert bool((t == -5).all())
+    c.launch(phase_flag=sv.FLAG_DECIDE_ONLY)
+    torch.cuda.synchronize()
+    for n in ref:
+        assert torch.equal(ref[n], c.out[n]), n
+    # a second request set on the same workspace in between the phases of
+    # its own call does not disturb the first call's plain rerun
+    o.launch(phase_flag=sv.FLAG_STATS_ONLY)
+    o.launch(phase_flag=sv.FLAG_DECIDE_ONLY)
+    c.launch()
+    torch.cuda.synchronize()
+    for n in ref:
+        assert torch.equal(ref[n], c.out[n]), n
+    out_o = {n: t.cpu().numpy() for n, t in o.out.items()}
+    _, plain_o = run_chain(other, dev)
+    for n in ("accept_len", "tokens", "status"):
+        np.testing.assert_array_equal(out_o[n], plain_o[n])
+
+
 def test_fp64_race_flag_gives_the_same_tokens(dev):
     inp = workloads.chain_fp32(1, bs=6, V=50000)
     _, a = run_chain(inp, dev)
