@@ -27,10 +27,14 @@
  * Randomness is a counter-based Philox4x32-10 stream (Salmon et al., SC'11)
  * keyed by the request's 64-bit seed: the coin of row r of request b is
  * word 0 of counter (0, r, b, 0); the sampling noise of vocabulary id y is
- * word (y & 3) of counter (y >> 2, r, b, 1); a word w maps to the uniform
- * (2*(w >> 9) + 1) / 2^24.  Every sample is an exponential race
- * argmax_y w(y) / E_y, E_y = -ln U_y, ties to the smallest y, so a call is
- * a pure function of its inputs: replaying it replays the result.
+ * word (y & 3) of counter (y >> 2, r, b, 1) and that of id chunk c is word 0
+ * of counter (c, r, b, 2); a word w maps to the uniform (2*(w >> 9) + 1) /
+ * 2^24.  Every sample is a two-level exponential race: the ids are cut into
+ * chunks of 2048; the chunk maximising W_c / E_c (W_c the chunk's weight
+ * sum, E = -ln U) wins, then the id of that chunk maximising w(y) / E_y,
+ * ties to the smaller index at both levels.  This draws y with probability
+ * w(y) / sum w exactly, and a call is a pure function of its inputs:
+ * replaying it replays the result.
  *
  * Conventions.  Every data pointer is DEVICE memory unless marked [host].
  * Logit rows are row-major: element y of row i is at logits + i*row_stride

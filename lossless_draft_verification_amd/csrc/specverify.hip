@@ -75,8 +75,7 @@ constexpr int kK1Depth = SV_K1_DEPTH;           // K1 sub-chunks in flight ahead
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
 constexpr int kK3Groups = 2;                    // groups of 4 vocabulary ids per thread in a sampling chunk
 constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 2048 ids per sampling chunk
-constexpr int kList = 512;                      // race entries a chunk compacts (more: every id is raced)
-constexpr int kCandMax = 64;                    // candidates a race's merge re-keys in fp64 (more: whole row)
+constexpr int kCandMax = 64;                    // candidates a race level re-keys in fp64 (more: fp64 race)
 constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second)
 
 enum { MODE_CHAIN = 0, MODE_TREE = 1, MODE_ROWS = 2 };
@@ -91,10 +90,13 @@ struct Ctrl {
   uint32_t aborted;   // a bounded wait expired (left set: the workspace must be re-initialised)
   uint32_t pad[63];
 };
+// One per request, each on its own 256 bytes: the fused schedule's waiting
+// workgroups poll these counters while K1 workgroups add to them, and
+// counters sharing cache lines serialise those accesses.
 struct Sync {
   uint32_t k1_count;  // K1 segments of the request (row, in row-statistics calls) done in this call,
                       // reset to 0 by its last user
-  uint32_t pad[3];
+  uint32_t pad[63];
 };
 // Target logit (and draft probability) at a draft token, gathered by the K1
 // segment that holds it: chain slot r = row r's draft, tree slot n = node n's
@@ -107,22 +109,13 @@ struct Partial {
   uint64_t s;         // bits of the segment sum of 2^((l - m_c) log2(e)/T) (fp64), or a NaN flag for greedy rows
   uint64_t m_amax;    // bits of the segment max (fp32, low half) and the smallest index attaining it (high half)
 };
-// A sampling chunk's result: its largest certified key lower bound L_c and
-// its candidates, the ids whose key upper bound reaches L_c (with the
-// logit and q, so that the merge can key them exactly without loads).
-constexpr int kRecCand = 4;
-struct K3Cand {
-  int32_t y;
-  float hi;           // upper bound of the key
-  float l, q;         // target logit and draft probability at y
-};
+// A sampling chunk's result: certified bounds on its race key W_c / E_c.
 struct K3Rec {
-  float lo;           // L_c (-inf: no id of the chunk has positive weight)
-  float ovf;          // the largest upper bound among candidates left out (-inf: none)
-  int32_t count;      // 0 until the record is complete, then 1 + the candidates listed (<= kRecCand);
-                      // cleared by the request's first K1 segment of each call
-  int32_t pad;
-  K3Cand cand[kRecCand];
+  double klo;         // lower bound (0: no weight of the chunk is certainly positive)
+  double khi;         // upper bound
+  int32_t count;      // 0 until the record is complete, then 1; reset by the request's first
+                      // K1 segment of each call
+  int32_t pad[3];
 };
 
 constexpr size_t kSyncOffset = 256;
@@ -300,6 +293,7 @@ struct Smem {
   float red_f[kWaves];
   int red_i[kWaves];
   double red_d[kWaves];
+  double red_d2[kWaves];
   uint64_t red_u[kWaves];
   int flag;
   float l0;
@@ -317,18 +311,9 @@ struct Smem {
   int path[SV_MAX_NODES];
   int a, kb, status, len, emit;
   Job job;
-  // sampling race of one chunk
-  int nlist;
-  int list_y[kList];
-  float list_whi[kList];  // weight upper bound, then key upper bound
-  float list_wlo[kList];
-  float list_l[kList];    // the id's logit and q, for the fp64 key
-  float list_q[kList];
+  // race candidates (chunks, then ids) re-keyed in fp64
   int ncand;
   int cand_y[kCandMax];
-  float cand_l[kCandMax];
-  float cand_q[kCandMax];
-  float cand_h[kCandMax];
   double cand_key[kCandMax];
 };
 
@@ -378,6 +363,26 @@ __device__ __forceinline__ double block_sum_d(double v, Smem& sm) {
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) r += sm.red_d[w];
   return r;
+}
+
+// Two block sums at once (every thread gets both).
+__device__ __forceinline__ void block_sum2_d(double& a, double& b, Smem& sm) {
+  a = wave_sum_d(a);
+  b = wave_sum_d(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    sm.red_d[wave] = a;
+    sm.red_d2[wave] = b;
+  }
+  __syncthreads();
+  a = sm.red_d[0];
+  b = sm.red_d2[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    a += sm.red_d[w];
+    b += sm.red_d2[w];
+  }
 }
 
 // Temperature of the request (chain/tree) or of the row (row statistics).
@@ -987,9 +992,9 @@ __device__ __forceinline__ void block_best(double& k, int& y, Smem& sm) {
     }
 }
 
-// Exact fp64 key of one id, kept out of line for the whole-row fallback
-// below: inlined into that loop, its fp64 constants would be held in
-// registers for the whole kernel.
+// Exact fp64 key of one id, kept out of line for the fp64 loops below:
+// inlined into them, its fp64 constants would be held in registers for the
+// whole kernel.
 __device__ __attribute__((noinline)) double race_key_cold(double l, double q, double m, double T, double S,
                                                           int resid, int use_p, uint64_t seed, int b, int r, int y) {
   const double p = exp((l - m) / T) / S;
@@ -998,29 +1003,47 @@ __device__ __attribute__((noinline)) double race_key_cold(double l, double q, do
   const double U = uniform_f64(noise_word(seed, b, r, y));
   return w / -log(U);
 }
+// Exact fp64 weight of one id (p, or the residual max(p - q, 0)).
+__device__ __attribute__((noinline)) double weight_cold(double l, double q, double m, double T, double S, int resid) {
+  const double p = exp((l - m) / T) / S;
+  if (resid) return (p - q > 0.0) ? p - q : 0.0;
+  return p;
+}
 
-// Whole-row race in fp64 by one workgroup: used when the fp32 screen
-// cannot certify its result, and on request.
+// Chunk noise of the race: word 0 of counter (c, r, b, 2), and E_c = -ln U_c.
+__device__ __forceinline__ double chunk_exp(uint64_t seed, int b, int r, int c) {
+  const u32x4 ctr = {(uint32_t)c, (uint32_t)r, (uint32_t)b, 2u};
+  return -log(uniform_f64(philox10(ctr, (uint32_t)seed, (uint32_t)(seed >> 32)).x));
+}
+
+// fp64 weight sum of chunk c (block-wide; every thread gets it).  use_p:
+// the weights are p itself (the fallback for an all-zero residual).
 template <bool BF16>
-__device__ __forceinline__ int race_row_f64(const Params& P, const Job& J, int b, Smem& sm) {
-  const int64_t row_off = (int64_t)J.row * P.lstride;
+__device__ double chunk_sum_f64(const Params& P, const Job& J, int c, bool use_p, Smem& sm) {
   const float* qrow = J.kind == JOB_RESID ? P.q + (int64_t)J.qrow * P.qstride : nullptr;
-  const uint64_t seed = P.seed[b];
-  // an all-zero weight vector falls back to p
-  int any_pos = 0;
+  const int resid = !use_p && J.kind == JOB_RESID;
+  const int y1 = min(P.V, (c + 1) * kK3Chunk);
+  double s = 0.0;
 #pragma unroll 1
-  for (int y = threadIdx.x; y < P.V; y += kWG) {
+  for (int y = c * kK3Chunk + (int)threadIdx.x; y < y1; y += kWG) {
+    if (!use_p && J.kind == JOB_EXCL && is_excluded(J, y)) continue;
     const double l = (double)load_logit<BF16>(P, J.row, y);
     const double q = qrow ? (double)qrow[y] : 0.0;
-    if (!(J.kind == JOB_EXCL && is_excluded(J, y)) &&
-        race_key_cold(l, q, J.m, J.t, J.s, J.kind == JOB_RESID, 0, seed, b, J.r, y) > 0.0)
-      any_pos = 1;
+    s += weight_cold(l, q, J.m, J.t, J.s, resid);
   }
-  const int use_p = block_min_i(any_pos ? 0 : 1, sm) == 1;
+  return block_sum_d(s, sm);
+}
+
+// The id race of chunk c in fp64 (block-wide): exact keys for every id.
+template <bool BF16>
+__device__ int chunk_race_f64(const Params& P, const Job& J, int b, int c, bool use_p, Smem& sm) {
+  const float* qrow = J.kind == JOB_RESID ? P.q + (int64_t)J.qrow * P.qstride : nullptr;
+  const uint64_t seed = P.seed[b];
+  const int y1 = min(P.V, (c + 1) * kK3Chunk);
   double best_k = -1.0;
   int best_y = INT32_MAX;
 #pragma unroll 1
-  for (int y = threadIdx.x; y < P.V; y += kWG) {
+  for (int y = c * kK3Chunk + (int)threadIdx.x; y < y1; y += kWG) {
     const double l = (double)load_logit<BF16>(P, J.row, y);
     const double q = qrow ? (double)qrow[y] : 0.0;
     const bool zero = !use_p && J.kind == JOB_EXCL && is_excluded(J, y);
@@ -1030,42 +1053,45 @@ __device__ __forceinline__ int race_row_f64(const Params& P, const Job& J, int b
       best_y = y;
     }
   }
-  (void)row_off;
   block_best(best_k, best_y, sm);
   return best_y;
 }
 
-// Sampling chunk c3 of request b (job in shared memory).  Screening in fp32
-// with certified bounds: e = 2^t approximates exp((l - m)/T) with relative
-// error at most eta = (|t| 2^-21 + 2^-17) (argument rounding plus
-// v_exp_f32, far above the measured 2^-23.5); E2 = -log2(U) and its
-// reciprocal are each within 2^-22 (v_log_f32 measured at 2^-23 over every
-// possible U, v_rcp_f32 at 2^-23.4).  The key w / E2 is a constant multiple
-// of w / E.  For a residual w = max(p - q, 0) with p = e/S; otherwise w = e
-// (the constant 1/S does not change the argmax).
-//   1. Each thread bounds the weights of its 8 ids: whi >= w >= wlo (a
-//      residual's whi is exactly 0 where p cannot exceed q).
-//   2. One thread keys the chunk's id of largest wlo (Philox, log, rcp):
-//      its lower bound L0 is a certified lower bound of the chunk's best
-//      key.  Since U <= 1 - 2^-24, E2 > 2^-24 and no key exceeds whi 2^25:
-//      an id with whi 2^25 < L0 cannot be the chunk's best, nor a
-//      candidate below, nor raise L.
-//   3. The other ids are compacted in LDS (with l and q) and keyed by one
-//      lane each; past kList entries every id of the chunk is keyed in
-//      place instead.
-//   4. L = the largest lower bound; the ids whose upper bound reaches L
-//      (the candidates) are re-keyed exactly in fp64 and the chunk records
-//      L, its best fp64 key and id, and, if more than kCandMax candidates
-//      qualified, the largest upper bound among those left out.
-template <bool BF16, int KIND>
-__device__ __forceinline__ void k3_sample(const Params& P, const Job& J, int b, int c3, Smem& sm) {
-  constexpr int NI = 4 * kK3Groups;  // ids per thread
-  const int tid = threadIdx.x;
+// The whole two-level race in fp64 by one workgroup: used when the fp32
+// screen cannot certify its result, and on request.  If every weight is
+// zero the race is run over p instead.
+template <bool BF16>
+__device__ int race_row_f64(const Params& P, const Job& J, int b, Smem& sm) {
   const uint64_t seed = P.seed[b];
-  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool use_p = pass == 1;
+    double best_k = -1.0;
+    int best_c = INT32_MAX;
+#pragma unroll 1
+    for (int c = 0; c < P.C3; ++c) {
+      const double key = chunk_sum_f64<BF16>(P, J, c, use_p, sm) / chunk_exp(seed, b, J.r, c);
+      if (better(key, c, best_k, best_c)) {
+        best_k = key;
+        best_c = c;
+      }
+    }
+    if (best_k > 0.0) return chunk_race_f64<BF16>(P, J, b, best_c, use_p, sm);
+  }
+  return 0;  // unreachable: p has a positive entry (the row maximum)
+}
+
+// fp32 bounds wlo <= w(y) <= whi of this thread's 8 ids of chunk c, ids
+// c*kK3Chunk + 4*(g*kWG + tid) + i (group g, lane i).  e = 2^t approximates exp((l - m)/T) with relative error at most
+// eta = (|t| 2^-21 + 2^-17) (argument rounding plus v_exp_f32, far above
+// the measured 2^-23.5); t is clamped to [-256, 0], where e is below every
+// fp32 weight that matters (and no NaN arises from a -inf logit).  For a
+// residual w = max(p - q, 0) with p = e/S; otherwise w = e/S.  Ids past
+// the vocabulary and removed ids get 0 for both bounds.
+template <bool BF16, int KIND>
+__device__ __forceinline__ void weight_bounds(const Params& P, const Job& J, int c, float* whi, float* wlo) {
+  const int tid = threadIdx.x;
   const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
-  const int jr = J.r;
-  const int y_base = c3 * kK3Chunk;
+  const int y_base = c * kK3Chunk;
   const int64_t lrow = (int64_t)J.row * P.lstride;
   const int64_t qrow = (int64_t)J.qrow * P.qstride;
   uint32_t excl_mask = 0;  // bit g*4+i: this thread's id is a removed token
@@ -1078,14 +1104,11 @@ __device__ __forceinline__ void k3_sample(const Params& P, const Job& J, int b, 
       }
     }
   }
-  // 1. weight bounds
-  float whi[NI], wlo[NI], lv[NI], qv[NI];
 #pragma unroll
   for (int g = 0; g < kK3Groups; ++g) {
     const int y0 = y_base + 4 * (g * kWG + tid);
     const bool full = y0 + 4 <= P.V;
-    float* l = &lv[g * 4];
-    float* q = &qv[g * 4];
+    float l[4], q[4];
     if (full && P.aligned) {
       if (BF16) {
         const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
@@ -1121,187 +1144,160 @@ __device__ __forceinline__ void k3_sample(const Params& P, const Job& J, int b, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float d = l[i] - m;
-      const float t = __builtin_fmaf(d, chi, d * clo);
+      const float t = fmaxf(__builtin_fmaf(d, chi, d * clo), -256.f);
       const float e = __builtin_amdgcn_exp2f(t);
-      const float eta = __builtin_fmaf(fminf(fabsf(t), 256.f), 0x1p-21f, 0x1p-17f);
+      const float eta = __builtin_fmaf(t, -0x1p-21f, 0x1p-17f);
+      const float p = e * inv_s;
       float h, lw;
       if (KIND == JOB_RESID) {
-        const float p = e * inv_s;
         h = fmaxf(__builtin_fmaf(p, eta, p) - q[i], 0.f) * (1.f + 0x1p-22f);
         lw = fmaxf(__builtin_fmaf(-p, eta, p) - q[i], 0.f) * (1.f - 0x1p-22f);
       } else {
-        h = __builtin_fmaf(e, eta, e);
-        lw = __builtin_fmaf(-e, eta, e);
+        h = __builtin_fmaf(p, eta, p) * (1.f + 0x1p-22f);
+        lw = __builtin_fmaf(-p, eta, p) * (1.f - 0x1p-22f);
       }
       const bool out = !(y0 + i < P.V) || (KIND == JOB_EXCL && ((excl_mask >> (g * 4 + i)) & 1u));
-      whi[g * 4 + i] = out ? -1.f : h;
-      wlo[g * 4 + i] = out ? -1.f : lw;
+      whi[g * 4 + i] = out ? 0.f : h;
+      wlo[g * 4 + i] = out ? 0.f : lw;
     }
   }
-  // 2. every key is at least wlo/32 (E2 <= 24): the chunk's largest wlo
-  // over 32 is a certified lower bound L0 of its best key
-  float wmax = 0.f;
+}
+
+// Id-race screen of this thread's 8 ids of chunk c, in fp32: E2 = -log2 U
+// and its reciprocal are each within 2^-22 (v_log_f32 measured at 2^-23
+// over every possible U, v_rcp_f32 at 2^-23.4), and w / E2 is a constant
+// multiple of w / E.  On return whi holds the key upper bounds; the
+// largest key lower bound is returned.
+__device__ __forceinline__ float race_screen(const Job& J, uint64_t seed, int b, int c, float* whi, const float* wlo) {
+  const int tid = threadIdx.x;
+  float lo_max = 0.f;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) wmax = fmaxf(wmax, wlo[i]);
-  const float L0 = block_max(wmax, sm) * 0x1p-5f;
-  // 3. count the ids that can still matter (ballots), then either compact
-  // them in LDS (one lane keys each) or, past kList, key every id in place
-  const int lane = tid & 63, wave = tid >> 6;
-  uint32_t qmask = 0;  // bit i: this thread's id i qualifies
-  int wcount = 0;
+  for (int g = 0; g < kK3Groups; ++g) {
+    const int y0 = c * kK3Chunk + 4 * (g * kWG + tid);
+    const u32x4 ctr = {(uint32_t)y0 >> 2, (uint32_t)J.r, (uint32_t)b, 1u};
+    const u32x4 rnd = philox10(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const uint32_t words[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float rE = __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uniform_f32(words[i])));
+      const int j = g * 4 + i;
+      lo_max = fmaxf(lo_max, wlo[j] * rE * (1.f - 0x1p-20f));
+      whi[j] = whi[j] * rE * (1.f + 0x1p-20f);
+    }
+  }
+  return lo_max;
+}
+
+// The id race of chunk c once the screen's bound L (block-wide) is known:
+// the ids whose key upper bound reaches L (the candidates) are re-keyed
+// exactly in fp64.  Returns the winner, or -1 when the screen cannot
+// certify it (L too small for fp32, or more than kCandMax candidates).
+template <bool BF16>
+__device__ __forceinline__ int race_pick(const Params& P, const Job& J, int b, int c, const float* khi, float L,
+                                         Smem& sm) {
+  const int tid = threadIdx.x;
+  if (!(L >= 0x1p-70f)) return -1;
+#pragma unroll
+  for (int j = 0; j < 4 * kK3Groups; ++j) {
+    if (khi[j] >= L) {
+      const int slot = atomicAdd(&sm.ncand, 1);
+      if (slot < kCandMax) sm.cand_y[slot] = c * kK3Chunk + 4 * ((j >> 2) * kWG + tid) + (j & 3);
+    }
+  }
+  __syncthreads();
+  const int nc = sm.ncand;
+  if (nc < 1 || nc > kCandMax) return -1;
+  if (nc == 1) return sm.cand_y[0];
+  if (tid < nc) {
+    const int y = sm.cand_y[tid];
+    const double l = (double)load_logit<BF16>(P, J.row, y);
+    const double q = J.kind == JOB_RESID ? (double)P.q[(int64_t)J.qrow * P.qstride + y] : 0.0;
+    sm.cand_key[tid] = race_key_from(J, P.seed[b], b, y, l, q, false);
+  }
+  __syncthreads();
+  double bk = -1.0;
+  int by = INT32_MAX;
+  for (int i = 0; i < nc; ++i)
+    if (better(sm.cand_key[i], sm.cand_y[i], bk, by)) {
+      bk = sm.cand_key[i];
+      by = sm.cand_y[i];
+    }
+  return bk > 0.0 ? by : -1;
+}
+
+// Chunk c3 of a race: certified bounds on its weight sum W_c and so on its
+// key W_c / E_c, stored in its record for the merge (only the winning
+// chunk's ids race, in the merge).  The fp32 sum of a thread's 8 non-negative bounds is within
+// 7 * 2^-24 of exact (widened by 2^-20), the fp64 block sum within 2^-40;
+// 2^-100 covers weights lost to underflow; the key's division and E_c's
+// log are within 2^-48.
+template <bool BF16, int KIND>
+__device__ __forceinline__ void k3_chunk(const Params& P, const Job& J, int b, int c3, Smem& sm) {
+  constexpr int NI = 4 * kK3Groups;
+  float whi[NI], wlo[NI];
+  weight_bounds<BF16, KIND>(P, J, c3, whi, wlo);
+  float shi = 0.f, slo = 0.f;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const bool qi = whi[i] > 0.f && whi[i] * 0x1p25f >= L0;
-    qmask |= (qi ? 1u : 0u) << i;
-    wcount += __popcll(__ballot(qi));
+    shi += whi[i];
+    slo += wlo[i];
   }
-  __syncthreads();
-  if (lane == 0) sm.red_i[wave] = wcount;
-  __syncthreads();
-  int n = 0, base = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    base += (w < wave) ? sm.red_i[w] : 0;
-    n += sm.red_i[w];
-  }
-  const bool dense = n > kList;
-  float lo_max = -INFINITY;
-  if (!dense) {
-    const uint64_t lt = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint64_t mask = __ballot((qmask >> i) & 1u);
-      if ((qmask >> i) & 1u) {
-        const int slot = base + __popcll(mask & lt);
-        sm.list_y[slot] = y_base + 4 * ((i >> 2) * kWG + tid) + (i & 3);
-        sm.list_whi[slot] = whi[i];
-        sm.list_wlo[slot] = wlo[i];
-        sm.list_l[slot] = lv[i];
-        sm.list_q[slot] = qv[i];
-      }
-      base += __popcll(mask);
-    }
-    __syncthreads();
-    for (int i = tid; i < n; i += kWG) {
-      const float rE = __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uniform_f32(noise_word(seed, b, jr, sm.list_y[i]))));
-      sm.list_whi[i] = sm.list_whi[i] * rE * (1.f + 0x1p-20f);
-      lo_max = fmaxf(lo_max, sm.list_wlo[i] * rE * (1.f - 0x1p-20f));
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < kK3Groups; ++g) {
-      const int y0 = y_base + 4 * (g * kWG + tid);
-      const u32x4 ctr = {(uint32_t)y0 >> 2, (uint32_t)jr, (uint32_t)b, 1u};
-      const u32x4 rnd = philox10(ctr, k0, k1);
-      const uint32_t words[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float rE = __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(uniform_f32(words[i])));
-        const int j = g * 4 + i;
-        if (whi[j] > 0.f) {
-          lo_max = fmaxf(lo_max, wlo[j] * rE * (1.f - 0x1p-20f));
-          whi[j] = whi[j] * rE * (1.f + 0x1p-20f);
-        }
-      }
-    }
-  }
-  if (tid == 0) sm.ncand = 0;
-  const float L = block_max(lo_max, sm);
-  // 4. the candidates (upper bound >= L), recorded for the merge
-  float ovf = -INFINITY;
-  if (!dense) {
-    for (int i = tid; i < n; i += kWG) {
-      const float h = sm.list_whi[i];
-      if (h >= L) {
-        const int slot = atomicAdd(&sm.ncand, 1);
-        if (slot < kRecCand) {
-          sm.cand_y[slot] = sm.list_y[i];
-          sm.cand_h[slot] = h;
-          sm.cand_l[slot] = sm.list_l[i];
-          sm.cand_q[slot] = sm.list_q[i];
-        } else {
-          ovf = fmaxf(ovf, h);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (whi[i] > 0.f && whi[i] >= L) {
-        const int slot = atomicAdd(&sm.ncand, 1);
-        if (slot < kRecCand) {
-          sm.cand_y[slot] = y_base + 4 * ((i >> 2) * kWG + tid) + (i & 3);
-          sm.cand_h[slot] = whi[i];
-          sm.cand_l[slot] = lv[i];
-          sm.cand_q[slot] = qv[i];
-        } else {
-          ovf = fmaxf(ovf, whi[i]);
-        }
-      }
-    }
-  }
-  ovf = block_max(ovf, sm);
-  if (tid < 64) {
+  double dhi = (double)shi * (1.0 + 0x1p-20), dlo = (double)slo * (1.0 - 0x1p-20);
+  block_sum2_d(dhi, dlo, sm);
+  if (threadIdx.x == 0) {
+    const double E = chunk_exp(P.seed[b], b, J.r, c3);
     K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c3];
-    const int nc = min(sm.ncand, kRecCand);
-    if (tid < nc) {
-      cst_i32(&rec->cand[tid].y, sm.cand_y[tid]);
-      cst_f32(&rec->cand[tid].hi, sm.cand_h[tid]);
-      cst_f32(&rec->cand[tid].l, sm.cand_l[tid]);
-      cst_f32(&rec->cand[tid].q, sm.cand_q[tid]);
-    }
-    if (tid == 0) {
-      cst_f32(&rec->lo, L);
-      cst_f32(&rec->ovf, ovf);
-      wait_mem();  // this wave's record stores are complete
-      cst_i32(&rec->count, nc + 1);
-    }
+    cst_f64(&rec->khi, (dhi * (1.0 + 0x1p-40) + 0x1p-100) / E * (1.0 + 0x1p-48));
+    cst_f64(&rec->klo, dlo * (1.0 - 0x1p-40) / E * (1.0 - 0x1p-48));
+    wait_mem();  // the record is stored before its marker
+    cst_i32(&rec->count, 1);
   }
 }
 
 template <bool BF16>
 __device__ __forceinline__ void sample_chunk(const Params& P, int b, int c3, Smem& sm) {
   const int kind = uniform_i(sm.job.kind);
-  if (kind == JOB_RESID) k3_sample<BF16, JOB_RESID>(P, sm.job, b, c3, sm);
-  else if (kind == JOB_EXCL) k3_sample<BF16, JOB_EXCL>(P, sm.job, b, c3, sm);
-  else k3_sample<BF16, JOB_P>(P, sm.job, b, c3, sm);
+  if (kind == JOB_RESID) k3_chunk<BF16, JOB_RESID>(P, sm.job, b, c3, sm);
+  else if (kind == JOB_EXCL) k3_chunk<BF16, JOB_EXCL>(P, sm.job, b, c3, sm);
+  else k3_chunk<BF16, JOB_P>(P, sm.job, b, c3, sm);
+}
+
+// The id race of chunk c by one workgroup: the fp32 screen, then fp64 where
+// it cannot certify the winner.
+template <bool BF16, int KIND>
+__device__ __forceinline__ int chunk_race(const Params& P, const Job& J, int b, int c, Smem& sm) {
+  constexpr int NI = 4 * kK3Groups;
+  float whi[NI], wlo[NI];
+  weight_bounds<BF16, KIND>(P, J, c, whi, wlo);
+  const float lo = race_screen(J, P.seed[b], b, c, whi, wlo);
+  if (threadIdx.x == 0) sm.ncand = 0;
+  const float L = block_max(lo, sm);
+  const int y = race_pick<BF16>(P, J, b, c, whi, L, sm);
+  if (y >= 0) return y;
+  return chunk_race_f64<BF16>(P, J, b, c, false, sm);
 }
 
 // Merge of one race by the request's last chunk, once every chunk's record
-// is complete: L = the largest certified
-// lower bound over all chunks.  The winner's upper bound reaches L, so it
-// is among the listed candidates whose upper bound reaches L, unless a
-// chunk had to leave out such a candidate (then, or when L is too small for
-// fp32 to certify, the whole row is raced in fp64).  A single such
-// candidate is the winner; several are re-keyed exactly in fp64.
+// is complete (lo: the largest key lower bound this thread read, kh0: the
+// upper bound of chunk `tid`).  L = the largest certified lower bound over
+// the chunks; the winning chunk's upper bound reaches L, so it is among the
+// chunks whose upper bound does: a single one is the winner, several are
+// keyed exactly in fp64.  Then the ids of the winning chunk race.  L = 0 (no
+// chunk certainly positive: an all-zero residual, or weights too small to
+// certify) and more than kCandMax candidates go to the fp64 race.
 template <bool BF16>
-__device__ __forceinline__ void k3_merge(const Params& P, int b, Smem& sm) {
+__device__ __forceinline__ void k3_merge(const Params& P, int b, double lo, double kh0, Smem& sm) {
   const Job& J = sm.job;
   const int tid = threadIdx.x;
-  float lo = -INFINITY, ov = -INFINITY;
-  for (int c = tid; c < P.C3; c += kWG) {
-    const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
-    lo = fmaxf(lo, cld_f32(&rec->lo));
-    ov = fmaxf(ov, cld_f32(&rec->ovf));
-  }
   if (tid == 0) sm.ncand = 0;
-  const float L = block_max(lo, sm);
-  const float OVF = block_max(ov, sm);
-  bool fallback = (P.flags & SV_FLAG_FP64_RACE) || !(L >= 0x1p-70f) || OVF >= L;
+  const double L = __longlong_as_double((long long)block_max_u64((uint64_t)__double_as_longlong(lo), sm));
+  bool fallback = (P.flags & SV_FLAG_FP64_RACE) || !(L > 0.0);
   if (!fallback) {
     for (int c = tid; c < P.C3; c += kWG) {
-      const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
-      const int cnt = min(max(cld_i32(&rec->count) - 1, 0), kRecCand);
-      for (int i = 0; i < cnt; ++i) {
-        const float h = cld_f32(&rec->cand[i].hi);
-        if (h >= L) {
-          const int slot = atomicAdd(&sm.ncand, 1);
-          if (slot < kCandMax) {
-            sm.cand_y[slot] = cld_i32(&rec->cand[i].y);
-            sm.cand_l[slot] = cld_f32(&rec->cand[i].l);
-            sm.cand_q[slot] = cld_f32(&rec->cand[i].q);
-          }
-        }
+      const double kh = (c == tid) ? kh0 : cld_f64(&P.k3[(int64_t)b * P.C3 + c].khi);
+      if (kh >= L) {
+        const int slot = atomicAdd(&sm.ncand, 1);
+        if (slot < kCandMax) sm.cand_y[slot] = c;
       }
     }
     __syncthreads();
@@ -1309,23 +1305,29 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, Smem& sm) {
   }
   int by = -1;
   if (!fallback) {
-    const int nc = sm.ncand;
-    if (nc == 1) {
-      by = sm.cand_y[0];
-    } else {
-      if (tid < nc)
-        sm.cand_key[tid] =
-            race_key_from(J, P.seed[b], b, sm.cand_y[tid], (double)sm.cand_l[tid], (double)sm.cand_q[tid], false);
-      __syncthreads();
+    const int nc = uniform_i(sm.ncand);
+    int best_c = sm.cand_y[0];
+    if (nc > 1) {
       double bk = -1.0;
-      int byy = INT32_MAX;
-      for (int i = 0; i < nc; ++i)
-        if (better(sm.cand_key[i], sm.cand_y[i], bk, byy)) {
-          bk = sm.cand_key[i];
-          byy = sm.cand_y[i];
+      best_c = INT32_MAX;
+#pragma unroll 1
+      for (int i = 0; i < nc; ++i) {
+        const int c = uniform_i(sm.cand_y[i]);
+        const double key = chunk_sum_f64<BF16>(P, J, c, false, sm) / chunk_exp(P.seed[b], b, J.r, c);
+        if (better(key, c, bk, best_c)) {
+          bk = key;
+          best_c = c;
         }
-      by = byy;
+      }
       fallback = !(bk > 0.0);
+    }
+    __syncthreads();  // every thread has read the candidates before LDS is reused
+    if (!fallback) {
+      const int c = uniform_i(best_c);
+      const int kind = uniform_i(J.kind);
+      if (kind == JOB_RESID) by = chunk_race<BF16, JOB_RESID>(P, J, b, c, sm);
+      else if (kind == JOB_EXCL) by = chunk_race<BF16, JOB_EXCL>(P, J, b, c, sm);
+      else by = chunk_race<BF16, JOB_P>(P, J, b, c, sm);
     }
   }
   if (fallback) by = race_row_f64<BF16>(P, J, b, sm);
@@ -1414,10 +1416,11 @@ __device__ __forceinline__ void run_k1_item(const Params& P, int b, int o, Smem&
   run_k1_seg<MODE, BF16>(P, b, r, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c, sm);
 }
 
-// Request order of the fused schedule: for batches of at most 64 requests
-// the sampling requests go first (then the others, each group in index
-// order), so that the requests whose decision steps end the launch are
-// the ones with no race to run; larger batches keep index order.
+// Request order of the decision/sampling work: for batches of at most 64
+// requests the sampling requests go first (then the others, each group in
+// index order), so that their chunks are dispatched first and the launch
+// ends with the requests that have no race to run; larger batches keep
+// index order.
 __device__ __forceinline__ int request_at(const Params& P, int g) {
   if (P.bs > 64) return g;
   const int lane = threadIdx.x & 63;
@@ -1449,7 +1452,7 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
       for (int r = 0; r < P.R; ++r) expect += (uint32_t)k1_segments(P, (int64_t)b * P.R + r);
       uint32_t spins = 0;
       while (cld32(&P.sync[b].k1_count) < expect) {
-        __builtin_amdgcn_s_sleep(8);
+        __builtin_amdgcn_s_sleep(40);  // about a microsecond between polls
         if (++spins > kSpinLimit || cld32(&P.ctrl->aborted)) {
           ok = 0;
           break;
@@ -1483,17 +1486,25 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
   if (c3 != P.C3 - 1) return;
   // The request's last chunk (dispatched after all its others, so none of
   // them waits on it) merges once every chunk's record is complete (bounded
-  // wait), then resets the request's counter.
+  // wait), then resets the request's counter.  A record's contents are
+  // read after its marker (they are stored before it).
   int done = ok;
+  double lo = 0.0, kh0 = -1.0;
   if (ok) {
     for (int c = tid; c < P.C3; c += kWG) {
+      const K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
       uint32_t spins = 0;
-      while (cld_i32(&P.k3[(int64_t)b * P.C3 + c].count) == 0) {
+      while (cld_i32(&rec->count) == 0) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins > kSpinLimit || cld32(&P.ctrl->aborted)) {
           done = 0;
           break;
         }
+      }
+      if (!done) break;
+      if (sampled) {
+        lo = fmax(lo, cld_f64(&rec->klo));
+        if (c == tid) kh0 = cld_f64(&rec->khi);
       }
     }
   }
@@ -1502,7 +1513,7 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
     cst32(&P.ctrl->aborted, 1u);
     if (P.status) P.status[b] = SV_REQ_INTERNAL;
   }
-  if (done && sampled) k3_merge<BF16>(P, b, sm);
+  if (done && sampled) k3_merge<BF16>(P, b, lo, kh0, sm);
   if (tid == 0 && P.sched == SCHED_FUSED) cst32(&P.sync[b].k1_count, 0u);
 }
 
@@ -1518,8 +1529,20 @@ template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, 8) void k23_kernel(Params P) {
   __shared__ Smem sm;
   if constexpr (MODE != MODE_ROWS) {
-    const int b = (int)(blockIdx.x / (uint32_t)P.C3);
-    run_k23<MODE, BF16, false>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.C3), sm);
+    // chunk 0 of every request first (it writes the request's outputs),
+    // then chunks 1.. of the requests in request_at order: the sampling
+    // requests' chunks before the greedy requests' idle ones
+    const uint32_t t = blockIdx.x, bs = (uint32_t)P.bs;
+    int b, c3;
+    if (t < bs) {
+      b = (int)t;
+      c3 = 0;
+    } else {
+      const uint32_t n = (uint32_t)P.C3 - 1u, g = (t - bs) / n;
+      b = uniform_i(request_at(P, (int)g));
+      c3 = (int)(t - bs - g * n) + 1;
+    }
+    run_k23<MODE, BF16, false>(P, b, c3, sm);
   }
 }
 
@@ -1603,24 +1626,19 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
 
 typedef void (*KernelFn)(Params);
 
+struct Kernels {
+  KernelFn k1, k23, fused;
+};
+
 template <int MODE, bool BF16>
-static void kernels_for(KernelFn& k1, KernelFn& k23, KernelFn& fused) {
-  k1 = k1_kernel<MODE, BF16>;
-  k23 = k23_kernel<MODE, BF16>;
-  fused = fused_kernel<MODE, BF16>;
+static Kernels kernels_for() {
+  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>};
 }
 
-static void select_kernels(int mode, bool bf16, KernelFn& k1, KernelFn& k23, KernelFn& fused) {
-  if (mode == MODE_CHAIN) {
-    if (bf16) kernels_for<MODE_CHAIN, true>(k1, k23, fused);
-    else kernels_for<MODE_CHAIN, false>(k1, k23, fused);
-  } else if (mode == MODE_TREE) {
-    if (bf16) kernels_for<MODE_TREE, true>(k1, k23, fused);
-    else kernels_for<MODE_TREE, false>(k1, k23, fused);
-  } else {
-    if (bf16) kernels_for<MODE_ROWS, true>(k1, k23, fused);
-    else kernels_for<MODE_ROWS, false>(k1, k23, fused);
-  }
+static Kernels select_kernels(int mode, bool bf16) {
+  if (mode == MODE_CHAIN) return bf16 ? kernels_for<MODE_CHAIN, true>() : kernels_for<MODE_CHAIN, false>();
+  if (mode == MODE_TREE) return bf16 ? kernels_for<MODE_TREE, true>() : kernels_for<MODE_TREE, false>();
+  return bf16 ? kernels_for<MODE_ROWS, true>() : kernels_for<MODE_ROWS, false>();
 }
 
 // Workgroups of fused kernel `slot` (mode * 2 + bf16) resident on the
@@ -1665,8 +1683,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).
   P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : SCHED_PHASED;
-  KernelFn k1, k23, fused;
-  select_kernels(P.mode, P.dtype == SV_BF16, k1, k23, fused);
+  const Kernels K = select_kernels(P.mode, P.dtype == SV_BF16);
   // fused: every K1 item first, then the sampling chunks (a lag of the
   // whole batch; smaller lags interleave them, SV_FUSED_LAG, for tuning)
   P.lag = P.bs;
@@ -1678,12 +1695,12 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
     }
   }
   if (P.mode == MODE_ROWS) {
-    hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+    hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
   } else if (P.sched == SCHED_PHASED) {
-    if (!(P.flags & SV_FLAG_DECIDE_ONLY)) hipLaunchKernelGGL(k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
-    if (!(P.flags & SV_FLAG_STATS_ONLY)) hipLaunchKernelGGL(k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
+    if (!(P.flags & SV_FLAG_DECIDE_ONLY)) hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+    if (!(P.flags & SV_FLAG_STATS_ONLY)) hipLaunchKernelGGL(K.k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
   } else {
-    hipLaunchKernelGGL(fused, dim3((unsigned)(P.G + grid23)), dim3(kWG), 0, stream, P);
+    hipLaunchKernelGGL(K.fused, dim3((unsigned)(P.G + grid23)), dim3(kWG), 0, stream, P);
   }
   if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
   return SV_OK;
