@@ -75,6 +75,11 @@ constexpr int kK1Depth = SV_K1_DEPTH;           // K1 sub-chunks in flight ahead
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
 constexpr int kK3Groups = 2;                    // groups of 4 vocabulary ids per thread in a sampling chunk
 constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 2048 ids per sampling chunk
+// K23 items per call the chunk grouping aims at: 256 CUs x 8 resident
+// workgroups.  Up to two rounds of one-chunk items are kept (each item
+// decides for itself, which is cheaper than a longer item); past that,
+// items take several chunks, so that large batches decide once per item.
+constexpr int kK3Slots = 2048;
 constexpr int kCandMax = 64;                    // candidates a race level re-keys in fp64 (more: fp64 race)
 constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second)
 
@@ -155,6 +160,8 @@ struct Params {
   int32_t G;          // K1 items: rows * Q
   int32_t CPR;        // partial slots per row (= Q)
   int32_t C3;         // sampling chunks per request
+  int32_t G3;         // sampling chunks per K23 item
+  int32_t CI;         // K23 items per request: ceil(C3 / G3)
   int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
   uint32_t flags;
@@ -1434,15 +1441,15 @@ __device__ __forceinline__ int request_at(const Params& P, int g) {
   return (int)__builtin_ctzll(hit);
 }
 
-// Sampling chunk c3 of request b, after its own run of the decision step.
-// Greedy requests (and bad temperatures) sample nothing: only their chunk 0
-// works, to decide and write the outputs.  The last chunk of a sampling
-// request to finish merges the chunks' results and resets the request's
-// counters.
+// K23 item `item` of request b: its own run of the decision step, then the
+// sampling chunks [item G3, (item + 1) G3).  Greedy requests (and bad
+// temperatures) sample nothing: only their item 0 works, to decide and
+// write the outputs.  The request's last item merges the chunks' results
+// and resets the request's counters.
 template <int MODE, bool BF16, bool COH>
-__device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm) {
+__device__ __forceinline__ void run_k23(const Params& P, int b, int item, Smem& sm) {
   const int tid = threadIdx.x;
-  const bool writer = (c3 == 0);
+  const bool writer = (item == 0);
   const bool stoch = uniform_i(is_stochastic(temp_of(P, b)));
   const bool work = stoch || writer;
   int ok = 1;
@@ -1468,14 +1475,17 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
     ok = uniform_i(sm.flag);
   }
   bool sampled = false;
+  const int c_lo = item * P.G3, c_hi = min(P.C3, c_lo + P.G3);  // this item's chunks
   if (work && ok) {
     if (MODE == MODE_CHAIN) decide_chain<BF16, COH>(P, b, writer, sm);
     else decide_tree<BF16, COH>(P, b, writer, sm);
     if (uniform_i(sm.job.kind) != JOB_NONE) {
-      sample_chunk<BF16>(P, b, c3, sm);
+#pragma unroll 1
+      for (int c3 = c_lo; c3 < c_hi; ++c3) sample_chunk<BF16>(P, b, c3, sm);
       sampled = true;
-    } else if (stoch && tid == 0) {
-      cst_i32(&P.k3[(int64_t)b * P.C3 + c3].count, 1);  // complete, nothing raced
+    } else if (stoch) {
+      for (int c3 = c_lo + tid; c3 < c_hi; c3 += kWG)
+        cst_i32(&P.k3[(int64_t)b * P.C3 + c3].count, 1);  // complete, nothing raced
     }
   }
   if (!stoch) {
@@ -1483,8 +1493,8 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int c3, Smem& sm
     if (P.sched == SCHED_FUSED && work && ok && tid == 0) cst32(&P.sync[b].k1_count, 0u);
     return;
   }
-  if (c3 != P.C3 - 1) return;
-  // The request's last chunk (dispatched after all its others, so none of
+  if (item != P.CI - 1) return;
+  // The request's last item (dispatched after all its others, so none of
   // them waits on it) merges once every chunk's record is complete (bounded
   // wait), then resets the request's counter.  A record's contents are
   // read after its marker (they are stored before it).
@@ -1529,20 +1539,20 @@ template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, 8) void k23_kernel(Params P) {
   __shared__ Smem sm;
   if constexpr (MODE != MODE_ROWS) {
-    // chunk 0 of every request first (it writes the request's outputs),
-    // then chunks 1.. of the requests in request_at order: the sampling
-    // requests' chunks before the greedy requests' idle ones
+    // item 0 of every request first (it writes the request's outputs),
+    // then items 1.. of the requests in request_at order: the sampling
+    // requests' items before the greedy requests' idle ones
     const uint32_t t = blockIdx.x, bs = (uint32_t)P.bs;
-    int b, c3;
+    int b, item;
     if (t < bs) {
       b = (int)t;
-      c3 = 0;
+      item = 0;
     } else {
-      const uint32_t n = (uint32_t)P.C3 - 1u, g = (t - bs) / n;
+      const uint32_t n = (uint32_t)P.CI - 1u, g = (t - bs) / n;
       b = uniform_i(request_at(P, (int)g));
-      c3 = (int)(t - bs - g * n) + 1;
+      item = (int)(t - bs - g * n) + 1;
     }
-    run_k23<MODE, BF16, false>(P, b, c3, sm);
+    run_k23<MODE, BF16, false>(P, b, item, sm);
   }
 }
 
@@ -1555,7 +1565,7 @@ template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
   __shared__ Smem sm;
   if constexpr (MODE != MODE_ROWS) {
-    const uint32_t n1 = (uint32_t)(P.R * P.Q), n3 = (uint32_t)P.C3, L = (uint32_t)P.lag, bs = (uint32_t)P.bs;
+    const uint32_t n1 = (uint32_t)(P.R * P.Q), n3 = (uint32_t)P.CI, L = (uint32_t)P.lag, bs = (uint32_t)P.bs;
     const uint32_t seg1 = L * n1, seg2 = (bs - L) * (n1 + n3);
     const uint32_t t = blockIdx.x;
     uint32_t g, o;
@@ -1595,7 +1605,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 
 // ===================================================================== host
 struct Shape {
-  int SUB, nsub, Q, Qp, G, CPR, C3;
+  int SUB, nsub, Q, Qp, G, CPR, C3, G3, CI;
   size_t gat_off, part_off, k3_off, total;
 };
 
@@ -1617,6 +1627,10 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   s.G = (int)(bs * R * q);
   s.CPR = q;
   s.C3 = races ? (int)((V + kK3Chunk - 1) / kK3Chunk) : 0;
+  s.G3 = 1;
+  if (races && bs * s.C3 > 2 * kK3Slots) s.G3 = (int)((bs * s.C3 + kK3Slots - 1) / kK3Slots);
+  if (s.G3 > s.C3 && s.C3 > 0) s.G3 = s.C3;
+  s.CI = races ? (s.C3 + s.G3 - 1) / s.G3 : 0;
   s.gat_off = kDataOffset;
   s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
@@ -1678,7 +1692,9 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.G = S.G;
   P.CPR = S.CPR;
   P.C3 = S.C3;
-  const int64_t grid23 = (int64_t)P.bs * P.C3;
+  P.G3 = S.G3;
+  P.CI = S.CI;
+  const int64_t grid23 = (int64_t)P.bs * P.CI;
   if (grid23 + P.G > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).

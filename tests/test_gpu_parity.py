@@ -162,6 +162,18 @@ def test_all_schedules_are_bit_identical(dev):
             np.testing.assert_array_equal(out[k], ref[k])
 
 
+def test_large_batch_groups_race_chunks(dev):
+    """96 requests x 49 race chunks exceed two rounds of one-chunk items, so
+    each decision/sampling item takes 3 chunks (the last item one): parity
+    with the oracle, and both schedules bit-identical."""
+    inp = workloads.chain_bf16_mixed(5, bs=96, V=100000)
+    ref, got = check_chain(inp, dev)
+    assert (ref["accept_len"][48:] < 7).any()  # stochastic requests with rejections
+    _, fused = run_chain(inp, dev, flags=sv.FLAG_FUSED)
+    for k in ("accept_len", "tokens", "status"):
+        np.testing.assert_array_equal(fused[k], got[k])
+
+
 @pytest.mark.parametrize("name", ["chain_bf16_mixed", "onehot_bf16"])
 def test_split_phases_equal_the_plain_call(dev, name):
     """STATS_ONLY leaves the outputs alone; STATS_ONLY then DECIDE_ONLY on
