@@ -80,7 +80,8 @@ constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 2048 ids per sampling chunk
 // decides for itself, which is cheaper than a longer item); past that,
 // items take several chunks, so that large batches decide once per item.
 constexpr int kK3Slots = 2048;
-constexpr int kCandMax = 64;                    // candidates a race level re-keys in fp64 (more: fp64 race)
+constexpr int kCandMax = 64;
+constexpr int kChunkE = 64;                     // chunk noise values an item computes up front                    // candidates a race level re-keys in fp64 (more: fp64 race)
 constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second)
 
 enum { MODE_CHAIN = 0, MODE_TREE = 1, MODE_ROWS = 2 };
@@ -318,6 +319,9 @@ struct Smem {
   int path[SV_MAX_NODES];
   int a, kb, status, len, emit;
   Job job;
+  // noise E_c of the item's first kChunkE chunks, from chunk chunk_e0 on
+  int chunk_e0;
+  double chunk_e[kChunkE];
   // race candidates (chunks, then ids) re-keyed in fp64
   int ncand;
   int cand_y[kCandMax];
@@ -1232,32 +1236,109 @@ __device__ __forceinline__ int race_pick(const Params& P, const Job& J, int b, i
   return bk > 0.0 ? by : -1;
 }
 
+// Certified bounds dlo <= W_c <= dhi on the weight sum of chunk c, this
+// thread's share before the block sum.  Per id, with e = 2^t as in
+// weight_bounds and p = e/S computed as e * fl(1/S): the fp32 p is within
+// (eta + 2^-23) p of the exact one, eta = |t| 2^-21 + 2^-17, and since
+// max(., 0) is 1-Lipschitz the fp32 residual max(p - q, 0) is within that
+// too (plus its own rounding, 2^-24 of itself).  So the thread sums the
+// fp32 weights and, for the error, e and |t| e: no per-id bounds.
+template <bool BF16, int KIND>
+__device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, int c, double& dhi, double& dlo) {
+  const int tid = threadIdx.x;
+  const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
+  const int y_base = c * kK3Chunk;
+  const int64_t lrow = (int64_t)J.row * P.lstride;
+  const int64_t qrow = (int64_t)J.qrow * P.qstride;
+  uint32_t excl_mask = 0;  // bit g*4+i: this thread's id is a removed token
+  if (KIND == JOB_EXCL) {
+    for (int i = 0; i < J.n_excl; ++i) {
+      const int z = J.excl[i] - y_base;
+      if (z >= 0 && z < kK3Chunk) {
+        const int gi = z >> 2;
+        if ((gi % kWG) == tid) excl_mask |= 1u << ((gi / kWG) * 4 + (z & 3));
+      }
+    }
+  }
+  float sw = 0.f, se = 0.f, ste = 0.f;  // sum of residual weights; of e; of |t| e
+#pragma unroll
+  for (int g = 0; g < kK3Groups; ++g) {
+    const int y0 = y_base + 4 * (g * kWG + tid);
+    const bool full = y0 + 4 <= P.V;
+    float l[4], q[4];
+    if (full && P.aligned) {
+      if (BF16) {
+        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
+        l[0] = __uint_as_float(w.x << 16);
+        l[1] = __uint_as_float(w.x & 0xffff0000u);
+        l[2] = __uint_as_float(w.y << 16);
+        l[3] = __uint_as_float(w.y & 0xffff0000u);
+      } else {
+        const u32x4 w = __builtin_nontemporal_load((const u32x4*)((const float*)P.logits + lrow + y0));
+        l[0] = __uint_as_float(w.x);
+        l[1] = __uint_as_float(w.y);
+        l[2] = __uint_as_float(w.z);
+        l[3] = __uint_as_float(w.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
+    }
+    if (KIND == JOB_RESID) {
+      if (full && P.q_aligned) {
+        const u32x4 w = __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
+        q[0] = __uint_as_float(w.x);
+        q[1] = __uint_as_float(w.y);
+        q[2] = __uint_as_float(w.z);
+        q[3] = __uint_as_float(w.w);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (y0 + i < P.V) ? P.q[qrow + y0 + i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = l[i] - m;
+      const float t = fmaxf(__builtin_fmaf(d, chi, d * clo), -256.f);  // a -inf logit gives e = 0
+      float e = __builtin_amdgcn_exp2f(t);
+      if (KIND == JOB_EXCL && ((excl_mask >> (g * 4 + i)) & 1u)) e = 0.f;
+      se += e;
+      ste = __builtin_fmaf(-t, e, ste);
+      if (KIND == JOB_RESID) sw += fmaxf(__builtin_fmaf(e, inv_s, -q[i]), 0.f);
+    }
+  }
+  // the fp32 sums of 8 non-negative terms are within 7 * 2^-24 of exact
+  // (widened by 2^-20); the error terms are scaled up generously
+  const double err = (double)inv_s * ((double)se * (0x1p-17 + 0x1p-22) + (double)ste * 0x1p-21) * (1.0 + 0x1p-10);
+  const double w = (KIND == JOB_RESID) ? (double)sw : (double)se * (double)inv_s;
+  dhi = w * (1.0 + 0x1p-20) + err;
+  dlo = w * (1.0 - 0x1p-20) - err;
+}
+
 // Chunk c3 of a race: certified bounds on its weight sum W_c and so on its
 // key W_c / E_c, stored in its record for the merge (only the winning
-// chunk's ids race, in the merge).  The fp32 sum of a thread's 8 non-negative bounds is within
-// 7 * 2^-24 of exact (widened by 2^-20), the fp64 block sum within 2^-40;
-// 2^-100 covers weights lost to underflow; the key's division and E_c's
-// log are within 2^-48.
+// chunk's ids race, in the merge).  With one chunk per item the record's
+// marker follows at once; otherwise the item publishes its markers together
+// once all its records are stored, and E_c comes from shared memory.  The
+// fp64 block sum is within 2^-40; 2^-100 covers weights lost to underflow;
+// the key's division and E_c's log are within 2^-48.
 template <bool BF16, int KIND>
 __device__ __forceinline__ void k3_chunk(const Params& P, const Job& J, int b, int c3, Smem& sm) {
-  constexpr int NI = 4 * kK3Groups;
-  float whi[NI], wlo[NI];
-  weight_bounds<BF16, KIND>(P, J, c3, whi, wlo);
-  float shi = 0.f, slo = 0.f;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    shi += whi[i];
-    slo += wlo[i];
-  }
-  double dhi = (double)shi * (1.0 + 0x1p-20), dlo = (double)slo * (1.0 - 0x1p-20);
+  double dhi, dlo;
+  chunk_sum_bounds<BF16, KIND>(P, J, c3, dhi, dlo);
   block_sum2_d(dhi, dlo, sm);
   if (threadIdx.x == 0) {
-    const double E = chunk_exp(P.seed[b], b, J.r, c3);
+    const int e = c3 - sm.chunk_e0;
+    const double E = (e >= 0 && e < kChunkE) ? sm.chunk_e[e] : chunk_exp(P.seed[b], b, J.r, c3);
     K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c3];
-    cst_f64(&rec->khi, (dhi * (1.0 + 0x1p-40) + 0x1p-100) / E * (1.0 + 0x1p-48));
-    cst_f64(&rec->klo, dlo * (1.0 - 0x1p-40) / E * (1.0 - 0x1p-48));
-    wait_mem();  // the record is stored before its marker
-    cst_i32(&rec->count, 1);
+    const double whi = dhi * (1.0 + 0x1p-40) + 0x1p-100;
+    const double wlo = dlo > 0.0 ? dlo * (1.0 - 0x1p-40) : 0.0;
+    cst_f64(&rec->khi, whi / E * (1.0 + 0x1p-48));
+    cst_f64(&rec->klo, wlo / E * (1.0 - 0x1p-48));
+    if (P.G3 == 1) {
+      wait_mem();  // the record is stored before its marker
+      cst_i32(&rec->count, 1);
+    }
   }
 }
 
@@ -1480,8 +1561,21 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int item, Smem& 
     if (MODE == MODE_CHAIN) decide_chain<BF16, COH>(P, b, writer, sm);
     else decide_tree<BF16, COH>(P, b, writer, sm);
     if (uniform_i(sm.job.kind) != JOB_NONE) {
+      if (P.G3 == 1) {
+        if (tid == 0) sm.chunk_e0 = INT32_MIN / 2;  // no precomputed noise
+        sample_chunk<BF16>(P, b, c_lo, sm);
+      } else {
+        // the item's chunk noise, one thread per chunk
+        if (tid == 0) sm.chunk_e0 = c_lo;
+        if (tid < min(c_hi - c_lo, kChunkE)) sm.chunk_e[tid] = chunk_exp(P.seed[b], b, sm.job.r, c_lo + tid);
+        __syncthreads();
 #pragma unroll 1
-      for (int c3 = c_lo; c3 < c_hi; ++c3) sample_chunk<BF16>(P, b, c3, sm);
+        for (int c3 = c_lo; c3 < c_hi; ++c3) sample_chunk<BF16>(P, b, c3, sm);
+        // one wait for all the item's records, then their markers
+        if (tid == 0) wait_mem();
+        __syncthreads();
+        for (int c3 = c_lo + tid; c3 < c_hi; c3 += kWG) cst_i32(&P.k3[(int64_t)b * P.C3 + c3].count, 1);
+      }
       sampled = true;
     } else if (stoch) {
       for (int c3 = c_lo + tid; c3 < c_hi; c3 += kWG)
