@@ -40,6 +40,7 @@
 // ready for the next call without any reset pass.  Both schedules give
 // bit-identical results.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <math.h>
 #include <stdint.h>
@@ -1236,15 +1237,44 @@ __device__ __forceinline__ int race_pick(const Params& P, const Job& J, int b, i
   return bk > 0.0 ? by : -1;
 }
 
-// Certified bounds dlo <= W_c <= dhi on the weight sum of chunk c, this
-// thread's share before the block sum.  Per id, with e = 2^t as in
-// weight_bounds and p = e/S computed as e * fl(1/S): the fp32 p is within
-// (eta + 2^-23) p of the exact one, eta = |t| 2^-21 + 2^-17, and since
-// max(., 0) is 1-Lipschitz the fp32 residual max(p - q, 0) is within that
-// too (plus its own rounding, 2^-24 of itself).  So the thread sums the
-// fp32 weights and, for the error, e and |t| e: no per-id bounds.
+// Raw loads of this thread's ids of one race chunk (a whole chunk in
+// aligned rows): the target logits (4 bf16 or 4 fp32 per group) and, for a
+// residual, q.
+template <bool BF16>
+struct ChunkRaw {
+  typename std::conditional<BF16, u32x2, u32x4>::type l[kK3Groups];
+  u32x4 q[kK3Groups];
+};
+
+// Whether chunk c of the job's rows can be loaded as whole vectors.
+__device__ __forceinline__ bool chunk_whole(const Params& P, const Job& J, int c) {
+  return (c + 1) * kK3Chunk <= P.V && P.aligned && (J.kind != JOB_RESID || P.q_aligned);
+}
+
 template <bool BF16, int KIND>
-__device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, int c, double& dhi, double& dlo) {
+__device__ __forceinline__ void chunk_load(const Params& P, const Job& J, int c, ChunkRaw<BF16>& r) {
+  const int64_t lrow = (int64_t)J.row * P.lstride;
+  const int64_t qrow = (int64_t)J.qrow * P.qstride;
+#pragma unroll
+  for (int g = 0; g < kK3Groups; ++g) {
+    const int y0 = c * kK3Chunk + 4 * (g * kWG + (int)threadIdx.x);
+    if constexpr (BF16) r.l[g] = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
+    else r.l[g] = __builtin_nontemporal_load((const u32x4*)((const float*)P.logits + lrow + y0));
+    if (KIND == JOB_RESID) r.q[g] = __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
+  }
+}
+
+// Certified bounds dlo <= W_c <= dhi on the weight sum of chunk c, this
+// thread's share before the block sum (r: the chunk's whole-vector loads,
+// or null to load here, entry by entry where needed).  Per id, with e = 2^t
+// as in weight_bounds and p = e/S computed as e * fl(1/S): the fp32 p is
+// within (eta + 2^-23) p of the exact one, eta = |t| 2^-21 + 2^-17, and
+// since max(., 0) is 1-Lipschitz the fp32 residual max(p - q, 0) is within
+// that too (plus its own rounding, 2^-24 of itself).  So the thread sums
+// the fp32 weights and, for the error, e and |t| e: no per-id bounds.
+template <bool BF16, int KIND>
+__device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, int c, double& dhi, double& dlo,
+                                                 const ChunkRaw<BF16>* r = nullptr) {
   const int tid = threadIdx.x;
   const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
   const int y_base = c * kK3Chunk;
@@ -1266,15 +1296,17 @@ __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, 
     const int y0 = y_base + 4 * (g * kWG + tid);
     const bool full = y0 + 4 <= P.V;
     float l[4], q[4];
-    if (full && P.aligned) {
-      if (BF16) {
-        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
+    if (r != nullptr || (full && P.aligned)) {
+      if constexpr (BF16) {
+        const u32x2 w = (r != nullptr) ? r->l[g]
+                                       : __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
         l[0] = __uint_as_float(w.x << 16);
         l[1] = __uint_as_float(w.x & 0xffff0000u);
         l[2] = __uint_as_float(w.y << 16);
         l[3] = __uint_as_float(w.y & 0xffff0000u);
       } else {
-        const u32x4 w = __builtin_nontemporal_load((const u32x4*)((const float*)P.logits + lrow + y0));
+        const u32x4 w = (r != nullptr) ? r->l[g]
+                                       : __builtin_nontemporal_load((const u32x4*)((const float*)P.logits + lrow + y0));
         l[0] = __uint_as_float(w.x);
         l[1] = __uint_as_float(w.y);
         l[2] = __uint_as_float(w.z);
@@ -1285,8 +1317,8 @@ __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, 
       for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
     if (KIND == JOB_RESID) {
-      if (full && P.q_aligned) {
-        const u32x4 w = __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
+      if (r != nullptr || (full && P.q_aligned)) {
+        const u32x4 w = (r != nullptr) ? r->q[g] : __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
         q[0] = __uint_as_float(w.x);
         q[1] = __uint_as_float(w.y);
         q[2] = __uint_as_float(w.z);
@@ -1322,10 +1354,10 @@ __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, 
 // once all its records are stored, and E_c comes from shared memory.  The
 // fp64 block sum is within 2^-40; 2^-100 covers weights lost to underflow;
 // the key's division and E_c's log are within 2^-48.
-template <bool BF16, int KIND>
-__device__ __forceinline__ void k3_chunk(const Params& P, const Job& J, int b, int c3, Smem& sm) {
-  double dhi, dlo;
-  chunk_sum_bounds<BF16, KIND>(P, J, c3, dhi, dlo);
+// A chunk's block sums and record, from this thread's share of its bounds.
+template <bool BF16>
+__device__ __forceinline__ void k3_chunk_record(const Params& P, const Job& J, int b, int c3, double dhi, double dlo,
+                                                Smem& sm) {
   block_sum2_d(dhi, dlo, sm);
   if (threadIdx.x == 0) {
     const int e = c3 - sm.chunk_e0;
@@ -1339,6 +1371,32 @@ __device__ __forceinline__ void k3_chunk(const Params& P, const Job& J, int b, i
       wait_mem();  // the record is stored before its marker
       cst_i32(&rec->count, 1);
     }
+  }
+}
+
+template <bool BF16, int KIND>
+__device__ __forceinline__ void k3_chunk(const Params& P, const Job& J, int b, int c3, Smem& sm) {
+  double dhi, dlo;
+  chunk_sum_bounds<BF16, KIND>(P, J, c3, dhi, dlo);
+  k3_chunk_record<BF16>(P, J, b, c3, dhi, dlo, sm);
+}
+
+// The chunks [c_lo, c_hi) of an item, software-pipelined: a chunk's loads
+// are issued before the previous chunk's block sums and record, which hide
+// their latency.
+template <bool BF16, int KIND>
+__device__ __forceinline__ void k3_item_chunks(const Params& P, const Job& J, int b, int c_lo, int c_hi, Smem& sm) {
+  ChunkRaw<BF16> r;
+  bool whole = chunk_whole(P, J, c_lo);
+  if (whole) chunk_load<BF16, KIND>(P, J, c_lo, r);
+#pragma unroll 1
+  for (int c3 = c_lo; c3 < c_hi; ++c3) {
+    double dhi, dlo;
+    if (whole) chunk_sum_bounds<BF16, KIND>(P, J, c3, dhi, dlo, &r);
+    else chunk_sum_bounds<BF16, KIND>(P, J, c3, dhi, dlo);
+    whole = c3 + 1 < c_hi && chunk_whole(P, J, c3 + 1);
+    if (whole) chunk_load<BF16, KIND>(P, J, c3 + 1, r);
+    k3_chunk_record<BF16>(P, J, b, c3, dhi, dlo, sm);
   }
 }
 
@@ -1569,8 +1627,10 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int item, Smem& 
         if (tid == 0) sm.chunk_e0 = c_lo;
         if (tid < min(c_hi - c_lo, kChunkE)) sm.chunk_e[tid] = chunk_exp(P.seed[b], b, sm.job.r, c_lo + tid);
         __syncthreads();
-#pragma unroll 1
-        for (int c3 = c_lo; c3 < c_hi; ++c3) sample_chunk<BF16>(P, b, c3, sm);
+        const int kind = uniform_i(sm.job.kind);
+        if (kind == JOB_RESID) k3_item_chunks<BF16, JOB_RESID>(P, sm.job, b, c_lo, c_hi, sm);
+        else if (kind == JOB_EXCL) k3_item_chunks<BF16, JOB_EXCL>(P, sm.job, b, c_lo, c_hi, sm);
+        else k3_item_chunks<BF16, JOB_P>(P, sm.job, b, c_lo, c_hi, sm);
         // one wait for all the item's records, then their markers
         if (tid == 0) wait_mem();
         __syncthreads();
