@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "libsvo.so")
 REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 DRAFT_PROBS, DRAFT_ONEHOT = 0, 1
+RULE_STANDARD, RULE_BLOCK = 0, 1
 
 
 def build(force: bool = True) -> str:
@@ -46,7 +47,7 @@ class _ChainArgs(ctypes.Structure):
                 ("draft_kind", _I32), ("draft_probs", _P), ("q_row_stride", _I64),
                 ("draft_ids", _P), ("temperature", _P), ("seed", _P),
                 ("accept_len", _P), ("tokens", _P), ("req_status", _P),
-                ("p_draft", _P), ("min_margin", _P), ("n_decisions", _P)]
+                ("p_draft", _P), ("min_margin", _P), ("n_decisions", _P), ("rule", _I32)]
 
 
 class _TreeArgs(ctypes.Structure):
@@ -154,8 +155,11 @@ def row_stats(logits, temperature):
     return m, am, s, st
 
 
-def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False):
+def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, rule="standard"):
     """Chain verification.
+
+    rule: "standard" (left-to-right rejection sampling) or "block" (block
+    verification); greedy requests ignore it.
 
     logits: [bs, k+1, V] float32 or uint16 (bf16 bits); draft_ids: [bs, k] int32;
     draft_probs: [bs, k, V] float32 (standard rule) or None with onehot=True.
@@ -178,9 +182,12 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
     out = dict(accept_len=np.empty(bs, np.int32), tokens=np.empty((bs, R), np.int32),
                status=np.empty(bs, np.int32), p_draft=np.empty((bs, max(k, 1)), np.float64),
                min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32))
+    if rule not in ("standard", "block"):
+        raise ValueError(f"unknown rule {rule!r}")
     a = _ChainArgs(bs, k, V, code, _ptr(x), V, kind, _ptr(q), V, _ptr(ids), _ptr(temp), _ptr(sd),
                    _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out["status"]),
-                   _ptr(out["p_draft"]), _ptr(out["min_margin"]), _ptr(out["n_decisions"]))
+                   _ptr(out["p_draft"]), _ptr(out["min_margin"]), _ptr(out["n_decisions"]),
+                   RULE_BLOCK if rule == "block" else RULE_STANDARD)
     lib().svo_verify_chain(ctypes.byref(a))
     out["p_draft"] = out["p_draft"][:, :k]
     return out

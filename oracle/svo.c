@@ -15,7 +15,11 @@
  *        default), "SGLang 默认：只看目标概率，可以验证一棵树" (target-only tree);
  *        section "对照：mistral.rs" (the q <= 0 rule).
  *  [ZOO] "The speculative decoding zoo" (section 6.6), mlinterviewnotes.com:
- *        "DFlash - the draft that borrows everything" (greedy prefix match).
+ *        "DFlash - the draft that borrows everything" (greedy prefix match);
+ *        the passage on vLLM's rejection methods (after "Multi-layer EAGLE
+ *        and STANDALONE"): the "block" rule's acceptance function.
+ *  [BLK] Sun et al. 2024, block verification (arXiv 2403.10444), which the
+ *        page cites for the prefix weight's clipped recursion.
  *  [PHX] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *        1, 2, 3", SC'11 (Philox4x32-10), which the pages do not fix.
  *
@@ -26,6 +30,9 @@
  *    the chunk noise for chunk c is word 0 of counter (c, r, b, 2);
  *  - uniforms are (2*(w>>9)+1)/2^24, inside (0,1) and exact in fp32;
  *  - the acceptance test is strict (u*q < p); q(x) <= 0 accepts iff p(x) > 0;
+ *  - block verification: the prefix weight is clipped at 1 at every step
+ *    ([BLK]); its test is eta <= h as the page's kernel writes it, with
+ *    eta_i the coin of draft row i - 1;
  *  - the residual / bonus sample is a two-level exponential race: the ids
  *    are cut into chunks of SVO_RACE_CHUNK; the chunk c maximising
  *    W_c / E_c (W_c its weight sum, E_c = -ln U_c) is chosen, then the id y
@@ -251,6 +258,76 @@ static double rel_gap(double a, double b) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block verification ([ZOO], the passage on vLLM's "block" rejection
+ * method, which points to [BLK]).  Instead of
+ * testing each draft against its own ratio, the rule keeps a prefix weight
+ * w_i (w_0 = 1, w_{i+1} = min(w_i p_i(x_i) / q_i(x_i), 1): the page's
+ * "prefix joint ratio", clipped at 1 at every step as in [BLK]) and,
+ * for every prefix length i = 1..kb, an acceptance probability
+ *   h_i = r_i / (r_i + 1 - w_i)   (1 when the denominator is 0),  i < kb,
+ *   h_kb = w_kb,
+ * where r_i = sum_y max(w_i p_i(y) - q_i(y), 0) is the residual mass at the
+ * next position.  With one uniform eta_i per prefix length, the accepted
+ * length is the largest i with eta_i <= h_i (0 if none), and the emitted
+ * token is drawn from max(w_a p_a - q_a, 0) (a < kb) or from p_kb.  A
+ * one-hot draft has q_i the point mass at x_i.  eta_i is the coin of the
+ * draft's row, coin(b, i - 1), so one draft gives the standard rule up to
+ * the comparison's tie.  Every decision's relative gap is logged. */
+
+/* q_i(y) of draft row i of request b (one-hot drafts: the point mass at x). */
+static double q_of(const svo_chain_args* a, int32_t b, int32_t i, int32_t x, int32_t y) {
+  if (a->draft_kind == SVO_DRAFT_ONEHOT) return y == x ? 1.0 : 0.0;
+  return (double)a->draft_probs[((int64_t)b * a->max_draft + i) * a->q_row_stride + y];
+}
+
+/* w(y) = max(w_i p_i(y) - q_i(y), 0) for every y; prow holds p_i. */
+static void block_residual(const svo_chain_args* a, int32_t b, int32_t i, int32_t x, double wi, const double* prow,
+                           double* w) {
+  for (int32_t y = 0; y < a->vocab; ++y) {
+    double d = wi * prow[y] - q_of(a, b, i, x, y);
+    w[y] = d > 0.0 ? d : 0.0;
+  }
+}
+
+/* Fills wpre[0..kb] and returns the accepted length. */
+static int32_t block_decisions(const svo_chain_args* a, int32_t b, int32_t kb, const row_stat* st, const double* px,
+                               double* wpre, double* min_margin, int32_t* n_dec) {
+  const int32_t R = a->max_draft + 1, V = a->vocab;
+  const int32_t* x = a->draft_ids + (int64_t)b * a->max_draft;
+  const double T = (double)a->temperature[b];
+  wpre[0] = 1.0;
+  for (int32_t i = 0; i < kb; ++i) {
+    double q = q_of(a, b, i, x[i], x[i]);
+    double ratio = q > 0.0 ? px[i] / q : (px[i] > 0.0 ? INFINITY : 0.0);
+    double w = wpre[i] * ratio;
+    if (wpre[i] == 0.0 || ratio == 0.0) w = 0.0;
+    wpre[i + 1] = w < 1.0 ? w : 1.0;
+  }
+  int32_t tau = 0;
+  for (int32_t i = 1; i <= kb; ++i) {
+    double h;
+    if (i < kb) {
+      int64_t off = ((int64_t)b * R + i) * a->logits_row_stride;
+      double r = 0.0;
+      for (int32_t y = 0; y < V; ++y) {
+        double d = wpre[i] * p_of(a->logits_dtype, a->logits, off, &st[i], T, y) - q_of(a, b, i, x[i], y);
+        if (d > 0.0) r += d;
+      }
+      double den = r + 1.0 - wpre[i];
+      h = den > 0.0 ? r / den : 1.0;
+    } else {
+      h = wpre[kb];
+    }
+    double eta = svo_coin(a->seed[b], b, i - 1);
+    ++*n_dec;
+    double g = rel_gap(eta, h);
+    if (g < *min_margin) *min_margin = g;
+    if (eta <= h) tau = i;
+  }
+  return tau;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Chain verification of one request.
  *
  * [SD] "采样：标准拒绝采样": accept x_i with probability min(1, p(x_i)/q(x_i)),
@@ -316,9 +393,16 @@ static void chain_one(const svo_chain_args* a, int32_t b, double* w, double* pro
     if (pd) pd[i] = px[i];
   }
 
-  /* 3. left-to-right decisions, stopping at the first rejection */
+  /* 3. decisions: block verification, or left to right stopping at the
+   *    first rejection */
   int32_t acc = 0;
-  for (int32_t i = 0; i < kb; ++i) {
+  double wpre[k + 1];  /* block rule: prefix weights w_0..w_kb */
+  wpre[0] = 1.0;
+  if (!greedy && a->rule == SVO_RULE_BLOCK) {
+    acc = block_decisions(a, b, kb, st, px, wpre, &min_margin, &n_dec);
+    for (int32_t i = 0; i < acc; ++i) tok[i] = x[i];
+  }
+  for (int32_t i = 0; i < kb && (greedy || a->rule != SVO_RULE_BLOCK); ++i) {
     int accept;
     ++n_dec;
     if (greedy) {
@@ -353,7 +437,11 @@ static void chain_one(const svo_chain_args* a, int32_t b, double* w, double* pro
   } else {
     int64_t off = ((int64_t)b * R + acc) * a->logits_row_stride;
     for (int32_t y = 0; y < V; ++y) prow[y] = p_of(a->logits_dtype, a->logits, off, &st[acc], T, y);
-    if (acc < kb && a->draft_kind == SVO_DRAFT_PROBS) {
+    if (acc < kb && a->rule == SVO_RULE_BLOCK) {
+      /* block rule: the residual of the prefix-weighted target,
+       * max(w_acc p - q, 0), q the draft row (one-hot: the point mass) */
+      block_residual(a, b, acc, x[acc], wpre[acc], prow, w);
+    } else if (acc < kb && a->draft_kind == SVO_DRAFT_PROBS) {
       const float* qrow = a->draft_probs + ((int64_t)b * k + acc) * a->q_row_stride;
       for (int32_t y = 0; y < V; ++y) {
         double d = prow[y] - (double)qrow[y];

@@ -31,6 +31,9 @@ enum {
 
 enum { SVO_F32 = 0, SVO_BF16 = 1 };
 enum { SVO_DRAFT_PROBS = 0, SVO_DRAFT_ONEHOT = 1 };
+/* Acceptance rule of stochastic chain requests: left-to-right rejection
+ * sampling, or block verification (greedy requests ignore it). */
+enum { SVO_RULE_STANDARD = 0, SVO_RULE_BLOCK = 1 };
 
 /* Philox4x32-10 block function: 10 rounds of the Philox-4x32 bijection keyed
  * by key[0..1], applied to the 128-bit counter ctr[0..3]. */
@@ -79,6 +82,7 @@ typedef struct {
   double* p_draft;                          /* [bs][k] out: p_i(x_i), NaN where unused; may be NULL */
   double* min_margin;                       /* [bs] out: smallest decision margin; may be NULL */
   int32_t* n_decisions;                     /* [bs] out: decisions taken; may be NULL */
+  int32_t rule;                             /* SVO_RULE_STANDARD or SVO_RULE_BLOCK */
 } svo_chain_args;
 
 typedef struct {
