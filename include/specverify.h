@@ -118,6 +118,23 @@ enum {
  * combined with SV_FLAG_FUSED or with each other. */
 #define SV_FLAG_STATS_ONLY 8u
 #define SV_FLAG_DECIDE_ONLY 16u
+/* Block verification for the stochastic requests of a chain call (page "The
+ * speculative decoding zoo", the passage on vLLM's "block" rejection method,
+ * after Sun et al. 2024, which it cites).  The drafts are judged as a block:
+ * with prefix weights w_0 = 1, w_{i+1} = min(w_i p_i(x_i) / q_i(x_i), 1)
+ * (q one-hot at the draft for SV_DRAFT_ONEHOT; q(x) = 0 gives ratio +inf if
+ * p(x) > 0, else 0) and residual masses r_i = sum_y max(w_i p_i(y) - q_i(y), 0),
+ * prefix length i = 1..kb passes with probability h_i = r_i / (r_i + 1 - w_i)
+ * (1 when that denominator is 0) for i < kb and h_kb = w_kb.  The accepted
+ * length a is the longest prefix whose coin passes (eta_i <= h_i, eta_i the
+ * coin of row i - 1; 0 if none), and the emitted token is drawn from
+ * max(w_a p_a - q_a, 0) (all zero: p_a), or from p_kb when a = kb.  One draft
+ * gives the standard rule.  Greedy requests are unaffected.  The residual
+ * masses of rows 1..kb-1 take one more pass over those target and q rows
+ * (a third launch); not available with SV_FLAG_FUSED (SV_ERR_UNSUPPORTED)
+ * nor for trees (SV_ERR_UNSUPPORTED).  With STATS_ONLY / DECIDE_ONLY the
+ * extra pass belongs to the DECIDE_ONLY call. */
+#define SV_FLAG_BLOCK 32u
 
 typedef struct {
   int32_t batch;              /* bs, 1..SV_MAX_BATCH */

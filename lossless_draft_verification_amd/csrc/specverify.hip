@@ -71,6 +71,7 @@ constexpr int kWaves = kWG / 64;
 #endif
 constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a K1 sub-chunk
 constexpr int kK1Depth = SV_K1_DEPTH;           // K1 sub-chunks in flight ahead of the one being folded
+constexpr int kKRWorkgroups = 256 * 8 * 2;      // block rule's residual-mass pass: workgroups it aims at
 // K1 workgroups per call: an MI355X holds 256 CUs x 7 of them at once (71
 // VGPRs), so the stream is one round.
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
@@ -164,6 +165,8 @@ struct Params {
   int32_t C3;         // sampling chunks per request
   int32_t G3;         // sampling chunks per K23 item
   int32_t CI;         // K23 items per request: ceil(C3 / G3)
+  int32_t CHr;        // block rule: residual-mass items per row (rows 1..k-1)
+  double* rpart;      // block rule: [bs][k][CHr] residual-mass partials
   int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
   uint32_t flags;
@@ -294,6 +297,7 @@ struct Job {
   int kind, row, qrow, r, out_slot, n_excl;
   float m, c_hi, c_lo, inv_s;  // row max; log2(e)/T as hi + lo; 1/S rounded
   double s, t;                  // S = sum exp((l - m)/T); T
+  double wmul;                  // JOB_RESID weight max(wmul p - q, 0): 1, or the block rule's prefix weight
   int excl[SV_MAX_NODES];       // ids removed from p (JOB_EXCL)
 };
 
@@ -712,6 +716,58 @@ __device__ __forceinline__ void k2_rows(const Params& P, int b, Smem& sm) {
   }
 }
 
+// Prefix weights of the block rule (page "The speculative decoding zoo",
+// vLLM's "block" method, after Sun et al. 2024): w_0 = 1 and
+// w_{j+1} = min(w_j p_j / q_j, 1), with p_j, q_j the target and draft
+// probabilities of draft j (lane j).  A zero draft probability gives ratio
+// +inf (p > 0) or 0, and a zero weight stays zero.  Every lane of the wave
+// calls it; lane j gets w_j (j <= n).
+__device__ __forceinline__ double prefix_weights(double p, double q, int n) {
+  const int lane = threadIdx.x & 63;
+  double w = 1.0, mine = 1.0;
+  for (int j = 0; j < n; ++j) {
+    const double pj = __shfl(p, j, 64), qj = __shfl(q, j, 64);
+    const double ratio = qj > 0.0 ? pj / qj : (pj > 0.0 ? INFINITY : 0.0);
+    double nw = w * ratio;
+    if (w == 0.0 || ratio == 0.0) nw = 0.0;
+    w = nw < 1.0 ? nw : 1.0;
+    if (lane == j + 1) mine = w;
+  }
+  return mine;
+}
+
+// Accepted length of chain request b under the block rule (wave 0, lane j
+// on draft j): prefix length j + 1 passes when its coin u_j is at most
+// h = r / (r + 1 - w) (1 when that denominator is 0; h = w for the whole
+// chain), with w and r the prefix weight and residual mass of row j + 1 --
+// for one-hot drafts r = w (1 - p(x)), otherwise the sum of the residual
+// pass's partials.  The longest passing prefix is accepted.  wa gets the
+// accepted length's prefix weight.
+__device__ __forceinline__ int block_accept(const Params& P, int b, int kb, int lane, int status, double p,
+                                            double u, uint64_t gl, double& wa) {
+  const bool onehot = P.draft_kind == SV_DRAFT_ONEHOT;
+  const double q = onehot ? 1.0 : (double)__uint_as_float((uint32_t)(gl >> 32));
+  const double wl = prefix_weights(p, q, kb);
+  const double wn = __shfl(wl, (lane + 1) & 63, 64);  // w of row lane + 1
+  const double pn = __shfl(p, (lane + 1) & 63, 64);   // p of draft lane + 1
+  double h = wn;
+  if (lane + 1 < kb) {
+    double r = 0.0;
+    if (onehot) {
+      r = wn * (1.0 - pn);
+    } else {
+      const double* rp = P.rpart + ((int64_t)b * P.k + lane + 1) * P.CHr;
+      for (int c = 0; c < P.CHr; ++c) r += rp[c];
+    }
+    const double den = r + 1.0 - wn;
+    h = den > 0.0 ? r / den : 1.0;
+  }
+  const uint64_t pass = __ballot(status == SV_REQ_OK && lane < kb && u <= h);
+  const int a = (status != SV_REQ_OK || !pass) ? 0 : 64 - __builtin_clzll(pass);
+  wa = __shfl(wl, a, 64);
+  return a;
+}
+
 // Decision step of chain request b, by wave 0 with lane r on row r (and on
 // draft r): every workgroup that samples for the request runs it (its
 // inputs are a few hundred bytes, in L2 after the first), so none waits for
@@ -763,8 +819,14 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
         }
       }
     }
-    const uint64_t rejected = __ballot(status == SV_REQ_OK && lane < kb && !accept);
-    const int a = status != SV_REQ_OK ? 0 : rejected ? (int)__builtin_ctzll(rejected) : kb;
+    int a;
+    double wa = 1.0;  // block rule: prefix weight of the emitted row
+    if ((P.flags & SV_FLAG_BLOCK) && !greedy) {
+      a = block_accept(P, b, kb, lane, status, p, u, gl, wa);
+    } else {
+      const uint64_t rejected = __ballot(status == SV_REQ_OK && lane < kb && !accept);
+      a = status != SV_REQ_OK ? 0 : rejected ? (int)__builtin_ctzll(rejected) : kb;
+    }
     sm.xs[lane] = xi;
     sm.px[lane] = p;
     sm.ramax[lane] = rs.amax;
@@ -785,7 +847,8 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
         J.s = rs.s;
         J.t = T;
         scale_pair(T, J.c_hi, J.c_lo);
-        J.inv_s = (float)(1.0 / rs.s);
+        J.wmul = (J.kind == JOB_RESID) ? wa : 1.0;
+        J.inv_s = (float)(J.wmul / rs.s);
         J.n_excl = (J.kind == JOB_EXCL) ? 1 : 0;
         J.excl[0] = xi;
       }
@@ -921,6 +984,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
       J.t = T;
       scale_pair(T, J.c_hi, J.c_lo);
       J.inv_s = (float)(1.0 / J.s);
+      J.wmul = 1.0;
       int ne = 0;
       if (kind == JOB_EXCL)
         for (int c = cur + 1; c < N; ++c)
@@ -967,7 +1031,7 @@ __device__ __forceinline__ double race_key_from(const Job& J, uint64_t seed, int
   const double p = p_at(l, J.m, J.t, J.s);
   double w = p;
   if (!use_p) {
-    if (J.kind == JOB_RESID) w = (p - q > 0.0) ? p - q : 0.0;
+    if (J.kind == JOB_RESID) w = (J.wmul * p - q > 0.0) ? J.wmul * p - q : 0.0;
     else if (J.kind == JOB_EXCL && is_excluded(J, y)) w = 0.0;
   }
   const double U = uniform_f64(noise_word(seed, b, J.r, y));
@@ -1008,17 +1072,19 @@ __device__ __forceinline__ void block_best(double& k, int& y, Smem& sm) {
 // inlined into them, its fp64 constants would be held in registers for the
 // whole kernel.
 __device__ __attribute__((noinline)) double race_key_cold(double l, double q, double m, double T, double S,
-                                                          int resid, int use_p, uint64_t seed, int b, int r, int y) {
+                                                          double wmul, int resid, int use_p, uint64_t seed, int b,
+                                                          int r, int y) {
   const double p = exp((l - m) / T) / S;
   double w = p;
-  if (!use_p && resid) w = (p - q > 0.0) ? p - q : 0.0;
+  if (!use_p && resid) w = (wmul * p - q > 0.0) ? wmul * p - q : 0.0;
   const double U = uniform_f64(noise_word(seed, b, r, y));
   return w / -log(U);
 }
-// Exact fp64 weight of one id (p, or the residual max(p - q, 0)).
-__device__ __attribute__((noinline)) double weight_cold(double l, double q, double m, double T, double S, int resid) {
+// Exact fp64 weight of one id (p, or the residual max(wmul p - q, 0)).
+__device__ __attribute__((noinline)) double weight_cold(double l, double q, double m, double T, double S,
+                                                        double wmul, int resid) {
   const double p = exp((l - m) / T) / S;
-  if (resid) return (p - q > 0.0) ? p - q : 0.0;
+  if (resid) return (wmul * p - q > 0.0) ? wmul * p - q : 0.0;
   return p;
 }
 
@@ -1041,7 +1107,7 @@ __device__ double chunk_sum_f64(const Params& P, const Job& J, int c, bool use_p
     if (!use_p && J.kind == JOB_EXCL && is_excluded(J, y)) continue;
     const double l = (double)load_logit<BF16>(P, J.row, y);
     const double q = qrow ? (double)qrow[y] : 0.0;
-    s += weight_cold(l, q, J.m, J.t, J.s, resid);
+    s += weight_cold(l, q, J.m, J.t, J.s, J.wmul, resid);
   }
   return block_sum_d(s, sm);
 }
@@ -1059,7 +1125,8 @@ __device__ int chunk_race_f64(const Params& P, const Job& J, int b, int c, bool 
     const double l = (double)load_logit<BF16>(P, J.row, y);
     const double q = qrow ? (double)qrow[y] : 0.0;
     const bool zero = !use_p && J.kind == JOB_EXCL && is_excluded(J, y);
-    const double key = zero ? 0.0 : race_key_cold(l, q, J.m, J.t, J.s, J.kind == JOB_RESID, use_p, seed, b, J.r, y);
+    const double key = zero ? 0.0 : race_key_cold(l, q, J.m, J.t, J.s, J.wmul, J.kind == JOB_RESID, use_p, seed, b,
+                                                          J.r, y);
     if (better(key, y, best_k, best_y)) {
       best_k = key;
       best_y = y;
@@ -1749,6 +1816,131 @@ __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
   }
 }
 
+// ===================================================================== KR
+// Residual masses of the block rule: r_i = sum_y max(w_i p_i(y) - q_i(y), 0)
+// for rows i = 1..kb-1 of the stochastic requests with draft probabilities
+// (one-hot drafts have the closed form w_i (1 - p_i(x_i)), taken by the
+// decision step).  One workgroup per (request, row i, item); an item is a
+// run of whole 2048-id chunks.  Each workgroup folds the request's row
+// statistics of rows 0..i and its gathered draft values to get w_i, then
+// streams its ids of target row i and draft row i.  A term is evaluated in
+// fp64 exactly as the definition reads (w (exp((l - m)/T) / S) - q) unless an
+// fp32 screen shows it is not positive: w S^-1 2^((l - m) log2(e)/T) in fp32
+// is within 2^-14 relative for every exponent above -128 (and below 2^-126
+// beneath), so a value below q (1 - 2^-12) cannot be positive, and a term it
+// could hide is under 2^-126.  The fp64 partial sums are reduced in a fixed
+// order: the decision step adds the items' partials in item order.
+template <bool BF16>
+__device__ __forceinline__ void kr_load4(const Params& P, int64_t lrow, int64_t qrow, int y0, float* l, float* q) {
+  if (y0 + 4 <= P.V && P.aligned && P.q_aligned) {
+    if (BF16) {
+      const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
+      l[0] = __uint_as_float(w.x << 16);
+      l[1] = __uint_as_float(w.x & 0xffff0000u);
+      l[2] = __uint_as_float(w.y << 16);
+      l[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      const u32x4 w = __builtin_nontemporal_load((const u32x4*)((const float*)P.logits + lrow + y0));
+      l[0] = __uint_as_float(w.x);
+      l[1] = __uint_as_float(w.y);
+      l[2] = __uint_as_float(w.z);
+      l[3] = __uint_as_float(w.w);
+    }
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
+    q[0] = __uint_as_float(v.x);
+    q[1] = __uint_as_float(v.y);
+    q[2] = __uint_as_float(v.z);
+    q[3] = __uint_as_float(v.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = y0 + i < P.V;
+      l[i] = in ? (BF16 ? bf16_to_f32(((const uint16_t*)P.logits)[lrow + y0 + i]) : ((const float*)P.logits)[lrow + y0 + i])
+                : -INFINITY;
+      q[i] = in ? P.q[qrow + y0 + i] : 0.f;
+    }
+  }
+}
+
+constexpr int kKRUnroll = 4;  // groups of 4 ids whose loads a thread issues together
+
+template <bool BF16>
+__global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t per_req = (uint32_t)((P.k - 1) * P.CHr);
+  const int b = (int)(blockIdx.x / per_req);
+  const int rem = (int)(blockIdx.x - (uint32_t)b * per_req);
+  const int i = 1 + rem / P.CHr;
+  const int c = rem - (i - 1) * P.CHr;
+  const float Tf = temp_of(P, b);
+  if (!is_stochastic(Tf) || P.draft_kind != SV_DRAFT_PROBS) return;
+  int xi;
+  const int kb = chain_kb(P, b, xi);
+  if (i >= kb) return;
+  uint64_t gl = 0;
+  if (tid < 64 && lane < i) gl = P.gat[(int64_t)b * SV_MAX_NODES + lane].l | ((uint64_t)P.gat[(int64_t)b * SV_MAX_NODES + lane].q << 32);
+  fold_rows<false>(P, (int64_t)b * P.R, i + 1, Tf, sm);
+  const double T = (double)Tf;
+  if (tid < 64) {
+    const bool bad = __ballot(lane <= i && sm.rbad[lane]) != 0;
+    double p = 0.0, q = 0.0;
+    if (lane < i && !bad) {
+      p = p_at((double)__uint_as_float((uint32_t)gl), sm.rm[lane], T, sm.rs[lane]);
+      q = (double)__uint_as_float((uint32_t)(gl >> 32));
+    }
+    const double w = __shfl(prefix_weights(p, q, i), i, 64);
+    if (lane == 0) {
+      sm.u[0] = w;
+      sm.flag = bad;
+    }
+  }
+  __syncthreads();
+  double* out = P.rpart + ((int64_t)b * P.k + i) * P.CHr + c;
+  if (uniform_i(sm.flag)) {  // the decision step reports the request as non-finite
+    if (tid == 0) *out = 0.0;
+    return;
+  }
+  const double w = sm.u[0], S = sm.rs[i];
+  const float m = sm.rm[i];
+  const float cf = (float)(1.4426950408889634074 / T);
+  const float ws = (float)(w / S);
+  const int c_lo = (int)((int64_t)c * P.C3 / P.CHr), c_hi = (int)((int64_t)(c + 1) * P.C3 / P.CHr);
+  const int y_lo = c_lo * kK3Chunk, y_hi = min(c_hi * kK3Chunk, P.V);
+  const int64_t lrow = ((int64_t)b * P.R + i) * P.lstride;
+  const int64_t qrow = ((int64_t)b * P.k + i) * P.qstride;
+  double acc = 0.0;
+#pragma unroll 1
+  for (int y = y_lo + 4 * tid; y < y_hi; y += 4 * kWG * kKRUnroll) {
+    float l[kKRUnroll][4], q[kKRUnroll][4];
+#pragma unroll
+    for (int g = 0; g < kKRUnroll; ++g) {
+      const int y0 = y + 4 * kWG * g;
+      if (y0 < y_hi) {
+        kr_load4<BF16>(P, lrow, qrow, y0, l[g], q[g]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l[g][e] = -INFINITY;
+          q[g][e] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kKRUnroll; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = __builtin_amdgcn_exp2f((l[g][e] - m) * cf) * ws;
+        if (!(v * (1.f + 0x1p-12f) < q[g][e])) {
+          const double term = w * (exp(((double)l[g][e] - (double)m) / T) / S) - (double)q[g][e];
+          if (term > 0.0) acc += term;
+        }
+      }
+  }
+  acc = block_sum_d(acc, sm);
+  if (tid == 0) *out = acc;
+}
+
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
   const size_t n16 = n / 16;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1759,8 +1951,8 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 
 // ===================================================================== host
 struct Shape {
-  int SUB, nsub, Q, Qp, G, CPR, C3, G3, CI;
-  size_t gat_off, part_off, k3_off, total;
+  int SUB, nsub, Q, Qp, G, CPR, C3, G3, CI, CHr;
+  size_t gat_off, part_off, k3_off, r_off, total;
 };
 
 // Work split of a call (a function of the shape alone, so results never
@@ -1785,22 +1977,32 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   if (races && bs * s.C3 > 2 * kK3Slots) s.G3 = (int)((bs * s.C3 + kK3Slots - 1) / kK3Slots);
   if (s.G3 > s.C3 && s.C3 > 0) s.G3 = s.C3;
   s.CI = races ? (s.C3 + s.G3 - 1) / s.G3 : 0;
+  // block rule: residual-mass items per row of rows 1..R-2, about two
+  // rounds of resident workgroups over the batch, whole chunks each
+  s.CHr = 0;
+  if (races && R >= 3) {
+    int64_t ch = kKRWorkgroups / (bs * (R - 2));
+    if (ch > s.C3) ch = s.C3;
+    if (ch < 1) ch = 1;
+    s.CHr = (int)ch;
+  }
   s.gat_off = kDataOffset;
   s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
-  s.total = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
+  s.r_off = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
+  s.total = s.r_off + align256(sizeof(double) * (size_t)(bs * (R - 1) * s.CHr));
   return s;
 }
 
 typedef void (*KernelFn)(Params);
 
 struct Kernels {
-  KernelFn k1, k23, fused;
+  KernelFn k1, k23, fused, kr;
 };
 
 template <int MODE, bool BF16>
 static Kernels kernels_for() {
-  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>};
+  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>, kr_kernel<BF16>};
 }
 
 static Kernels select_kernels(int mode, bool bf16) {
@@ -1839,6 +2041,8 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.gat = (Gather*)(base + S.gat_off);
   P.part = (Partial*)(base + S.part_off);
   P.k3 = (K3Rec*)(base + S.k3_off);
+  P.rpart = (double*)(base + S.r_off);
+  P.CHr = S.CHr;
   P.SUB = S.SUB;
   P.nsub = S.nsub;
   P.Q = S.Q;
@@ -1850,6 +2054,8 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.CI = S.CI;
   const int64_t grid23 = (int64_t)P.bs * P.CI;
   if (grid23 + P.G > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
+  const int64_t gridr = (int64_t)P.bs * (P.k >= 2 ? P.k - 1 : 0) * P.CHr;
+  if (gridr > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).
   P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : SCHED_PHASED;
@@ -1868,7 +2074,11 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
     hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
   } else if (P.sched == SCHED_PHASED) {
     if (!(P.flags & SV_FLAG_DECIDE_ONLY)) hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
-    if (!(P.flags & SV_FLAG_STATS_ONLY)) hipLaunchKernelGGL(K.k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
+    if (!(P.flags & SV_FLAG_STATS_ONLY)) {
+      if ((P.flags & SV_FLAG_BLOCK) && P.k >= 2 && P.draft_kind == SV_DRAFT_PROBS)
+        hipLaunchKernelGGL(K.kr, dim3((unsigned)gridr), dim3(kWG), 0, stream, P);
+      hipLaunchKernelGGL(K.k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
+    }
   } else {
     hipLaunchKernelGGL(K.fused, dim3((unsigned)(P.G + grid23)), dim3(kWG), 0, stream, P);
   }
@@ -1902,7 +2112,7 @@ const char* sv_status_string(sv_status s) {
 static bool dtype_ok(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
 
 static const uint32_t kKnownFlags =
-    SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY;
+    SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY | SV_FLAG_BLOCK;
 // At most one of PHASED, FUSED, STATS_ONLY, DECIDE_ONLY, except PHASED with
 // one of the split-phase bits.
 static bool one_schedule(uint32_t flags) {
@@ -1950,6 +2160,7 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
   if (d->draft_kind != SV_DRAFT_PROBS && d->draft_kind != SV_DRAFT_ONEHOT) return SV_ERR_UNSUPPORTED;
   if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
   if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
+  if ((d->flags & SV_FLAG_BLOCK) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
   if (d->logits == nullptr || d->temperature == nullptr || d->seed == nullptr || d->accept_len == nullptr ||
       d->tokens == nullptr)
     return SV_ERR_INVALID_ARGUMENT;
@@ -1993,6 +2204,7 @@ sv_status sv_verify_tree(const sv_tree_desc* d, void* ws, size_t ws_bytes, void*
     return SV_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
   if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
+  if (d->flags & SV_FLAG_BLOCK) return SV_ERR_UNSUPPORTED;
   if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
   if (d->logits == nullptr || d->node_tokens == nullptr || d->parent == nullptr || d->temperature == nullptr ||
       d->seed == nullptr || d->accept_len == nullptr || d->accept_path == nullptr || d->tokens == nullptr)

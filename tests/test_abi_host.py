@@ -79,7 +79,7 @@ def _call_chain(desc, ws_bytes=1 << 30, ws=0x200000):
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, 1), ("batch", sv.MAX_BATCH + 1, 1), ("max_draft", -1, 1), ("max_draft", 64, 1),
-    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3), ("flags", 32, 3),
+    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3), ("flags", 64, 3),
     ("logits", None, 1), ("temperature", None, 1), ("seed", None, 1), ("accept_len", None, 1),
     ("tokens", None, 1), ("draft_ids", None, 1), ("logits_row_stride", 99, 1), ("draft_probs", None, 1),
     ("q_row_stride", 50, 1),
@@ -95,6 +95,12 @@ def test_schedule_flags_are_exclusive():
         assert _call_chain(_chain_desc(flags=f)) == 1
         d = _tree_desc(flags=f)
         assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 1
+
+
+def test_block_rule_needs_the_phased_schedule_and_a_chain():
+    assert _call_chain(_chain_desc(flags=sv.FLAG_BLOCK | sv.FLAG_FUSED)) == 3
+    d = _tree_desc(flags=sv.FLAG_BLOCK)
+    assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 3
 
 
 def test_chain_null_descriptor_and_workspace_checks():

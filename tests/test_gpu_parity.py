@@ -80,7 +80,8 @@ def _compare_p(ref_p, got_p, ref_status, name):
 
 def run_chain(inp, dev, flags=0):
     ref = oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds,
-                              draft_probs=inp.draft_probs, onehot=inp.onehot)
+                              draft_probs=inp.draft_probs, onehot=inp.onehot,
+                              rule="block" if flags & sv.FLAG_BLOCK else "standard")
     out = sv.verify_chain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev),
                           _t(inp.seeds, dev), draft_probs=None if inp.onehot else _t(inp.draft_probs, dev),
                           onehot=inp.onehot, flags=flags, return_p_draft=True)
@@ -491,6 +492,71 @@ def test_row_stats_parity(dev, dtype):
         assert (rel < 2e-6).all(), (V, float(rel.max()))
         assert np.isnan(out["row_sumexp"][~stoch]).all()
         print(f"[parity] row stats V={V} {dtype}: max rel err of S {rel.max() if rel.size else 0:.2e}", flush=True)
+
+
+# ---------------------------------------------------- block verification
+BLOCK_SHAPES = [(2, 3, 1, 2), (3, 5, 3, 7), (4, 33, 7, 1000), (5, 17, 2, 4095), (7, 9, 3, 4097),
+                (8, 4, 7, 8191), (11, 6, 3, 12345), (12, 3, 63, 300), (13, 7, 2, 33001), (15, 12, 3, 1001)]
+
+
+@pytest.mark.parametrize("seed,bs,k,V", BLOCK_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["probs", "onehot"])
+def test_block_rule_random_chain_shapes(dev, seed, bs, k, V, dtype, kind):
+    inp = _random_chain(seed * 11 + (dtype == "bf16") * 5 + (kind == "onehot") + 500, bs, k, V, dtype, kind)
+    check_chain(inp, dev, flags=sv.FLAG_BLOCK)
+
+
+@pytest.mark.parametrize("name", ["chain_bf16_mixed", "chain_fp32", "onehot_bf16"])
+def test_block_rule_workloads(dev, name):
+    check_chain(getattr(workloads, name)(0), dev, flags=sv.FLAG_BLOCK)
+
+
+def test_block_rule_with_one_draft_equals_the_standard_rule_on_gpu(dev):
+    for kind in ("probs", "onehot"):
+        inp = _random_chain(61 + (kind == "onehot"), 40, 1, 5000, "bf16", kind, pad_frac=0.0)
+        _, std = run_chain(inp, dev)
+        _, blk = run_chain(inp, dev, flags=sv.FLAG_BLOCK)
+        for key in ("accept_len", "tokens", "status"):
+            np.testing.assert_array_equal(std[key], blk[key], err_msg=f"{kind} {key}")
+
+
+def test_block_rule_split_phases_and_identical_drafts(dev):
+    inp = workloads.chain_bf16_mixed(1, bs=16, k=5, V=20000)
+    _, plain = run_chain(inp, dev, flags=sv.FLAG_BLOCK)
+    pc = sv.PreparedChain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev), _t(inp.seeds, dev),
+                          draft_probs=_t(inp.draft_probs, dev), flags=sv.FLAG_BLOCK)
+    pc.launch(phase_flag=sv.FLAG_STATS_ONLY)
+    pc.launch(phase_flag=sv.FLAG_DECIDE_ONLY)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "tokens", "status"):
+        np.testing.assert_array_equal(pc.out[key].cpu().numpy(), plain[key], err_msg=key)
+    # p = q uniform on a support of 4 is exact on both sides: all drafts pass
+    n, V, k = 32, 3000, 6
+    support = np.array([3, 700, 701, 2999])
+    l = np.full((n, k + 1, V), -np.inf, np.float32)
+    l[:, :, support] = 1.5
+    q = np.zeros((n, k, V), np.float32)
+    q[:, :, support] = 0.25
+    ids = support[np.random.default_rng(4).integers(0, 4, size=(n, k))].astype(np.int32)
+    same = workloads.ChainInputs(l, ids, q, np.ones(n, np.float32), np.arange(n, dtype=np.uint64), False,
+                                 "block identical")
+    ref, got = check_chain(same, dev, flags=sv.FLAG_BLOCK)
+    assert (got["accept_len"] == k).all()
+
+
+def test_block_rule_zero_draft_probabilities(dev):
+    """q(x) = 0 (ratio +inf) and p(x) = 0 (the prefix weight drops to 0)."""
+    bs, k, V = 8, 4, 3000
+    rng = np.random.default_rng(19)
+    l = rng.standard_normal((bs, k + 1, V)).astype(np.float32)
+    q = workloads._softmax_rows(rng.standard_normal((bs * k, V)).astype(np.float32)).reshape(bs, k, V)
+    ids = rng.integers(0, V, (bs, k)).astype(np.int32)
+    q[np.arange(bs), 0, ids[:, 0]] = 0.0
+    l[1::2, 1, ids[1::2, 1]] = -np.inf
+    inp = workloads.ChainInputs(l, ids, q, np.ones(bs, np.float32), np.arange(bs, dtype=np.uint64) + 40, False,
+                                "block zero probabilities")
+    check_chain(inp, dev, flags=sv.FLAG_BLOCK)
 
 
 def test_exemption_rate_is_small():
