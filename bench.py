@@ -51,14 +51,16 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(inp, accept_len):
+def algorithmic_bytes(inp, accept_len, block=False):
     """Bytes the method must move for one call, from the actual outcomes,
     split by phase.  Row statistics: every read logit row (rows 0..k_b of
     each request) once, the gathers at the draft ids (logit, id, q value)
     and the temperature.  Decision/sampling: per-request scalars, the
     re-read of the one sampled row per stochastic request (its logits, plus
-    its q row after a standard rejection), and the outputs.  Returns
-    (stats_bytes, decide_bytes)."""
+    its q row after a rejection), and the outputs; under the block rule
+    with draft probabilities also the residual-mass pass over target and q
+    rows 1..k_b-1 of each stochastic request.  Returns (stats_bytes,
+    decide_bytes)."""
     bs, R, V = inp.logits.shape
     k = R - 1
     bl = inp.logits.dtype.itemsize
@@ -74,6 +76,8 @@ def algorithmic_bytes(inp, accept_len):
         if stoch[b]:
             reject = accept_len[b] < kb[b]
             decide += V * bl + (V * 4 if (reject and not inp.onehot) else 0)  # sampled row (+ q row)
+            if block and not inp.onehot and kb[b] >= 2:
+                decide += (kb[b] - 1) * V * (bl + 4)                          # residual masses
         decide += 4 + 4 * R + 4                                               # accept_len, tokens, status
     return int(stats), int(decide)
 
@@ -92,7 +96,7 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, seconds: float):
+def cpu_baseline(inputs, seconds: float, rule: str = "standard"):
     import oracle
 
     inp = inputs[0]
@@ -101,7 +105,7 @@ def cpu_baseline(inputs, seconds: float):
     t0 = time.perf_counter()
     while True:
         oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=inp.draft_probs,
-                            onehot=inp.onehot)
+                            onehot=inp.onehot, rule=rule)
         calls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -118,6 +122,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="chain_bf16_mixed", choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated over the timed steps")
+    ap.add_argument("--rule", choices=["standard", "block"], default="standard",
+                    help="acceptance rule of the stochastic requests (block: block verification)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
@@ -163,6 +169,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     flags = {"auto": 0, "phased": sv.FLAG_PHASED, "fused": sv.FLAG_FUSED}[args.schedule]
+    block = args.rule == "block"
+    if block:
+        flags |= sv.FLAG_BLOCK
     calls = []
     for inp in inputs:
         calls.append(sv.PreparedChain(to_dev(inp.logits), to_dev(inp.draft_ids), to_dev(inp.temperature),
@@ -178,7 +187,7 @@ def main():
         torch.cuda.synchronize()
         if (c.out["status"] != 0).any():
             raise RuntimeError("a request reported a non-OK status on the benchmark inputs")
-        alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy()))
+        alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy(), block))
         if args.schedule != "fused":
             # the split phases must reproduce the plain call
             ref = {n: t.clone() for n, t in c.out.items()}
@@ -241,7 +250,7 @@ def main():
         kernel = "fused verify (fused_kernel)"
         kbytes = stats_bytes + decide_bytes
     achieved = kbytes.sum() / (first_ms.sum() * S * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, "k1_kernel" if split else "fused_kernel")
+    traffic = None if block else load_traffic(args.workload, "k1_kernel" if split else "fused_kernel")
     line = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
         "value": value,
@@ -256,7 +265,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOADS[args.workload],
+            "workload": WORKLOADS[args.workload] + (", block verification" if block else ""),
+            "rule": args.rule,
             "batch": int(inputs[0].batch),
             "k": int(inputs[0].max_draft),
             "vocab": int(inputs[0].vocab),
@@ -281,14 +291,15 @@ def main():
     }
     if split:
         line["roofline"]["other_kernel"] = {
-            "kernel": "decisions and sampling (k23_kernel)",
+            "kernel": ("residual masses, decisions and sampling (kr_kernel + k23_kernel)" if block
+                       else "decisions and sampling (k23_kernel)"),
             "algorithmic_bytes_per_launch": float(decide_bytes.mean()),
             "launch_us_mean": float(second_ms.mean() * 1e3),
             "achieved": float(decide_bytes.sum() / (second_ms.sum() * S * 1e-3) / 1e9),
         }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds, args.rule)
     print(json.dumps(line), flush=True)
 
 

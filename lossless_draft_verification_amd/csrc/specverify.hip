@@ -71,7 +71,13 @@ constexpr int kWaves = kWG / 64;
 #endif
 constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a K1 sub-chunk
 constexpr int kK1Depth = SV_K1_DEPTH;           // K1 sub-chunks in flight ahead of the one being folded
-constexpr int kKRWorkgroups = 256 * 8 * 2;      // block rule's residual-mass pass: workgroups it aims at
+#ifndef SV_KR_WORKGROUPS
+#define SV_KR_WORKGROUPS (256 * 7)
+#endif
+#ifndef SV_KR_UNROLL
+#define SV_KR_UNROLL 4
+#endif
+constexpr int kKRWorkgroups = SV_KR_WORKGROUPS;  // block rule's residual-mass pass: workgroups it aims at
 // K1 workgroups per call: an MI355X holds 256 CUs x 7 of them at once (71
 // VGPRs), so the stream is one round.
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
@@ -1823,16 +1829,41 @@ __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
 // decision step).  One workgroup per (request, row i, item); an item is a
 // run of whole 2048-id chunks.  Each workgroup folds the request's row
 // statistics of rows 0..i and its gathered draft values to get w_i, then
-// streams its ids of target row i and draft row i.  A term is evaluated in
-// fp64 exactly as the definition reads (w (exp((l - m)/T) / S) - q) unless an
-// fp32 screen shows it is not positive: w S^-1 2^((l - m) log2(e)/T) in fp32
-// is within 2^-14 relative for every exponent above -128 (and below 2^-126
-// beneath), so a value below q (1 - 2^-12) cannot be positive, and a term it
-// could hide is under 2^-126.  The fp64 partial sums are reduced in a fixed
+// streams its ids of target row i and draft row i.  Every term is evaluated
+// in fp64 as 2^((l - m) log2(e)/T) (w/S) - q, within about 1e-11 relative
+// of the definition's w exp((l - m)/T)/S - q (an fp32 screen that skipped
+// the clearly negative terms cost more than it saved: its branch diverges
+// within a wave).  The fp64 partial sums are reduced in a fixed
 // order: the decision step adds the items' partials in item order.
-template <bool BF16>
+//
+// 2^t for t <= 0 in fp64 without a division, a library call or a branch:
+// t = n + f with n = rint(t), |f| <= 1/2, and e^(f ln 2) by its Taylor
+// polynomial of degree 9 (remainder below 1e-11 relative for
+// |f ln 2| <= 0.347), scaled by 2^n exactly.  Below 2^-1022 (t = -inf
+// included) it returns 0.
+__device__ __forceinline__ double exp2_f64_nonpos(double t) {
+  const double tc = fmax(t, -1022.0);
+  const double n = __builtin_rint(tc);
+  const double x = (tc - n) * 0.69314718055994530942;
+  double p = 2.7557319223985888e-06;                // 1/9!
+  p = __builtin_fma(p, x, 2.4801587301587302e-05);  // 1/8!
+  p = __builtin_fma(p, x, 1.9841269841269841e-04);  // 1/7!
+  p = __builtin_fma(p, x, 1.3888888888888889e-03);  // 1/6!
+  p = __builtin_fma(p, x, 8.3333333333333333e-03);  // 1/5!
+  p = __builtin_fma(p, x, 4.1666666666666667e-02);  // 1/4!
+  p = __builtin_fma(p, x, 1.6666666666666667e-01);  // 1/3!
+  p = __builtin_fma(p, x, 0.5);
+  p = __builtin_fma(p, x, 1.0);
+  p = __builtin_fma(p, x, 1.0);
+  const double r = __builtin_ldexp(p, (int)n);
+  return t > -1022.0 ? r : 0.0;
+}
+
+// Target logits and q of ids y0..y0+3.  VEC: the rows are 16-byte aligned
+// and V is a multiple of 4, so the group is loaded whole, unconditionally.
+template <bool BF16, bool VEC>
 __device__ __forceinline__ void kr_load4(const Params& P, int64_t lrow, int64_t qrow, int y0, float* l, float* q) {
-  if (y0 + 4 <= P.V && P.aligned && P.q_aligned) {
+  if (VEC || (y0 + 4 <= P.V && P.aligned && P.q_aligned)) {
     if (BF16) {
       const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)P.logits + lrow + y0));
       l[0] = __uint_as_float(w.x << 16);
@@ -1862,7 +1893,38 @@ __device__ __forceinline__ void kr_load4(const Params& P, int64_t lrow, int64_t 
   }
 }
 
-constexpr int kKRUnroll = 4;  // groups of 4 ids whose loads a thread issues together
+constexpr int kKRUnroll = SV_KR_UNROLL;  // groups of 4 ids whose loads a thread issues together
+
+// The thread's share of sum_y max(2^((l - m) cd) wS - q, 0) over ids
+// [y_lo, y_hi): kKRUnroll groups of 4 ids per step, all loads first.  Ids
+// past y_hi load the range's first group again and count as l = -inf,
+// q = 0 (a zero term), so with VEC every load is unconditional.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ double kr_stream(const Params& P, int64_t lrow, int64_t qrow, int y_lo, int y_hi,
+                                            double m, double cd, double wS) {
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+#pragma unroll 1
+  for (int base = y_lo; base < y_hi; base += 4 * kWG * kKRUnroll) {
+    float l[kKRUnroll][4], q[kKRUnroll][4];
+    bool in[kKRUnroll];
+#pragma unroll
+    for (int g = 0; g < kKRUnroll; ++g) {
+      const int y0 = base + 4 * (g * kWG + tid);
+      in[g] = y0 < y_hi;
+      kr_load4<BF16, VEC>(P, lrow, qrow, in[g] ? y0 : y_lo, l[g], q[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < kKRUnroll; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double ex = exp2_f64_nonpos(((double)l[g][e] - m) * cd);
+        const double term = __builtin_fma(ex, wS, -(double)q[g][e]);
+        acc += in[g] ? fmax(term, 0.0) : 0.0;
+      }
+  }
+  return acc;
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
@@ -1903,40 +1965,16 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
   }
   const double w = sm.u[0], S = sm.rs[i];
   const float m = sm.rm[i];
-  const float cf = (float)(1.4426950408889634074 / T);
-  const float ws = (float)(w / S);
+  const double wS = w / S, cd = 1.4426950408889634074 / T;
   const int c_lo = (int)((int64_t)c * P.C3 / P.CHr), c_hi = (int)((int64_t)(c + 1) * P.C3 / P.CHr);
   const int y_lo = c_lo * kK3Chunk, y_hi = min(c_hi * kK3Chunk, P.V);
   const int64_t lrow = ((int64_t)b * P.R + i) * P.lstride;
   const int64_t qrow = ((int64_t)b * P.k + i) * P.qstride;
-  double acc = 0.0;
-#pragma unroll 1
-  for (int y = y_lo + 4 * tid; y < y_hi; y += 4 * kWG * kKRUnroll) {
-    float l[kKRUnroll][4], q[kKRUnroll][4];
-#pragma unroll
-    for (int g = 0; g < kKRUnroll; ++g) {
-      const int y0 = y + 4 * kWG * g;
-      if (y0 < y_hi) {
-        kr_load4<BF16>(P, lrow, qrow, y0, l[g], q[g]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l[g][e] = -INFINITY;
-          q[g][e] = 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < kKRUnroll; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = __builtin_amdgcn_exp2f((l[g][e] - m) * cf) * ws;
-        if (!(v * (1.f + 0x1p-12f) < q[g][e])) {
-          const double term = w * (exp(((double)l[g][e] - (double)m) / T) / S) - (double)q[g][e];
-          if (term > 0.0) acc += term;
-        }
-      }
-  }
+  double acc;
+  if (P.aligned && P.q_aligned && (P.V & 3) == 0)
+    acc = kr_stream<BF16, true>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS);
+  else
+    acc = kr_stream<BF16, false>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS);
   acc = block_sum_d(acc, sm);
   if (tid == 0) *out = acc;
 }
