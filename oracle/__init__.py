@@ -29,7 +29,7 @@ def build(force: bool = True) -> str:
     """Compile svo.c into libsvo.so with gcc (-O2, no fast-math)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra",
                                "-Wno-unused-parameter", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -48,6 +48,12 @@ class _ChainArgs(ctypes.Structure):
                 ("draft_ids", _P), ("temperature", _P), ("seed", _P),
                 ("accept_len", _P), ("tokens", _P), ("req_status", _P),
                 ("p_draft", _P), ("min_margin", _P), ("n_decisions", _P), ("rule", _I32)]
+
+
+class _PlanArgs(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("max_steps", _I32), ("confidence", _P), ("num_steps", _P),
+                ("max_budget", _I32), ("cost", _P), ("base_tokens", _D),
+                ("budget", _P), ("draft_len", _P), ("rate", _P), ("margin", _P)]
 
 
 class _TreeArgs(ctypes.Structure):
@@ -86,6 +92,8 @@ def lib():
         L.svo_verify_chain.restype = None
         L.svo_verify_tree.argtypes = [ctypes.POINTER(_TreeArgs)]
         L.svo_verify_tree.restype = None
+        L.svo_plan_budget.argtypes = [ctypes.POINTER(_PlanArgs)]
+        L.svo_plan_budget.restype = None
         _lib = L
     return _lib
 
@@ -215,3 +223,24 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, threshold_acc=1
                   float(threshold_acc), float(threshold_single))
     lib().svo_verify_tree(ctypes.byref(a))
     return out
+
+
+def plan_budget(confidence, cost, base_tokens, num_steps=None):
+    """Survival top-k draft budget.
+
+    confidence: [bs, K] float32; cost: [max_budget + 1] float64 (the step cost
+    when B draft positions are verified); base_tokens: tokens a step yields
+    with none; num_steps: [bs] int32 drafted positions per request or None.
+    Returns a dict with budget, draft_len [bs], rate, margin.
+    """
+    c = np.ascontiguousarray(np.asarray(confidence, dtype=np.float32))
+    bs, K = c.shape
+    cost = np.ascontiguousarray(np.asarray(cost, dtype=np.float64).reshape(-1))
+    ns = None if num_steps is None else np.ascontiguousarray(np.asarray(num_steps, dtype=np.int32).reshape(bs))
+    out = dict(budget=np.zeros(1, np.int32), draft_len=np.zeros(bs, np.int32), rate=np.zeros(1, np.float64),
+               margin=np.zeros(1, np.float64))
+    a = _PlanArgs(bs, K, _ptr(c), _ptr(ns), len(cost) - 1, _ptr(cost), float(base_tokens),
+                  _ptr(out["budget"]), _ptr(out["draft_len"]), _ptr(out["rate"]), _ptr(out["margin"]))
+    lib().svo_plan_budget(ctypes.byref(a))
+    return dict(budget=int(out["budget"][0]), draft_len=out["draft_len"], rate=float(out["rate"][0]),
+                margin=float(out["margin"][0]))

@@ -20,6 +20,14 @@
  *        and STANDALONE"): the "block" rule's acceptance function.
  *  [BLK] Sun et al. 2024, block verification (arXiv 2403.10444), which the
  *        page cites for the prefix weight's clipped recursion.
+ *  [NEW] "New approaches to speculative decoding: block drafts, load-aware
+ *        verification and PD disaggregation", anrans.github.io (AI infra
+ *        handbooks): section "Deciding how much to verify by load" (the
+ *        adaptive-verification planner and its worked example) and "The
+ *        higher the load, the smaller K should be" (its cost model); with
+ *        [ZOO] "The finer loop: DSpark's confidence budget" (the global
+ *        top-k of survival scores, the earlier-position-first tie rule and
+ *        the argmax of expected tokens over the cost table).
  *  [PHX] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *        1, 2, 3", SC'11 (Philox4x32-10), which the pages do not fix.
  *
@@ -598,4 +606,78 @@ void svo_verify_tree(const svo_tree_args* a) {
   for (int32_t b = 0; b < a->batch; ++b) tree_one(a, b, w, prow);
   free(w);
   free(prow);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Survival top-k draft budget ([NEW] "Deciding how much to verify by load";
+ * [ZOO] "The finer loop: DSpark's confidence budget").  Each (request,
+ * position) slot is scored by its survival probability, the running product
+ * of the request's confidences up to that position (fp32, as the pages'
+ * cumprod of fp32 confidences); the slots are ranked by score, higher first,
+ * ties to the earlier position and then to the smaller request index (the
+ * deterministic tie rule [ZOO] asks for, which makes every request's
+ * admitted slots a prefix).  Admitting the top B slots yields
+ * base + (sum of their scores) expected tokens at cost[B]; the budget is the
+ * B in 0..min(max_budget, slots) that maximises their ratio (the first
+ * maximum).  Confidences are clamped to [0, 1] (NaN counts as 0), so scores
+ * never increase along a request. */
+typedef struct {
+  float s;
+  int32_t j, b;
+} plan_slot;
+
+static int plan_order(const void* x, const void* y) {
+  const plan_slot* p = (const plan_slot*)x;
+  const plan_slot* q = (const plan_slot*)y;
+  if (p->s != q->s) return p->s > q->s ? -1 : 1;
+  if (p->j != q->j) return p->j < q->j ? -1 : 1;
+  return p->b < q->b ? -1 : (p->b > q->b ? 1 : 0);
+}
+
+void svo_plan_budget(const svo_plan_args* a) {
+  const int32_t bs = a->batch, K = a->max_steps;
+  plan_slot* slot = (plan_slot*)malloc(sizeof(plan_slot) * (size_t)(bs * K > 0 ? bs * K : 1));
+  int32_t n = 0;
+  for (int32_t b = 0; b < bs; ++b) {
+    int32_t len = a->num_steps ? a->num_steps[b] : K;
+    if (len < 0) len = 0;
+    if (len > K) len = K;
+    float s = 1.0f;
+    for (int32_t j = 0; j < len; ++j) {
+      float c = a->confidence[(int64_t)b * K + j];
+      if (!(c > 0.0f)) c = 0.0f; /* NaN and negatives */
+      if (c > 1.0f) c = 1.0f;
+      s = s * c;
+      slot[n].s = s;
+      slot[n].j = j;
+      slot[n].b = b;
+      ++n;
+    }
+  }
+  qsort(slot, (size_t)n, sizeof(plan_slot), plan_order);
+  const int32_t bmax = a->max_budget < n ? a->max_budget : n;
+  double* rate = (double*)malloc(sizeof(double) * (size_t)(bmax + 1));
+  double gain = 0.0, best = -INFINITY;
+  int32_t bstar = 0;
+  for (int32_t B = 0; B <= bmax; ++B) {
+    if (B > 0) gain += (double)slot[B - 1].s;
+    rate[B] = (a->base_tokens + gain) / a->cost[B];
+    if (rate[B] > best) {
+      best = rate[B];
+      bstar = B;
+    }
+  }
+  double gap = INFINITY;
+  for (int32_t B = 0; B <= bmax; ++B)
+    if (B != bstar && rate[B] != best && best > 0.0) {
+      double g = (best - rate[B]) / best;
+      if (g < gap) gap = g;
+    }
+  for (int32_t b = 0; b < bs; ++b) a->draft_len[b] = 0;
+  for (int32_t r = 0; r < bstar; ++r) a->draft_len[slot[r].b] += 1;
+  *a->budget = bstar;
+  *a->rate = best;
+  if (a->margin) *a->margin = gap;
+  free(rate);
+  free(slot);
 }

@@ -109,6 +109,22 @@ typedef struct {
 void svo_verify_chain(const svo_chain_args* a);
 void svo_verify_tree(const svo_tree_args* a);
 
+/* Survival top-k draft budget: which draft positions of a batch to verify. */
+typedef struct {
+  int32_t batch, max_steps;                 /* bs, K */
+  const float* confidence;                  /* [bs][K] per-position confidences */
+  const int32_t* num_steps;                 /* [bs] drafted positions (clamped to [0, K]); NULL: K each */
+  int32_t max_budget;                       /* cost table covers budgets 0..max_budget */
+  const double* cost;                       /* [max_budget + 1] step cost when B positions are verified */
+  double base_tokens;                       /* tokens a step yields with no draft position verified */
+  int32_t* budget;                          /* [1] out: the chosen budget B* */
+  int32_t* draft_len;                       /* [bs] out: admitted positions of each request (a prefix) */
+  double* rate;                             /* [1] out: (base + gain(B*)) / cost[B*] */
+  double* margin;                           /* [1] out, may be NULL: relative gap to the next distinct rate */
+} svo_plan_args;
+
+void svo_plan_budget(const svo_plan_args* a);
+
 #ifdef __cplusplus
 }
 #endif
