@@ -115,6 +115,39 @@ def cpu_baseline(inputs, seconds: float, rule: str = "standard"):
                       f"{el:.1f} s"}
 
 
+def bench_plan(args, sv, torch, dev):
+    """Latency of one survival top-k plan (a single-workgroup kernel): the
+    page's adaptive-verification shape (512 requests x 7 positions, half
+    with accurate drafts) and the largest supported one (1024 x 8)."""
+    rng = np.random.default_rng(11)
+    lines = []
+    for bs, K in ((512, 7), (1024, 8)):
+        level = np.where(np.arange(bs)[:, None] < bs // 2, 0.9, 0.55)
+        conf = np.minimum(level * (0.9 + 0.2 * rng.random((bs, K))), 0.99).astype(np.float32)
+        n = bs * K
+        # the pages' step-cost model: weights read once, compute-bound beyond
+        step = np.maximum(16e9 / (3.35e12 * 0.8), (bs + np.arange(n + 1)) * 16e9 / (989e12 * 0.5))
+        cost = torch.from_numpy(0.25e-3 + step).to(dev)
+        c = torch.from_numpy(conf).to(dev)
+        for _ in range(args.warmup):
+            sv.plan_budget(c, cost, float(bs))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream(dev)
+        e0.record(stream)
+        for _ in range(args.steps):
+            out = sv.plan_budget(c, cost, float(bs))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        lines.append({"batch": bs, "K": K, "slots": n, "us_per_plan": us, "budget": int(out["budget"].item())})
+    print(json.dumps({"metric": "survival top-k draft budget latency, 1 MI355X", "value": lines[0]["us_per_plan"],
+                      "unit": "us/plan", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": False, "data": "synthetic",
+                      "config": {"workload": "plan 512 requests x 7 positions (and 1024 x 8)", "cases": lines},
+                      "roofline": {"bound": "latency", "note": "one workgroup; a few thousand slots"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +161,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
                     help="library schedule (auto: the library's default for the shape)")
+    ap.add_argument("--plan", action="store_true",
+                    help="time the survival top-k draft budget (sv_plan_budget) instead and print its line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB a few times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -155,6 +190,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.plan:
+        bench_plan(args, sv, torch, dev)
+        return
     gen = getattr(workloads, args.workload)
     print(f"[bench] generating {args.sets} input sets of {args.workload}", file=sys.stderr, flush=True)
     inputs = [gen(s) for s in range(args.sets)]

@@ -207,6 +207,43 @@ sv_status sv_row_stats(int32_t rows, int32_t vocab, sv_dtype logits_dtype, const
 const char* sv_status_string(sv_status status);
 int32_t sv_abi_version(void);
 
+/* Survival top-k draft budget: which draft positions of a batch to verify
+ * this step (page "New approaches to speculative decoding: block drafts,
+ * load-aware verification and PD disaggregation", section "Deciding how
+ * much to verify by load", with the cost model of its section "The higher
+ * the load, the smaller K should be"; page "The speculative decoding zoo",
+ * section "The finer loop: DSpark's confidence budget").
+ *
+ * Slot (b, j) is scored by its survival probability: the running fp32
+ * product of confidence[b][0..j], each confidence clamped to [0, 1] (NaN
+ * counts as 0), for j < num_steps[b] (clamped to [0, K]; NULL: K).  Slots
+ * are ranked by score, higher first; ties go to the earlier position, then
+ * to the smaller request index, so every request's admitted slots form a
+ * prefix.  Admitting the top B slots is worth
+ *   rate(B) = (base_tokens + sum of their scores) / cost[B];
+ * the budget B* is the first B in 0..min(max_budget, slots) with the largest
+ * rate (sums in fp64; a NaN rate never wins; none that beats -inf: B* = 0).
+ * Outputs: budget[0] = B*, draft_len[b] = admitted positions of request b
+ * (pad its draft ids after that with -1 for sv_verify_chain), rate[0] =
+ * rate(B*).  One workgroup does the whole plan; no workspace.  bs * K must
+ * not exceed SV_PLAN_MAX_SLOTS (else SV_ERR_UNSUPPORTED). */
+#define SV_PLAN_MAX_SLOTS 8192
+
+typedef struct {
+  int32_t batch;              /* bs >= 1 */
+  int32_t max_steps;          /* K, 1..64: confidence columns per request */
+  const float* confidence;    /* [bs][K] */
+  const int32_t* num_steps;   /* [bs] drafted positions per request, or NULL */
+  int32_t max_budget;         /* >= 0: the cost table covers budgets 0..max_budget */
+  const double* cost;         /* [max_budget + 1] cost of a step that verifies B draft positions */
+  double base_tokens;         /* tokens a step yields with no draft position verified */
+  int32_t* budget;            /* [1] out: B* */
+  int32_t* draft_len;         /* [bs] out */
+  double* rate;               /* [1] out, may be NULL */
+} sv_plan_desc;
+
+sv_status sv_plan_budget(const sv_plan_desc* desc /* [host] */, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

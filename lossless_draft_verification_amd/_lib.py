@@ -29,6 +29,7 @@ REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE, REQ_
 FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED, FLAG_STATS_ONLY, FLAG_DECIDE_ONLY, FLAG_BLOCK = 1, 2, 4, 8, 16, 32
 
 MAX_BATCH, MAX_DRAFT, MAX_NODES, MAX_VOCAB = 65536, 63, 64, 1 << 24
+PLAN_MAX_SLOTS = 8192
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -50,6 +51,12 @@ class TreeDesc(ctypes.Structure):
                 ("logits", _P), ("logits_row_stride", _I64), ("node_tokens", _P), ("parent", _P),
                 ("temperature", _P), ("seed", _P), ("accept_len", _P), ("accept_path", _P), ("tokens", _P),
                 ("req_status", _P), ("flags", _U32)]
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("max_steps", _I32), ("confidence", _P), ("num_steps", _P),
+                ("max_budget", _I32), ("cost", _P), ("base_tokens", ctypes.c_double),
+                ("budget", _P), ("draft_len", _P), ("rate", _P)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -87,6 +94,8 @@ def lib():
                 L.sv_verify_chain.argtypes = [ctypes.POINTER(ChainDesc), _P, _SZ, _P]
                 L.sv_verify_tree.restype = ctypes.c_int
                 L.sv_verify_tree.argtypes = [ctypes.POINTER(TreeDesc), _P, _SZ, _P]
+                L.sv_plan_budget.restype = ctypes.c_int
+                L.sv_plan_budget.argtypes = [ctypes.POINTER(PlanDesc), _P]
                 L.sv_row_stats.restype = ctypes.c_int
                 L.sv_row_stats.argtypes = [_I32, _I32, ctypes.c_int, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
                 _lib = L
@@ -307,6 +316,38 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, wor
                               _stream(device))
     if st != OK:
         raise SpecVerifyError(st, "sv_verify_tree")
+    return out
+
+
+def plan_budget(confidence, cost, base_tokens, num_steps=None):
+    """Survival top-k draft budget on the current stream (asynchronous).
+
+    confidence [bs, K] float32; cost [max_budget + 1] float64 (step cost when
+    B draft positions are verified); base_tokens: tokens a step yields with
+    none; num_steps [bs] int32 or None.  Returns device tensors: budget [1]
+    int32, draft_len [bs] int32, rate [1] float64.
+    """
+    if confidence.dim() != 2 or confidence.dtype != torch.float32:
+        raise ValueError("confidence must be a [batch, K] float32 tensor")
+    if cost.dim() != 1 or cost.dtype != torch.float64 or cost.numel() < 1:
+        raise ValueError("cost must be a non-empty 1-D float64 tensor")
+    dev = confidence.device
+    conf = confidence.contiguous()
+    c = cost.to(dev).contiguous()
+    bs, K = conf.shape
+    ns = None
+    if num_steps is not None:
+        ns = num_steps.to(device=dev, dtype=torch.int32).contiguous()
+        if ns.numel() != bs:
+            raise ValueError("need one num_steps entry per request")
+    out = dict(budget=torch.empty(1, dtype=torch.int32, device=dev),
+               draft_len=torch.empty(bs, dtype=torch.int32, device=dev),
+               rate=torch.empty(1, dtype=torch.float64, device=dev))
+    d = PlanDesc(bs, K, conf.data_ptr(), ns.data_ptr() if ns is not None else None, c.numel() - 1, c.data_ptr(),
+                 float(base_tokens), out["budget"].data_ptr(), out["draft_len"].data_ptr(), out["rate"].data_ptr())
+    st = lib().sv_plan_budget(ctypes.byref(d), _stream(dev))
+    if st != OK:
+        raise SpecVerifyError(st, "sv_plan_budget")
     return out
 
 

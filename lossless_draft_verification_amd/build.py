@@ -8,6 +8,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "specverify.hip")
+SRCS = [SRC, os.path.join(PKG, "csrc", "planner.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 
@@ -28,7 +29,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INC}", SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INC}", *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

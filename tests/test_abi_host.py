@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for expected in ("sv_verify_chain", "sv_verify_tree", "sv_row_stats", "sv_chain_workspace_bytes",
                      "sv_tree_workspace_bytes", "sv_row_stats_workspace_bytes", "sv_workspace_init",
-                     "sv_status_string", "sv_abi_version"):
+                     "sv_status_string", "sv_abi_version", "sv_plan_budget"):
         assert expected in names
 
 
@@ -167,3 +167,21 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "svo_" not in text and "oracle/" not in text, f
+
+
+def _plan_desc(**kw):
+    fake = 0x100000
+    d = dict(batch=4, max_steps=7, confidence=fake, num_steps=None, max_budget=28, cost=fake, base_tokens=4.0,
+             budget=fake, draft_len=fake, rate=None)
+    d.update(kw)
+    return _lib.PlanDesc(**d)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 1), ("max_steps", 0, 1), ("max_steps", 65, 1), ("max_budget", -1, 1), ("confidence", None, 1),
+    ("cost", None, 1), ("budget", None, 1), ("draft_len", None, 1), ("batch", 1171, 3),
+])
+def test_plan_argument_validation(field, value, code):
+    d = _plan_desc(**{field: value})
+    assert sv.lib().sv_plan_budget(ctypes.byref(d), None) == code
+    assert sv.lib().sv_plan_budget(None, None) == 1
