@@ -56,6 +56,12 @@ class _PlanArgs(ctypes.Structure):
                 ("budget", _P), ("draft_len", _P), ("rate", _P), ("margin", _P)]
 
 
+class _CompactArgs(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("num_nodes", _I32), ("accept_len", _P), ("accept_path", _P), ("node_slot", _P),
+                ("kv", _P), ("num_layers", _I32), ("num_slots", _I64), ("slot_stride", _I64),
+                ("layer_stride", _I64), ("row_bytes", _I64), ("moved", _P)]
+
+
 class _TreeArgs(ctypes.Structure):
     _fields_ = [("batch", _I32), ("num_nodes", _I32), ("vocab", _I32),
                 ("logits_dtype", _I32), ("logits", _P), ("logits_row_stride", _I64),
@@ -94,6 +100,8 @@ def lib():
         L.svo_verify_tree.restype = None
         L.svo_plan_budget.argtypes = [ctypes.POINTER(_PlanArgs)]
         L.svo_plan_budget.restype = None
+        L.svo_compact_kv.argtypes = [ctypes.POINTER(_CompactArgs)]
+        L.svo_compact_kv.restype = None
         _lib = L
     return _lib
 
@@ -244,3 +252,23 @@ def plan_budget(confidence, cost, base_tokens, num_steps=None):
     lib().svo_plan_budget(ctypes.byref(a))
     return dict(budget=int(out["budget"][0]), draft_len=out["draft_len"], rate=float(out["rate"][0]),
                 margin=float(out["margin"][0]))
+
+
+def compact_kv(kv, accept_len, accept_path, node_slot):
+    """Accepted-path KV compaction in place on a host pool.
+
+    kv: uint8/any array [layers, slots, row] (contiguous, modified in place);
+    accept_len [bs] int32; accept_path [bs, N] int32; node_slot [bs, N] int64.
+    Returns moved [bs] int32 (rows moved per layer, -1: request skipped).
+    """
+    assert kv.flags.c_contiguous and kv.ndim == 3
+    L, S = kv.shape[0], kv.shape[1]
+    row = kv.shape[2] * kv.itemsize
+    al = np.ascontiguousarray(np.asarray(accept_len, np.int32))
+    ap = np.ascontiguousarray(np.asarray(accept_path, np.int32))
+    ns = np.ascontiguousarray(np.asarray(node_slot, np.int64))
+    bs, N = ap.shape
+    moved = np.zeros(bs, np.int32)
+    a = _CompactArgs(bs, N, _ptr(al), _ptr(ap), _ptr(ns), kv.ctypes.data, L, S, row, S * row, row, _ptr(moved))
+    lib().svo_compact_kv(ctypes.byref(a))
+    return moved

@@ -28,6 +28,14 @@
  *        [ZOO] "The finer loop: DSpark's confidence budget" (the global
  *        top-k of survival scores, the earlier-position-first tie rule and
  *        the argmax of expected tokens over the cost table).
+ *  [KV]  "投机解码" (Speculative decoding), rustineverything.app, section
+ *        "与调度、KV 的交互" (interaction with scheduling and KV), sub-section
+ *        "SGLang：按最坏情况预留，结束时归还": with topk > 1 the accepted path
+ *        is not contiguous in the tree and its KV is moved to contiguous
+ *        positions after verification; and "Draft sources: draft models,
+ *        n-gram, suffix decoding" (mlinterviewnotes.com, section 6.3),
+ *        "SGLang's suffix automaton, in tree": a tree's accepted path is
+ *        scattered, so its KV is moved into the target cache.
  *  [PHX] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *        1, 2, 3", SC'11 (Philox4x32-10), which the pages do not fix.
  *
@@ -680,4 +688,45 @@ void svo_plan_budget(const svo_plan_args* a) {
   if (a->margin) *a->margin = gap;
   free(rate);
   free(slot);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Accepted-path KV compaction ([KV]).  After tree verification the accepted
+ * nodes p_1..p_a (from the root down; node 0, the root, is already in
+ * place) hold their KV rows wherever the tree put them.  Their rows move,
+ * in path order, to the slots of nodes 1..a, so the accepted tokens follow
+ * the committed prefix contiguously: for i = 1..a, every layer's row at
+ * node_slot[p_i] is copied to node_slot[i] (a no-op when p_i = i).  Node
+ * ids grow along a path, so p_i >= i and a copy never reads a slot that an
+ * earlier copy of the same request wrote; doing them in order is the
+ * definition.  A request whose accept_len or path lies outside the tree,
+ * or whose slots lie outside the pool, is left untouched (moved = -1). */
+void svo_compact_kv(const svo_compact_args* a) {
+  const int32_t N = a->num_nodes;
+  for (int32_t b = 0; b < a->batch; ++b) {
+    const int32_t len = a->accept_len[b];
+    const int32_t* path = a->accept_path + (int64_t)b * N;
+    const int64_t* slot = a->node_slot + (int64_t)b * N;
+    int ok = len >= 0 && len < N;
+    for (int32_t i = 0; ok && i < len; ++i) {
+      const int32_t p = path[i];
+      if (p < i + 1 || p >= N || (i > 0 && p <= path[i - 1])) ok = 0;
+      else if (slot[p] < 0 || slot[p] >= a->num_slots || slot[i + 1] < 0 || slot[i + 1] >= a->num_slots) ok = 0;
+    }
+    if (!ok) {
+      if (a->moved) a->moved[b] = -1;
+      continue;
+    }
+    int32_t moved = 0;
+    for (int32_t i = 0; i < len; ++i) {
+      const int32_t p = path[i];
+      if (p == i + 1) continue;
+      ++moved;
+      for (int32_t l = 0; l < a->num_layers; ++l) {
+        uint8_t* base = a->kv + (int64_t)l * a->layer_stride;
+        memmove(base + slot[i + 1] * a->slot_stride, base + slot[p] * a->slot_stride, (size_t)a->row_bytes);
+      }
+    }
+    if (a->moved) a->moved[b] = moved;
+  }
 }

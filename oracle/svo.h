@@ -125,6 +125,20 @@ typedef struct {
 
 void svo_plan_budget(const svo_plan_args* a);
 
+/* Accepted-path KV compaction after tree verification. */
+typedef struct {
+  int32_t batch, num_nodes;                 /* bs, N */
+  const int32_t* accept_len;                /* [bs] */
+  const int32_t* accept_path;               /* [bs][N] accepted node ids from the root down */
+  const int64_t* node_slot;                 /* [bs][N] KV slot of each node */
+  uint8_t* kv;                              /* layer l, slot s at kv + l*layer_stride + s*slot_stride */
+  int32_t num_layers;
+  int64_t num_slots, slot_stride, layer_stride, row_bytes;
+  int32_t* moved;                           /* [bs] out, may be NULL: rows moved per layer (-1: request skipped) */
+} svo_compact_args;
+
+void svo_compact_kv(const svo_compact_args* a);
+
 #ifdef __cplusplus
 }
 #endif
