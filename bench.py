@@ -115,6 +115,84 @@ def cpu_baseline(inputs, seconds: float, rule: str = "standard"):
                       f"{el:.1f} s"}
 
 
+def bench_compact(args, sv, torch, dev, workloads):
+    """Accepted-path KV compaction on a Llama-3-8B-shaped pool: 32 layers,
+    one 4 KB row per token and layer (8 KV heads x 128 x K and V, bf16), the
+    nodes' slots a random permutation.  Two cases of 48 requests x 8 nodes:
+    the accepted paths of the GPU tree verification of the tree workload's
+    input sets (few rows move: most accepted nodes are already in place),
+    and every request accepting 4 nodes off the first-child chain (path
+    2, 4, 6, 7: 4 rows move).  Descriptors are built once, so the timed
+    loop is launches only.  Algorithmic bytes: every moved row read once and
+    written once; the roofline line is the second case."""
+    import ctypes
+
+    from lossless_draft_verification_amd import _lib
+
+    rng = np.random.default_rng(23)
+    layers, row = 32, 4096
+    bs, N = 48, 8
+    kv = torch.zeros((layers, bs * N, row), dtype=torch.uint8, device=dev)
+    stream = _lib._stream(dev)
+
+    def prepared(al, ap, sl):
+        moved = torch.empty(bs, dtype=torch.int32, device=dev)
+        keep = (al, ap, sl, moved)
+        d = _lib.CompactDesc(bs, N, al.data_ptr(), ap.data_ptr(), sl.data_ptr(), kv.data_ptr(), layers, bs * N,
+                             row, bs * N * row, row, moved.data_ptr())
+        return d, keep
+
+    cases = {}
+    verified = []
+    for s_i in range(args.sets):
+        t = workloads.tree_fp32(s_i)
+        out = sv.verify_tree(torch.from_numpy(t.logits).to(dev), torch.from_numpy(t.node_tokens).to(dev),
+                             torch.from_numpy(t.parent).to(dev), torch.from_numpy(t.temperature).to(dev),
+                             torch.from_numpy(t.seeds.view(np.int64)).to(dev))
+        sl = torch.from_numpy(rng.permutation(bs * N).reshape(bs, N).astype(np.int64)).to(dev)
+        verified.append(prepared(out["accept_len"].contiguous(), out["accept_path"].contiguous(), sl))
+    cases["verified"] = verified
+    moved_all = []
+    for s_i in range(args.sets):
+        al = torch.full((bs,), 4, dtype=torch.int32, device=dev)
+        ap = torch.tensor([[2, 4, 6, 7, -1, -1, -1, -1]] * bs, dtype=torch.int32, device=dev)
+        sl = torch.from_numpy(rng.permutation(bs * N).reshape(bs, N).astype(np.int64)).to(dev)
+        moved_all.append(prepared(al, ap, sl))
+    cases["all_moved"] = moved_all
+    L = _lib.lib()
+    res = {}
+    for name, preps in cases.items():
+        rows = []
+        for d, keep in preps:
+            assert L.sv_compact_kv(ctypes.byref(d), stream) == 0
+            torch.cuda.synchronize()
+            rows.append(int(keep[3].clamp(min=0).sum().item()))
+        for i in range(args.warmup):
+            L.sv_compact_kv(ctypes.byref(preps[i % len(preps)][0]), stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = torch.cuda.current_stream(dev)
+        e0.record(ts)
+        for i in range(args.steps):
+            L.sv_compact_kv(ctypes.byref(preps[i % len(preps)][0]), stream)
+        e1.record(ts)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        alg = float(np.mean([rows[i % len(preps)] for i in range(args.steps)]) * layers * row * 2)
+        res[name] = {"us_per_call": us, "moved_rows_per_layer": rows, "algorithmic_bytes": alg,
+                     "gb_per_s": alg / (us * 1e-6) / 1e9}
+    r = res["all_moved"]
+    print(json.dumps({"metric": "accepted-path KV compaction, 1 MI355X", "value": r["us_per_call"], "unit": "us/call",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+                      "data": "synthetic",
+                      "config": {"workload": "KV compaction, 48 requests x 8 nodes, 32 layers x 4 KB rows",
+                                 "cases": res},
+                      "roofline": {"bound": "hbm", "achieved": r["gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": r["gb_per_s"] / HBM_PEAK_GBS, "traffic": None, "kernel": "compact_kernel",
+                                   "algorithmic_bytes_per_launch": r["algorithmic_bytes"],
+                                   "launch_us_mean": r["us_per_call"]}}), flush=True)
+
+
 def bench_plan(args, sv, torch, dev):
     """Latency of one survival top-k plan (a single-workgroup kernel): the
     page's adaptive-verification shape (512 requests x 7 positions, half
@@ -161,6 +239,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
                     help="library schedule (auto: the library's default for the shape)")
+    ap.add_argument("--compact", action="store_true",
+                    help="time accepted-path KV compaction (sv_compact_kv) after tree verification instead")
     ap.add_argument("--plan", action="store_true",
                     help="time the survival top-k draft budget (sv_plan_budget) instead and print its line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -192,6 +272,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.plan:
         bench_plan(args, sv, torch, dev)
+        return
+    if args.compact:
+        bench_compact(args, sv, torch, dev, workloads)
         return
     gen = getattr(workloads, args.workload)
     print(f"[bench] generating {args.sets} input sets of {args.workload}", file=sys.stderr, flush=True)

@@ -244,6 +244,41 @@ typedef struct {
 
 sv_status sv_plan_budget(const sv_plan_desc* desc /* [host] */, void* stream);
 
+/* Accepted-path KV compaction after tree verification (page "投机解码", section
+ * "与调度、KV 的交互", sub-section "SGLang：按最坏情况预留，结束时归还"; page "Draft
+ * sources: draft models, n-gram, suffix decoding", section "SGLang's suffix
+ * automaton, in tree"): a tree's accepted path is scattered over the tree's
+ * KV slots and is moved so that the accepted tokens follow the committed
+ * prefix contiguously.
+ *
+ * For each request b with accepted nodes p_1..p_a (accept_len and
+ * accept_path as sv_verify_tree writes them; node 0, the root, is already in
+ * place), for i = 1..a in order, every layer's row at slot node_slot[p_i] is
+ * copied to slot node_slot[i] (no copy when p_i = i).  Row l, s of the pool
+ * is the row_bytes at kv + l*layer_stride + s*slot_stride (bytes; all
+ * multiples of 16 and kv 16-byte aligned, else SV_ERR_UNSUPPORTED).  A
+ * request whose accept_len is outside [0, N), whose path does not rise from
+ * node 1 up inside the tree, or whose slots fall outside the pool is left
+ * untouched and reports moved = -1; otherwise moved[b] = the rows moved per
+ * layer.  Different requests must not share slots.  Device pointers except
+ * the descriptor. */
+typedef struct {
+  int32_t batch;              /* bs, 1..SV_MAX_BATCH */
+  int32_t num_nodes;          /* N, 1..SV_MAX_NODES */
+  const int32_t* accept_len;  /* [bs] */
+  const int32_t* accept_path; /* [bs][N] */
+  const int64_t* node_slot;   /* [bs][N] KV slot of each node's token */
+  void* kv;                   /* the pool, modified in place */
+  int32_t num_layers;         /* >= 1 */
+  int64_t num_slots;          /* slots per layer */
+  int64_t slot_stride;        /* bytes between slots, >= row_bytes */
+  int64_t layer_stride;       /* bytes between layers, >= num_slots * slot_stride when num_layers > 1 */
+  int64_t row_bytes;          /* bytes of one token's row in one layer */
+  int32_t* moved;             /* [bs] out, may be NULL */
+} sv_compact_desc;
+
+sv_status sv_compact_kv(const sv_compact_desc* desc /* [host] */, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

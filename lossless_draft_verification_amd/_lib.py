@@ -59,6 +59,12 @@ class PlanDesc(ctypes.Structure):
                 ("budget", _P), ("draft_len", _P), ("rate", _P)]
 
 
+class CompactDesc(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("num_nodes", _I32), ("accept_len", _P), ("accept_path", _P), ("node_slot", _P),
+                ("kv", _P), ("num_layers", _I32), ("num_slots", _I64), ("slot_stride", _I64),
+                ("layer_stride", _I64), ("row_bytes", _I64), ("moved", _P)]
+
+
 class SpecVerifyError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {status_string(status)} (sv_status {status})")
@@ -94,6 +100,8 @@ def lib():
                 L.sv_verify_chain.argtypes = [ctypes.POINTER(ChainDesc), _P, _SZ, _P]
                 L.sv_verify_tree.restype = ctypes.c_int
                 L.sv_verify_tree.argtypes = [ctypes.POINTER(TreeDesc), _P, _SZ, _P]
+                L.sv_compact_kv.restype = ctypes.c_int
+                L.sv_compact_kv.argtypes = [ctypes.POINTER(CompactDesc), _P]
                 L.sv_plan_budget.restype = ctypes.c_int
                 L.sv_plan_budget.argtypes = [ctypes.POINTER(PlanDesc), _P]
                 L.sv_row_stats.restype = ctypes.c_int
@@ -317,6 +325,34 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, wor
     if st != OK:
         raise SpecVerifyError(st, "sv_verify_tree")
     return out
+
+
+def compact_kv(kv, accept_len, accept_path, node_slot):
+    """Accepted-path KV compaction in place on the current stream.
+
+    kv: device tensor [layers, slots, ...] (contiguous; each slot's trailing
+    dimensions are one token's row); accept_len [bs] and accept_path [bs, N]
+    int32 as verify_tree returns them; node_slot [bs, N] int64.  Returns
+    moved [bs] int32 (rows moved per layer, -1: request left untouched).
+    """
+    if kv.dim() < 2 or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [layers, slots, ...] tensor")
+    dev = kv.device
+    L, S = kv.shape[0], kv.shape[1]
+    row = kv[0, 0].numel() * kv.element_size()
+    al = accept_len.to(device=dev, dtype=torch.int32).contiguous()
+    ap = accept_path.to(device=dev, dtype=torch.int32).contiguous()
+    ns = node_slot.to(device=dev, dtype=torch.int64).contiguous()
+    bs, N = ap.shape
+    if al.numel() != bs or ns.shape != ap.shape:
+        raise ValueError("accept_len [bs], accept_path and node_slot [bs, N] expected")
+    moved = torch.empty(bs, dtype=torch.int32, device=dev)
+    d = CompactDesc(bs, N, al.data_ptr(), ap.data_ptr(), ns.data_ptr(), kv.data_ptr(), L, S, row, S * row, row,
+                    moved.data_ptr())
+    st = lib().sv_compact_kv(ctypes.byref(d), _stream(dev))
+    if st != OK:
+        raise SpecVerifyError(st, "sv_compact_kv")
+    return moved
 
 
 def plan_budget(confidence, cost, base_tokens, num_steps=None):

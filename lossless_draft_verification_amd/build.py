@@ -8,7 +8,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "specverify.hip")
-SRCS = [SRC, os.path.join(PKG, "csrc", "planner.hip")]
+SRCS = [SRC, os.path.join(PKG, "csrc", "planner.hip"), os.path.join(PKG, "csrc", "compact.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for expected in ("sv_verify_chain", "sv_verify_tree", "sv_row_stats", "sv_chain_workspace_bytes",
                      "sv_tree_workspace_bytes", "sv_row_stats_workspace_bytes", "sv_workspace_init",
-                     "sv_status_string", "sv_abi_version", "sv_plan_budget"):
+                     "sv_status_string", "sv_abi_version", "sv_plan_budget", "sv_compact_kv"):
         assert expected in names
 
 
@@ -185,3 +185,23 @@ def test_plan_argument_validation(field, value, code):
     d = _plan_desc(**{field: value})
     assert sv.lib().sv_plan_budget(ctypes.byref(d), None) == code
     assert sv.lib().sv_plan_budget(None, None) == 1
+
+
+def _compact_desc(**kw):
+    fake = 0x100000
+    d = dict(batch=2, num_nodes=8, accept_len=fake, accept_path=fake, node_slot=fake, kv=fake, num_layers=4,
+             num_slots=100, slot_stride=4096, layer_stride=409600, row_bytes=4096, moved=None)
+    d.update(kw)
+    return _lib.CompactDesc(**d)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 1), ("num_nodes", 65, 1), ("num_layers", 0, 1), ("num_slots", 0, 1), ("row_bytes", 8, 1),
+    ("accept_len", None, 1), ("accept_path", None, 1), ("node_slot", None, 1), ("kv", None, 1),
+    ("row_bytes", 4100, 3), ("slot_stride", 4104, 3), ("kv", 0x100008, 3), ("slot_stride", 2048, 1),
+    ("layer_stride", 4096, 1),
+])
+def test_compact_argument_validation(field, value, code):
+    d = _compact_desc(**{field: value})
+    assert sv.lib().sv_compact_kv(ctypes.byref(d), None) == code
+    assert sv.lib().sv_compact_kv(None, None) == 1
