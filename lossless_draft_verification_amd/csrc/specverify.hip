@@ -787,9 +787,10 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
-  // the loads first, none depending on another: the drafts and the gathered
-  // target logit and q at each draft (wave 0), every row's partials (rows
-  // after the chain's end hold stale values, ignored)
+  // the loads first, none depending on another: the seed, the drafts and the
+  // gathered target logit and q at each draft (wave 0), every row's partials
+  // (rows after the chain's end hold stale values, ignored)
+  const uint64_t seed = P.seed[b];
   int xi = -1, kb = 0;
   uint64_t gl = 0;
   if (tid < 64) {
@@ -807,7 +808,7 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
     const bool bad_id = __ballot(lane < kb && (xi < 0 || xi >= V)) != 0;
     int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_id ? SV_REQ_BAD_DRAFT_ID : SV_REQ_OK;
     double u = 0.0;
-    if (status == SV_REQ_OK && !greedy && lane < kb) u = coin(P.seed[b], b, lane);
+    if (status == SV_REQ_OK && !greedy && lane < kb) u = coin(seed, b, lane);
     if (status == SV_REQ_OK && __ballot(lane <= kb && rs.bad)) status = SV_REQ_NONFINITE;
     bool accept = false;
     double p = 0.0;
@@ -891,6 +892,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
   const float Tf = temp_of(P, b);
   const double T = (double)Tf;
   const bool greedy = !(Tf > 0.f);
+  const uint64_t seed = P.seed[b];  // loaded with the others, used after the fold
   uint32_t gl = 0;  // node lane's token's logit in its parent's row (K1 gathered it)
   int par = -2, tok = -1;
   if (tid < 64) {
@@ -920,7 +922,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
     rs.bad = false;
     if (lane < N) rs = row_stats_of(sm, lane);
     double u = 0.0;
-    if (status == SV_REQ_OK && !greedy && lane < N) u = coin(P.seed[b], b, lane);
+    if (status == SV_REQ_OK && !greedy && lane < N) u = coin(seed, b, lane);
     if (status == SV_REQ_OK && __ballot(lane < N && rs.bad)) status = SV_REQ_NONFINITE;
     // p_parent(tok_n), from the parent lane's row statistics
     const int src = (lane >= 1 && lane < N && status == SV_REQ_OK) ? par : 0;
