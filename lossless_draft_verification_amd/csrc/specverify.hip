@@ -1832,37 +1832,30 @@ __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
 // run of whole 2048-id chunks.  Each workgroup folds the request's row
 // statistics of rows 0..i and its gathered draft values to get w_i, then
 // streams its ids of target row i and draft row i.  Every term is evaluated
-// in fp64 as 2^((l - m) log2(e)/T) (w/S) - q, within about 1e-11 relative
+// in fp64 as 2^((l - m) log2(e)/T) (w/S) - q, within about 1e-13 relative
 // of the definition's w exp((l - m)/T)/S - q (an fp32 screen that skipped
 // the clearly negative terms cost more than it saved: its branch diverges
 // within a wave).  The fp64 partial sums are reduced in a fixed
 // order: the decision step adds the items' partials in item order.
 //
-// 2^t for t <= 0 in fp64 without a division, a library call or a branch:
-// t = n + f with n = rint(t), |f| <= 1/2, and e^(f ln 2) by its Taylor
-// polynomial of degree 9 (remainder below 1e-11 relative for
-// |f ln 2| <= 0.347), scaled by 2^n exactly.  Below 2^-1022 (t = -inf
-// included) it returns 0.
-__device__ __forceinline__ double exp2_f64_nonpos(double t) {
+// 2^t for t <= 0 in fp64 without a division or a branch: t = n/64 + f with
+// n = rint(64 t) and |f| <= 1/128; 2^f by its Taylor polynomial of degree 4
+// (remainder below 4e-14 relative for |f ln 2| <= 0.0055), times 2^((n mod
+// 64)/64) from a table of 64 entries (`tab`, in LDS), scaled by 2^(n div 64)
+// exactly.  Below 2^-1022 (t = -inf included) it returns 0.
+__device__ __forceinline__ double exp2_f64_nonpos(double t, const double* tab) {
   const double tc = fmax(t, -1022.0);
-  const double n = __builtin_rint(tc);
-  const double x = (tc - n) * 0.69314718055994530942;
-  double p = 2.7557319223985888e-06;                // 1/9!
-  p = __builtin_fma(p, x, 2.4801587301587302e-05);  // 1/8!
-  p = __builtin_fma(p, x, 1.9841269841269841e-04);  // 1/7!
-  p = __builtin_fma(p, x, 1.3888888888888889e-03);  // 1/6!
-  p = __builtin_fma(p, x, 8.3333333333333333e-03);  // 1/5!
-  p = __builtin_fma(p, x, 4.1666666666666667e-02);  // 1/4!
-  p = __builtin_fma(p, x, 1.6666666666666667e-01);  // 1/3!
-  p = __builtin_fma(p, x, 0.5);
-  p = __builtin_fma(p, x, 1.0);
-  p = __builtin_fma(p, x, 1.0);
-  const double r = __builtin_ldexp(p, (int)n);
+  const double n = __builtin_rint(tc * 64.0);
+  const double f = __builtin_fma(n, -0.015625, tc);
+  const int ni = (int)n;
+  double p = __builtin_fma(0.009618129107628477, f, 0.055504108664821576);  // (ln 2)^4/4!, (ln 2)^3/3!
+  p = __builtin_fma(p, f, 0.2402265069591007);                                // (ln 2)^2/2!
+  p = __builtin_fma(p, f, 0.6931471805599453);                                // ln 2
+  p = __builtin_fma(p, f, 1.0);
+  const double r = __builtin_ldexp(tab[ni & 63] * p, ni >> 6);
   return t > -1022.0 ? r : 0.0;
 }
 
-// Target logits and q of ids y0..y0+3.  VEC: the rows are 16-byte aligned
-// and V is a multiple of 4, so the group is loaded whole, unconditionally.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void kr_load4(const Params& P, int64_t lrow, int64_t qrow, int y0, float* l, float* q) {
   if (VEC || (y0 + 4 <= P.V && P.aligned && P.q_aligned)) {
@@ -1903,7 +1896,7 @@ constexpr int kKRUnroll = SV_KR_UNROLL;  // groups of 4 ids whose loads a thread
 // q = 0 (a zero term), so with VEC every load is unconditional.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ double kr_stream(const Params& P, int64_t lrow, int64_t qrow, int y_lo, int y_hi,
-                                            double m, double cd, double wS) {
+                                            double m, double cd, double wS, const double* tab) {
   const int tid = threadIdx.x;
   double acc = 0.0;
 #pragma unroll 1
@@ -1920,7 +1913,7 @@ __device__ __forceinline__ double kr_stream(const Params& P, int64_t lrow, int64
     for (int g = 0; g < kKRUnroll; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double ex = exp2_f64_nonpos(((double)l[g][e] - m) * cd);
+        const double ex = exp2_f64_nonpos(((double)l[g][e] - m) * cd, tab);
         const double term = __builtin_fma(ex, wS, -(double)q[g][e]);
         acc += in[g] ? fmax(term, 0.0) : 0.0;
       }
@@ -1928,9 +1921,63 @@ __device__ __forceinline__ double kr_stream(const Params& P, int64_t lrow, int64
   return acc;
 }
 
+// Aligned rows: two register stages of kKRPipe groups each, alternating, so
+// the next stage's loads are in flight while the current one is folded; the
+// first stage is issued before the workgroup's prologue.  Loads past y_hi
+// re-read the range's first group (and count as zero), so every load is
+// unconditional and no stage is copied.
+constexpr int kKRPipe = 2;
+struct KRStage {
+  float l[kKRPipe][4], q[kKRPipe][4];
+};
+template <bool BF16>
+__device__ __forceinline__ void kr_issue(const Params& P, int64_t lrow, int64_t qrow, int base, int y_lo, int y_hi,
+                                         KRStage& st) {
+#pragma unroll
+  for (int g = 0; g < kKRPipe; ++g) {
+    const int y0 = base + 4 * (g * kWG + (int)threadIdx.x);
+    kr_load4<BF16, true>(P, lrow, qrow, y0 < y_hi ? y0 : y_lo, st.l[g], st.q[g]);
+  }
+}
+__device__ __forceinline__ double kr_fold(const KRStage& st, int base, int y_hi, double m, double cd, double wS,
+                                          const double* tab) {
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < kKRPipe; ++g) {
+    const bool in = base + 4 * (g * kWG + (int)threadIdx.x) < y_hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double ex = exp2_f64_nonpos(((double)st.l[g][e] - m) * cd, tab);
+      const double term = __builtin_fma(ex, wS, -(double)st.q[g][e]);
+      acc += in ? fmax(term, 0.0) : 0.0;
+    }
+  }
+  return acc;
+}
+template <bool BF16>
+__device__ __forceinline__ double kr_stream_pipe(const Params& P, int64_t lrow, int64_t qrow, int y_lo, int y_hi,
+                                                 double m, double cd, double wS, const double* tab, KRStage& a) {
+  constexpr int step = 4 * kWG * kKRPipe;
+  double acc = 0.0;
+  KRStage bst;
+#pragma unroll 1
+  for (int base = y_lo;;) {
+    kr_issue<BF16>(P, lrow, qrow, base + step, y_lo, y_hi, bst);
+    acc += kr_fold(a, base, y_hi, m, cd, wS, tab);
+    base += step;
+    if (base >= y_hi) break;
+    kr_issue<BF16>(P, lrow, qrow, base + step, y_lo, y_hi, a);
+    acc += kr_fold(bst, base, y_hi, m, cd, wS, tab);
+    base += step;
+    if (base >= y_hi) break;
+  }
+  return acc;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
   __shared__ Smem sm;
+  __shared__ double tab[64];  // 2^(j/64)
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t per_req = (uint32_t)((P.k - 1) * P.CHr);
   const int b = (int)(blockIdx.x / per_req);
@@ -1942,9 +1989,18 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
   int xi;
   const int kb = chain_kb(P, b, xi);
   if (i >= kb) return;
+  // this item's ids and the first stage of its stream, issued before the prologue
+  const int c_lo = (int)((int64_t)c * P.C3 / P.CHr), c_hi = (int)((int64_t)(c + 1) * P.C3 / P.CHr);
+  const int y_lo = c_lo * kK3Chunk, y_hi = min(c_hi * kK3Chunk, P.V);
+  const int64_t lrow = ((int64_t)b * P.R + i) * P.lstride;
+  const int64_t qrow = ((int64_t)b * P.k + i) * P.qstride;
+  const bool vec = P.aligned && P.q_aligned && (P.V & 3) == 0;
+  KRStage first;
+  if (vec) kr_issue<BF16>(P, lrow, qrow, y_lo, y_lo, y_hi, first);
   uint64_t gl = 0;
   if (tid < 64 && lane < i) gl = P.gat[(int64_t)b * SV_MAX_NODES + lane].l | ((uint64_t)P.gat[(int64_t)b * SV_MAX_NODES + lane].q << 32);
-  fold_rows<false>(P, (int64_t)b * P.R, i + 1, Tf, sm);
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  fold_rows<false>(P, (int64_t)b * P.R, i + 1, Tf, sm);  // ends with a barrier
   const double T = (double)Tf;
   if (tid < 64) {
     const bool bad = __ballot(lane <= i && sm.rbad[lane]) != 0;
@@ -1968,15 +2024,9 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
   const double w = sm.u[0], S = sm.rs[i];
   const float m = sm.rm[i];
   const double wS = w / S, cd = 1.4426950408889634074 / T;
-  const int c_lo = (int)((int64_t)c * P.C3 / P.CHr), c_hi = (int)((int64_t)(c + 1) * P.C3 / P.CHr);
-  const int y_lo = c_lo * kK3Chunk, y_hi = min(c_hi * kK3Chunk, P.V);
-  const int64_t lrow = ((int64_t)b * P.R + i) * P.lstride;
-  const int64_t qrow = ((int64_t)b * P.k + i) * P.qstride;
   double acc;
-  if (P.aligned && P.q_aligned && (P.V & 3) == 0)
-    acc = kr_stream<BF16, true>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS);
-  else
-    acc = kr_stream<BF16, false>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS);
+  if (vec) acc = kr_stream_pipe<BF16>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab, first);
+  else acc = kr_stream<BF16, false>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab);
   acc = block_sum_d(acc, sm);
   if (tid == 0) *out = acc;
 }
