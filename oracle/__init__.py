@@ -47,7 +47,8 @@ class _ChainArgs(ctypes.Structure):
                 ("draft_kind", _I32), ("draft_probs", _P), ("q_row_stride", _I64),
                 ("draft_ids", _P), ("temperature", _P), ("seed", _P),
                 ("accept_len", _P), ("tokens", _P), ("req_status", _P),
-                ("p_draft", _P), ("min_margin", _P), ("n_decisions", _P), ("rule", _I32)]
+                ("p_draft", _P), ("min_margin", _P), ("n_decisions", _P), ("rule", _I32),
+                ("top_k", _P), ("top_p", _P)]
 
 
 class _PlanArgs(ctypes.Structure):
@@ -171,11 +172,14 @@ def row_stats(logits, temperature):
     return m, am, s, st
 
 
-def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, rule="standard"):
+def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, rule="standard",
+                 top_k=None, top_p=None):
     """Chain verification.
 
     rule: "standard" (left-to-right rejection sampling) or "block" (block
-    verification); greedy requests ignore it.
+    verification); greedy requests ignore it.  top_k [bs] int32 / top_p [bs]
+    float32 (or None): the stochastic requests' target is top-k / top-p
+    filtered before verification.
 
     logits: [bs, k+1, V] float32 or uint16 (bf16 bits); draft_ids: [bs, k] int32;
     draft_probs: [bs, k, V] float32 (standard rule) or None with onehot=True.
@@ -200,10 +204,13 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
                min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32))
     if rule not in ("standard", "block"):
         raise ValueError(f"unknown rule {rule!r}")
+    tk = None if top_k is None else np.ascontiguousarray(np.asarray(top_k, np.int32).reshape(bs))
+    tp = None if top_p is None else np.ascontiguousarray(np.asarray(top_p, np.float32).reshape(bs))
     a = _ChainArgs(bs, k, V, code, _ptr(x), V, kind, _ptr(q), V, _ptr(ids), _ptr(temp), _ptr(sd),
                    _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out["status"]),
                    _ptr(out["p_draft"]), _ptr(out["min_margin"]), _ptr(out["n_decisions"]),
-                   RULE_BLOCK if rule == "block" else RULE_STANDARD)
+                   RULE_BLOCK if rule == "block" else RULE_STANDARD,
+                   _ptr(tk), _ptr(tp))
     lib().svo_verify_chain(ctypes.byref(a))
     out["p_draft"] = out["p_draft"][:, :k]
     return out

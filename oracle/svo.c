@@ -146,7 +146,8 @@ static double logit_at(int32_t dtype, const void* base, int64_t idx) {
  * distribution is p(y) = exp((l_y - m)/T)/S: the softmax of the tempered
  * logits ([SD] "接受规则为什么不改变分布": p is taken after temperature). */
 typedef struct {
-  double m, S;
+  double m, S;    /* S: the sum over the kept tokens (all tokens when the row is not filtered) */
+  double tau;     /* tokens with a logit below tau are filtered out (-inf: none) */
   int32_t amax;
   int32_t status;
 } row_stat;
@@ -154,6 +155,7 @@ typedef struct {
 static row_stat scan_row(int32_t dtype, const void* logits, int64_t row_off, int32_t V, double T, int stochastic) {
   row_stat st;
   st.m = -INFINITY;
+  st.tau = -INFINITY;
   st.amax = 0;
   st.S = NAN;
   st.status = SVO_REQ_OK;
@@ -178,7 +180,65 @@ static row_stat scan_row(int32_t dtype, const void* logits, int64_t row_off, int
 static int is_finite_num(double x) { return !isnan(x) && !isinf(x); }
 
 static double p_of(int32_t dtype, const void* logits, int64_t row_off, const row_stat* st, double T, int32_t y) {
-  return exp((logit_at(dtype, logits, row_off + y) - st->m) / T) / st->S;
+  const double l = logit_at(dtype, logits, row_off + y);
+  if (l < st->tau) return 0.0;
+  return exp((l - st->m) / T) / st->S;
+}
+
+/* Top-k / top-p filtering of a stochastic row's target ([SD]
+ * "接受规则为什么不改变分布": p is the target after temperature and top-k / top-p).
+ * Top-k keeps the tokens whose logit is at least the k-th largest logit
+ * (ties at it are kept); top-p then keeps, among those, the fewest
+ * highest-probability tokens whose probability mass reaches p times the
+ * top-k mass, whole groups of equal logits at a time (so the kept set is
+ * again "logit >= threshold").  The row's p becomes p restricted to the kept
+ * tokens and renormalised: st->tau is the threshold and st->S the kept sum
+ * (left to right).  k <= 0 or k >= V, and p outside (0, 1), switch a filter
+ * off.  *margin gets the top-p decision's relative gap (how far the chosen
+ * group's cumulative mass, and the one before it, are from the target). */
+static int cmp_desc(const void* x, const void* y) {
+  const double a = *(const double*)x, b = *(const double*)y;
+  return a > b ? -1 : (a < b ? 1 : 0);
+}
+
+static void filter_row(row_stat* st, int32_t dtype, const void* logits, int64_t row_off, int32_t V, double T,
+                       int32_t topk, float topp, double* margin) {
+  const int use_k = topk > 0 && topk < V, use_p = topp > 0.0f && topp < 1.0f;
+  *margin = INFINITY;
+  if (!use_k && !use_p) return;
+  double* v = (double*)malloc(sizeof(double) * (size_t)V);
+  for (int32_t y = 0; y < V; ++y) v[y] = logit_at(dtype, logits, row_off + y);
+  qsort(v, (size_t)V, sizeof(double), cmp_desc);
+  double tau = use_k ? v[topk - 1] : -INFINITY;
+  if (use_p) {
+    int32_t n = 0;
+    double pk = 0.0;
+    while (n < V && v[n] >= tau) pk += exp((v[n++] - st->m) / T);
+    const double target = (double)topp * pk;
+    double cum = 0.0;
+    for (int32_t i = 0; i < n;) {
+      int32_t j = i;
+      double g = 0.0;
+      while (j < n && v[j] == v[i]) g += exp((v[j++] - st->m) / T);
+      const double prev = cum;
+      cum += g;
+      if (cum >= target) {
+        tau = v[i];
+        const double g1 = (cum - target) / target, g0 = (target - prev) / target;
+        *margin = g1 < g0 ? g1 : g0;
+        break;
+      }
+      i = j;
+    }
+  }
+  free(v);
+  double S = 0.0;
+  for (int32_t y = 0; y < V; ++y) {
+    const double l = logit_at(dtype, logits, row_off + y);
+    if (l >= tau) S += exp((l - st->m) / T);
+  }
+  st->S = S;
+  st->tau = tau;
 }
 
 void svo_row_stats(int32_t rows, int32_t vocab, int32_t dtype, const void* logits, int64_t row_stride,
@@ -389,6 +449,14 @@ static void chain_one(const svo_chain_args* a, int32_t b, double* w, double* pro
     for (int32_t r = 0; r <= kb; ++r) {
       st[r] = scan_row(a->logits_dtype, a->logits, ((int64_t)b * R + r) * a->logits_row_stride, V, T, !greedy);
       if (st[r].status != SVO_REQ_OK) status = st[r].status;
+    }
+  }
+  if (status == SVO_REQ_OK && !greedy && (a->top_k || a->top_p)) {
+    for (int32_t r = 0; r <= kb; ++r) {
+      double g;
+      filter_row(&st[r], a->logits_dtype, a->logits, ((int64_t)b * R + r) * a->logits_row_stride, V, T,
+                 a->top_k ? a->top_k[b] : 0, a->top_p ? a->top_p[b] : 1.0f, &g);
+      if (g < min_margin) min_margin = g;
     }
   }
   if (status != SVO_REQ_OK) {

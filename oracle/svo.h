@@ -83,6 +83,8 @@ typedef struct {
   double* min_margin;                       /* [bs] out: smallest decision margin; may be NULL */
   int32_t* n_decisions;                     /* [bs] out: decisions taken; may be NULL */
   int32_t rule;                             /* SVO_RULE_STANDARD or SVO_RULE_BLOCK */
+  const int32_t* top_k;                     /* [bs] or NULL: top-k of each stochastic request (<= 0: off) */
+  const float* top_p;                       /* [bs] or NULL: top-p (outside (0, 1): off) */
 } svo_chain_args;
 
 typedef struct {
