@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 
 /* Limits of one call. */
 #define SV_MAX_BATCH 65536   /* requests per call */
@@ -155,6 +155,25 @@ typedef struct {
   double* p_draft;            /* [bs][k] out, may be NULL: p_i(x_i) for used slots, NaN elsewhere
                                  (greedy rows: 1 at the argmax, else 0) */
   uint32_t flags;             /* SV_FLAG_* bits, 0 by default */
+  /* Top-k / top-p filtering of the target (page "投机解码", section
+   * "接受规则为什么不改变分布": p is the target after temperature and the
+   * top-k / top-p sampling parameters).  Per request, both may be NULL (no
+   * filtering).  top_k[b] keeps the tokens whose logit is at least the k-th
+   * largest of the row (ties at it kept); top_p[b] then keeps, within that
+   * set, the fewest groups of equal logits, highest first, whose probability
+   * mass reaches top_p[b] times the set's mass.  The kept set is {l >= tau}
+   * for one threshold tau per row; p is restricted to it and renormalised,
+   * on every row read (0..k_b) of a stochastic request, so the ratio test,
+   * the residual and the bonus all see the filtered p.  top_k <= 0 or >= V,
+   * and top_p outside (0, 1) (NaN included), switch a filter off; greedy
+   * requests ignore both.  q is taken as given (the drafter's own, already
+   * filtered if it filters).  A filtered call takes one more launch per row
+   * read (the thresholds) between the statistics and the decisions; not
+   * available with SV_FLAG_FUSED (SV_ERR_UNSUPPORTED).  With STATS_ONLY /
+   * DECIDE_ONLY the thresholds belong to the STATS_ONLY call, and both calls
+   * must pass the same arrays. */
+  const int32_t* top_k;       /* [bs] or NULL */
+  const float* top_p;         /* [bs] or NULL */
 } sv_chain_desc;
 
 typedef struct {

@@ -43,7 +43,7 @@ class ChainDesc(ctypes.Structure):
                 ("logits", _P), ("logits_row_stride", _I64), ("draft_kind", ctypes.c_int),
                 ("draft_probs", _P), ("q_row_stride", _I64), ("draft_ids", _P), ("temperature", _P),
                 ("seed", _P), ("accept_len", _P), ("tokens", _P), ("req_status", _P), ("p_draft", _P),
-                ("flags", _U32)]
+                ("flags", _U32), ("top_k", _P), ("top_p", _P)]
 
 
 class TreeDesc(ctypes.Structure):
@@ -236,12 +236,14 @@ def _seed_tensor(seeds, bs, device):
 
 # ------------------------------------------------------------------ calls
 def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, *, flags=0,
-                 return_p_draft=False, workspace=None):
+                 return_p_draft=False, workspace=None, top_k=None, top_p=None):
     """Chain verification on the current stream (asynchronous).
 
     logits [bs, k+1, V] float32/bfloat16; draft_ids [bs, k] int32 (-1 ends a
     chain); temperature [bs] float32 (<= 0: greedy); seeds [bs] int64 (raw
-    64-bit Philox keys); draft_probs [bs, k, V] float32, or onehot=True.
+    64-bit Philox keys); draft_probs [bs, k, V] float32, or onehot=True;
+    top_k [bs] int32 / top_p [bs] float32 (or None): the stochastic requests'
+    target is top-k / top-p filtered.
     Returns a dict of device tensors: accept_len [bs], tokens [bs, k+1],
     status [bs] (int32), and p_draft [bs, k] float64 if requested.
     """
@@ -274,6 +276,8 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
                status=torch.empty(bs, dtype=torch.int32, device=device))
     if return_p_draft:
         out["p_draft"] = torch.empty(bs, k, dtype=torch.float64, device=device)
+    tk = None if top_k is None else _on(top_k.reshape(bs), device, torch.int32, "top_k")
+    tp = None if top_p is None else _on(top_p.reshape(bs), device, torch.float32, "top_p")
     need = chain_workspace_bytes(bs, k, V, code)
     if need == 0:
         raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_chain_workspace_bytes")
@@ -282,7 +286,8 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
     d = ChainDesc(bs, k, V, code, logits.data_ptr(), lstride, DRAFT_ONEHOT if onehot else DRAFT_PROBS,
                   q.data_ptr() if q is not None else None, qstride, ids.data_ptr() if k > 0 else None,
                   temp.data_ptr(), sd.data_ptr(), out["accept_len"].data_ptr(), out["tokens"].data_ptr(),
-                  out["status"].data_ptr(), out["p_draft"].data_ptr() if return_p_draft else None, int(flags))
+                  out["status"].data_ptr(), out["p_draft"].data_ptr() if return_p_draft else None, int(flags),
+                  tk.data_ptr() if tk is not None else None, tp.data_ptr() if tp is not None else None)
     st = lib().sv_verify_chain(ctypes.byref(d), ctypes.c_void_p(ws.base), ctypes.c_size_t(ws.nbytes),
                                _stream(device))
     if st != OK:
@@ -429,7 +434,7 @@ class PreparedChain:
     stream; outputs are overwritten in place."""
 
     def __init__(self, logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, *, flags=0,
-                 workspace=None):
+                 workspace=None, top_k=None, top_p=None):
         device = logits.device
         bs, R, V = (int(x) for x in logits.shape)
         k = R - 1
@@ -444,6 +449,8 @@ class PreparedChain:
         self.out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=device),
                         tokens=torch.empty(bs, R, dtype=torch.int32, device=device),
                         status=torch.empty(bs, dtype=torch.int32, device=device))
+        self.top_k = None if top_k is None else _on(top_k.reshape(bs), device, torch.int32, "top_k")
+        self.top_p = None if top_p is None else _on(top_p.reshape(bs), device, torch.float32, "top_p")
         self.ws = workspace if workspace is not None else default_workspace(device)
         self.ws.ensure(chain_workspace_bytes(bs, k, V, code))
         self.device = device
@@ -452,7 +459,9 @@ class PreparedChain:
                               self.q.data_ptr() if self.q is not None else None, qstride,
                               self.ids.data_ptr() if k > 0 else None, self.temp.data_ptr(), self.seeds.data_ptr(),
                               self.out["accept_len"].data_ptr(), self.out["tokens"].data_ptr(),
-                              self.out["status"].data_ptr(), None, int(flags))
+                              self.out["status"].data_ptr(), None, int(flags),
+                              self.top_k.data_ptr() if self.top_k is not None else None,
+                              self.top_p.data_ptr() if self.top_p is not None else None)
         self._fn = lib().sv_verify_chain
         self._ref = ctypes.byref(self.desc)
         self._phase_descs, self._phase_refs = [], {}

@@ -132,6 +132,13 @@ struct K3Rec {
   int32_t pad[3];
 };
 
+// A filtered row's threshold and kept sum (written by the thresholds pass).
+struct FiltRec {
+  double s;           // S' = sum over kept ids of exp((l - m)/T)
+  float tau;          // ids with a logit below tau are cut (p = 0)
+  int32_t pad;
+};
+
 constexpr size_t kSyncOffset = 256;
 constexpr size_t kDataOffset = kSyncOffset + sizeof(Sync) * SV_MAX_BATCH;
 
@@ -173,6 +180,9 @@ struct Params {
   int32_t CI;         // K23 items per request: ceil(C3 / G3)
   int32_t CHr;        // block rule: residual-mass items per row (rows 1..k-1)
   double* rpart;      // block rule: [bs][k][CHr] residual-mass partials
+  const int32_t* top_k;  // chain: per-request top-k (NULL: off)
+  const float* top_p;    // chain: per-request top-p (NULL: off)
+  FiltRec* filt;         // [bs*R] thresholds and kept sums of filtered rows
   int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
   uint32_t flags;
@@ -304,6 +314,7 @@ struct Job {
   float m, c_hi, c_lo, inv_s;  // row max; log2(e)/T as hi + lo; 1/S rounded
   double s, t;                  // S = sum exp((l - m)/T); T
   double wmul;                  // JOB_RESID weight max(wmul p - q, 0): 1, or the block rule's prefix weight
+  float tau;                    // ids with a logit below tau have p = 0 (top-k / top-p; -inf: none)
   int excl[SV_MAX_NODES];       // ids removed from p (JOB_EXCL)
 };
 
@@ -410,6 +421,15 @@ __device__ __forceinline__ void block_sum2_d(double& a, double& b, Smem& sm) {
 // Temperature of the request (chain/tree) or of the row (row statistics).
 __device__ __forceinline__ float temp_of(const Params& P, int b) { return P.temp[b]; }
 __device__ __forceinline__ bool is_stochastic(float T) { return T > 0.f && isfinite(T); }
+
+// Whether chain request b's target is top-k / top-p filtered: stochastic,
+// and k in (0, V) or p in (0, 1).
+__device__ __forceinline__ bool request_filtered(const Params& P, int b, float T) {
+  if (!is_stochastic(T)) return false;
+  const int tk = P.top_k ? P.top_k[b] : 0;
+  const float tp = P.top_p ? P.top_p[b] : 1.f;
+  return (tk > 0 && tk < P.V) || (tp > 0.f && tp < 1.f);
+}
 
 // Number of chain drafts in use: the index of the first -1, else k.  Every
 // wave computes the same value (k <= 63 fits one wave).
@@ -805,6 +825,11 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
     rs.s = 1.0;
     rs.bad = false;
     if (lane < R) rs = row_stats_of(sm, lane);
+    float ftau = -INFINITY;  // top-k / top-p: the row's threshold (and its kept sum replaces S)
+    if (request_filtered(P, b, Tf) && lane <= kb) {
+      rs.s = P.filt[(int64_t)b * R + lane].s;
+      ftau = P.filt[(int64_t)b * R + lane].tau;
+    }
     const bool bad_id = __ballot(lane < kb && (xi < 0 || xi >= V)) != 0;
     int status = !isfinite(Tf) ? SV_REQ_BAD_TEMPERATURE : bad_id ? SV_REQ_BAD_DRAFT_ID : SV_REQ_OK;
     double u = 0.0;
@@ -817,7 +842,8 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
         accept = (xi == rs.amax);
         p = accept ? 1.0 : 0.0;
       } else {
-        p = p_at((double)__uint_as_float((uint32_t)gl), rs.m, T, rs.s);
+        const float lx = __uint_as_float((uint32_t)gl);
+        p = lx < ftau ? 0.0 : p_at((double)lx, rs.m, T, rs.s);
         if (P.draft_kind == SV_DRAFT_ONEHOT) {
           accept = u < p;
         } else {
@@ -855,6 +881,7 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
         J.t = T;
         scale_pair(T, J.c_hi, J.c_lo);
         J.wmul = (J.kind == JOB_RESID) ? wa : 1.0;
+        J.tau = ftau;
         J.inv_s = (float)(J.wmul / rs.s);
         J.n_excl = (J.kind == JOB_EXCL) ? 1 : 0;
         J.excl[0] = xi;
@@ -993,6 +1020,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
       scale_pair(T, J.c_hi, J.c_lo);
       J.inv_s = (float)(1.0 / J.s);
       J.wmul = 1.0;
+      J.tau = -INFINITY;
       int ne = 0;
       if (kind == JOB_EXCL)
         for (int c = cur + 1; c < N; ++c)
@@ -1036,7 +1064,7 @@ __device__ __forceinline__ bool is_excluded(const Job& J, int y) {
 }
 __device__ __forceinline__ double race_key_from(const Job& J, uint64_t seed, int b, int y, double l, double q,
                                                 bool use_p) {
-  const double p = p_at(l, J.m, J.t, J.s);
+  const double p = l < (double)J.tau ? 0.0 : p_at(l, J.m, J.t, J.s);
   double w = p;
   if (!use_p) {
     if (J.kind == JOB_RESID) w = (J.wmul * p - q > 0.0) ? J.wmul * p - q : 0.0;
@@ -1081,8 +1109,8 @@ __device__ __forceinline__ void block_best(double& k, int& y, Smem& sm) {
 // whole kernel.
 __device__ __attribute__((noinline)) double race_key_cold(double l, double q, double m, double T, double S,
                                                           double wmul, int resid, int use_p, uint64_t seed, int b,
-                                                          int r, int y) {
-  const double p = exp((l - m) / T) / S;
+                                                          int r, int y, double tau) {
+  const double p = l < tau ? 0.0 : exp((l - m) / T) / S;
   double w = p;
   if (!use_p && resid) w = (wmul * p - q > 0.0) ? wmul * p - q : 0.0;
   const double U = uniform_f64(noise_word(seed, b, r, y));
@@ -1090,8 +1118,8 @@ __device__ __attribute__((noinline)) double race_key_cold(double l, double q, do
 }
 // Exact fp64 weight of one id (p, or the residual max(wmul p - q, 0)).
 __device__ __attribute__((noinline)) double weight_cold(double l, double q, double m, double T, double S,
-                                                        double wmul, int resid) {
-  const double p = exp((l - m) / T) / S;
+                                                        double wmul, int resid, double tau) {
+  const double p = l < tau ? 0.0 : exp((l - m) / T) / S;
   if (resid) return (wmul * p - q > 0.0) ? wmul * p - q : 0.0;
   return p;
 }
@@ -1115,7 +1143,7 @@ __device__ double chunk_sum_f64(const Params& P, const Job& J, int c, bool use_p
     if (!use_p && J.kind == JOB_EXCL && is_excluded(J, y)) continue;
     const double l = (double)load_logit<BF16>(P, J.row, y);
     const double q = qrow ? (double)qrow[y] : 0.0;
-    s += weight_cold(l, q, J.m, J.t, J.s, J.wmul, resid);
+    s += weight_cold(l, q, J.m, J.t, J.s, J.wmul, resid, (double)J.tau);
   }
   return block_sum_d(s, sm);
 }
@@ -1134,7 +1162,7 @@ __device__ int chunk_race_f64(const Params& P, const Job& J, int b, int c, bool 
     const double q = qrow ? (double)qrow[y] : 0.0;
     const bool zero = !use_p && J.kind == JOB_EXCL && is_excluded(J, y);
     const double key = zero ? 0.0 : race_key_cold(l, q, J.m, J.t, J.s, J.wmul, J.kind == JOB_RESID, use_p, seed, b,
-                                                          J.r, y);
+                                                          J.r, y, (double)J.tau);
     if (better(key, y, best_k, best_y)) {
       best_k = key;
       best_y = y;
@@ -1173,7 +1201,8 @@ __device__ int race_row_f64(const Params& P, const Job& J, int b, Smem& sm) {
 // the measured 2^-23.5); t is clamped to [-256, 0], where e is below every
 // fp32 weight that matters (and no NaN arises from a -inf logit).  For a
 // residual w = max(p - q, 0) with p = e/S; otherwise w = e/S.  Ids past
-// the vocabulary and removed ids get 0 for both bounds.
+// the vocabulary, removed ids and ids whose logit is below the job's
+// threshold get 0 for both bounds.
 template <bool BF16, int KIND>
 __device__ __forceinline__ void weight_bounds(const Params& P, const Job& J, int c, float* whi, float* wlo) {
   const int tid = threadIdx.x;
@@ -1214,6 +1243,8 @@ __device__ __forceinline__ void weight_bounds(const Params& P, const Job& J, int
 #pragma unroll
       for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l[i] = l[i] < J.tau ? -INFINITY : l[i];  // cut by top-k / top-p
 #pragma unroll
     for (int i = 0; i < 4; ++i) q[i] = 0.f;
     if (KIND == JOB_RESID) {
@@ -1346,7 +1377,8 @@ __device__ __forceinline__ void chunk_load(const Params& P, const Job& J, int c,
 // within (eta + 2^-23) p of the exact one, eta = |t| 2^-21 + 2^-17, and
 // since max(., 0) is 1-Lipschitz the fp32 residual max(p - q, 0) is within
 // that too (plus its own rounding, 2^-24 of itself).  So the thread sums
-// the fp32 weights and, for the error, e and |t| e: no per-id bounds.
+// the fp32 weights and, for the error, e and |t| e: no per-id bounds.  Ids
+// whose logit is below the job's threshold count as -inf logits.
 template <bool BF16, int KIND>
 __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, int c, double& dhi, double& dlo,
                                                  const ChunkRaw<BF16>* r = nullptr) {
@@ -1391,6 +1423,8 @@ __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l[i] = l[i] < J.tau ? -INFINITY : l[i];  // cut by top-k / top-p
     if (KIND == JOB_RESID) {
       if (r != nullptr || (full && P.q_aligned)) {
         const u32x4 w = (r != nullptr) ? r->q[g] : __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
@@ -1893,10 +1927,11 @@ constexpr int kKRUnroll = SV_KR_UNROLL;  // groups of 4 ids whose loads a thread
 // The thread's share of sum_y max(2^((l - m) cd) wS - q, 0) over ids
 // [y_lo, y_hi): kKRUnroll groups of 4 ids per step, all loads first.  Ids
 // past y_hi load the range's first group again and count as l = -inf,
-// q = 0 (a zero term), so with VEC every load is unconditional.
-template <bool BF16, bool VEC>
+// q = 0 (a zero term), so with VEC every load is unconditional.  With
+// FILT, ids whose logit is below tau count as -inf logits.
+template <bool BF16, bool VEC, bool FILT>
 __device__ __forceinline__ double kr_stream(const Params& P, int64_t lrow, int64_t qrow, int y_lo, int y_hi,
-                                            double m, double cd, double wS, const double* tab) {
+                                            double m, double cd, double wS, const double* tab, float tau) {
   const int tid = threadIdx.x;
   double acc = 0.0;
 #pragma unroll 1
@@ -1913,7 +1948,8 @@ __device__ __forceinline__ double kr_stream(const Params& P, int64_t lrow, int64
     for (int g = 0; g < kKRUnroll; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double ex = exp2_f64_nonpos(((double)l[g][e] - m) * cd, tab);
+        const float le = (FILT && l[g][e] < tau) ? -INFINITY : l[g][e];
+        const double ex = exp2_f64_nonpos(((double)le - m) * cd, tab);
         const double term = __builtin_fma(ex, wS, -(double)q[g][e]);
         acc += in[g] ? fmax(term, 0.0) : 0.0;
       }
@@ -1939,35 +1975,38 @@ __device__ __forceinline__ void kr_issue(const Params& P, int64_t lrow, int64_t 
     kr_load4<BF16, true>(P, lrow, qrow, y0 < y_hi ? y0 : y_lo, st.l[g], st.q[g]);
   }
 }
+template <bool FILT>
 __device__ __forceinline__ double kr_fold(const KRStage& st, int base, int y_hi, double m, double cd, double wS,
-                                          const double* tab) {
+                                          const double* tab, float tau) {
   double acc = 0.0;
 #pragma unroll
   for (int g = 0; g < kKRPipe; ++g) {
     const bool in = base + 4 * (g * kWG + (int)threadIdx.x) < y_hi;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const double ex = exp2_f64_nonpos(((double)st.l[g][e] - m) * cd, tab);
+      const float le = (FILT && st.l[g][e] < tau) ? -INFINITY : st.l[g][e];
+      const double ex = exp2_f64_nonpos(((double)le - m) * cd, tab);
       const double term = __builtin_fma(ex, wS, -(double)st.q[g][e]);
       acc += in ? fmax(term, 0.0) : 0.0;
     }
   }
   return acc;
 }
-template <bool BF16>
+template <bool BF16, bool FILT>
 __device__ __forceinline__ double kr_stream_pipe(const Params& P, int64_t lrow, int64_t qrow, int y_lo, int y_hi,
-                                                 double m, double cd, double wS, const double* tab, KRStage& a) {
+                                                 double m, double cd, double wS, const double* tab, KRStage& a,
+                                                 float tau) {
   constexpr int step = 4 * kWG * kKRPipe;
   double acc = 0.0;
   KRStage bst;
 #pragma unroll 1
   for (int base = y_lo;;) {
     kr_issue<BF16>(P, lrow, qrow, base + step, y_lo, y_hi, bst);
-    acc += kr_fold(a, base, y_hi, m, cd, wS, tab);
+    acc += kr_fold<FILT>(a, base, y_hi, m, cd, wS, tab, tau);
     base += step;
     if (base >= y_hi) break;
     kr_issue<BF16>(P, lrow, qrow, base + step, y_lo, y_hi, a);
-    acc += kr_fold(bst, base, y_hi, m, cd, wS, tab);
+    acc += kr_fold<FILT>(bst, base, y_hi, m, cd, wS, tab, tau);
     base += step;
     if (base >= y_hi) break;
   }
@@ -1998,7 +2037,14 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
   KRStage first;
   if (vec) kr_issue<BF16>(P, lrow, qrow, y_lo, y_lo, y_hi, first);
   uint64_t gl = 0;
+  const bool filt = request_filtered(P, b, Tf);
+  double fs = 0.0;  // top-k / top-p: kept sum and threshold of row `lane`
+  float ftau = -INFINITY;
   if (tid < 64 && lane < i) gl = P.gat[(int64_t)b * SV_MAX_NODES + lane].l | ((uint64_t)P.gat[(int64_t)b * SV_MAX_NODES + lane].q << 32);
+  if (tid < 64 && filt && lane <= i) {
+    fs = P.filt[(int64_t)b * P.R + lane].s;
+    ftau = P.filt[(int64_t)b * P.R + lane].tau;
+  }
   if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
   fold_rows<false>(P, (int64_t)b * P.R, i + 1, Tf, sm);  // ends with a barrier
   const double T = (double)Tf;
@@ -2006,13 +2052,18 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
     const bool bad = __ballot(lane <= i && sm.rbad[lane]) != 0;
     double p = 0.0, q = 0.0;
     if (lane < i && !bad) {
-      p = p_at((double)__uint_as_float((uint32_t)gl), sm.rm[lane], T, sm.rs[lane]);
+      const float lx = __uint_as_float((uint32_t)gl);
+      p = lx < ftau ? 0.0 : p_at((double)lx, sm.rm[lane], T, filt ? fs : sm.rs[lane]);
       q = (double)__uint_as_float((uint32_t)(gl >> 32));
     }
     const double w = __shfl(prefix_weights(p, q, i), i, 64);
     if (lane == 0) {
       sm.u[0] = w;
       sm.flag = bad;
+    }
+    if (lane == i) {
+      sm.u[1] = filt ? fs : sm.rs[i];
+      sm.l0 = ftau;
     }
   }
   __syncthreads();
@@ -2021,14 +2072,335 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
     if (tid == 0) *out = 0.0;
     return;
   }
-  const double w = sm.u[0], S = sm.rs[i];
-  const float m = sm.rm[i];
+  const double w = sm.u[0], S = sm.u[1];
+  const float m = sm.rm[i], tau = sm.l0;
   const double wS = w / S, cd = 1.4426950408889634074 / T;
   double acc;
-  if (vec) acc = kr_stream_pipe<BF16>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab, first);
-  else acc = kr_stream<BF16, false>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab);
+  if (filt) {
+    if (vec) acc = kr_stream_pipe<BF16, true>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab, first, tau);
+    else acc = kr_stream<BF16, false, true>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab, tau);
+  } else {
+    if (vec) acc = kr_stream_pipe<BF16, false>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab, first, tau);
+    else acc = kr_stream<BF16, false, false>(P, lrow, qrow, y_lo, y_hi, (double)m, cd, wS, tab, tau);
+  }
   acc = block_sum_d(acc, sm);
   if (tid == 0) *out = acc;
+}
+
+// ===================================================================== KF
+// Top-k / top-p thresholds (page "投机解码", section
+// "接受规则为什么不改变分布": the target p is the one after the top-k /
+// top-p sampling parameters).  One workgroup per row r <= k_b of a chain
+// request that is stochastic and has a filter on; it writes the row's
+// threshold tau (the kept ids are those with l >= tau) and its kept sum
+// S' = sum over them of exp((l - m)/T).
+//
+// Logits map to 32-bit keys that order like their values (-0 as +0, so
+// equal logits share one key).  A threshold is found by a radix descent
+// over the keys, most significant digit first (11, 11 and 10 bits), one
+// pass over the row per digit with a histogram of the digit in LDS:
+//  - top-k counts the keys under the prefix found so far; the k-th largest
+//    key lies in the first bin, from the top, at which the count of keys at
+//    or above it reaches k;
+//  - top-p adds the masses e = 2^((l - m) log2(e)/T) of the top-k set's
+//    keys in 96-bit fixed point (two integer parts of e 2^32 and of its
+//    fraction 2^32: exact up to 2^-64 per id, and independent of the order
+//    of the atomic adds); the cut is the first group of equal logits, from
+//    the top, at which the mass at or above it reaches top_p times the set's
+//    mass (the first digit's histogram total).
+// The kept sum is the fixed-point mass at or above the cut (top-p), or an
+// fp64 sum in a fixed order (top-k alone).  Passes after the first re-read
+// the row from L2 / MALL; the work per id is a key, a compare and an LDS
+// atomic, plus an fp64 exponential in the mass passes.
+constexpr int kKFBins = 2048;
+constexpr int kKFUnroll = 4;  // groups of 4 ids whose loads a thread issues together
+
+__device__ __forceinline__ uint32_t kf_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float kf_val(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// Digit levels: shift and width.
+__device__ __forceinline__ int kf_shift(int L) { return L == 0 ? 21 : (L == 1 ? 10 : 0); }
+__device__ __forceinline__ int kf_width(int L) { return L == 2 ? 10 : 11; }
+// Whether a key lies under the prefix of the levels above L.
+__device__ __forceinline__ bool kf_under(uint32_t key, int L, uint32_t pre) {
+  return L == 0 || (key >> (kf_shift(L) + kf_width(L))) == pre;
+}
+// Fixed-point values h 2^-32 + l 2^-64 (both parts may exceed 2^32 in a
+// sum): comparison and subtraction after carrying l's high part into h.
+__device__ __forceinline__ bool kf_ge(uint64_t h, uint64_t l, uint64_t nh, uint64_t nl) {
+  h += l >> 32;
+  l &= 0xFFFFFFFFull;
+  return h > nh || (h == nh && l >= nl);
+}
+__device__ __forceinline__ void kf_sub(uint64_t& nh, uint64_t& nl, uint64_t ah, uint64_t al) {
+  ah += al >> 32;
+  al &= 0xFFFFFFFFull;
+  if (nl >= al) {
+    nl -= al;
+    nh -= ah;
+  } else {
+    nl = nl + 0x100000000ull - al;
+    nh -= ah + 1;
+  }
+}
+__device__ __forceinline__ void kf_fix(double x, uint64_t& h, uint64_t& l) {
+  x = fmin(fmax(x, 0.0), 4294967296.0) * 4294967296.0;  // a NaN becomes 0
+  const double fh = floor(x);
+  h = (uint64_t)fh;
+  l = (uint64_t)floor((x - fh) * 4294967296.0);
+}
+__device__ __forceinline__ double kf_float(uint64_t h, uint64_t l) {
+  return (double)h * 0x1p-32 + (double)l * 0x1p-64;
+}
+
+struct KFShared {
+  uint64_t hh[kKFBins];  // per bin: integer parts of e 2^32 (top-p)
+  uint64_t hl[kKFBins];  // per bin: counts (top-k) or fraction parts 2^32 (top-p)
+  uint64_t th[kWG], tl[kWG];  // per thread: the sums of its bins
+  uint64_t xh[kWG], xl[kWG];  // per thread: the sums of the bins above its own
+  uint64_t toth, totl;        // the histogram's total
+  uint64_t ah, al;            // found bin: the sum of the bins above it
+  uint64_t bh, bl;            // found bin: its own sum
+  int digit;                  // found bin (-1: none)
+  float red_f[kWaves];
+  double red_d[kWaves];
+};
+
+// One pass over row `row`: f(l) for every logit, each thread on groups of 4
+// consecutive ids, kKFUnroll groups' loads issued together.
+template <bool BF16, typename F>
+__device__ __forceinline__ void kf_pass(const Params& P, int64_t row, F&& f) {
+  const int V = P.V, tid = threadIdx.x;
+  const int64_t off = row * P.lstride;
+#pragma unroll 1
+  for (int base = 0; base < V; base += 4 * kWG * kKFUnroll) {
+    float l[kKFUnroll][4];
+#pragma unroll
+    for (int g = 0; g < kKFUnroll; ++g) {
+      const int y0 = base + 4 * (g * kWG + tid);
+      if (P.aligned && y0 + 4 <= V) {
+        if (BF16) {
+          const u32x2 w = *(const u32x2*)((const uint16_t*)P.logits + off + y0);
+          l[g][0] = __uint_as_float(w.x << 16);
+          l[g][1] = __uint_as_float(w.x & 0xffff0000u);
+          l[g][2] = __uint_as_float(w.y << 16);
+          l[g][3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+          const u32x4 w = *(const u32x4*)((const float*)P.logits + off + y0);
+          l[g][0] = __uint_as_float(w.x);
+          l[g][1] = __uint_as_float(w.y);
+          l[g][2] = __uint_as_float(w.z);
+          l[g][3] = __uint_as_float(w.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l[g][i] = (y0 + i < V) ? load_logit<BF16>(P, row, y0 + i) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kKFUnroll; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (base + 4 * (g * kWG + tid) + i < V) f(l[g][i]);
+  }
+}
+
+__device__ __forceinline__ void kf_clear(KFShared& s) {
+  for (int i = threadIdx.x; i < kKFBins; i += kWG) {
+    s.hh[i] = 0;
+    s.hl[i] = 0;
+  }
+  __syncthreads();
+}
+
+// Sums of a complete histogram of `nbins` bins (every thread calls it, after
+// the barrier that ends the histogram's pass): each thread's bins, the sums
+// of the bins above each thread's, and the total.
+template <bool MASS>
+__device__ __forceinline__ void kf_scan(KFShared& s, int nbins) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int per = nbins / kWG;
+  uint64_t sh = 0, sl = 0;
+  for (int j = 0; j < per; ++j) {
+    if (MASS) sh += s.hh[tid * per + j];
+    sl += s.hl[tid * per + j];
+  }
+  s.th[tid] = sh;
+  s.tl[tid] = sl;
+  if (tid == 0) s.digit = -1;
+  __syncthreads();
+  if (tid < 64) {
+    uint64_t gh = 0, gl = 0;
+    for (int j = 0; j < kWG / 64; ++j) {
+      gh += s.th[(kWG / 64) * lane + j];
+      gl += s.tl[(kWG / 64) * lane + j];
+    }
+    uint64_t ih = gh, il = gl;  // sums over lanes >= lane
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t vh = __shfl_down(ih, o, 64), vl = __shfl_down(il, o, 64);
+      if (lane + o < 64) {
+        ih += vh;
+        il += vl;
+      }
+    }
+    if (lane == 0) {
+      s.toth = ih;
+      s.totl = il;
+    }
+    uint64_t rh = ih - gh, rl = il - gl;
+    for (int j = kWG / 64 - 1; j >= 0; --j) {
+      const int t = (kWG / 64) * lane + j;
+      s.xh[t] = rh;
+      s.xl[t] = rl;
+      rh += s.th[t];
+      rl += s.tl[t];
+    }
+  }
+  __syncthreads();
+}
+
+// The first bin from the top at which the sum of the bins at or above it
+// reaches (nh, nl) (a normalised fixed-point value, or a count in nl), after
+// kf_scan: s.digit, s.ah/al (bins above) and s.bh/bl (the bin itself).
+template <bool MASS>
+__device__ __forceinline__ void kf_search(KFShared& s, int nbins, uint64_t nh, uint64_t nl) {
+  const int tid = threadIdx.x;
+  const int per = nbins / kWG;
+  uint64_t rh = s.xh[tid], rl = s.xl[tid];
+  for (int j = per - 1; j >= 0; --j) {
+    const uint64_t ph = rh, pl = rl;
+    const uint64_t bh = MASS ? s.hh[tid * per + j] : 0, bl = s.hl[tid * per + j];
+    rh += bh;
+    rl += bl;
+    if (!kf_ge(ph, pl, nh, nl) && kf_ge(rh, rl, nh, nl)) {
+      s.digit = tid * per + j;
+      s.ah = ph;
+      s.al = pl;
+      s.bh = bh;
+      s.bl = bl;
+    }
+  }
+  __syncthreads();
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kWG) void kf_kernel(Params P) {
+  __shared__ KFShared s;
+  __shared__ double tab[64];  // 2^(j/64)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = (int)(blockIdx.x / (uint32_t)P.R);
+  const int r = (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.R);
+  const float Tf = temp_of(P, b);
+  if (!request_filtered(P, b, Tf)) return;
+  int xi;
+  if (r > chain_kb(P, b, xi)) return;
+  const int tk = P.top_k ? P.top_k[b] : 0;
+  const float tp = P.top_p ? P.top_p[b] : 1.f;
+  const bool use_k = tk > 0 && tk < P.V, use_p = tp > 0.f && tp < 1.f;
+  const int64_t row = (int64_t)b * P.R + r;
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  kf_clear(s);
+  // the row max, and the first digit's counts for top-k
+  float m = -INFINITY;
+  kf_pass<BF16>(P, row, [&](float l) {
+    m = fmaxf(m, l);
+    if (use_k) atomicAdd((unsigned long long*)&s.hl[kf_key(l) >> 21], 1ull);
+  });
+  m = wave_max(m);
+  if (lane == 0) s.red_f[wave] = m;
+  __syncthreads();
+  m = s.red_f[0];
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s.red_f[w]);
+  const double md = (double)m, cd = 1.4426950408889634074 / (double)Tf;
+  // top-k: the k-th largest key
+  uint32_t kmin = 0;  // the top-k set is the keys >= kmin
+  if (use_k) {
+    uint64_t nh = 0, nl = (uint64_t)tk;
+    uint32_t pre = 0;
+    for (int L = 0; L < 3; ++L) {
+      if (L > 0) {
+        kf_clear(s);
+        const int sh = kf_shift(L);
+        const uint32_t mask = (1u << kf_width(L)) - 1u;
+        kf_pass<BF16>(P, row, [&](float l) {
+          const uint32_t key = kf_key(l);
+          if (kf_under(key, L, pre)) atomicAdd((unsigned long long*)&s.hl[(key >> sh) & mask], 1ull);
+        });
+        __syncthreads();
+      }
+      kf_scan<false>(s, 1 << kf_width(L));
+      kf_search<false>(s, 1 << kf_width(L), nh, nl);
+      const int d = s.digit < 0 ? 0 : s.digit;  // always found: the counts reach k
+      kf_sub(nh, nl, s.ah, s.al);
+      pre = (pre << kf_width(L)) | (uint32_t)d;
+    }
+    kmin = pre;
+  }
+  uint32_t kcut = kmin;
+  double S = 0.0;
+  if (use_p) {
+    uint64_t nh = 0, nl = 0, ch = 0, cl = 0;  // need left; mass above the current prefix
+    uint32_t pre = 0;
+    bool found = true;
+    for (int L = 0; L < 3 && found; ++L) {
+      kf_clear(s);
+      const int sh = kf_shift(L);
+      const uint32_t mask = (1u << kf_width(L)) - 1u;
+      kf_pass<BF16>(P, row, [&](float l) {
+        const uint32_t key = kf_key(l);
+        if (key >= kmin && kf_under(key, L, pre)) {
+          uint64_t h, lo;
+          kf_fix(exp2_f64_nonpos(((double)l - md) * cd, tab), h, lo);
+          const int d = (int)((key >> sh) & mask);
+          atomicAdd((unsigned long long*)&s.hh[d], (unsigned long long)h);
+          atomicAdd((unsigned long long*)&s.hl[d], (unsigned long long)lo);
+        }
+      });
+      __syncthreads();
+      kf_scan<true>(s, 1 << kf_width(L));
+      if (L == 0) {
+        // target = top_p times the set's mass, in fixed point
+        kf_fix((double)tp * kf_float(s.toth, s.totl), nh, nl);
+      }
+      kf_search<true>(s, 1 << kf_width(L), nh, nl);
+      const int d = s.digit;
+      found = d >= 0;
+      if (!found) break;
+      kf_sub(nh, nl, s.ah, s.al);
+      ch += s.ah;
+      cl += s.al;
+      if (L == 2) {
+        ch += s.bh;
+        cl += s.bl;
+      }
+      pre = (pre << kf_width(L)) | (uint32_t)d;
+    }
+    if (found) {
+      kcut = pre;
+      S = kf_float(ch + (cl >> 32), cl & 0xFFFFFFFFull);
+    } else {
+      S = __builtin_nan("");  // only for rows the decision step reports as non-finite
+    }
+  } else {
+    double acc = 0.0;
+    kf_pass<BF16>(P, row, [&](float l) {
+      if (kf_key(l) >= kmin) acc += exp2_f64_nonpos(((double)l - md) * cd, tab);
+    });
+    acc = wave_sum_d(acc);
+    if (lane == 0) s.red_d[wave] = acc;
+    __syncthreads();
+    S = s.red_d[0];
+    for (int w = 1; w < kWaves; ++w) S += s.red_d[w];
+  }
+  if (tid == 0) {
+    P.filt[row].s = S;
+    P.filt[row].tau = kcut ? kf_val(kcut) : -INFINITY;
+  }
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -2042,7 +2414,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 // ===================================================================== host
 struct Shape {
   int SUB, nsub, Q, Qp, G, CPR, C3, G3, CI, CHr;
-  size_t gat_off, part_off, k3_off, r_off, total;
+  size_t gat_off, part_off, k3_off, r_off, f_off, total;
 };
 
 // Work split of a call (a function of the shape alone, so results never
@@ -2080,19 +2452,21 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
   s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
   s.r_off = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
-  s.total = s.r_off + align256(sizeof(double) * (size_t)(bs * (R - 1) * s.CHr));
+  s.f_off = s.r_off + align256(sizeof(double) * (size_t)(bs * (R - 1) * s.CHr));
+  s.total = s.f_off + (races ? align256(sizeof(FiltRec) * (size_t)(bs * R)) : 0);
   return s;
 }
 
 typedef void (*KernelFn)(Params);
 
 struct Kernels {
-  KernelFn k1, k23, fused, kr;
+  KernelFn k1, k23, fused, kr, kf;
 };
 
 template <int MODE, bool BF16>
 static Kernels kernels_for() {
-  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>, kr_kernel<BF16>};
+  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>, kr_kernel<BF16>,
+                 kf_kernel<BF16>};
 }
 
 static Kernels select_kernels(int mode, bool bf16) {
@@ -2132,6 +2506,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.part = (Partial*)(base + S.part_off);
   P.k3 = (K3Rec*)(base + S.k3_off);
   P.rpart = (double*)(base + S.r_off);
+  P.filt = (FiltRec*)(base + S.f_off);
   P.CHr = S.CHr;
   P.SUB = S.SUB;
   P.nsub = S.nsub;
@@ -2146,6 +2521,8 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   if (grid23 + P.G > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   const int64_t gridr = (int64_t)P.bs * (P.k >= 2 ? P.k - 1 : 0) * P.CHr;
   if (gridr > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
+  const bool filtered = P.mode == MODE_CHAIN && (P.top_k != nullptr || P.top_p != nullptr);
+  const int64_t gridf = (int64_t)P.bs * P.R;  // thresholds: one workgroup per row
   // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).
   P.sched = (P.flags & SV_FLAG_FUSED) ? SCHED_FUSED : SCHED_PHASED;
@@ -2163,7 +2540,10 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   if (P.mode == MODE_ROWS) {
     hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
   } else if (P.sched == SCHED_PHASED) {
-    if (!(P.flags & SV_FLAG_DECIDE_ONLY)) hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+    if (!(P.flags & SV_FLAG_DECIDE_ONLY)) {
+      hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+      if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kWG), 0, stream, P);
+    }
     if (!(P.flags & SV_FLAG_STATS_ONLY)) {
       if ((P.flags & SV_FLAG_BLOCK) && P.k >= 2 && P.draft_kind == SV_DRAFT_PROBS)
         hipLaunchKernelGGL(K.kr, dim3((unsigned)gridr), dim3(kWG), 0, stream, P);
@@ -2251,6 +2631,7 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
   if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
   if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
   if ((d->flags & SV_FLAG_BLOCK) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
+  if ((d->top_k != nullptr || d->top_p != nullptr) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
   if (d->logits == nullptr || d->temperature == nullptr || d->seed == nullptr || d->accept_len == nullptr ||
       d->tokens == nullptr)
     return SV_ERR_INVALID_ARGUMENT;
@@ -2283,6 +2664,8 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
   P.status = d->req_status;
   P.p_draft = d->p_draft;
   P.flags = d->flags;
+  P.top_k = d->top_k;
+  P.top_p = d->top_p;
   const Shape S = shape_of(P.bs, P.R, P.V, P.dtype, true);
   return launch(P, S, ws, ws_bytes, (hipStream_t)stream);
 }

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.abi_version() == 1
+    assert sv.abi_version() == 2
     assert sv.status_string(0) == "ok"
     assert "workspace" in sv.status_string(2)
     assert sv.status_string(99) == "unknown status"
@@ -101,6 +101,19 @@ def test_block_rule_needs_the_phased_schedule_and_a_chain():
     assert _call_chain(_chain_desc(flags=sv.FLAG_BLOCK | sv.FLAG_FUSED)) == 3
     d = _tree_desc(flags=sv.FLAG_BLOCK)
     assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 3
+
+
+def test_filtering_needs_the_phased_schedule():
+    fake = 0x300000
+    assert _call_chain(_chain_desc(flags=sv.FLAG_FUSED, top_k=fake)) == 3
+    assert _call_chain(_chain_desc(flags=sv.FLAG_FUSED, top_p=fake)) == 3
+
+
+def test_filtered_workspace_holds_a_record_per_row():
+    # the thresholds take 16 bytes per row of a chain call (rounded to 256)
+    a = sv.chain_workspace_bytes(64, 7, 128256, sv.BF16)
+    b = sv.chain_workspace_bytes(65, 7, 128256, sv.BF16)
+    assert b > a
 
 
 def test_chain_null_descriptor_and_workspace_checks():

@@ -78,20 +78,21 @@ def _compare_p(ref_p, got_p, ref_status, name):
     return float(rel.max()) if rel.size else 0.0
 
 
-def run_chain(inp, dev, flags=0):
+def run_chain(inp, dev, flags=0, top_k=None, top_p=None):
     ref = oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds,
                               draft_probs=inp.draft_probs, onehot=inp.onehot,
-                              rule="block" if flags & sv.FLAG_BLOCK else "standard")
+                              rule="block" if flags & sv.FLAG_BLOCK else "standard", top_k=top_k, top_p=top_p)
     out = sv.verify_chain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev),
                           _t(inp.seeds, dev), draft_probs=None if inp.onehot else _t(inp.draft_probs, dev),
-                          onehot=inp.onehot, flags=flags, return_p_draft=True)
+                          onehot=inp.onehot, flags=flags, return_p_draft=True, top_k=_t(top_k, dev),
+                          top_p=_t(top_p, dev))
     torch.cuda.synchronize()
     return ref, _np(out)
 
 
-def check_chain(inp, dev, flags=0):
-    print(f"[parity] chain {inp.name} flags={flags}", flush=True)
-    ref, got = run_chain(inp, dev, flags)
+def check_chain(inp, dev, flags=0, top_k=None, top_p=None):
+    print(f"[parity] chain {inp.name} flags={flags} filtered={top_k is not None or top_p is not None}", flush=True)
+    ref, got = run_chain(inp, dev, flags, top_k, top_p)
     n_ok, n_ex = _compare(ref, got, inp.name)
     prel = _compare_p(ref["p_draft"], got["p_draft"], ref["status"], inp.name)
     print(f"[parity]   compared {n_ok} requests, exempt {n_ex}, max p rel err {prel:.2e}", flush=True)
@@ -566,3 +567,86 @@ def test_exemption_rate_is_small():
         pytest.skip("no parity comparisons ran")
     print(f"[parity] decisions {STATS['decisions']}, exempt requests {STATS['exempt']}", flush=True)
     assert STATS["exempt"] <= max(2, 1e-4 * STATS["decisions"])
+
+
+# ---------------------------------------------- top-k / top-p filtered target
+def _filters(rng, bs, V):
+    """Per-request top-k / top-p: switched off in several ways, k = 1, small
+    and large k, p from 0.3 to 0.99, and both together."""
+    tk = rng.choice(np.array([0, 0, 1, 3, 20, 300, V, -5], np.int64), size=bs).astype(np.int32)
+    tp = rng.choice(np.array([1.0, 1.0, 0.3, 0.8, 0.95, 0.99, 0.0, np.nan]), size=bs).astype(np.float32)
+    return tk, tp
+
+
+FILTER_SHAPES = [(1, 9, 3, 7), (2, 17, 2, 1000), (3, 12, 4, 4097), (4, 8, 7, 8191), (5, 6, 3, 12345),
+                 (6, 5, 2, 33001)]
+
+
+@pytest.mark.parametrize("seed,bs,k,V", FILTER_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["probs", "onehot"])
+@pytest.mark.parametrize("rule", ["standard", "block"])
+def test_filtered_random_chain_shapes(dev, seed, bs, k, V, dtype, kind, rule):
+    s = seed * 13 + (dtype == "bf16") * 5 + (kind == "onehot") * 2 + (rule == "block") + 900
+    inp = _random_chain(s, bs, k, V, dtype, kind)
+    tk, tp = _filters(np.random.default_rng(s), bs, V)
+    check_chain(inp, dev, flags=sv.FLAG_BLOCK if rule == "block" else 0, top_k=tk, top_p=tp)
+
+
+@pytest.mark.parametrize("rule", ["standard", "block"])
+def test_filtered_bf16_mixed_workload(dev, rule):
+    """The bs 64, k 7, V 128256 bf16 workload, every stochastic request filtered."""
+    inp = workloads.chain_bf16_mixed(0)
+    bs = inp.batch
+    tk = np.where(np.arange(bs) % 3 == 0, 0, 50).astype(np.int32)
+    tp = np.where(np.arange(bs) % 3 == 1, 1.0, 0.9).astype(np.float32)
+    ref, got = check_chain(inp, dev, flags=sv.FLAG_BLOCK if rule == "block" else 0, top_k=tk, top_p=tp)
+    assert (ref["accept_len"][32:] < 7).any()
+
+
+def test_filtered_onehot_workload(dev):
+    inp = workloads.onehot_bf16(0, bs=64)
+    tk = np.full(inp.batch, 40, np.int32)
+    tp = np.full(inp.batch, 0.95, np.float32)
+    check_chain(inp, dev, top_k=tk, top_p=tp)
+
+
+def test_filtered_split_phases(dev):
+    inp = workloads.chain_bf16_mixed(2, bs=16, k=5, V=20000)
+    tk, tp = _filters(np.random.default_rng(3), inp.batch, inp.vocab)
+    for flags in (0, sv.FLAG_BLOCK):
+        _, plain = run_chain(inp, dev, flags=flags, top_k=tk, top_p=tp)
+        pc = sv.PreparedChain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev),
+                              _t(inp.seeds, dev), draft_probs=_t(inp.draft_probs, dev), flags=flags,
+                              top_k=_t(tk, dev), top_p=_t(tp, dev))
+        pc.launch(phase_flag=sv.FLAG_STATS_ONLY)
+        pc.launch(phase_flag=sv.FLAG_DECIDE_ONLY)
+        pc.launch()
+        torch.cuda.synchronize()
+        for key in ("accept_len", "tokens", "status"):
+            np.testing.assert_array_equal(pc.out[key].cpu().numpy(), plain[key], err_msg=f"{flags} {key}")
+
+
+def test_filtered_edge_rows(dev):
+    """Ties at the cut (integer logits), -inf entries counted by top-k, a
+    cut that keeps only the largest group, top-k = 1, and a non-finite row."""
+    rng = np.random.default_rng(77)
+    bs, k, V = 12, 3, 5000
+    l = np.round(rng.standard_normal((bs, k + 1, V)) * 2).astype(np.float32)
+    l[1, :, 100:] = -np.inf                      # 100 finite entries, top-k of 400 counts -inf ones
+    l[5, 2, 7] = np.nan                          # reported non-finite
+    q = workloads._softmax_rows(l[:, :k].reshape(-1, V) * 0.5).reshape(bs, k, V)
+    q = np.nan_to_num(q, nan=0.0).astype(np.float32)
+    ids = np.argmax(l[:, :k] - np.log(-np.log(rng.random((bs, k, V)))), axis=-1).astype(np.int32)
+    ids[1] = rng.integers(0, 100, size=k)
+    temp = np.full(bs, 0.9, np.float32)
+    temp[[3, 9]] = 0.0
+    tk = np.array([5, 400, 1, 7, 0, 3, 1, 0, 2, 5, 4999, 64], np.int32)
+    tp = np.array([1.0, 1.0, 1.0, 0.6, 1e-6, 0.5, 0.9, 0.999, 1.0, 0.7, 0.5, 0.25], np.float32)
+    for kind in ("probs", "onehot"):
+        inp = workloads.ChainInputs(l, ids, q if kind == "probs" else None, temp,
+                                    rng.integers(0, 2**63, size=bs).astype(np.uint64), kind == "onehot",
+                                    f"filter edges {kind}")
+        for flags in (0, sv.FLAG_BLOCK):
+            ref, got = check_chain(inp, dev, flags=flags, top_k=tk, top_p=tp)
+            assert ref["status"][5] == 3
