@@ -51,6 +51,21 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def filter_bytes(inp, top_k, top_p):
+    """Bytes the top-k / top-p thresholds must move at least: one read of
+    every filtered row (rows 0..k_b of each stochastic request, when a filter
+    is on) and its 16-byte record."""
+    bs, R, V = inp.logits.shape
+    k = R - 1
+    if not ((0 < top_k < V) or (0.0 < top_p < 1.0)):
+        return 0
+    bl = inp.logits.dtype.itemsize
+    ids = inp.draft_ids
+    kb = np.where((ids == -1).any(axis=1), np.argmax(ids == -1, axis=1), k) if k else np.zeros(bs, np.int64)
+    stoch = (inp.temperature > 0) & np.isfinite(inp.temperature)
+    return int(((kb + 1) * stoch).sum() * (V * bl + 16))
+
+
 def algorithmic_bytes(inp, accept_len, block=False):
     """Bytes the method must move for one call, from the actual outcomes,
     split by phase.  Row statistics: every read logit row (rows 0..k_b of
@@ -96,16 +111,20 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, seconds: float, rule: str = "standard"):
+def cpu_baseline(inputs, seconds: float, rule: str = "standard", top_k: int = 0, top_p: float = 1.0):
     import oracle
 
     inp = inputs[0]
+    bs = inp.batch
+    filt = {}
+    if top_k or top_p != 1.0:
+        filt = dict(top_k=np.full(bs, top_k, np.int32), top_p=np.full(bs, top_p, np.float32))
     positions = int((inp.draft_ids >= 0).cumprod(axis=1).sum()) if inp.max_draft else 0
     calls = 0
     t0 = time.perf_counter()
     while True:
         oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=inp.draft_probs,
-                            onehot=inp.onehot, rule=rule)
+                            onehot=inp.onehot, rule=rule, **filt)
         calls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -235,6 +254,10 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated over the timed steps")
     ap.add_argument("--rule", choices=["standard", "block"], default="standard",
                     help="acceptance rule of the stochastic requests (block: block verification)")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="top-k filtering of every stochastic request's target (0: off)")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="top-p filtering of every stochastic request's target (1: off)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
@@ -293,11 +316,23 @@ def main():
     block = args.rule == "block"
     if block:
         flags |= sv.FLAG_BLOCK
-    calls = []
+    V0 = inputs[0].vocab
+    filtered = (0 < args.top_k < V0) or (0.0 < args.top_p < 1.0)
+    if filtered and args.schedule == "fused":
+        raise SystemExit("top-k / top-p filtering needs the phased schedule")
+    calls, plain_calls = [], []
     for inp in inputs:
-        calls.append(sv.PreparedChain(to_dev(inp.logits), to_dev(inp.draft_ids), to_dev(inp.temperature),
-                                      to_dev(inp.seeds), draft_probs=to_dev(inp.draft_probs), onehot=inp.onehot,
-                                      flags=flags, workspace=sv.Workspace(1 << 20, dev)))
+        dl, di, dt, ds = to_dev(inp.logits), to_dev(inp.draft_ids), to_dev(inp.temperature), to_dev(inp.seeds)
+        dq = to_dev(inp.draft_probs)
+        fk = fp = None
+        if filtered:
+            fk = torch.full((inp.batch,), args.top_k, dtype=torch.int32, device=dev)
+            fp = torch.full((inp.batch,), args.top_p, dtype=torch.float32, device=dev)
+            # the same call without the filter: its statistics pass alone, for timing
+            plain_calls.append(sv.PreparedChain(dl, di, dt, ds, draft_probs=dq, onehot=inp.onehot, flags=flags,
+                                                workspace=sv.Workspace(1 << 20, dev)))
+        calls.append(sv.PreparedChain(dl, di, dt, ds, draft_probs=dq, onehot=inp.onehot, flags=flags,
+                                      workspace=sv.Workspace(1 << 20, dev), top_k=fk, top_p=fp))
     resident = sum(c.logits.numel() * c.logits.element_size() + (c.q.numel() * 4 if c.q is not None else 0)
                    for c in calls)
     stream = torch.cuda.current_stream(dev)
@@ -308,7 +343,8 @@ def main():
         torch.cuda.synchronize()
         if (c.out["status"] != 0).any():
             raise RuntimeError("a request reported a non-OK status on the benchmark inputs")
-        alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy(), block))
+        alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy(), block)
+                   + (filter_bytes(inp, args.top_k, args.top_p),))
         if args.schedule != "fused":
             # the split phases must reproduce the plain call
             ref = {n: t.clone() for n, t in c.out.items()}
@@ -344,9 +380,14 @@ def main():
     split = args.schedule != "fused"
     S = len(calls)
     groups = max(1, K // S)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(groups)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(groups)]
     torch.cuda.synchronize()
     for g in range(groups):
+        if filtered:
+            # the statistics pass alone (the unfiltered call's first phase)
+            ev[g][3].record(stream)
+            for c in plain_calls:
+                c.launch(phase_flag=sv.FLAG_STATS_ONLY)
         ev[g][0].record(stream)
         if split:
             for c in calls:
@@ -361,17 +402,26 @@ def main():
         ev[g][2].record(stream)
     torch.cuda.synchronize()
     first_ms = np.array([e[0].elapsed_time(e[1]) for e in ev]) / S
+    k1_ms = np.array([e[3].elapsed_time(e[0]) for e in ev]) / S if filtered else None
+    filt_bytes = np.array([a[2] for a in alg] * groups, dtype=np.float64)
     second_ms = np.array([e[1].elapsed_time(e[2]) for e in ev]) / S if split else None
     stats_bytes = np.array([a[0] for a in alg] * groups, dtype=np.float64)
     decide_bytes = np.array([a[1] for a in alg] * groups, dtype=np.float64)
-    if split:
+    if split and filtered:
+        # the first phase is the statistics pass then the thresholds pass;
+        # the roofline covers the statistics pass timed alone
+        kf_ms = first_ms - k1_ms
+        first_ms = k1_ms
+        kernel = "row statistics (k1_kernel)"
+        kbytes = stats_bytes
+    elif split:
         kernel = "row statistics (k1_kernel)"
         kbytes = stats_bytes
     else:
         kernel = "fused verify (fused_kernel)"
         kbytes = stats_bytes + decide_bytes
     achieved = kbytes.sum() / (first_ms.sum() * S * 1e-3) / 1e9
-    traffic = None if block else load_traffic(args.workload, "k1_kernel" if split else "fused_kernel")
+    traffic = None if (block or filtered) else load_traffic(args.workload, "k1_kernel" if split else "fused_kernel")
     line = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
         "value": value,
@@ -386,7 +436,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOADS[args.workload] + (", block verification" if block else ""),
+            "workload": WORKLOADS[args.workload] + (", block verification" if block else "")
+                        + (f", target filtered top-k {args.top_k} top-p {args.top_p}" if filtered else ""),
             "rule": args.rule,
             "batch": int(inputs[0].batch),
             "k": int(inputs[0].max_draft),
@@ -396,6 +447,8 @@ def main():
             "input_sets": len(calls),
             "resident_input_bytes": int(resident),
             "schedule": args.schedule,
+            "top_k": args.top_k,
+            "top_p": args.top_p,
         },
         "roofline": {
             "bound": "hbm",
@@ -418,9 +471,18 @@ def main():
             "launch_us_mean": float(second_ms.mean() * 1e3),
             "achieved": float(decide_bytes.sum() / (second_ms.sum() * S * 1e-3) / 1e9),
         }
+    if split and filtered:
+        line["roofline"]["filter_kernel"] = {
+            "kernel": "top-k / top-p thresholds (kf_kernel)",
+            "algorithmic_bytes_per_launch": float(filt_bytes.mean()),
+            "launch_us_mean": float(kf_ms.mean() * 1e3),
+            "achieved": float(filt_bytes.sum() / (kf_ms.sum() * S * 1e-3) / 1e9),
+            "timing": "first phase minus the statistics pass timed alone",
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds, args.rule)
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds, args.rule,
+                                            args.top_k if filtered else 0, args.top_p if filtered else 1.0)
     print(json.dumps(line), flush=True)
 
 

@@ -2090,30 +2090,35 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
 // ===================================================================== KF
 // Top-k / top-p thresholds (page "投机解码", section
 // "接受规则为什么不改变分布": the target p is the one after the top-k /
-// top-p sampling parameters).  One workgroup per row r <= k_b of a chain
-// request that is stochastic and has a filter on; it writes the row's
-// threshold tau (the kept ids are those with l >= tau) and its kept sum
-// S' = sum over them of exp((l - m)/T).
+// top-p sampling parameters).  One workgroup of 1024 threads per row
+// r <= k_b of a chain request that is stochastic and has a filter on; it
+// writes the row's threshold tau (the kept ids are those with l >= tau) and
+// its kept sum S' = sum over them of exp((l - m)/T), m the row max from the
+// statistics pass's partials.
 //
 // Logits map to 32-bit keys that order like their values (-0 as +0, so
 // equal logits share one key).  A threshold is found by a radix descent
-// over the keys, most significant digit first (11, 11 and 10 bits), one
-// pass over the row per digit with a histogram of the digit in LDS:
-//  - top-k counts the keys under the prefix found so far; the k-th largest
-//    key lies in the first bin, from the top, at which the count of keys at
-//    or above it reaches k;
-//  - top-p adds the masses e = 2^((l - m) log2(e)/T) of the top-k set's
-//    keys in 96-bit fixed point (two integer parts of e 2^32 and of its
-//    fraction 2^32: exact up to 2^-64 per id, and independent of the order
-//    of the atomic adds); the cut is the first group of equal logits, from
-//    the top, at which the mass at or above it reaches top_p times the set's
-//    mass (the first digit's histogram total).
-// The kept sum is the fixed-point mass at or above the cut (top-p), or an
-// fp64 sum in a fixed order (top-k alone).  Passes after the first re-read
-// the row from L2 / MALL; the work per id is a key, a compare and an LDS
-// atomic, plus an fp64 exponential in the mass passes.
+// over the keys, most significant digit first (11, 11 and 10 bits), with a
+// histogram of the digit in LDS per level:
+//  - top-k counts keys; the k-th largest key lies in the first bin, from the
+//    top, at which the count of keys at or above it reaches k;
+//  - top-p adds the masses e = 2^((l - m) log2(e)/T) of the top-k set's keys
+//    in 96-bit fixed point (integer parts of e 2^32 and of its fraction
+//    2^32: exact up to 2^-64 per id, and independent of the order of the
+//    atomic adds); the cut is the first group of equal logits, from the top,
+//    at which the mass at or above it reaches top_p times the set's mass.
+// Only the first level reads the row from memory: a second pass copies the
+// keys that can still matter into LDS (top-k: every key in or above the
+// first level's bin, which holds the whole top-k set; top-p alone: the keys
+// of the bin the cut falls in, the mass above it being known), and the
+// descent finishes there.  When those keys exceed the LDS list, every level
+// reads the row again.  The kept sum is the fixed-point mass at or above the
+// cut (exact up to the same truncation, whatever the order).
+constexpr int kKF = 1024;                // threads of a thresholds workgroup
+constexpr int kKFWaves = kKF / 64;
 constexpr int kKFBins = 2048;
-constexpr int kKFUnroll = 4;  // groups of 4 ids whose loads a thread issues together
+constexpr int kKFList = 8192;            // keys the LDS list holds
+constexpr int kKFUnroll = 4;             // groups of 4 ids whose loads a thread issues together
 
 __device__ __forceinline__ uint32_t kf_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -2159,30 +2164,36 @@ __device__ __forceinline__ double kf_float(uint64_t h, uint64_t l) {
 }
 
 struct KFShared {
-  uint64_t hh[kKFBins];  // per bin: integer parts of e 2^32 (top-p)
-  uint64_t hl[kKFBins];  // per bin: counts (top-k) or fraction parts 2^32 (top-p)
-  uint64_t th[kWG], tl[kWG];  // per thread: the sums of its bins
-  uint64_t xh[kWG], xl[kWG];  // per thread: the sums of the bins above its own
-  uint64_t toth, totl;        // the histogram's total
-  uint64_t ah, al;            // found bin: the sum of the bins above it
-  uint64_t bh, bl;            // found bin: its own sum
-  int digit;                  // found bin (-1: none)
-  float red_f[kWaves];
-  double red_d[kWaves];
+  uint64_t hh[kKFBins];   // per bin: integer parts of e 2^32 (top-p)
+  uint64_t hl[kKFBins];   // per bin: counts (top-k) or fraction parts 2^32 (top-p)
+  uint32_t list[kKFList];
+  int nlist;
+  uint64_t wh[kKFWaves], wl[kKFWaves];  // per wave: sums of its threads' bins
+  uint64_t toth, totl;    // the histogram's total
+  uint64_t ah, al;        // found bin: the sum of the bins above it
+  uint64_t bh, bl;        // found bin: its own sum
+  int digit;              // found bin (-1: none)
 };
 
-// One pass over row `row`: f(l) for every logit, each thread on groups of 4
-// consecutive ids, kKFUnroll groups' loads issued together.
-template <bool BF16, typename F>
-__device__ __forceinline__ void kf_pass(const Params& P, int64_t row, F&& f) {
-  const int V = P.V, tid = threadIdx.x;
+// One pass over the row's logits (LIST: over the keys in the LDS list):
+// f(l) for each, in groups of 4 consecutive ids per thread, kKFUnroll
+// groups' loads issued together.
+template <bool BF16, bool LIST, typename F>
+__device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFShared& s, F&& f) {
+  const int tid = threadIdx.x;
+  if (LIST) {
+    const int n = min(s.nlist, kKFList);
+    for (int i = tid; i < n; i += kKF) f(kf_val(s.list[i]));
+    return;
+  }
+  const int V = P.V;
   const int64_t off = row * P.lstride;
 #pragma unroll 1
-  for (int base = 0; base < V; base += 4 * kWG * kKFUnroll) {
+  for (int base = 0; base < V; base += 4 * kKF * kKFUnroll) {
     float l[kKFUnroll][4];
 #pragma unroll
     for (int g = 0; g < kKFUnroll; ++g) {
-      const int y0 = base + 4 * (g * kWG + tid);
+      const int y0 = base + 4 * (g * kKF + tid);
       if (P.aligned && y0 + 4 <= V) {
         if (BF16) {
           const u32x2 w = *(const u32x2*)((const uint16_t*)P.logits + off + y0);
@@ -2206,72 +2217,60 @@ __device__ __forceinline__ void kf_pass(const Params& P, int64_t row, F&& f) {
     for (int g = 0; g < kKFUnroll; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (base + 4 * (g * kWG + tid) + i < V) f(l[g][i]);
+        if (base + 4 * (g * kKF + tid) + i < V) f(l[g][i]);
   }
 }
 
 __device__ __forceinline__ void kf_clear(KFShared& s) {
-  for (int i = threadIdx.x; i < kKFBins; i += kWG) {
+  for (int i = threadIdx.x; i < kKFBins; i += kKF) {
     s.hh[i] = 0;
     s.hl[i] = 0;
   }
   __syncthreads();
 }
 
-// Sums of a complete histogram of `nbins` bins (every thread calls it, after
-// the barrier that ends the histogram's pass): each thread's bins, the sums
-// of the bins above each thread's, and the total.
+// The first bin from the top of a complete histogram of `nbins` bins at
+// which the sum of the bins at or above it reaches (nh, nl) (a normalised
+// fixed-point value, or a count in nl; with frac > 0 the need is frac times
+// the histogram's total instead): s.digit, s.ah/al (bins above), s.bh/bl
+// (the bin) and s.toth/totl.  Every thread calls it after the barrier that
+// ends the histogram's pass; it ends with a barrier.  Thread t owns bins
+// [t per, (t + 1) per); the sums of the bins above a thread's come from a
+// suffix scan within its wave and the totals of the waves above.
 template <bool MASS>
-__device__ __forceinline__ void kf_scan(KFShared& s, int nbins) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int per = nbins / kWG;
+__device__ __forceinline__ void kf_find(KFShared& s, int nbins, uint64_t& nh, uint64_t& nl, float frac) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = nbins / kKF;
   uint64_t sh = 0, sl = 0;
   for (int j = 0; j < per; ++j) {
     if (MASS) sh += s.hh[tid * per + j];
     sl += s.hl[tid * per + j];
   }
-  s.th[tid] = sh;
-  s.tl[tid] = sl;
-  if (tid == 0) s.digit = -1;
-  __syncthreads();
-  if (tid < 64) {
-    uint64_t gh = 0, gl = 0;
-    for (int j = 0; j < kWG / 64; ++j) {
-      gh += s.th[(kWG / 64) * lane + j];
-      gl += s.tl[(kWG / 64) * lane + j];
-    }
-    uint64_t ih = gh, il = gl;  // sums over lanes >= lane
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t vh = __shfl_down(ih, o, 64), vl = __shfl_down(il, o, 64);
-      if (lane + o < 64) {
-        ih += vh;
-        il += vl;
-      }
-    }
-    if (lane == 0) {
-      s.toth = ih;
-      s.totl = il;
-    }
-    uint64_t rh = ih - gh, rl = il - gl;
-    for (int j = kWG / 64 - 1; j >= 0; --j) {
-      const int t = (kWG / 64) * lane + j;
-      s.xh[t] = rh;
-      s.xl[t] = rl;
-      rh += s.th[t];
-      rl += s.tl[t];
+  uint64_t ih = sh, il = sl;  // sums over the wave's lanes >= lane
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t vh = __shfl_down(ih, o, 64), vl = __shfl_down(il, o, 64);
+    if (lane + o < 64) {
+      ih += vh;
+      il += vl;
     }
   }
+  if (lane == 0) {
+    s.wh[wave] = ih;
+    s.wl[wave] = il;
+  }
+  if (tid == 0) s.digit = -1;
   __syncthreads();
-}
-
-// The first bin from the top at which the sum of the bins at or above it
-// reaches (nh, nl) (a normalised fixed-point value, or a count in nl), after
-// kf_scan: s.digit, s.ah/al (bins above) and s.bh/bl (the bin itself).
-template <bool MASS>
-__device__ __forceinline__ void kf_search(KFShared& s, int nbins, uint64_t nh, uint64_t nl) {
-  const int tid = threadIdx.x;
-  const int per = nbins / kWG;
-  uint64_t rh = s.xh[tid], rl = s.xl[tid];
+  uint64_t rh = ih - sh, rl = il - sl, th = 0, tl = 0;
+  for (int w = 0; w < kKFWaves; ++w) {
+    const uint64_t a = s.wh[w], b = s.wl[w];
+    th += a;
+    tl += b;
+    if (w > wave) {
+      rh += a;
+      rl += b;
+    }
+  }
+  if (frac > 0.f) kf_fix((double)frac * kf_float(th, tl), nh, nl);
   for (int j = per - 1; j >= 0; --j) {
     const uint64_t ph = rh, pl = rl;
     const uint64_t bh = MASS ? s.hh[tid * per + j] : 0, bl = s.hl[tid * per + j];
@@ -2285,13 +2284,93 @@ __device__ __forceinline__ void kf_search(KFShared& s, int nbins, uint64_t nh, u
       s.bl = bl;
     }
   }
+  if (tid == 0) {
+    s.toth = th;
+    s.totl = tl;
+  }
+  __syncthreads();
+}
+
+// Mass of a key's logit, in fixed point.
+__device__ __forceinline__ void kf_mass(float l, double md, double cd, const double* tab, uint64_t& h, uint64_t& lo) {
+  kf_fix(exp2_f64_nonpos(((double)l - md) * cd, tab), h, lo);
+}
+
+// Radix descent over the keys >= kmin, from memory or from the LDS list
+// (LIST): the count descent (MASS false)
+// finds the key at which the count from the top reaches (nh, nl); the mass
+// descent finds the group at which the mass from the top reaches its need
+// (frac > 0: frac times the set's mass), adding the masses above the found
+// group, and the group's own, to (ch, cl).  Returns the key (0: not found).
+template <bool BF16, bool LIST, bool MASS>
+__device__ __forceinline__ uint32_t kf_descent(const Params& P, int64_t row, KFShared& s, const double* tab, double md, double cd,
+                               uint32_t kmin, uint64_t nh, uint64_t nl, float frac, uint64_t& ch, uint64_t& cl) {
+  uint32_t pre = 0;
+  for (int L = 0; L < 3; ++L) {
+    kf_clear(s);
+    const int sh = kf_shift(L);
+    const uint32_t mask = (1u << kf_width(L)) - 1u;
+    kf_pass<BF16, LIST>(P, row, s, [&](float l) {
+      const uint32_t key = kf_key(l);
+      if (key >= kmin && kf_under(key, L, pre)) {
+        const int d = (int)((key >> sh) & mask);
+        if (MASS) {
+          uint64_t h, lo;
+          kf_mass(l, md, cd, tab, h, lo);
+          atomicAdd((unsigned long long*)&s.hh[d], (unsigned long long)h);
+          atomicAdd((unsigned long long*)&s.hl[d], (unsigned long long)lo);
+        } else {
+          atomicAdd((unsigned long long*)&s.hl[d], 1ull);
+        }
+      }
+    });
+    __syncthreads();
+    kf_find<MASS>(s, 1 << kf_width(L), nh, nl, L == 0 ? frac : 0.f);
+    const int d = s.digit;
+    if (d < 0) return 0;  // only for rows the decision step reports as non-finite
+    kf_sub(nh, nl, s.ah, s.al);
+    ch += s.ah;
+    cl += s.al;
+    if (L == 2) {
+      ch += s.bh;
+      cl += s.bl;
+    }
+    pre = (pre << kf_width(L)) | (uint32_t)d;
+  }
+  return pre;
+}
+
+// Copy the row's keys with kf_key(l) in [lo, hi] into the LDS list (one
+// atomic per wave for the positions).
+template <bool BF16>
+__device__ __forceinline__ void kf_collect(const Params& P, int64_t row, KFShared& s, uint32_t lo, uint32_t hi) {
+  if (threadIdx.x == 0) s.nlist = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  kf_pass<BF16, false>(P, row, s, [&](float l) {
+    const uint32_t key = kf_key(l);
+    const bool take = key >= lo && key <= hi;
+    const uint64_t mask = __ballot(take);
+    if (mask) {
+      const int leader = __builtin_ctzll(mask);
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&s.nlist, __popcll(mask));
+      base = __shfl(base, leader, 64);
+      if (take) {
+        const int i = base + __popcll(mask & ((1ull << lane) - 1ull));
+        if (i < kKFList) s.list[i] = key;
+      }
+    }
+  });
   __syncthreads();
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kWG) void kf_kernel(Params P) {
+__global__ __launch_bounds__(kKF) void kf_kernel(Params P) {
   __shared__ KFShared s;
   __shared__ double tab[64];  // 2^(j/64)
+  __shared__ float red_m[kKFWaves];
+  __shared__ uint64_t red_h[kKFWaves], red_l[kKFWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = (int)(blockIdx.x / (uint32_t)P.R);
   const int r = (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.R);
@@ -2303,99 +2382,111 @@ __global__ __launch_bounds__(kWG) void kf_kernel(Params P) {
   const float tp = P.top_p ? P.top_p[b] : 1.f;
   const bool use_k = tk > 0 && tk < P.V, use_p = tp > 0.f && tp < 1.f;
   const int64_t row = (int64_t)b * P.R + r;
-  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
-  kf_clear(s);
-  // the row max, and the first digit's counts for top-k
+  // the row max, from the statistics pass's partials
   float m = -INFINITY;
-  kf_pass<BF16>(P, row, [&](float l) {
-    m = fmaxf(m, l);
-    if (use_k) atomicAdd((unsigned long long*)&s.hl[kf_key(l) >> 21], 1ull);
-  });
-  m = wave_max(m);
-  if (lane == 0) s.red_f[wave] = m;
-  __syncthreads();
-  m = s.red_f[0];
-  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s.red_f[w]);
-  const double md = (double)m, cd = 1.4426950408889634074 / (double)Tf;
-  // top-k: the k-th largest key
-  uint32_t kmin = 0;  // the top-k set is the keys >= kmin
+  if (tid < P.Q) m = __uint_as_float((uint32_t)P.part[row * P.CPR + tid].m_amax);
+  if (tid < 64) {
+    m = wave_max(m);
+    if (lane == 0) red_m[0] = m;
+    tab[tid] = exp2((double)tid / 64.0);
+  }
+  kf_clear(s);
+  const double md = (double)red_m[0], cd = 1.4426950408889634074 / (double)Tf;
+  // first level, from memory: top-k counts, or top-p masses
+  uint64_t ch = 0, cl = 0;  // mass above the current prefix (top-p)
+  uint64_t nh = 0, nl = 0;
+  bool listed = false;
+  uint32_t kmin = 0;
   if (use_k) {
-    uint64_t nh = 0, nl = (uint64_t)tk;
-    uint32_t pre = 0;
-    for (int L = 0; L < 3; ++L) {
-      if (L > 0) {
-        kf_clear(s);
-        const int sh = kf_shift(L);
-        const uint32_t mask = (1u << kf_width(L)) - 1u;
-        kf_pass<BF16>(P, row, [&](float l) {
-          const uint32_t key = kf_key(l);
-          if (kf_under(key, L, pre)) atomicAdd((unsigned long long*)&s.hl[(key >> sh) & mask], 1ull);
-        });
-        __syncthreads();
-      }
-      kf_scan<false>(s, 1 << kf_width(L));
-      kf_search<false>(s, 1 << kf_width(L), nh, nl);
-      const int d = s.digit < 0 ? 0 : s.digit;  // always found: the counts reach k
-      kf_sub(nh, nl, s.ah, s.al);
-      pre = (pre << kf_width(L)) | (uint32_t)d;
+    kf_pass<BF16, false>(P, row, s, [&](float l) { atomicAdd((unsigned long long*)&s.hl[kf_key(l) >> 21], 1ull); });
+    __syncthreads();
+    nl = (uint64_t)tk;
+    kf_find<false>(s, kKFBins, nh, nl, 0.f);
+    const int d = s.digit < 0 ? 0 : s.digit;  // always found: the counts reach k
+    // every key in or above bin d: the top-k set and the rest of bin d
+    const uint64_t n = (s.ah + s.al) + (s.bh + s.bl);
+    if (n <= (uint64_t)kKFList) {
+      kf_collect<BF16>(P, row, s, (uint32_t)d << 21, 0xFFFFFFFFu);
+      listed = true;
+      kmin = kf_descent<BF16, true, false>(P, row, s, tab, md, cd, 0u, 0, (uint64_t)tk, 0.f, ch, cl);
+    } else {
+      kmin = kf_descent<BF16, false, false>(P, row, s, tab, md, cd, 0u, 0, (uint64_t)tk, 0.f, ch, cl);
     }
-    kmin = pre;
+    ch = cl = 0;
   }
   uint32_t kcut = kmin;
-  double S = 0.0;
+  double S;
   if (use_p) {
-    uint64_t nh = 0, nl = 0, ch = 0, cl = 0;  // need left; mass above the current prefix
-    uint32_t pre = 0;
-    bool found = true;
-    for (int L = 0; L < 3 && found; ++L) {
-      kf_clear(s);
-      const int sh = kf_shift(L);
-      const uint32_t mask = (1u << kf_width(L)) - 1u;
-      kf_pass<BF16>(P, row, [&](float l) {
+    uint32_t cut;
+    if (use_k) {
+      cut = listed ? kf_descent<BF16, true, true>(P, row, s, tab, md, cd, kmin, 0, 0, tp, ch, cl)
+                   : kf_descent<BF16, false, true>(P, row, s, tab, md, cd, kmin, 0, 0, tp, ch, cl);
+    } else {
+      // first level of the masses from memory, with each bin's count (in
+      // the list's first entries, free until the list is filled)
+      for (int i = tid; i < kKFBins; i += kKF) s.list[i] = 0;
+      __syncthreads();
+      kf_pass<BF16, false>(P, row, s, [&](float l) {
         const uint32_t key = kf_key(l);
-        if (key >= kmin && kf_under(key, L, pre)) {
-          uint64_t h, lo;
-          kf_fix(exp2_f64_nonpos(((double)l - md) * cd, tab), h, lo);
-          const int d = (int)((key >> sh) & mask);
-          atomicAdd((unsigned long long*)&s.hh[d], (unsigned long long)h);
-          atomicAdd((unsigned long long*)&s.hl[d], (unsigned long long)lo);
-        }
+        uint64_t h, lo;
+        kf_mass(l, md, cd, tab, h, lo);
+        atomicAdd((unsigned long long*)&s.hh[key >> 21], (unsigned long long)h);
+        atomicAdd((unsigned long long*)&s.hl[key >> 21], (unsigned long long)lo);
+        atomicAdd(&s.list[key >> 21], 1u);
       });
       __syncthreads();
-      kf_scan<true>(s, 1 << kf_width(L));
-      if (L == 0) {
-        // target = top_p times the set's mass, in fixed point
-        kf_fix((double)tp * kf_float(s.toth, s.totl), nh, nl);
-      }
-      kf_search<true>(s, 1 << kf_width(L), nh, nl);
+      uint32_t bin_count = 0;
+      kf_find<true>(s, kKFBins, nh, nl, tp);
       const int d = s.digit;
-      found = d >= 0;
-      if (!found) break;
-      kf_sub(nh, nl, s.ah, s.al);
-      ch += s.ah;
-      cl += s.al;
-      if (L == 2) {
-        ch += s.bh;
-        cl += s.bl;
+      if (d >= 0) bin_count = s.list[d];
+      __syncthreads();
+      if (d < 0) {
+        cut = 0;
+      } else if (bin_count <= (uint32_t)kKFList) {
+        kf_sub(nh, nl, s.ah, s.al);
+        ch = s.ah;
+        cl = s.al;
+        kf_collect<BF16>(P, row, s, (uint32_t)d << 21, ((uint32_t)d << 21) | 0x1FFFFFu);
+        // the need left within the bin, as a plain need (frac 0)
+        cut = kf_descent<BF16, true, true>(P, row, s, tab, md, cd, 0u, nh, nl, 0.f, ch, cl);
+      } else {
+        cut = kf_descent<BF16, false, true>(P, row, s, tab, md, cd, 0u, 0, 0, tp, ch, cl);
       }
-      pre = (pre << kf_width(L)) | (uint32_t)d;
     }
-    if (found) {
-      kcut = pre;
+    if (cut) {
+      kcut = cut;
       S = kf_float(ch + (cl >> 32), cl & 0xFFFFFFFFull);
     } else {
       S = __builtin_nan("");  // only for rows the decision step reports as non-finite
     }
   } else {
-    double acc = 0.0;
-    kf_pass<BF16>(P, row, [&](float l) {
-      if (kf_key(l) >= kmin) acc += exp2_f64_nonpos(((double)l - md) * cd, tab);
-    });
-    acc = wave_sum_d(acc);
-    if (lane == 0) s.red_d[wave] = acc;
+    // top-k alone: the fixed-point mass of the keys >= kmin
+    uint64_t th = 0, tl = 0;
+    auto add = [&](float l) {
+      if (kf_key(l) >= kmin) {
+        uint64_t h, lo;
+        kf_mass(l, md, cd, tab, h, lo);
+        th += h;
+        tl += lo;
+      }
+    };
+    if (listed) kf_pass<BF16, true>(P, row, s, add);
+    else kf_pass<BF16, false>(P, row, s, add);
+    for (int o = 32; o > 0; o >>= 1) {
+      th += __shfl_xor(th, o, 64);
+      tl += __shfl_xor(tl, o, 64);
+    }
+    if (lane == 0) {
+      red_h[wave] = th;
+      red_l[wave] = tl;
+    }
     __syncthreads();
-    S = s.red_d[0];
-    for (int w = 1; w < kWaves; ++w) S += s.red_d[w];
+    th = tl = 0;
+    for (int w = 0; w < kKFWaves; ++w) {
+      th += red_h[w];
+      tl += red_l[w];
+    }
+    S = kf_float(th + (tl >> 32), tl & 0xFFFFFFFFull);
   }
   if (tid == 0) {
     P.filt[row].s = S;
@@ -2542,7 +2633,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   } else if (P.sched == SCHED_PHASED) {
     if (!(P.flags & SV_FLAG_DECIDE_ONLY)) {
       hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
-      if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kWG), 0, stream, P);
+      if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kKF), 0, stream, P);
     }
     if (!(P.flags & SV_FLAG_STATS_ONLY)) {
       if ((P.flags & SV_FLAG_BLOCK) && P.k >= 2 && P.draft_kind == SV_DRAFT_PROBS)

@@ -650,3 +650,24 @@ def test_filtered_edge_rows(dev):
         for flags in (0, sv.FLAG_BLOCK):
             ref, got = check_chain(inp, dev, flags=flags, top_k=tk, top_p=tp)
             assert ref["status"][5] == 3
+
+
+def test_filtered_crowded_bins(dev):
+    """Rows whose logits take a handful of values, so one first-level bin
+    holds more keys than the thresholds pass keeps in LDS (it then reads the
+    row once per level), beside rows where the list suffices."""
+    rng = np.random.default_rng(91)
+    bs, k, V = 8, 2, 40000
+    vals = np.array([-1.0, 0.0, 0.5, 0.75, 1.0, 2.0], np.float32)
+    l = vals[rng.integers(0, len(vals), size=(bs, k + 1, V))]
+    l[::2] += (rng.standard_normal((bs // 2, k + 1, V)) * 3).astype(np.float32)  # spread rows
+    q = workloads._softmax_rows(l[:, :k].reshape(-1, V) + rng.standard_normal((bs * k, V)).astype(np.float32)
+                                ).reshape(bs, k, V)
+    ids = workloads._sample_rows(rng, q.reshape(-1, V)).reshape(bs, k).astype(np.int32)
+    temp = np.full(bs, 1.0, np.float32)
+    tk = np.array([5, 5, 20000, 20000, 0, 0, 9000, 30], np.int32)
+    tp = np.array([1.0, 0.5, 1.0, 0.97, 0.5, 0.97, 0.8, 0.9], np.float32)
+    inp = workloads.ChainInputs(l, ids, q, temp, rng.integers(0, 2**63, size=bs).astype(np.uint64), False,
+                                "filter crowded bins")
+    for flags in (0, sv.FLAG_BLOCK):
+        check_chain(inp, dev, flags=flags, top_k=tk, top_p=tp)
