@@ -1207,6 +1207,7 @@ template <bool BF16, int KIND>
 __device__ __forceinline__ void weight_bounds(const Params& P, const Job& J, int c, float* whi, float* wlo) {
   const int tid = threadIdx.x;
   const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
+  const float tau = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(J.tau)));
   const int y_base = c * kK3Chunk;
   const int64_t lrow = (int64_t)J.row * P.lstride;
   const int64_t qrow = (int64_t)J.qrow * P.qstride;
@@ -1243,8 +1244,9 @@ __device__ __forceinline__ void weight_bounds(const Params& P, const Job& J, int
 #pragma unroll
       for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
+    if (tau > -INFINITY)  // a scalar branch: top-k / top-p cut ids count as -inf
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l[i] = l[i] < J.tau ? -INFINITY : l[i];  // cut by top-k / top-p
+      for (int i = 0; i < 4; ++i) l[i] = l[i] < tau ? -INFINITY : l[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) q[i] = 0.f;
     if (KIND == JOB_RESID) {
@@ -1384,6 +1386,7 @@ __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, 
                                                  const ChunkRaw<BF16>* r = nullptr) {
   const int tid = threadIdx.x;
   const float m = J.m, chi = J.c_hi, clo = J.c_lo, inv_s = J.inv_s;
+  const float tau = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(J.tau)));
   const int y_base = c * kK3Chunk;
   const int64_t lrow = (int64_t)J.row * P.lstride;
   const int64_t qrow = (int64_t)J.qrow * P.qstride;
@@ -1423,8 +1426,9 @@ __device__ __forceinline__ void chunk_sum_bounds(const Params& P, const Job& J, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) l[i] = (y0 + i < P.V) ? load_logit<BF16>(P, J.row, y0 + i) : -INFINITY;
     }
+    if (tau > -INFINITY)  // a scalar branch: top-k / top-p cut ids count as -inf
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l[i] = l[i] < J.tau ? -INFINITY : l[i];  // cut by top-k / top-p
+      for (int i = 0; i < 4; ++i) l[i] = l[i] < tau ? -INFINITY : l[i];
     if (KIND == JOB_RESID) {
       if (r != nullptr || (full && P.q_aligned)) {
         const u32x4 w = (r != nullptr) ? r->q[g] : __builtin_nontemporal_load((const u32x4*)(P.q + qrow + y0));
@@ -2118,7 +2122,7 @@ constexpr int kKF = 1024;                // threads of a thresholds workgroup
 constexpr int kKFWaves = kKF / 64;
 constexpr int kKFBins = 2048;
 constexpr int kKFList = 8192;            // keys the LDS list holds
-constexpr int kKFUnroll = 4;             // groups of 4 ids whose loads a thread issues together
+constexpr int kKFUnroll = 8;             // groups of 4 ids whose loads a thread issues together
 
 __device__ __forceinline__ uint32_t kf_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -2176,8 +2180,48 @@ struct KFShared {
 };
 
 // One pass over the row's logits (LIST: over the keys in the LDS list):
-// f(l) for each, in groups of 4 consecutive ids per thread, kKFUnroll
-// groups' loads issued together.
+// f(l) for each.  From memory each thread takes groups of 4 consecutive ids,
+// kKFUnroll groups per step; in rows of whole aligned groups the next
+// step's loads are in flight while the current step is processed (loads
+// past the row re-read its first group and are not processed, so every load
+// is unconditional).
+template <bool BF16>
+struct KFRaw {
+  typename std::conditional<BF16, u32x2, u32x4>::type v[kKFUnroll];
+};
+template <bool BF16>
+__device__ __forceinline__ void kf_issue(const Params& P, int64_t off, int base, KFRaw<BF16>& r) {
+#pragma unroll
+  for (int g = 0; g < kKFUnroll; ++g) {
+    int y0 = base + 4 * (g * kKF + (int)threadIdx.x);
+    y0 = y0 < P.V ? y0 : 0;
+    if constexpr (BF16) r.v[g] = *(const u32x2*)((const uint16_t*)P.logits + off + y0);
+    else r.v[g] = *(const u32x4*)((const float*)P.logits + off + y0);
+  }
+}
+template <bool BF16, typename F>
+__device__ __forceinline__ void kf_fold(const KFRaw<BF16>& r, int base, int V, F&& f) {
+#pragma unroll
+  for (int g = 0; g < kKFUnroll; ++g) {
+    const int y0 = base + 4 * (g * kKF + (int)threadIdx.x);
+    if (y0 < V) {
+      float l[4];
+      if constexpr (BF16) {
+        l[0] = __uint_as_float(r.v[g].x << 16);
+        l[1] = __uint_as_float(r.v[g].x & 0xffff0000u);
+        l[2] = __uint_as_float(r.v[g].y << 16);
+        l[3] = __uint_as_float(r.v[g].y & 0xffff0000u);
+      } else {
+        l[0] = __uint_as_float(r.v[g].x);
+        l[1] = __uint_as_float(r.v[g].y);
+        l[2] = __uint_as_float(r.v[g].z);
+        l[3] = __uint_as_float(r.v[g].w);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f(l[i]);
+    }
+  }
+}
 template <bool BF16, bool LIST, typename F>
 __device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFShared& s, F&& f) {
   const int tid = threadIdx.x;
@@ -2188,30 +2232,31 @@ __device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFSh
   }
   const int V = P.V;
   const int64_t off = row * P.lstride;
+  constexpr int step = 4 * kKF * kKFUnroll;
+  if (P.aligned && (V & 3) == 0) {
+    KFRaw<BF16> a, b;
+    kf_issue<BF16>(P, off, 0, a);
 #pragma unroll 1
-  for (int base = 0; base < V; base += 4 * kKF * kKFUnroll) {
+    for (int base = 0;;) {
+      kf_issue<BF16>(P, off, base + step, b);
+      kf_fold<BF16>(a, base, V, f);
+      base += step;
+      if (base >= V) break;
+      kf_issue<BF16>(P, off, base + step, a);
+      kf_fold<BF16>(b, base, V, f);
+      base += step;
+      if (base >= V) break;
+    }
+    return;
+  }
+#pragma unroll 1
+  for (int base = 0; base < V; base += step) {
     float l[kKFUnroll][4];
 #pragma unroll
     for (int g = 0; g < kKFUnroll; ++g) {
       const int y0 = base + 4 * (g * kKF + tid);
-      if (P.aligned && y0 + 4 <= V) {
-        if (BF16) {
-          const u32x2 w = *(const u32x2*)((const uint16_t*)P.logits + off + y0);
-          l[g][0] = __uint_as_float(w.x << 16);
-          l[g][1] = __uint_as_float(w.x & 0xffff0000u);
-          l[g][2] = __uint_as_float(w.y << 16);
-          l[g][3] = __uint_as_float(w.y & 0xffff0000u);
-        } else {
-          const u32x4 w = *(const u32x4*)((const float*)P.logits + off + y0);
-          l[g][0] = __uint_as_float(w.x);
-          l[g][1] = __uint_as_float(w.y);
-          l[g][2] = __uint_as_float(w.z);
-          l[g][3] = __uint_as_float(w.w);
-        }
-      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l[g][i] = (y0 + i < V) ? load_logit<BF16>(P, row, y0 + i) : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) l[g][i] = (y0 + i < V) ? load_logit<BF16>(P, row, y0 + i) : 0.f;
     }
 #pragma unroll
     for (int g = 0; g < kKFUnroll; ++g)
@@ -2398,7 +2443,12 @@ __global__ __launch_bounds__(kKF) void kf_kernel(Params P) {
   bool listed = false;
   uint32_t kmin = 0;
   if (use_k) {
-    kf_pass<BF16, false>(P, row, s, [&](float l) { atomicAdd((unsigned long long*)&s.hl[kf_key(l) >> 21], 1ull); });
+    // 32-bit counters (in the list's first entries) for the pass, then widened
+    for (int i = tid; i < kKFBins; i += kKF) s.list[i] = 0;
+    __syncthreads();
+    kf_pass<BF16, false>(P, row, s, [&](float l) { atomicAdd(&s.list[kf_key(l) >> 21], 1u); });
+    __syncthreads();
+    for (int i = tid; i < kKFBins; i += kKF) s.hl[i] = s.list[i];
     __syncthreads();
     nl = (uint64_t)tk;
     kf_find<false>(s, kKFBins, nh, nl, 0.f);
