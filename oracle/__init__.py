@@ -69,7 +69,7 @@ class _TreeArgs(ctypes.Structure):
                 ("node_tokens", _P), ("parent", _P), ("temperature", _P), ("seed", _P),
                 ("accept_len", _P), ("accept_path", _P), ("tokens", _P), ("req_status", _P),
                 ("min_margin", _P), ("n_decisions", _P),
-                ("threshold_acc", _D), ("threshold_single", _D)]
+                ("threshold_acc", _D), ("threshold_single", _D), ("top_k", _P), ("top_p", _P)]
 
 
 _lib = None
@@ -216,10 +216,12 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
     return out
 
 
-def verify_tree(logits, node_tokens, parent, temperature, seeds, threshold_acc=1.0, threshold_single=1.0):
+def verify_tree(logits, node_tokens, parent, temperature, seeds, threshold_acc=1.0, threshold_single=1.0,
+                top_k=None, top_p=None):
     """Target-only tree verification.
 
-    logits: [bs, N, V]; node_tokens, parent: [bs, N] int32.
+    logits: [bs, N, V]; node_tokens, parent: [bs, N] int32; top_k [bs] int32 /
+    top_p [bs] float32 (or None) filter the stochastic requests' target rows.
     threshold_acc / threshold_single other than 1.0 give the lossy relaxed
     rule and exist only for the statistical tests' negative controls.
     """
@@ -232,10 +234,12 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, threshold_acc=1
     out = dict(accept_len=np.empty(bs, np.int32), accept_path=np.empty((bs, N), np.int32),
                tokens=np.empty((bs, N), np.int32), status=np.empty(bs, np.int32),
                min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32))
+    tk = None if top_k is None else np.ascontiguousarray(np.asarray(top_k, np.int32).reshape(bs))
+    tp = None if top_p is None else np.ascontiguousarray(np.asarray(top_p, np.float32).reshape(bs))
     a = _TreeArgs(bs, N, V, code, _ptr(x), V, _ptr(nt), _ptr(par), _ptr(temp), _ptr(sd),
                   _ptr(out["accept_len"]), _ptr(out["accept_path"]), _ptr(out["tokens"]),
                   _ptr(out["status"]), _ptr(out["min_margin"]), _ptr(out["n_decisions"]),
-                  float(threshold_acc), float(threshold_single))
+                  float(threshold_acc), float(threshold_single), _ptr(tk), _ptr(tp))
     lib().svo_verify_tree(ctypes.byref(a))
     return out
 

@@ -601,6 +601,14 @@ static void tree_one(const svo_tree_args* a, int32_t b, double* w, double* prow)
       if (st[n].status != SVO_REQ_OK) status = st[n].status;
     }
   }
+  if (status == SVO_REQ_OK && !greedy && (a->top_k || a->top_p)) {
+    for (int32_t n = 0; n < N; ++n) {
+      double g;
+      filter_row(&st[n], a->logits_dtype, a->logits, ((int64_t)b * N + n) * a->logits_row_stride, V, T,
+                 a->top_k ? a->top_k[b] : 0, a->top_p ? a->top_p[b] : 1.0f, &g);
+      if (g < min_margin) min_margin = g;
+    }
+  }
   if (status != SVO_REQ_OK) {
     if (a->req_status) a->req_status[b] = status;
     if (a->min_margin) a->min_margin[b] = INFINITY;

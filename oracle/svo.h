@@ -106,6 +106,10 @@ typedef struct {
    * exact rule; any other value makes the rule lossy and exists only so the
    * statistical tests can show they detect a changed distribution. */
   double threshold_acc, threshold_single;
+  /* Top-k / top-p filtering of the stochastic requests' target rows, as for
+   * chains (NULL: off). */
+  const int32_t* top_k;
+  const float* top_p;
 } svo_tree_args;
 
 void svo_verify_chain(const svo_chain_args* a);

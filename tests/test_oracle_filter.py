@@ -177,3 +177,57 @@ def test_filtered_probability_of_each_token():
             T[j], tk[j], tp[j], want[j] = t, k, p, f[x]
     o = oracle.verify_chain(logits, ids, T, _seeds(n, 9), onehot=True, top_k=tk, top_p=tp)
     np.testing.assert_allclose(o["p_draft"][:, 0], want, rtol=1e-12, atol=0)
+
+
+# ------------------------------------------------------------------ trees
+@pytest.mark.parametrize("seed", [0, 1])
+def test_filtered_tree_exact_joint(seed):
+    """The tree rule under a filtered target: outcomes (accepted path,
+    emitted token) against the exact joint built from the filtered rows."""
+    import workloads
+    from test_oracle_stats import _tree_joint
+    rng = np.random.default_rng(700 + seed)
+    N, V, n = 6, 6, 400_000
+    parent = workloads.random_tree(rng, N, max_depth=3, max_children=3)
+    tok = np.full(N, -1, np.int32)
+    for node in range(N):
+        kids = [c for c in range(1, N) if parent[c] == node]
+        for c, t in zip(kids, rng.choice(V, size=len(kids), replace=False)):
+            tok[c] = t
+    l = np.round(rng.standard_normal((N, V)) * 1.3, 1).astype(np.float32)
+    top_k, top_p = (3, 0.9) if seed == 0 else (0, 0.7)
+    pf = np.stack([_filtered(l[r], 1.0, top_k, top_p) for r in range(N)])
+    o = oracle.verify_tree(np.broadcast_to(l, (n, N, V)).copy(), np.broadcast_to(tok, (n, N)).copy(),
+                           np.broadcast_to(parent, (n, N)).copy(), np.ones(n, np.float32), _seeds(n, 60 + seed),
+                           top_k=np.full(n, top_k, np.int32), top_p=np.full(n, top_p, np.float32))
+    joint = _tree_joint(pf, parent, tok)
+    keys = [kk for kk in joint if joint[kk] > 0]
+    index = {kk: i for i, kk in enumerate(keys)}
+    counts = np.zeros(len(keys))
+    for path_row, L, tk in zip(o["accept_path"], o["accept_len"], o["tokens"]):
+        key = (tuple(int(v) for v in path_row[:L]), int(tk[L]))
+        assert key in index, key        # nothing outside the filtered support
+        counts[index[key]] += 1
+    probs = np.array([joint[kk] for kk in keys])
+    chi2, pv, dof = chi2_pvalue(counts, probs / probs.sum())
+    assert pv > P_PASS, (chi2, dof, pv)
+
+
+def test_filtered_chain_shaped_tree_equals_onehot_chain():
+    rng = np.random.default_rng(31)
+    bs, k, V = 300, 4, 40
+    l = np.round(rng.standard_normal((bs, k + 1, V)) * 2, 1).astype(np.float32)
+    ids = rng.integers(0, V, size=(bs, k)).astype(np.int32)
+    ids[:, 0] = np.argmax(l[:, 0], axis=1)
+    T = rng.choice([0.0, 0.6, 1.0], size=bs).astype(np.float32)
+    tk = rng.choice([0, 1, 3, 10], size=bs).astype(np.int32)
+    tp = rng.choice([1.0, 0.5, 0.9], size=bs).astype(np.float32)
+    seeds = _seeds(bs, 5)
+    chain = oracle.verify_chain(l, ids, T, seeds, onehot=True, top_k=tk, top_p=tp)
+    node_tokens = np.concatenate([np.full((bs, 1), -1, np.int32), ids], axis=1)
+    parent = np.tile(np.arange(-1, k, dtype=np.int32), (bs, 1))
+    tree = oracle.verify_tree(l, node_tokens, parent, T, seeds, top_k=tk, top_p=tp)
+    np.testing.assert_array_equal(tree["accept_len"], chain["accept_len"])
+    np.testing.assert_array_equal(tree["tokens"], chain["tokens"])
+    off = oracle.verify_tree(l, node_tokens, parent, T, seeds)
+    assert (off["tokens"] != tree["tokens"]).any()
