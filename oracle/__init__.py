@@ -48,7 +48,7 @@ class _ChainArgs(ctypes.Structure):
                 ("draft_ids", _P), ("temperature", _P), ("seed", _P),
                 ("accept_len", _P), ("tokens", _P), ("req_status", _P),
                 ("p_draft", _P), ("min_margin", _P), ("n_decisions", _P), ("rule", _I32),
-                ("top_k", _P), ("top_p", _P)]
+                ("top_k", _P), ("top_p", _P), ("cut_margin", _P)]
 
 
 class _PlanArgs(ctypes.Structure):
@@ -69,7 +69,8 @@ class _TreeArgs(ctypes.Structure):
                 ("node_tokens", _P), ("parent", _P), ("temperature", _P), ("seed", _P),
                 ("accept_len", _P), ("accept_path", _P), ("tokens", _P), ("req_status", _P),
                 ("min_margin", _P), ("n_decisions", _P),
-                ("threshold_acc", _D), ("threshold_single", _D), ("top_k", _P), ("top_p", _P)]
+                ("threshold_acc", _D), ("threshold_single", _D), ("top_k", _P), ("top_p", _P),
+                ("cut_margin", _P)]
 
 
 _lib = None
@@ -183,7 +184,8 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
 
     logits: [bs, k+1, V] float32 or uint16 (bf16 bits); draft_ids: [bs, k] int32;
     draft_probs: [bs, k, V] float32 (standard rule) or None with onehot=True.
-    Returns a dict with accept_len, tokens, status, p_draft, min_margin, n_decisions.
+    Returns a dict with accept_len, tokens, status, p_draft, min_margin, n_decisions and
+    cut_margin (the smallest relative gap of a top-p cut; +inf without one).
     """
     x, code, V = _logits_view(logits)
     bs, R = x.shape[0], x.shape[1]
@@ -201,7 +203,8 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
         kind = DRAFT_PROBS
     out = dict(accept_len=np.empty(bs, np.int32), tokens=np.empty((bs, R), np.int32),
                status=np.empty(bs, np.int32), p_draft=np.empty((bs, max(k, 1)), np.float64),
-               min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32))
+               min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32),
+               cut_margin=np.empty(bs, np.float64))
     if rule not in ("standard", "block"):
         raise ValueError(f"unknown rule {rule!r}")
     tk = None if top_k is None else np.ascontiguousarray(np.asarray(top_k, np.int32).reshape(bs))
@@ -210,7 +213,7 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
                    _ptr(out["accept_len"]), _ptr(out["tokens"]), _ptr(out["status"]),
                    _ptr(out["p_draft"]), _ptr(out["min_margin"]), _ptr(out["n_decisions"]),
                    RULE_BLOCK if rule == "block" else RULE_STANDARD,
-                   _ptr(tk), _ptr(tp))
+                   _ptr(tk), _ptr(tp), _ptr(out["cut_margin"]))
     lib().svo_verify_chain(ctypes.byref(a))
     out["p_draft"] = out["p_draft"][:, :k]
     return out
@@ -233,13 +236,15 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, threshold_acc=1
     sd = np.ascontiguousarray(np.asarray(seeds, dtype=np.uint64).reshape(bs))
     out = dict(accept_len=np.empty(bs, np.int32), accept_path=np.empty((bs, N), np.int32),
                tokens=np.empty((bs, N), np.int32), status=np.empty(bs, np.int32),
-               min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32))
+               min_margin=np.empty(bs, np.float64), n_decisions=np.empty(bs, np.int32),
+               cut_margin=np.empty(bs, np.float64))
     tk = None if top_k is None else np.ascontiguousarray(np.asarray(top_k, np.int32).reshape(bs))
     tp = None if top_p is None else np.ascontiguousarray(np.asarray(top_p, np.float32).reshape(bs))
     a = _TreeArgs(bs, N, V, code, _ptr(x), V, _ptr(nt), _ptr(par), _ptr(temp), _ptr(sd),
                   _ptr(out["accept_len"]), _ptr(out["accept_path"]), _ptr(out["tokens"]),
                   _ptr(out["status"]), _ptr(out["min_margin"]), _ptr(out["n_decisions"]),
-                  float(threshold_acc), float(threshold_single), _ptr(tk), _ptr(tp))
+                  float(threshold_acc), float(threshold_single), _ptr(tk), _ptr(tp),
+                  _ptr(out["cut_margin"]))
     lib().svo_verify_tree(ctypes.byref(a))
     return out
 

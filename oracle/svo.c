@@ -451,17 +451,19 @@ static void chain_one(const svo_chain_args* a, int32_t b, double* w, double* pro
       if (st[r].status != SVO_REQ_OK) status = st[r].status;
     }
   }
+  double cut_margin = INFINITY;
   if (status == SVO_REQ_OK && !greedy && (a->top_k || a->top_p)) {
     for (int32_t r = 0; r <= kb; ++r) {
       double g;
       filter_row(&st[r], a->logits_dtype, a->logits, ((int64_t)b * R + r) * a->logits_row_stride, V, T,
                  a->top_k ? a->top_k[b] : 0, a->top_p ? a->top_p[b] : 1.0f, &g);
-      if (g < min_margin) min_margin = g;
+      if (g < cut_margin) cut_margin = g;
     }
   }
   if (status != SVO_REQ_OK) {
     if (a->req_status) a->req_status[b] = status;
     if (a->min_margin) a->min_margin[b] = INFINITY;
+    if (a->cut_margin) a->cut_margin[b] = INFINITY;
     if (a->n_decisions) a->n_decisions[b] = 0;
     return;
   }
@@ -545,6 +547,7 @@ static void chain_one(const svo_chain_args* a, int32_t b, double* w, double* pro
   a->accept_len[b] = acc;
   if (a->req_status) a->req_status[b] = SVO_REQ_OK;
   if (a->min_margin) a->min_margin[b] = min_margin;
+  if (a->cut_margin) a->cut_margin[b] = cut_margin;
   if (a->n_decisions) a->n_decisions[b] = n_dec;
 }
 
@@ -601,17 +604,19 @@ static void tree_one(const svo_tree_args* a, int32_t b, double* w, double* prow)
       if (st[n].status != SVO_REQ_OK) status = st[n].status;
     }
   }
+  double cut_margin = INFINITY;
   if (status == SVO_REQ_OK && !greedy && (a->top_k || a->top_p)) {
     for (int32_t n = 0; n < N; ++n) {
       double g;
       filter_row(&st[n], a->logits_dtype, a->logits, ((int64_t)b * N + n) * a->logits_row_stride, V, T,
                  a->top_k ? a->top_k[b] : 0, a->top_p ? a->top_p[b] : 1.0f, &g);
-      if (g < min_margin) min_margin = g;
+      if (g < cut_margin) cut_margin = g;
     }
   }
   if (status != SVO_REQ_OK) {
     if (a->req_status) a->req_status[b] = status;
     if (a->min_margin) a->min_margin[b] = INFINITY;
+    if (a->cut_margin) a->cut_margin[b] = INFINITY;
     if (a->n_decisions) a->n_decisions[b] = 0;
     return;
   }
@@ -681,6 +686,7 @@ static void tree_one(const svo_tree_args* a, int32_t b, double* w, double* prow)
   a->accept_len[b] = len;
   if (a->req_status) a->req_status[b] = SVO_REQ_OK;
   if (a->min_margin) a->min_margin[b] = min_margin;
+  if (a->cut_margin) a->cut_margin[b] = cut_margin;
   if (a->n_decisions) a->n_decisions[b] = n_dec;
 }
 

@@ -85,6 +85,9 @@ typedef struct {
   int32_t rule;                             /* SVO_RULE_STANDARD or SVO_RULE_BLOCK */
   const int32_t* top_k;                     /* [bs] or NULL: top-k of each stochastic request (<= 0: off) */
   const float* top_p;                       /* [bs] or NULL: top-p (outside (0, 1): off) */
+  double* cut_margin;                       /* [bs] out, may be NULL: smallest relative gap of a top-p cut
+                                               (its cumulative mass against the target, either side;
+                                               +inf without one) */
 } svo_chain_args;
 
 typedef struct {
@@ -110,6 +113,7 @@ typedef struct {
    * chains (NULL: off). */
   const int32_t* top_k;
   const float* top_p;
+  double* cut_margin;                       /* [bs] out, may be NULL: as for chains */
 } svo_tree_args;
 
 void svo_verify_chain(const svo_chain_args* a);
