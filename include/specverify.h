@@ -192,6 +192,11 @@ typedef struct {
   int32_t* tokens;            /* [bs][N] out: accepted nodes' tokens, then the emitted token, -1 after */
   int32_t* req_status;        /* [bs] out, may be NULL */
   uint32_t flags;
+  /* Top-k / top-p filtering of the target, as for chains (sv_chain_desc):
+   * every row of a filtered stochastic request (all N) is filtered, so the
+   * walk's sibling sums and the residual use the filtered p.  NULL: off. */
+  const int32_t* top_k;       /* [bs] or NULL */
+  const float* top_p;         /* [bs] or NULL */
 } sv_tree_desc;
 
 /* Bytes of workspace a call of the given shape needs (0 if the shape is

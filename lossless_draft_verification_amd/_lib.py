@@ -50,7 +50,7 @@ class TreeDesc(ctypes.Structure):
     _fields_ = [("batch", _I32), ("num_nodes", _I32), ("vocab", _I32), ("logits_dtype", ctypes.c_int),
                 ("logits", _P), ("logits_row_stride", _I64), ("node_tokens", _P), ("parent", _P),
                 ("temperature", _P), ("seed", _P), ("accept_len", _P), ("accept_path", _P), ("tokens", _P),
-                ("req_status", _P), ("flags", _U32)]
+                ("req_status", _P), ("flags", _U32), ("top_k", _P), ("top_p", _P)]
 
 
 class PlanDesc(ctypes.Structure):
@@ -295,10 +295,12 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
     return out
 
 
-def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, workspace=None):
+def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, workspace=None, top_k=None,
+                top_p=None):
     """Target-only tree verification on the current stream (asynchronous).
 
-    logits [bs, N, V]; node_tokens, parent [bs, N] int32.  Returns
+    logits [bs, N, V]; node_tokens, parent [bs, N] int32; top_k [bs] int32 /
+    top_p [bs] float32 (or None) filter the stochastic requests' target.  Returns
     accept_len [bs], accept_path [bs, N], tokens [bs, N], status [bs].
     """
     if logits.dim() != 3:
@@ -317,6 +319,8 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, wor
                accept_path=torch.empty(bs, N, dtype=torch.int32, device=device),
                tokens=torch.empty(bs, N, dtype=torch.int32, device=device),
                status=torch.empty(bs, dtype=torch.int32, device=device))
+    tk = None if top_k is None else _on(top_k.reshape(bs), device, torch.int32, "top_k")
+    tp = None if top_p is None else _on(top_p.reshape(bs), device, torch.float32, "top_p")
     need = tree_workspace_bytes(bs, N, V, code)
     if need == 0:
         raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_tree_workspace_bytes")
@@ -324,7 +328,8 @@ def verify_tree(logits, node_tokens, parent, temperature, seeds, *, flags=0, wor
     ws.ensure(need)
     d = TreeDesc(bs, N, V, code, logits.data_ptr(), lstride, nt.data_ptr(), par.data_ptr(), temp.data_ptr(),
                  sd.data_ptr(), out["accept_len"].data_ptr(), out["accept_path"].data_ptr(),
-                 out["tokens"].data_ptr(), out["status"].data_ptr(), int(flags))
+                 out["tokens"].data_ptr(), out["status"].data_ptr(), int(flags),
+                 tk.data_ptr() if tk is not None else None, tp.data_ptr() if tp is not None else None)
     st = lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(ws.base), ctypes.c_size_t(ws.nbytes),
                               _stream(device))
     if st != OK:

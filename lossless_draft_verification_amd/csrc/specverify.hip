@@ -180,8 +180,8 @@ struct Params {
   int32_t CI;         // K23 items per request: ceil(C3 / G3)
   int32_t CHr;        // block rule: residual-mass items per row (rows 1..k-1)
   double* rpart;      // block rule: [bs][k][CHr] residual-mass partials
-  const int32_t* top_k;  // chain: per-request top-k (NULL: off)
-  const float* top_p;    // chain: per-request top-p (NULL: off)
+  const int32_t* top_k;  // per-request top-k (NULL: off)
+  const float* top_p;    // per-request top-p (NULL: off)
   FiltRec* filt;         // [bs*R] thresholds and kept sums of filtered rows
   int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
@@ -422,8 +422,8 @@ __device__ __forceinline__ void block_sum2_d(double& a, double& b, Smem& sm) {
 __device__ __forceinline__ float temp_of(const Params& P, int b) { return P.temp[b]; }
 __device__ __forceinline__ bool is_stochastic(float T) { return T > 0.f && isfinite(T); }
 
-// Whether chain request b's target is top-k / top-p filtered: stochastic,
-// and k in (0, V) or p in (0, 1).
+// Whether request b's target is top-k / top-p filtered: stochastic, and k
+// in (0, V) or p in (0, 1).
 __device__ __forceinline__ bool request_filtered(const Params& P, int b, float T) {
   if (!is_stochastic(T)) return false;
   const int tk = P.top_k ? P.top_k[b] : 0;
@@ -948,6 +948,11 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
     rs.s = 1.0;
     rs.bad = false;
     if (lane < N) rs = row_stats_of(sm, lane);
+    float ftau = -INFINITY;  // top-k / top-p: the row's threshold (and its kept sum replaces S)
+    if (request_filtered(P, b, Tf) && lane < N) {
+      rs.s = P.filt[(int64_t)b * N + lane].s;
+      ftau = P.filt[(int64_t)b * N + lane].tau;
+    }
     double u = 0.0;
     if (status == SV_REQ_OK && !greedy && lane < N) u = coin(seed, b, lane);
     if (status == SV_REQ_OK && __ballot(lane < N && rs.bad)) status = SV_REQ_NONFINITE;
@@ -956,6 +961,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
     const float pm = __shfl(rs.m, src, 64);
     const double ps = __shfl(rs.s, src, 64);
     const int pa = __shfl(rs.amax, src, 64);
+    const float ptau = __shfl(ftau, src, 64);
     if (lane < N) {
       sm.par[lane] = par;
       sm.tok[lane] = tok;
@@ -963,8 +969,10 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
       sm.rm[lane] = rs.m;
       sm.rs[lane] = rs.s;
       sm.u[lane] = u;
+      sm.qx[lane] = (double)ftau;  // the row's threshold, for the sampling job
+      const float lx = __uint_as_float(gl);
       if (lane >= 1 && status == SV_REQ_OK)
-        sm.px[lane] = greedy ? (tok == pa ? 1.0 : 0.0) : p_at((double)__uint_as_float(gl), pm, T, ps);
+        sm.px[lane] = greedy ? (tok == pa ? 1.0 : 0.0) : (lx < ptau ? 0.0 : p_at((double)lx, pm, T, ps));
     }
     if (lane == 0) sm.status = status;
   }
@@ -1020,7 +1028,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
       scale_pair(T, J.c_hi, J.c_lo);
       J.inv_s = (float)(1.0 / J.s);
       J.wmul = 1.0;
-      J.tau = -INFINITY;
+      J.tau = (float)sm.qx[cur];
       int ne = 0;
       if (kind == JOB_EXCL)
         for (int c = cur + 1; c < N; ++c)
@@ -2422,7 +2430,7 @@ __global__ __launch_bounds__(kKF) void kf_kernel(Params P) {
   const float Tf = temp_of(P, b);
   if (!request_filtered(P, b, Tf)) return;
   int xi;
-  if (r > chain_kb(P, b, xi)) return;
+  if (P.mode == MODE_CHAIN && r > chain_kb(P, b, xi)) return;  // a tree reads all its rows
   const int tk = P.top_k ? P.top_k[b] : 0;
   const float tp = P.top_p ? P.top_p[b] : 1.f;
   const bool use_k = tk > 0 && tk < P.V, use_p = tp > 0.f && tp < 1.f;
@@ -2662,7 +2670,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   if (grid23 + P.G > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   const int64_t gridr = (int64_t)P.bs * (P.k >= 2 ? P.k - 1 : 0) * P.CHr;
   if (gridr > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
-  const bool filtered = P.mode == MODE_CHAIN && (P.top_k != nullptr || P.top_p != nullptr);
+  const bool filtered = P.mode != MODE_ROWS && (P.top_k != nullptr || P.top_p != nullptr);
   const int64_t gridf = (int64_t)P.bs * P.R;  // thresholds: one workgroup per row
   // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).
@@ -2819,6 +2827,7 @@ sv_status sv_verify_tree(const sv_tree_desc* d, void* ws, size_t ws_bytes, void*
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
   if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
   if (d->flags & SV_FLAG_BLOCK) return SV_ERR_UNSUPPORTED;
+  if ((d->top_k != nullptr || d->top_p != nullptr) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
   if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
   if (d->logits == nullptr || d->node_tokens == nullptr || d->parent == nullptr || d->temperature == nullptr ||
       d->seed == nullptr || d->accept_len == nullptr || d->accept_path == nullptr || d->tokens == nullptr)
@@ -2845,6 +2854,8 @@ sv_status sv_verify_tree(const sv_tree_desc* d, void* ws, size_t ws_bytes, void*
   P.tokens = d->tokens;
   P.status = d->req_status;
   P.flags = d->flags;
+  P.top_k = d->top_k;
+  P.top_p = d->top_p;
   const Shape S = shape_of(P.bs, P.R, P.V, P.dtype, true);
   return launch(P, S, ws, ws_bytes, (hipStream_t)stream);
 }

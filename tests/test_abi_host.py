@@ -107,6 +107,9 @@ def test_filtering_needs_the_phased_schedule():
     fake = 0x300000
     assert _call_chain(_chain_desc(flags=sv.FLAG_FUSED, top_k=fake)) == 3
     assert _call_chain(_chain_desc(flags=sv.FLAG_FUSED, top_p=fake)) == 3
+    for kw in (dict(top_k=fake), dict(top_p=fake)):
+        d = _tree_desc(flags=sv.FLAG_FUSED, **kw)
+        assert sv.lib().sv_verify_tree(ctypes.byref(d), ctypes.c_void_p(0x200000), ctypes.c_size_t(1 << 30), None) == 3
 
 
 def test_filtered_workspace_holds_a_record_per_row():
