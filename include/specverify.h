@@ -167,11 +167,12 @@ typedef struct {
    * the residual and the bonus all see the filtered p.  top_k <= 0 or >= V,
    * and top_p outside (0, 1) (NaN included), switch a filter off; greedy
    * requests ignore both.  q is taken as given (the drafter's own, already
-   * filtered if it filters).  A filtered call takes one more launch per row
-   * read (the thresholds) between the statistics and the decisions; not
-   * available with SV_FLAG_FUSED (SV_ERR_UNSUPPORTED).  With STATS_ONLY /
-   * DECIDE_ONLY the thresholds belong to the STATS_ONLY call, and both calls
-   * must pass the same arrays. */
+   * filtered if it filters).  A call with either array non-NULL takes one
+   * more launch (the thresholds of every row read, one workgroup each)
+   * between the statistics and the decisions; not available with
+   * SV_FLAG_FUSED (SV_ERR_UNSUPPORTED).  With STATS_ONLY / DECIDE_ONLY the
+   * thresholds belong to the STATS_ONLY call, and both calls must pass the
+   * same arrays.  The arrays are read on the device (device pointers). */
   const int32_t* top_k;       /* [bs] or NULL */
   const float* top_p;         /* [bs] or NULL */
 } sv_chain_desc;

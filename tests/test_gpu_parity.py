@@ -713,3 +713,23 @@ def test_filtered_chain_shaped_tree_matches_onehot_chain_on_gpu(dev):
     t = _np(tree)
     np.testing.assert_array_equal(t["accept_len"], chain["accept_len"])
     np.testing.assert_array_equal(t["tokens"], chain["tokens"])
+
+
+def test_filtered_calls_are_deterministic(dev):
+    """The thresholds pass sums masses in integer fixed point and its LDS list
+    order does not reach the results: repeated filtered calls agree bit for
+    bit, p at the drafts included."""
+    inp = workloads.chain_bf16_mixed(3, bs=32, k=5, V=50000)
+    tk, tp = _filters(np.random.default_rng(8), inp.batch, inp.vocab)
+    tp[::2] = 0.9  # top-p over the whole row on half the requests
+    outs = []
+    for _ in range(3):
+        out = sv.verify_chain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev),
+                              _t(inp.seeds, dev), draft_probs=_t(inp.draft_probs, dev), return_p_draft=True,
+                              top_k=_t(tk, dev), top_p=_t(tp, dev))
+        torch.cuda.synchronize()
+        outs.append(_np(out))
+    for o in outs[1:]:
+        for key in ("accept_len", "tokens", "status"):
+            np.testing.assert_array_equal(o[key], outs[0][key])
+        np.testing.assert_array_equal(o["p_draft"].view(np.uint64), outs[0]["p_draft"].view(np.uint64))
