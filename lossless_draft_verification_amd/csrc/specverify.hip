@@ -2130,7 +2130,7 @@ constexpr int kKF = 1024;                // threads of a thresholds workgroup
 constexpr int kKFWaves = kKF / 64;
 constexpr int kKFBins = 2048;
 constexpr int kKFList = 8192;            // keys the LDS list holds
-constexpr int kKFUnroll = 8;             // groups of 4 ids whose loads a thread issues together
+constexpr int kKFUnroll = 8;             // groups of 4 ids per step on unaligned rows
 
 __device__ __forceinline__ uint32_t kf_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -2188,45 +2188,48 @@ struct KFShared {
 };
 
 // One pass over the row's logits (LIST: over the keys in the LDS list):
-// f(l) for each.  From memory each thread takes groups of 4 consecutive ids,
-// kKFUnroll groups per step; in rows of whole aligned groups the next
+// f(l) for each.  From memory each thread takes groups of consecutive ids
+// (16 bytes: 8 bf16 or 4 fp32), kKFUnroll groups per step; in rows of whole
+// aligned groups the next
 // step's loads are in flight while the current step is processed (loads
 // past the row re-read its first group and are not processed, so every load
 // is unconditional).
 template <bool BF16>
+constexpr int kf_group() { return BF16 ? 8 : 4; }
+template <bool BF16>
+constexpr int kf_unroll() { return BF16 ? 4 : 8; }  // 64 or 128 bytes per thread per step
+template <bool BF16>
 struct KFRaw {
-  typename std::conditional<BF16, u32x2, u32x4>::type v[kKFUnroll];
+  u32x4 v[kf_unroll<BF16>()];  // 8 bf16 or 4 fp32 logits per group
 };
 template <bool BF16>
 __device__ __forceinline__ void kf_issue(const Params& P, int64_t off, int base, KFRaw<BF16>& r) {
+  constexpr int E = kf_group<BF16>();
 #pragma unroll
-  for (int g = 0; g < kKFUnroll; ++g) {
-    int y0 = base + 4 * (g * kKF + (int)threadIdx.x);
+  for (int g = 0; g < kf_unroll<BF16>(); ++g) {
+    int y0 = base + E * (g * kKF + (int)threadIdx.x);
     y0 = y0 < P.V ? y0 : 0;
-    if constexpr (BF16) r.v[g] = *(const u32x2*)((const uint16_t*)P.logits + off + y0);
+    if constexpr (BF16) r.v[g] = *(const u32x4*)((const uint16_t*)P.logits + off + y0);
     else r.v[g] = *(const u32x4*)((const float*)P.logits + off + y0);
   }
 }
 template <bool BF16, typename F>
 __device__ __forceinline__ void kf_fold(const KFRaw<BF16>& r, int base, int V, F&& f) {
+  constexpr int E = kf_group<BF16>();
 #pragma unroll
-  for (int g = 0; g < kKFUnroll; ++g) {
-    const int y0 = base + 4 * (g * kKF + (int)threadIdx.x);
+  for (int g = 0; g < kf_unroll<BF16>(); ++g) {
+    const int y0 = base + E * (g * kKF + (int)threadIdx.x);
     if (y0 < V) {
-      float l[4];
-      if constexpr (BF16) {
-        l[0] = __uint_as_float(r.v[g].x << 16);
-        l[1] = __uint_as_float(r.v[g].x & 0xffff0000u);
-        l[2] = __uint_as_float(r.v[g].y << 16);
-        l[3] = __uint_as_float(r.v[g].y & 0xffff0000u);
-      } else {
-        l[0] = __uint_as_float(r.v[g].x);
-        l[1] = __uint_as_float(r.v[g].y);
-        l[2] = __uint_as_float(r.v[g].z);
-        l[3] = __uint_as_float(r.v[g].w);
-      }
+      const uint32_t w[4] = {r.v[g].x, r.v[g].y, r.v[g].z, r.v[g].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f(l[i]);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+          f(__uint_as_float(w[i] << 16));
+          f(__uint_as_float(w[i] & 0xffff0000u));
+        } else {
+          f(__uint_as_float(w[i]));
+        }
+      }
     }
   }
 }
@@ -2240,8 +2243,9 @@ __device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFSh
   }
   const int V = P.V;
   const int64_t off = row * P.lstride;
-  constexpr int step = 4 * kKF * kKFUnroll;
-  if (P.aligned && (V & 3) == 0) {
+  constexpr int E = kf_group<BF16>();
+  constexpr int step = E * kKF * kf_unroll<BF16>();
+  if (P.aligned && (V % E) == 0) {
     KFRaw<BF16> a, b;
     kf_issue<BF16>(P, off, 0, a);
 #pragma unroll 1
@@ -2257,8 +2261,9 @@ __device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFSh
     }
     return;
   }
+  constexpr int sstep = 4 * kKF * kKFUnroll;
 #pragma unroll 1
-  for (int base = 0; base < V; base += step) {
+  for (int base = 0; base < V; base += sstep) {
     float l[kKFUnroll][4];
 #pragma unroll
     for (int g = 0; g < kKFUnroll; ++g) {
