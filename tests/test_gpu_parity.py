@@ -733,3 +733,16 @@ def test_filtered_calls_are_deterministic(dev):
         for key in ("accept_len", "tokens", "status"):
             np.testing.assert_array_equal(o[key], outs[0][key])
         np.testing.assert_array_equal(o["p_draft"].view(np.uint64), outs[0]["p_draft"].view(np.uint64))
+
+
+def test_filtered_with_one_array_only(dev):
+    """top_k alone and top_p alone (the other pointer NULL), chain and tree."""
+    inp = _random_chain(71, 10, 4, 7000, "bf16", "probs")
+    tk, tp = _filters(np.random.default_rng(71), 10, 7000)
+    check_chain(inp, dev, top_k=tk)
+    check_chain(inp, dev, top_p=tp)
+    check_chain(inp, dev, flags=sv.FLAG_BLOCK, top_p=tp)
+    tree = _random_tree_inputs(72, 6, 8, 5000, "f32")
+    tk6, tp6 = _filters(np.random.default_rng(72), 6, 5000)
+    check_tree(tree, dev, top_k=tk6)
+    check_tree(tree, dev, top_p=tp6)
