@@ -105,9 +105,11 @@ def test_ties_at_the_threshold_are_kept():
     assert pv > P_PASS
 
 
-def test_filtered_target_is_kept_over_rounds():
+@pytest.mark.parametrize("rule", ["standard", "block"])
+def test_filtered_target_is_kept_over_rounds(rule):
     """Markov rounds as in the unfiltered pin, with top-k = 3 of 5 tokens and
-    top-p = 0.9: sequences follow the filtered target chain's exact joint."""
+    top-p = 0.9: sequences follow the filtered target chain's exact joint,
+    under both acceptance rules."""
     rng = np.random.default_rng(20261202)
     V, n, s0 = 5, 200_000, 0
     Pm = rng.dirichlet(np.ones(V), size=V)
@@ -127,7 +129,8 @@ def test_filtered_target_is_kept_over_rounds():
         logits = np.stack([lP[last[active]], lP[d1], lP[d2]], axis=1)
         q = np.stack([Qm[last[active]], Qm[d1]], axis=1).astype(np.float32)
         o = oracle.verify_chain(logits, ids, np.ones(m, np.float32), _seeds(m, 1 + rnd * 7919) + np.uint64(rnd << 40),
-                                draft_probs=q, top_k=np.full(m, 3, np.int32), top_p=np.full(m, 0.9, np.float32))
+                                draft_probs=q, top_k=np.full(m, 3, np.int32), top_p=np.full(m, 0.9, np.float32),
+                                rule=rule)
         still = []
         for j, b in enumerate(active):
             a = o["accept_len"][j]
