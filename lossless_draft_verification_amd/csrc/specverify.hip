@@ -12,11 +12,10 @@
 //   K1  a streaming segment of one logit row: max, first argmax and
 //       sum exp((l - m)/T) over a run of sub-chunks (16-byte nontemporal
 //       loads, wave shuffles, a cross-wave LDS reduction).  Almost all HBM
-//       bytes are read here, once.  The rows' sub-chunks, flattened, are
-//       split evenly over a fixed number of workgroups that are all
-//       resident at once, so the stream ends in one round with no tail; a
-//       workgroup whose range crosses a row boundary writes one partial per
-//       row it touches.
+//       bytes are read here, once.  Every row is cut into Q segments, Q
+//       chosen from the shape alone so that all the segments' workgroups
+//       are resident at once and the stream ends in one round; each
+//       segment writes one partial of its row.
 //   K23 one chunk of 2048 vocabulary ids of one request's sampling race.
 //       The workgroup first runs the request's decision step itself (K2):
 //       combine the row partials in fp64, take p (and q) at the draft ids
@@ -31,6 +30,10 @@
 //       key; the chunk's near-maximal keys are re-evaluated in fp64 and its
 //       best (key, id) recorded.  The last chunk of the request to finish
 //       takes the best record and writes the emitted token.
+// Two optional passes sit between them in the phased schedule: KR, the
+// block rule's residual masses of draft rows 1..k_b-1 (SV_FLAG_BLOCK), and
+// KF, the top-k / top-p thresholds and kept sums of every filtered row read
+// (the descriptors' top_k / top_p).
 // The phased schedule is two stream-ordered launches (K1, then K23).  The
 // fused schedule is one launch: the K23 items come after every K1 item in
 // dispatch order and wait (bounded, about a second, then SV_REQ_INTERNAL)
