@@ -2488,35 +2488,35 @@ __global__ __launch_bounds__(kKF) void kf_kernel(Params P) {
       cut = listed ? kf_descent<BF16, true, true>(P, row, s, tab, md, cd, kmin, 0, 0, tp, ch, cl)
                    : kf_descent<BF16, false, true>(P, row, s, tab, md, cd, kmin, 0, 0, tp, ch, cl);
     } else {
-      // first level of the masses from memory, with each bin's count (in
-      // the list's first entries, free until the list is filled)
-      for (int i = tid; i < kKFBins; i += kKF) s.list[i] = 0;
-      __syncthreads();
+      // first level of the masses from memory
+      nh = nl = 0;
+      kf_clear(s);
       kf_pass<BF16, false>(P, row, s, [&](float l) {
         const uint32_t key = kf_key(l);
         uint64_t h, lo;
         kf_mass(l, md, cd, tab, h, lo);
         atomicAdd((unsigned long long*)&s.hh[key >> 21], (unsigned long long)h);
         atomicAdd((unsigned long long*)&s.hl[key >> 21], (unsigned long long)lo);
-        atomicAdd(&s.list[key >> 21], 1u);
       });
       __syncthreads();
-      uint32_t bin_count = 0;
       kf_find<true>(s, kKFBins, nh, nl, tp);
       const int d = s.digit;
-      if (d >= 0) bin_count = s.list[d];
-      __syncthreads();
       if (d < 0) {
         cut = 0;
-      } else if (bin_count <= (uint32_t)kKFList) {
-        kf_sub(nh, nl, s.ah, s.al);
-        ch = s.ah;
-        cl = s.al;
-        kf_collect<BF16>(P, row, s, (uint32_t)d << 21, ((uint32_t)d << 21) | 0x1FFFFFu);
-        // the need left within the bin, as a plain need (frac 0)
-        cut = kf_descent<BF16, true, true>(P, row, s, tab, md, cd, 0u, nh, nl, 0.f, ch, cl);
       } else {
-        cut = kf_descent<BF16, false, true>(P, row, s, tab, md, cd, 0u, 0, 0, tp, ch, cl);
+        kf_sub(nh, nl, s.ah, s.al);
+        const uint64_t ah = s.ah, al = s.al;
+        // the bin's keys to the list; the list's counter tells whether they fit
+        kf_collect<BF16>(P, row, s, (uint32_t)d << 21, ((uint32_t)d << 21) | 0x1FFFFFu);
+        if (s.nlist <= kKFList) {
+          ch = ah;
+          cl = al;
+          // the need left within the bin, as a plain need (frac 0)
+          cut = kf_descent<BF16, true, true>(P, row, s, tab, md, cd, 0u, nh, nl, 0.f, ch, cl);
+        } else {
+          ch = cl = 0;
+          cut = kf_descent<BF16, false, true>(P, row, s, tab, md, cd, 0u, 0, 0, tp, ch, cl);
+        }
       }
     }
     if (cut) {
