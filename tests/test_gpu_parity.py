@@ -588,7 +588,7 @@ def _filters(rng, bs, V):
     return tk, tp
 
 
-FILTER_SHAPES = [(1, 9, 3, 7), (2, 17, 2, 1000), (3, 12, 4, 4097), (4, 8, 7, 8191), (5, 6, 3, 12345),
+FILTER_SHAPES = [(7, 4, 1, 1), (8, 6, 2, 2), (1, 9, 3, 7), (2, 17, 2, 1000), (3, 12, 4, 4097), (4, 8, 7, 8191), (5, 6, 3, 12345),
                  (6, 5, 2, 33001)]
 
 
