@@ -239,9 +239,9 @@ int32_t sv_abi_version(void);
  * the load, the smaller K should be"; page "The speculative decoding zoo",
  * section "The finer loop: DSpark's confidence budget").
  *
- * Slot (b, j) is scored by its survival probability: the running fp32
- * product of confidence[b][0..j], each confidence clamped to [0, 1] (NaN
- * counts as 0), for j < num_steps[b] (clamped to [0, K]; NULL: K).  Slots
+ * Slot (b, j) scores the chance that request b's drafts 0..j all pass: the
+ * fp32 product of confidence[b][0..j], each confidence clamped to [0, 1]
+ * (NaN counts as 0), for j < num_steps[b] (clamped to [0, K]; NULL: K).  Slots
  * are ranked by score, higher first; ties go to the earlier position, then
  * to the smaller request index, so every request's admitted slots form a
  * prefix.  Admitting the top B slots is worth

@@ -165,15 +165,27 @@ class Workspace:
 
 
 _workspaces: dict = {}
+_workspaces_lock = threading.Lock()
 
 
 def default_workspace(device) -> Workspace:
+    """The workspace used when a call passes none: one per (device, current
+    stream), so calls on different streams never share scheduling counters
+    or partial results.  A workspace only ever serves its own stream, so
+    growing it (which returns the old buffer to torch's caching allocator)
+    is ordered after every earlier call that used the old buffer.  If a call
+    reports REQ_INTERNAL for a request, call reset() on the workspace it used
+    (for the default one: default_workspace(device).reset(), on the same
+    stream) before the next call."""
     device = torch.device(device)
-    key = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(key)
-    if ws is None:
-        ws = Workspace(1 << 20, torch.device("cuda", key))
-        _workspaces[key] = ws
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    stream = torch.cuda.current_stream(index).cuda_stream
+    key = (index, stream)
+    with _workspaces_lock:
+        ws = _workspaces.get(key)
+        if ws is None:
+            ws = Workspace(1 << 20, torch.device("cuda", index))
+            _workspaces[key] = ws
     return ws
 
 

@@ -4,9 +4,9 @@
 // how much to verify by load"; page "The speculative decoding zoo", section
 // "The finer loop: DSpark's confidence budget").
 //
-// Every (request, position) slot is scored by its survival probability, the
-// running fp32 product of the request's confidences (clamped to [0, 1], NaN
-// as 0).  Slots are ranked by score, higher first, ties to the earlier
+// A (request, position) slot's score is the chance that all of the
+// request's drafts up to that position are accepted: the fp32 product of its
+// confidences so far (each clamped to [0, 1], NaN as 0).  Slots are ranked by score, higher first, ties to the earlier
 // position and then to the smaller request index, so each request's admitted
 // slots form a prefix.  Admitting the top B slots is worth
 // (base + sum of their scores) / cost[B] expected tokens per unit of cost;

@@ -16,20 +16,22 @@
 //       chosen from the shape alone so that all the segments' workgroups
 //       are resident at once and the stream ends in one round; each
 //       segment writes one partial of its row.
-//   K23 one chunk of 2048 vocabulary ids of one request's sampling race.
+//   K23 a run of race chunks (2048 vocabulary ids each) of one request.
 //       The workgroup first runs the request's decision step itself (K2):
 //       combine the row partials in fp64, take p (and q) at the draft ids
 //       that K1 gathered, draw the Philox coins, find the first rejection
-//       (chain) or walk the tree.  Every chunk of the request computes the
+//       (chain) or walk the tree.  Every item of the request computes the
 //       same decision from the same few hundred bytes, so no workgroup
-//       waits for another's result; chunk 0 writes the request's outputs.
-//       Then (K3) it races its ids: one exp per id gives certified bounds
-//       on the id's weight; only ids whose weight could still beat a
-//       certified lower bound of some key (few, for any peaked
-//       distribution) are compacted in LDS and pay for Philox noise and the
-//       key; the chunk's near-maximal keys are re-evaluated in fp64 and its
-//       best (key, id) recorded.  The last chunk of the request to finish
-//       takes the best record and writes the emitted token.
+//       waits for another's result; item 0 writes the request's outputs.
+//       Then (K3) the sampling race runs on two levels.  Each item bounds
+//       the weight sum W_c of each of its chunks from one fp32 exp per id
+//       (certified lower and upper bounds, no Philox) and stores the
+//       chunk's key bounds W_c / E_c in a record.  The request's last item
+//       waits for every record, keeps the chunks whose upper bound reaches
+//       the largest lower bound (several are re-summed exactly in fp64),
+//       and races the ids of the winning chunk alone: fp32 key bounds, the
+//       near-maximal keys re-evaluated in fp64; it writes the emitted
+//       token.
 // Two optional passes sit between them in the phased schedule: KR, the
 // block rule's residual masses of draft rows 1..k_b-1 (SV_FLAG_BLOCK), and
 // KF, the top-k / top-p thresholds and kept sums of every filtered row read
@@ -84,15 +86,20 @@ constexpr int kKRWorkgroups = SV_KR_WORKGROUPS;  // block rule's residual-mass p
 // K1 workgroups per call: an MI355X holds 256 CUs x 7 of them at once (71
 // VGPRs), so the stream is one round.
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
-constexpr int kK3Groups = 2;                    // groups of 4 vocabulary ids per thread in a sampling chunk
-constexpr int kK3Chunk = 4 * kWG * kK3Groups;   // 2048 ids per sampling chunk
+// Ids per chunk of the sampling race: part of the sampler's definition (the
+// race picks a chunk, then an id inside it), fixed independently of any
+// workgroup shape; the kernels' tiles are sized to it.
+constexpr int kK3Chunk = 2048;
+constexpr int kK3Groups = 2;                    // groups of 4 vocabulary ids per thread in a race chunk
+static_assert(kK3Chunk % (4 * kWG) == 0 && kK3Chunk == 4 * kWG * kK3Groups,
+              "a race chunk is a whole number of 4-id groups per thread");
 // K23 items per call the chunk grouping aims at: 256 CUs x 8 resident
 // workgroups.  Up to two rounds of one-chunk items are kept (each item
 // decides for itself, which is cheaper than a longer item); past that,
 // items take several chunks, so that large batches decide once per item.
 constexpr int kK3Slots = 2048;
-constexpr int kCandMax = 64;
-constexpr int kChunkE = 64;                     // chunk noise values an item computes up front                    // candidates a race level re-keys in fp64 (more: fp64 race)
+constexpr int kCandMax = 64;                    // candidates a race level re-keys in fp64 (more: fp64 race)
+constexpr int kChunkE = 64;                     // chunk noise values an item computes up front
 constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second)
 
 enum { MODE_CHAIN = 0, MODE_TREE = 1, MODE_ROWS = 2 };

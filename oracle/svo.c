@@ -700,10 +700,10 @@ void svo_verify_tree(const svo_tree_args* a) {
 
 /* ------------------------------------------------------------------------ */
 /* Survival top-k draft budget ([NEW] "Deciding how much to verify by load";
- * [ZOO] "The finer loop: DSpark's confidence budget").  Each (request,
- * position) slot is scored by its survival probability, the running product
- * of the request's confidences up to that position (fp32, as the pages'
- * cumprod of fp32 confidences); the slots are ranked by score, higher first,
+ * [ZOO] "The finer loop: DSpark's confidence budget").  A (request,
+ * position) slot's score is the chance that the request's drafts all pass up
+ * to that position: the product of its confidences so far (in fp32, as the
+ * pages' cumprod of fp32 confidences); the slots are ranked by score, higher first,
  * ties to the earlier position and then to the smaller request index (the
  * deterministic tie rule [ZOO] asks for, which makes every request's
  * admitted slots a prefix).  Admitting the top B slots yields

@@ -48,7 +48,11 @@ double svo_noise_uniform(uint64_t seed, int32_t b, int32_t r, int32_t y);
 /* Chunk noise of the two-level race: word 0 of counter (c, r, b, 2). */
 double svo_chunk_uniform(uint64_t seed, int32_t b, int32_t r, int32_t c);
 
-/* Ids per chunk of the sampling race. */
+/* Ids per chunk of the sampling race.  A constant of the sampler's
+ * definition (the race first picks a chunk by its weight sum, then an id
+ * inside it), fixed with that definition: two levels keep the per-id Philox
+ * noise to one chunk per sample.  Any implementation of the same sampler
+ * must use the same value to give the same tokens. */
 #define SVO_RACE_CHUNK 2048
 
 /* The two-level exponential race over w[0..V) with `chunk` ids per chunk

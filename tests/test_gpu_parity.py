@@ -15,6 +15,7 @@ import torch
 import lossless_draft_verification_amd as sv
 import oracle
 import workloads
+from _parity import count
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +26,11 @@ MARGIN = 1e-6
 # A request is exempt for its cut only below this gap.
 CUT_MARGIN = 1e-9
 P_RTOL = 1e-5
+# p at the drafts of a filtered stochastic row uses the thresholds pass's
+# kept sum S', which both sides hold to about 1e-13 (fixed-point sums of an
+# fp64 exponential on the GPU, sequential fp64 sums in the oracle); the
+# 1e-9 cut exemption above relies on that precision, so it is pinned here.
+P_RTOL_FILTERED = 1e-10
 
 
 @pytest.fixture(scope="module")
@@ -50,18 +56,14 @@ def _np(out):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-STATS = {"decisions": 0, "exempt": 0}
-
-
-def _compare(ref, got, name, tokens_key="tokens", extra=()):
+def _compare(ref, got, name, tokens_key="tokens", extra=(), kind="chain"):
     np.testing.assert_array_equal(got["status"], ref["status"], err_msg=f"{name}: status")
     bad = ref["status"] != 0
     assert (got["accept_len"][bad] == 0).all() and (got[tokens_key][bad] == -1).all(), name
     near = (ref["min_margin"] < MARGIN) | (ref["cut_margin"] < CUT_MARGIN)
     ok = (ref["status"] == 0) & ~near
     exempt = (ref["status"] == 0) & near
-    STATS["decisions"] += int(ref["n_decisions"].sum())
-    STATS["exempt"] += int(exempt.sum())
+    count(kind, int(ref["n_decisions"].sum()), int(exempt.sum()), int(ref["status"].size))
     np.testing.assert_array_equal(got["accept_len"][ok], ref["accept_len"][ok], err_msg=f"{name}: accept_len")
     np.testing.assert_array_equal(got[tokens_key][ok], ref[tokens_key][ok], err_msg=f"{name}: tokens")
     for k in extra:
@@ -71,7 +73,7 @@ def _compare(ref, got, name, tokens_key="tokens", extra=()):
     return int(ok.sum()), int(exempt.sum())
 
 
-def _compare_p(ref_p, got_p, ref_status, name, cut_ok=None):
+def _compare_p(ref_p, got_p, ref_status, name, cut_ok=None, filtered=None):
     m = (ref_status == 0)[:, None] & np.isfinite(ref_p)
     if cut_ok is not None:
         m &= cut_ok[:, None]
@@ -80,10 +82,33 @@ def _compare_p(ref_p, got_p, ref_status, name, cut_ok=None):
     big = r >= 1e-30
     rel = np.abs(g[big] - r[big]) / r[big]
     assert (rel <= P_RTOL).all(), (name, float(rel.max()))
+    if filtered is not None and filtered.any():
+        mf = m & filtered[:, None]
+        rf, gf = ref_p[mf], got_p[mf]
+        bf = rf >= 1e-30
+        relf = np.abs(gf[bf] - rf[bf]) / rf[bf]
+        assert (relf <= P_RTOL_FILTERED).all(), (name, "filtered rows", float(relf.max()))
+        assert (gf[~bf] == rf[~bf]).all() or (np.abs(gf[~bf] - rf[~bf]) <= 1e-30).all(), name
     assert (np.abs(g[~big] - r[~big]) <= 1e-30).all(), name
     # unused slots are NaN on both sides
     np.testing.assert_array_equal(np.isnan(got_p[ref_status == 0]), np.isnan(ref_p[ref_status == 0]))
     return float(rel.max()) if rel.size else 0.0
+
+
+def _filtered_requests(inp, top_k, top_p):
+    """Requests whose target is filtered: stochastic, with top-k in (0, V)
+    or top-p in (0, 1)."""
+    bs, V = inp.temperature.shape[0], inp.logits.shape[-1]
+    t = inp.temperature
+    stoch = (t > 0) & np.isfinite(t)
+    on = np.zeros(bs, bool)
+    if top_k is not None:
+        tk = np.asarray(top_k).reshape(bs)
+        on |= (tk > 0) & (tk < V)
+    if top_p is not None:
+        tp = np.asarray(top_p, np.float32).reshape(bs)
+        on |= (tp > 0) & (tp < 1)
+    return stoch & on
 
 
 def run_chain(inp, dev, flags=0, top_k=None, top_p=None):
@@ -101,8 +126,11 @@ def run_chain(inp, dev, flags=0, top_k=None, top_p=None):
 def check_chain(inp, dev, flags=0, top_k=None, top_p=None):
     print(f"[parity] chain {inp.name} flags={flags} filtered={top_k is not None or top_p is not None}", flush=True)
     ref, got = run_chain(inp, dev, flags, top_k, top_p)
-    n_ok, n_ex = _compare(ref, got, inp.name)
-    prel = _compare_p(ref["p_draft"], got["p_draft"], ref["status"], inp.name, ref["cut_margin"] >= CUT_MARGIN)
+    filtered = _filtered_requests(inp, top_k, top_p)
+    kind = "filtered chain" if filtered.any() else ("block chain" if flags & sv.FLAG_BLOCK else "chain")
+    n_ok, n_ex = _compare(ref, got, inp.name, kind=kind)
+    prel = _compare_p(ref["p_draft"], got["p_draft"], ref["status"], inp.name, ref["cut_margin"] >= CUT_MARGIN,
+                      filtered)
     print(f"[parity]   compared {n_ok} requests, exempt {n_ex}, max p rel err {prel:.2e}", flush=True)
     return ref, got
 
@@ -120,7 +148,8 @@ def run_tree(inp, dev, flags=0, top_k=None, top_p=None):
 def check_tree(inp, dev, flags=0, top_k=None, top_p=None):
     print(f"[parity] tree {inp.name} flags={flags} filtered={top_k is not None or top_p is not None}", flush=True)
     ref, got = run_tree(inp, dev, flags, top_k, top_p)
-    n_ok, n_ex = _compare(ref, got, inp.name, extra=("accept_path",))
+    kind = "filtered tree" if _filtered_requests(inp, top_k, top_p).any() else "tree"
+    n_ok, n_ex = _compare(ref, got, inp.name, extra=("accept_path",), kind=kind)
     print(f"[parity]   compared {n_ok} requests, exempt {n_ex}", flush=True)
     return ref, got
 
@@ -282,7 +311,7 @@ def test_workspace_reuse_chain_then_tree(dev, flags):
         out = sv.verify_tree(_t(t.logits, dev), _t(t.node_tokens, dev), _t(t.parent, dev), _t(t.temperature, dev),
                              _t(t.seeds, dev), flags=flags, workspace=ws)
         torch.cuda.synchronize()
-        _compare(ref, _np(out), f"reuse tree {i}", extra=("accept_path",))
+        _compare(ref, _np(out), f"reuse tree {i}", extra=("accept_path",), kind="tree")
 
 
 # ---------------------------------------------------- random small shapes
@@ -568,15 +597,6 @@ def test_block_rule_zero_draft_probabilities(dev):
     inp = workloads.ChainInputs(l, ids, q, np.ones(bs, np.float32), np.arange(bs, dtype=np.uint64) + 40, False,
                                 "block zero probabilities")
     check_chain(inp, dev, flags=sv.FLAG_BLOCK)
-
-
-def test_exemption_rate_is_small():
-    """Runs last in this module: the near-tie exemptions over every parity
-    comparison above stay well below 1e-4 of the decisions."""
-    if STATS["decisions"] == 0:
-        pytest.skip("no parity comparisons ran")
-    print(f"[parity] decisions {STATS['decisions']}, exempt requests {STATS['exempt']}", flush=True)
-    assert STATS["exempt"] <= max(2, 1e-4 * STATS["decisions"])
 
 
 # ---------------------------------------------- top-k / top-p filtered target

@@ -80,3 +80,22 @@ def test_noise_uniforms_are_uniform():
     from scipy import stats
     u = np.array([oracle.noise_uniform(42, 3, 1, y) for y in range(20000)])
     assert stats.kstest(u, "uniform").pvalue > 1e-4
+
+
+# Known-answer vectors of Philox4x32 with 10 rounds, as distributed with the
+# Random123 library of Salmon et al. (its kat_vectors file): counter words
+# c0..c3 and key words k0, k1 in, four output words out.
+PHILOX_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff, 0xffffffff, 0xffffffff, 0xffffffff), (0xffffffff, 0xffffffff),
+     (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", PHILOX_KAT)
+def test_philox_known_answer_vectors(ctr, key, want):
+    got = oracle.philox4x32_10(ctr, key)
+    assert [int(w) for w in got] == list(want)

@@ -2,9 +2,10 @@
 
 Page "New approaches to speculative decoding: block drafts, load-aware
 verification and PD disaggregation", section "Deciding how much to verify by
-load", defines adaptive verification: every (request, position) slot is
-scored by its survival probability (the running product of the request's
-confidences), all slots are admitted from the highest score down, and the
+load", defines adaptive verification: a (request, position) slot is worth
+the chance that the request's drafts are all still accepted at that
+position, the product of its confidences up to there; slots are admitted
+best first, and the
 number admitted maximises expected tokens over the step's cost; page "The
 speculative decoding zoo", section "The finer loop: DSpark's confidence
 budget", adds the earlier-position-first tie rule.
@@ -43,9 +44,19 @@ def _page_example():
     out = []
     for case in g["cases"]:
         batch = case["batch"]
-        level = torch.cat([torch.full((batch // 2, K), 0.9), torch.full((batch - batch // 2, K), 0.55)])
-        conf = (level * torch.rand(batch, K).mul(0.2).add(0.9)).clamp(max=0.99).numpy()
-        cost = np.array([g["t_draft"] + step_time(batch + b) for b in range(batch * K + 1)])
+        half = batch // 2
+        # one [batch, K] uniform draw per batch, in the page's order; each
+        # confidence is a base level (0.9 for the first half of the batch,
+        # 0.55 for the rest) scaled by a jitter in [0.9, 1.1), in fp32,
+        # capped at 0.99
+        u = torch.rand(batch, K).numpy()
+        jitter = u * np.float32(0.2) + np.float32(0.9)
+        accurate = np.float32(0.9) * jitter[:half]
+        other = np.float32(0.55) * jitter[half:]
+        conf = np.minimum(np.concatenate([accurate, other]), np.float32(0.99)).astype(np.float32)
+        cost = np.empty(batch * K + 1)
+        for b in range(batch * K + 1):
+            cost[b] = g["t_draft"] + step_time(batch + b)
         out.append((case, conf, cost, step_time, g["t_draft"], K))
     return out
 
