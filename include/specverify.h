@@ -214,6 +214,23 @@ sv_status sv_workspace_init(void* workspace, size_t bytes, void* stream);
 sv_status sv_verify_chain(const sv_chain_desc* desc /* [host] */, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Chain verification without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It is sv_verify_chain with the
+ * workspace replaced by a fixed array of SV_SCRATCH_BYTES in the library's
+ * device memory (one per GPU, held until the process ends); it allocates
+ * nothing.  Shapes whose workspace would not fit it, and batches above
+ * SV_SCRATCH_MAX_BATCH, return SV_ERR_WORKSPACE_TOO_SMALL and enqueue
+ * nothing.  Each call first clears the array's control block and its
+ * requests' counters with a small fill kernel (so a call after one that
+ * reported SV_REQ_INTERNAL needs no reset).  Every call on one GPU uses that
+ * GPU's one array: calls that may overlap in time on the same GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Same descriptor, flags, results and errors as sv_verify_chain otherwise. */
+#define SV_SCRATCH_BYTES (8u << 20)
+#define SV_SCRATCH_MAX_BATCH 1024
+sv_status sv_verify_chain_noalloc(const sv_chain_desc* desc /* [host] */, void* stream);
+
 /* Target-only tree verification (stochastic or greedy per request). */
 sv_status sv_verify_tree(const sv_tree_desc* desc /* [host] */, void* workspace, size_t workspace_bytes,
                          void* stream);

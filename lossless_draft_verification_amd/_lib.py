@@ -29,6 +29,7 @@ REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE, REQ_
 FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED, FLAG_STATS_ONLY, FLAG_DECIDE_ONLY, FLAG_BLOCK = 1, 2, 4, 8, 16, 32
 
 MAX_BATCH, MAX_DRAFT, MAX_NODES, MAX_VOCAB = 65536, 63, 64, 1 << 24
+SCRATCH_BYTES, SCRATCH_MAX_BATCH = 8 << 20, 1024
 PLAN_MAX_SLOTS = 8192
 
 _P = ctypes.c_void_p
@@ -98,6 +99,8 @@ def lib():
                 L.sv_workspace_init.argtypes = [_P, _SZ, _P]
                 L.sv_verify_chain.restype = ctypes.c_int
                 L.sv_verify_chain.argtypes = [ctypes.POINTER(ChainDesc), _P, _SZ, _P]
+                L.sv_verify_chain_noalloc.restype = ctypes.c_int
+                L.sv_verify_chain_noalloc.argtypes = [ctypes.POINTER(ChainDesc), _P]
                 L.sv_verify_tree.restype = ctypes.c_int
                 L.sv_verify_tree.argtypes = [ctypes.POINTER(TreeDesc), _P, _SZ, _P]
                 L.sv_compact_kv.restype = ctypes.c_int
@@ -259,6 +262,22 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
     Returns a dict of device tensors: accept_len [bs], tokens [bs, k+1],
     status [bs] (int32), and p_draft [bs, k] float64 if requested.
     """
+    return _verify_chain(logits, draft_ids, temperature, seeds, draft_probs, onehot, flags, return_p_draft,
+                         workspace, top_k, top_p, noalloc=False)
+
+
+def verify_chain_noalloc(logits, draft_ids, temperature, seeds, draft_probs=None, onehot=False, *, flags=0,
+                         return_p_draft=False, top_k=None, top_p=None):
+    """verify_chain through sv_verify_chain_noalloc: the library's fixed
+    per-GPU scratch array instead of a workspace (the C call allocates
+    nothing; this wrapper still allocates the output tensors).  Calls on one
+    GPU must not overlap in time."""
+    return _verify_chain(logits, draft_ids, temperature, seeds, draft_probs, onehot, flags, return_p_draft,
+                         None, top_k, top_p, noalloc=True)
+
+
+def _verify_chain(logits, draft_ids, temperature, seeds, draft_probs, onehot, flags, return_p_draft, workspace,
+                  top_k, top_p, noalloc):
     if logits.dim() != 3:
         raise ValueError("logits must be [batch, k+1, vocab]")
     device = logits.device
@@ -290,16 +309,23 @@ def verify_chain(logits, draft_ids, temperature, seeds, draft_probs=None, onehot
         out["p_draft"] = torch.empty(bs, k, dtype=torch.float64, device=device)
     tk = None if top_k is None else _on(top_k.reshape(bs), device, torch.int32, "top_k")
     tp = None if top_p is None else _on(top_p.reshape(bs), device, torch.float32, "top_p")
-    need = chain_workspace_bytes(bs, k, V, code)
-    if need == 0:
-        raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_chain_workspace_bytes")
-    ws = workspace if workspace is not None else default_workspace(device)
-    ws.ensure(need)
+    ws = None
+    if not noalloc:
+        need = chain_workspace_bytes(bs, k, V, code)
+        if need == 0:
+            raise SpecVerifyError(ERR_INVALID_ARGUMENT, "sv_chain_workspace_bytes")
+        ws = workspace if workspace is not None else default_workspace(device)
+        ws.ensure(need)
     d = ChainDesc(bs, k, V, code, logits.data_ptr(), lstride, DRAFT_ONEHOT if onehot else DRAFT_PROBS,
                   q.data_ptr() if q is not None else None, qstride, ids.data_ptr() if k > 0 else None,
                   temp.data_ptr(), sd.data_ptr(), out["accept_len"].data_ptr(), out["tokens"].data_ptr(),
                   out["status"].data_ptr(), out["p_draft"].data_ptr() if return_p_draft else None, int(flags),
                   tk.data_ptr() if tk is not None else None, tp.data_ptr() if tp is not None else None)
+    if noalloc:
+        st = lib().sv_verify_chain_noalloc(ctypes.byref(d), _stream(device))
+        if st != OK:
+            raise SpecVerifyError(st, "sv_verify_chain_noalloc")
+        return out
     st = lib().sv_verify_chain(ctypes.byref(d), ctypes.c_void_p(ws.base), ctypes.c_size_t(ws.nbytes),
                                _stream(device))
     if st != OK:

@@ -2585,7 +2585,7 @@ struct Shape {
 // depend on the device or the schedule): every row in Q segments, as many
 // as the K1 workgroups that are resident at once allow (at most 64 and at
 // most one per sub-chunk; one when there are more rows than that).
-static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
+static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races, size_t data_off = kDataOffset) {
   Shape s;
   s.SUB = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
   s.nsub = (int)((V + s.SUB - 1) / s.SUB);
@@ -2612,7 +2612,7 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races) {
     if (ch < 1) ch = 1;
     s.CHr = (int)ch;
   }
-  s.gat_off = kDataOffset;
+  s.gat_off = data_off;
   s.part_off = s.gat_off + align256(sizeof(Gather) * SV_MAX_NODES * (size_t)bs);
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
   s.r_off = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
@@ -2724,6 +2724,28 @@ static bool aligned16(const void* p, int64_t stride_bytes) {
   return ((uintptr_t)p & 15u) == 0 && (stride_bytes & 15) == 0;
 }
 
+// Scratch of sv_verify_chain_noalloc: a fixed device array in place of the
+// caller's workspace, for callers that cannot allocate.  Its layout is the
+// workspace's, with a per-request counter area for SV_SCRATCH_MAX_BATCH
+// requests.  Each device holds its own copy; the host learns its address
+// with hipGetSymbolAddress once per device (the array's name is not a device
+// address in host code).
+static __device__ __align__(256) uint8_t scratch[SV_SCRATCH_BYTES];
+constexpr size_t kScratchDataOffset = kSyncOffset + sizeof(Sync) * SV_SCRATCH_MAX_BATCH;
+static std::atomic<void*> g_scratch[64];
+
+static sv_status scratch_address(void*& out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_ERR_LAUNCH;
+  void* p = g_scratch[dev].load();
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SV_ERR_LAUNCH;
+    g_scratch[dev].store(p);
+  }
+  out = p;
+  return SV_OK;
+}
+
 }  // namespace sv
 
 using namespace sv;
@@ -2785,7 +2807,8 @@ sv_status sv_workspace_init(void* ws, size_t bytes, void* stream) {
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
-sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, void* stream) {
+// Checks a chain descriptor on the host and fills the launch parameters.
+static sv_status chain_params(const sv_chain_desc* d, Params& P) {
   if (d == nullptr) return SV_ERR_INVALID_ARGUMENT;
   if (d->batch < 1 || d->batch > SV_MAX_BATCH || d->max_draft < 0 || d->max_draft > SV_MAX_DRAFT ||
       d->vocab < 1 || d->vocab > SV_MAX_VOCAB)
@@ -2805,7 +2828,6 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
   if (probs && d->max_draft > 0 && (d->draft_probs == nullptr || d->q_row_stride < d->vocab))
     return SV_ERR_INVALID_ARGUMENT;
   const size_t esz = d->logits_dtype == SV_BF16 ? 2 : 4;
-  Params P;
   memset(&P, 0, sizeof P);
   P.mode = MODE_CHAIN;
   P.bs = d->batch;
@@ -2830,8 +2852,36 @@ sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, voi
   P.flags = d->flags;
   P.top_k = d->top_k;
   P.top_p = d->top_p;
+  return SV_OK;
+}
+
+sv_status sv_verify_chain(const sv_chain_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  Params P;
+  const sv_status st = chain_params(d, P);
+  if (st != SV_OK) return st;
   const Shape S = shape_of(P.bs, P.R, P.V, P.dtype, true);
   return launch(P, S, ws, ws_bytes, (hipStream_t)stream);
+}
+
+sv_status sv_verify_chain_noalloc(const sv_chain_desc* d, void* stream) {
+  Params P;
+  sv_status st = chain_params(d, P);
+  if (st != SV_OK) return st;
+  if (P.bs > SV_SCRATCH_MAX_BATCH) return SV_ERR_WORKSPACE_TOO_SMALL;
+  const Shape S = shape_of(P.bs, P.R, P.V, P.dtype, true, kScratchDataOffset);
+  if (S.total > (size_t)SV_SCRATCH_BYTES) return SV_ERR_WORKSPACE_TOO_SMALL;
+  void* base = nullptr;
+  st = scratch_address(base);
+  if (st != SV_OK) return st;
+  // The control block and this call's per-request counters must start at
+  // zero.  A completed call leaves them so, but one that gave up a bounded
+  // wait does not, and the array outlives every caller: clear them with the
+  // fill kernel (no memset node, so the call may be captured in a graph).
+  const size_t clear = kSyncOffset + sizeof(Sync) * (size_t)P.bs;
+  const unsigned blocks = (unsigned)((clear / 16 + kWG - 1) / kWG);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kWG), 0, (hipStream_t)stream, (uint8_t*)base, clear);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+  return launch(P, S, base, (size_t)SV_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 sv_status sv_verify_tree(const sv_tree_desc* d, void* ws, size_t ws_bytes, void* stream) {

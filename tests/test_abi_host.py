@@ -221,3 +221,17 @@ def test_compact_argument_validation(field, value, code):
     d = _compact_desc(**{field: value})
     assert sv.lib().sv_compact_kv(ctypes.byref(d), None) == code
     assert sv.lib().sv_compact_kv(None, None) == 1
+
+
+def test_noalloc_entry_point_rejects_before_any_hip_call():
+    """sv_verify_chain_noalloc checks the descriptor and the scratch's limits
+    on the host first: no device is touched for a bad call."""
+    L = sv.lib()
+    assert L.sv_verify_chain_noalloc(None, None) == _lib.ERR_INVALID_ARGUMENT
+    d = _chain_desc(batch=sv.SCRATCH_MAX_BATCH + 1)
+    assert L.sv_verify_chain_noalloc(ctypes.byref(d), None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    d = _chain_desc(batch=64, max_draft=0, vocab=1 << 24, logits_row_stride=1 << 24, draft_kind=sv.DRAFT_ONEHOT,
+                    draft_probs=None, draft_ids=None)
+    assert L.sv_verify_chain_noalloc(ctypes.byref(d), None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    d = _chain_desc(vocab=0)
+    assert L.sv_verify_chain_noalloc(ctypes.byref(d), None) == _lib.ERR_INVALID_ARGUMENT
