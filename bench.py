@@ -1,27 +1,35 @@
 """Benchmark: batched lossless draft verification on one MI355X.
 
-One step = one sv_verify_chain call (the whole hot path: streaming row
-statistics, per-request decisions, residual/bonus sampling) over one batch
-of the chain workload bs=64, k=7, V=128256, bf16 target logits, half the
-requests greedy and half at T=0.8 with fp32 draft probabilities.  Inputs
-are resident in HBM before the timed region; the timed steps rotate over
-several input sets whose total size exceeds the 256 MB Infinity Cache, so
-the stream really comes from HBM.
+One step = one verification call (the whole hot path: streaming row
+statistics, per-request decisions, residual/bonus sampling) over one batch.
+The default workload is the chain workload bs=64, k=7, V=128256, bf16 target
+logits, half the requests greedy and half at T=0.8 with fp32 draft
+probabilities; --workload picks the others (chain_small, chain_fp32,
+onehot_bf16, tree_fp32).  Inputs are resident in HBM before the timed
+region; the timed steps rotate over several input sets whose total size
+exceeds the 256 MB Infinity Cache, so the stream really comes from HBM.
 
 The call is two stream-ordered kernels: the row-statistics pass (streams
 every logit row once; the dominant kernel) and the decision/sampling pass.
-Two timed passes over the same K steps:
+Three timed passes:
   1. throughput: K plain calls between two events -> value, ms_per_step;
   2. kernels: the same K calls, split into their two phases
      (FLAG_STATS_ONLY, FLAG_DECIDE_ONLY) and grouped by input set: the
      row-statistics launches of all sets between one event pair, then their
      decision launches between the next (each set has its own workspace)
-     -> each kernel's mean launch duration, and the roofline of the
-     row-statistics kernel (its algorithmic bytes / that duration, against
-     the 8 TB/s HBM peak).
-The fused schedule is one launch; there the roofline covers the whole call.
+     -> each kernel's mean launch duration;
+  3. read ceiling: sv_stream_read over the same sets' logit buffers (the
+     row-statistics pass's bytes, access pattern and rotation) at a few grid
+     sizes -> the attainable read bandwidth of the chip for this stream.
+`roofline` is the row-statistics kernel (its algorithmic bytes / its launch
+time, against the 8 TB/s HBM peak), with `roofline.call` for the whole call
+(all its algorithmic bytes over the call time, and over the sum of its
+kernels' times; HBM bytes by counters over the kernels' times when a counter
+record of this kernel source is committed) and `pct_of_ceiling`.
 
-Prints one JSON line, with the oracle timed on the host as a CPU baseline.
+Prints one JSON line, with the acceptance statistics of the timed inputs and
+the oracle timed on the host (one core, and sharded by request over the
+host's cores) as a CPU baseline.
 """
 from __future__ import annotations
 
@@ -39,10 +47,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOADS = {
-    "chain_bf16_mixed": "chain verify bs=64 k=7 V=128256, bf16 target logits, half greedy, half T=0.8 with fp32 draft probs",
+    "chain_small": "chain verify bs=1 k=3 V=1000, fp32 target logits, T=1, fp32 draft probs (launch-bound)",
     "chain_fp32": "chain verify bs=8 k=3 V=128256, fp32 target logits, T=1, fp32 draft probs",
+    "chain_bf16_mixed": "chain verify bs=64 k=7 V=128256, bf16 target logits, half greedy, half T=0.8 with fp32 draft probs",
     "onehot_bf16": "one-hot (target-only) chain verify bs=256 k=3 V=151936, bf16 target logits, T=1",
+    "tree_fp32": "target-only tree verify bs=48 N=8 (5 steps x top-4 topology) V=128256, fp32 target logits, T=1",
 }
+# grid sizes of the read-ceiling stream (workgroups of 256 threads)
+CEILING_GRIDS = (1024, 1536, 2048, 4096, 8192)
 KERNEL_SOURCE = os.path.join(ROOT, "lossless_draft_verification_amd", "csrc", "specverify.hip")
 
 
@@ -97,6 +109,27 @@ def algorithmic_bytes(inp, accept_len, block=False):
     return int(stats), int(decide)
 
 
+def tree_algorithmic_bytes(inp, accept_len):
+    """Bytes a tree call must move, from the actual outcomes, split by
+    phase.  Row statistics: every node's logit row once (all N rows are
+    read), the gather of each node's token logit in its parent's row, the
+    temperature.  Decision/sampling: per-request scalars (temperature, seed,
+    parents, node tokens), the re-read of the one sampled row per stochastic
+    request (p with the tried children removed, or the bonus p: no q), and
+    the outputs (accept_len, accept_path, tokens, status)."""
+    bs, N, V = inp.logits.shape
+    bl = inp.logits.dtype.itemsize
+    stoch = (inp.temperature > 0) & np.isfinite(inp.temperature)
+    stats = decide = 0
+    for b in range(bs):
+        stats += N * V * bl + (N - 1) * (bl + 4 + 4) + 4
+        decide += 4 + 8 + 8 * N
+        if stoch[b]:
+            decide += V * bl
+        decide += 4 + 8 * N + 4
+    return int(stats), int(decide)
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` measured with rocprofv3 counters for
     this kernel source (committed under profiles/), or None if there is no
@@ -111,27 +144,138 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, seconds: float, rule: str = "standard", top_k: int = 0, top_p: float = 1.0):
+def _pmc_per_dispatch(db_path, counter):
+    """Mean value of `counter` per dispatch of each kernel in a rocprofv3
+    results database."""
+    import sqlite3
+    import collections
+
+    con = sqlite3.connect(db_path)
+    q = """select ks.kernel_name, ip.name, pe.value, kd.id from rocpd_pmc_event pe
+           join rocpd_info_pmc ip on pe.pmc_id = ip.id
+           join rocpd_event ev on pe.event_id = ev.id
+           join rocpd_kernel_dispatch kd on kd.event_id = ev.id
+           join rocpd_info_kernel_symbol ks on kd.kernel_id = ks.id"""
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for kname, cname, value, did in con.execute(q):
+        if cname == counter:
+            tot[kname] += value
+            disp[kname].add(did)
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def write_traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, kernels=("k1_kernel", "k23_kernel")):
+    """Write profiles/traffic_<workload>.json from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the benchmark, and of a
+    plain device copy of known size (bench.py --copy-calibration-mib 1024),
+    whose counts scale the kernel's to bytes."""
+    copy_bytes = 1024 << 20
+
+    def pick(d, name):
+        vals = [v for k, v in d.items() if name in k]
+        if not vals:
+            raise SystemExit(f"no dispatch of {name} in the database")
+        return vals[0]
+
+    cf = pick(_pmc_per_dispatch(copy_fetch_db, "FETCH_SIZE"), "copyBuffer")
+    cw = pick(_pmc_per_dispatch(copy_write_db, "WRITE_SIZE"), "copyBuffer")
+    ff, wf = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    fetch = _pmc_per_dispatch(fetch_db, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_db, "WRITE_SIZE")
+    rec = {"workload": WORKLOADS[workload], "kernel_source_sha256_16": kernel_source_hash(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": cf, "write_size_kib": cw,
+                           "fetch_factor": ff, "write_factor": wf},
+           "kernels": {}}
+    for k in kernels:
+        fk, wk = pick(fetch, k), pick(write, k)
+        rec["kernels"][k] = {"fetch_size_kib_per_dispatch": round(fk, 1), "write_size_kib_per_dispatch": round(wk, 1),
+                             "bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf))}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def positions_of(inp):
+    """Verified draft positions of one call: sum of k_b (chain) or N - 1 per
+    request (tree)."""
+    if hasattr(inp, "parent"):
+        return int(inp.batch * (inp.num_nodes - 1))
+    return int((inp.draft_ids >= 0).cumprod(axis=1).sum()) if inp.max_draft else 0
+
+
+def _oracle_call(inp, lo, hi, rule, filt):
+    """The oracle on requests [lo, hi) of one input set (slices along the
+    batch axis are contiguous views; the oracle's C loop runs without the
+    interpreter lock)."""
     import oracle
+
+    f = {k: v[lo:hi] for k, v in filt.items()}
+    if hasattr(inp, "parent"):
+        return oracle.verify_tree(inp.logits[lo:hi], inp.node_tokens[lo:hi], inp.parent[lo:hi],
+                                  inp.temperature[lo:hi], inp.seeds[lo:hi], **f)
+    return oracle.verify_chain(inp.logits[lo:hi], inp.draft_ids[lo:hi], inp.temperature[lo:hi], inp.seeds[lo:hi],
+                               draft_probs=None if inp.draft_probs is None else inp.draft_probs[lo:hi],
+                               onehot=inp.onehot, rule=rule, **f)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inputs, seconds: float, threads: int, rule: str = "standard", top_k: int = 0, top_p: float = 1.0):
+    """The oracle timed on the host on full calls of input set 0: on one
+    core, then sharded by request over `threads` threads (each thread runs
+    the unchanged oracle on a contiguous slice of the batch).  Also returns
+    the oracle's decision count and near-tie (margin < 1e-6) requests of
+    that set."""
+    from concurrent.futures import ThreadPoolExecutor
 
     inp = inputs[0]
     bs = inp.batch
     filt = {}
     if top_k or top_p != 1.0:
         filt = dict(top_k=np.full(bs, top_k, np.int32), top_p=np.full(bs, top_p, np.float32))
-    positions = int((inp.draft_ids >= 0).cumprod(axis=1).sum()) if inp.max_draft else 0
+    positions = positions_of(inp)
+    ref = _oracle_call(inp, 0, bs, rule, filt)
+    margins = {"decisions": int(ref["n_decisions"].sum()),
+               "near_tie_requests": int(((ref["min_margin"] < 1e-6) & (ref["status"] == 0)).sum())}
     calls = 0
     t0 = time.perf_counter()
     while True:
-        oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=inp.draft_probs,
-                            onehot=inp.onehot, rule=rule, **filt)
+        _oracle_call(inp, 0, bs, rule, filt)
         calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
+        el1 = time.perf_counter() - t0
+        if el1 >= seconds:
             break
-    return {"value": positions * calls / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} full calls of the same workload (input set 0), single-threaded C oracle, "
-                      f"{el:.1f} s"}
+    one = positions * calls / el1
+    nt = max(1, min(threads, bs))
+    bounds = [(i * bs // nt, (i + 1) * bs // nt) for i in range(nt)]
+    calls_n = 0
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(lambda lh: _oracle_call(inp, lh[0], lh[1], rule, filt), bounds))
+            calls_n += 1
+            eln = time.perf_counter() - t0
+            if eln >= seconds:
+                break
+    many = positions * calls_n / eln
+    return ({"value": many, "unit": "positions/s", "cores": nt, "kind": "oracle", "cpu_model": cpu_model(),
+             "host_cpu_count": os.cpu_count(),
+             "sample": f"{calls_n} full calls of the same workload (input set 0), the C oracle sharded by request "
+                       f"over {nt} threads, {eln:.1f} s",
+             "single_core": {"value": one, "unit": "positions/s", "cores": 1,
+                             "sample": f"{calls} full calls, single-threaded, {el1:.1f} s"}},
+            margins)
 
 
 def bench_compact(args, sv, torch, dev, workloads):
@@ -245,6 +389,56 @@ def bench_plan(args, sv, torch, dev):
                       "roofline": {"bound": "latency", "note": "one workgroup; a few thousand slots"}}), flush=True)
 
 
+def read_ceiling(sv, torch, dev, buffers, steps):
+    """Attainable read bandwidth for the row-statistics pass's stream: the
+    same buffers (one per input set, rotated), each launch reading one whole
+    buffer with sv_stream_read, at each grid size of CEILING_GRIDS.
+    Returns (best GB/s, its grid, {grid: GB/s}, bytes per launch)."""
+    sink = torch.zeros(max(CEILING_GRIDS), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nbytes = [b.numel() * b.element_size() for b in buffers]
+    per = {}
+    for g in CEILING_GRIDS:
+        for i in range(len(buffers)):
+            sv.stream_read(buffers[i], sink, g)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            sv.stream_read(buffers[i % len(buffers)], sink, g)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3
+        per[g] = sum(nbytes[i % len(buffers)] for i in range(steps)) / sec / 1e9
+    best = max(per, key=per.get)
+    return per[best], best, per, float(np.mean(nbytes))
+
+
+def acceptance_stats(outs, inputs, tree):
+    """Acceptance of the timed inputs, from the GPU's outputs: drafts
+    accepted at each position (the per-position counter the zoo page names
+    for vLLM), the mean accepted length, and tokens per round (accepted + the
+    emitted one)."""
+    acc = np.concatenate([o["accept_len"] for o in outs])
+    ok = np.concatenate([o["status"] for o in outs]) == 0
+    stoch = np.concatenate([(i.temperature > 0) & np.isfinite(i.temperature) for i in inputs])
+    R = inputs[0].logits.shape[1]
+    depth = R - 1
+    hist = [int(((acc > i) & ok).sum()) for i in range(depth)]
+
+    def summary(sel):
+        if not sel.any():
+            return None
+        return {"requests": int(sel.sum()), "mean_accepted": float(acc[sel].mean()),
+                "mean_tokens_per_round": float(acc[sel].mean() + 1.0),
+                "accepted_per_position": [int(((acc > i) & sel).sum()) for i in range(depth)]}
+
+    return {"calls": len(outs), "accepted_per_position": hist, "mean_accepted": float(acc[ok].mean()),
+            "mean_tokens_per_round": float(acc[ok].mean() + 1.0),
+            "stochastic": summary(ok & stoch), "greedy": summary(ok & ~stoch),
+            "note": "positions are tree depths" if tree else "positions are draft indices"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,10 +452,15 @@ def main():
                     help="top-k filtering of every stochastic request's target (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="top-p filtering of every stochastic request's target (1: off)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds of each oracle timing (one core, all)")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="threads of the sharded oracle timing (capped by the host's cores and the batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["auto", "phased", "fused"], default="auto",
                     help="library schedule (auto: the library's default for the shape)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the attainable read bandwidth (sv_stream_read) over the workload's "
+                         "logit buffers and print its line")
     ap.add_argument("--compact", action="store_true",
                     help="time accepted-path KV compaction (sv_compact_kv) after tree verification instead")
     ap.add_argument("--plan", action="store_true",
@@ -269,11 +468,17 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB a few times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="write profiles/traffic_<workload>.json from four rocprofv3 --pmc result databases "
+                         "(no GPU needed) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verification hot path runs on a single MI355X here; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        write_traffic(args.workload, *args.traffic_from)
+        return
 
     import torch
 
@@ -299,6 +504,7 @@ def main():
     if args.compact:
         bench_compact(args, sv, torch, dev, workloads)
         return
+    tree = args.workload.startswith("tree")
     gen = getattr(workloads, args.workload)
     print(f"[bench] generating {args.sets} input sets of {args.workload}", file=sys.stderr, flush=True)
     inputs = [gen(s) for s in range(args.sets)]
@@ -312,9 +518,23 @@ def main():
             return torch.from_numpy(a.view(np.int64)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    if args.read_ceiling:
+        bufs = [to_dev(inp.logits) for inp in inputs]
+        gbs, grid, per, nb = read_ceiling(sv, torch, dev, bufs, args.steps)
+        print(json.dumps({"metric": "attainable HBM read bandwidth (sv_stream_read), 1 MI355X", "value": gbs,
+                          "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "higher_is_better": True,
+                          "data": "synthetic",
+                          "config": {"workload": WORKLOADS[args.workload] + ": its logit buffers, one per launch",
+                                     "bytes_per_launch": nb, "buffers": len(bufs), "best_grid": grid,
+                                     "gbs_by_grid": {str(k): v for k, v in per.items()}},
+                          "frac_of_peak": gbs / HBM_PEAK_GBS, "us_per_launch": nb / (gbs * 1e3)}), flush=True)
+        return
+
     flags = {"auto": 0, "phased": sv.FLAG_PHASED, "fused": sv.FLAG_FUSED}[args.schedule]
     block = args.rule == "block"
     if block:
+        if tree:
+            raise SystemExit("the block rule is defined for chains only")
         flags |= sv.FLAG_BLOCK
     V0 = inputs[0].vocab
     filtered = (0 < args.top_k < V0) or (0.0 < args.top_p < 1.0)
@@ -322,29 +542,40 @@ def main():
         raise SystemExit("top-k / top-p filtering needs the phased schedule")
     calls, plain_calls = [], []
     for inp in inputs:
-        dl, di, dt, ds = to_dev(inp.logits), to_dev(inp.draft_ids), to_dev(inp.temperature), to_dev(inp.seeds)
-        dq = to_dev(inp.draft_probs)
         fk = fp = None
         if filtered:
             fk = torch.full((inp.batch,), args.top_k, dtype=torch.int32, device=dev)
             fp = torch.full((inp.batch,), args.top_p, dtype=torch.float32, device=dev)
+        dl, dt, ds = to_dev(inp.logits), to_dev(inp.temperature), to_dev(inp.seeds)
+        if tree:
+            dn, dp = to_dev(inp.node_tokens), to_dev(inp.parent)
+            mk = lambda f, w, k=None, p=None: sv.PreparedTree(dl, dn, dp, dt, ds, flags=f, workspace=w, top_k=k,
+                                                              top_p=p)
+        else:
+            di, dq = to_dev(inp.draft_ids), to_dev(inp.draft_probs)
+            mk = lambda f, w, k=None, p=None: sv.PreparedChain(dl, di, dt, ds, draft_probs=dq, onehot=inp.onehot,
+                                                               flags=f, workspace=w, top_k=k, top_p=p)
+        if filtered:
             # the same call without the filter: its statistics pass alone, for timing
-            plain_calls.append(sv.PreparedChain(dl, di, dt, ds, draft_probs=dq, onehot=inp.onehot, flags=flags,
-                                                workspace=sv.Workspace(1 << 20, dev)))
-        calls.append(sv.PreparedChain(dl, di, dt, ds, draft_probs=dq, onehot=inp.onehot, flags=flags,
-                                      workspace=sv.Workspace(1 << 20, dev), top_k=fk, top_p=fp))
-    resident = sum(c.logits.numel() * c.logits.element_size() + (c.q.numel() * 4 if c.q is not None else 0)
-                   for c in calls)
+            plain_calls.append(mk(flags, sv.Workspace(1 << 20, dev)))
+        calls.append(mk(flags, sv.Workspace(1 << 20, dev), fk, fp))
+    resident = sum(c.logits.numel() * c.logits.element_size()
+                   + (c.q.numel() * 4 if getattr(c, "q", None) is not None else 0) for c in calls)
     stream = torch.cuda.current_stream(dev)
-    # algorithmic bytes of each set, from its outcome
-    alg = []
+    # algorithmic bytes of each set, from its outcome; the outcomes' acceptance
+    alg, outs = [], []
     for c, inp in zip(calls, inputs):
         c.launch()
         torch.cuda.synchronize()
         if (c.out["status"] != 0).any():
             raise RuntimeError("a request reported a non-OK status on the benchmark inputs")
-        alg.append(algorithmic_bytes(inp, c.out["accept_len"].cpu().numpy(), block)
-                   + (filter_bytes(inp, args.top_k, args.top_p),))
+        out = {n: t.cpu().numpy() for n, t in c.out.items()}
+        outs.append(out)
+        if tree:
+            alg.append(tree_algorithmic_bytes(inp, out["accept_len"]) + (0,))
+        else:
+            alg.append(algorithmic_bytes(inp, out["accept_len"], block)
+                       + (filter_bytes(inp, args.top_k, args.top_p),))
         if args.schedule != "fused":
             # the split phases must reproduce the plain call
             ref = {n: t.clone() for n, t in c.out.items()}
@@ -355,7 +586,7 @@ def main():
             torch.cuda.synchronize()
             if any(not torch.equal(ref[n], c.out[n]) for n in ref):
                 raise RuntimeError("split-phase call differs from the plain call")
-    positions = [int((inp.draft_ids >= 0).cumprod(axis=1).sum()) for inp in inputs]
+    positions = [positions_of(inp) for inp in inputs]
 
     for i in range(args.warmup):
         calls[i % len(calls)].launch()
@@ -407,6 +638,7 @@ def main():
     second_ms = np.array([e[1].elapsed_time(e[2]) for e in ev]) / S if split else None
     stats_bytes = np.array([a[0] for a in alg] * groups, dtype=np.float64)
     decide_bytes = np.array([a[1] for a in alg] * groups, dtype=np.float64)
+    kf_ms = None
     if split and filtered:
         # the first phase is the statistics pass then the thresholds pass;
         # the roofline covers the statistics pass timed alone
@@ -421,7 +653,34 @@ def main():
         kernel = "fused verify (fused_kernel)"
         kbytes = stats_bytes + decide_bytes
     achieved = kbytes.sum() / (first_ms.sum() * S * 1e-3) / 1e9
-    traffic = None if (block or filtered) else load_traffic(args.workload, "k1_kernel" if split else "fused_kernel")
+
+    # pass 3: the attainable read bandwidth of the same stream
+    gbs_ceiling, grid_ceiling, ceiling_by_grid, _ = read_ceiling(sv, torch, dev, [c.logits for c in calls], K)
+
+    # the whole call
+    call_bytes = (stats_bytes + decide_bytes + filt_bytes).mean()
+    call_us = total_ms * 1e3 / K
+    kernel_us = float(first_ms.mean() * 1e3 + (second_ms.mean() * 1e3 if split else 0.0)
+                      + (kf_ms.mean() * 1e3 if kf_ms is not None else 0.0))
+    k1_name = "k1_kernel" if split else "fused_kernel"
+    traffic = None if (block or filtered) else load_traffic(args.workload, k1_name)
+    traffic23 = None if (block or filtered or not split) else load_traffic(args.workload, "k23_kernel")
+    call = {
+        "kernels": ("k1_kernel + k23_kernel" if split else "fused_kernel")
+                   + (" + kf_kernel" if filtered else "") + (" + kr_kernel" if block else ""),
+        "algorithmic_bytes": float(call_bytes),
+        "us_per_call": call_us,
+        "achieved_gbs_by_call_time": call_bytes / (call_us * 1e3),
+        "frac_by_call_time": call_bytes / (call_us * 1e3) / HBM_PEAK_GBS,
+        "kernel_us_sum": kernel_us,
+        "achieved_gbs_by_kernel_time": call_bytes / (kernel_us * 1e3),
+        "frac_by_kernel_time": call_bytes / (kernel_us * 1e3) / HBM_PEAK_GBS,
+    }
+    if traffic is not None and (traffic23 is not None or not split):
+        hbm = traffic + (traffic23 or 0)
+        call["hbm_bytes_by_counters"] = hbm
+        call["hbm_gbs_by_kernel_time"] = hbm / (kernel_us * 1e3)
+        call["hbm_frac_by_kernel_time"] = hbm / (kernel_us * 1e3) / HBM_PEAK_GBS
     line = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% of peak), 1 MI355X",
         "value": value,
@@ -430,6 +689,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": total_ms / K,
+        "us_per_call": call_us,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -440,7 +700,7 @@ def main():
                         + (f", target filtered top-k {args.top_k} top-p {args.top_p}" if filtered else ""),
             "rule": args.rule,
             "batch": int(inputs[0].batch),
-            "k": int(inputs[0].max_draft),
+            ("nodes" if tree else "k"): int(inputs[0].num_nodes if tree else inputs[0].max_draft),
             "vocab": int(inputs[0].vocab),
             "logits_dtype": "bf16" if inputs[0].logits.dtype == np.uint16 else "f32",
             "positions_per_step": positions[0],
@@ -461,8 +721,15 @@ def main():
             "algorithmic_bytes_per_launch": float(kbytes.mean()),
             "launch_us_mean": float(first_ms.mean() * 1e3),
             "launch_us_p50": float(np.median(first_ms) * 1e3),
+            "ceiling_gbs": gbs_ceiling,
+            "ceiling_grid": grid_ceiling,
+            "ceiling_gbs_by_grid": {str(k): v for k, v in ceiling_by_grid.items()},
+            "pct_of_ceiling": 100.0 * achieved / gbs_ceiling,
+            "call": call,
         },
+        "acceptance": acceptance_stats(outs, inputs, tree),
     }
+    line["roofline"]["call"]["pct_of_ceiling_by_kernel_time"] = 100.0 * call["achieved_gbs_by_kernel_time"] / gbs_ceiling
     if split:
         line["roofline"]["other_kernel"] = {
             "kernel": ("residual masses, decisions and sampling (kr_kernel + k23_kernel)" if block
@@ -470,6 +737,7 @@ def main():
             "algorithmic_bytes_per_launch": float(decide_bytes.mean()),
             "launch_us_mean": float(second_ms.mean() * 1e3),
             "achieved": float(decide_bytes.sum() / (second_ms.sum() * S * 1e-3) / 1e9),
+            "traffic": traffic23,
         }
     if split and filtered:
         line["roofline"]["filter_kernel"] = {
@@ -481,8 +749,10 @@ def main():
         }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds, args.rule,
-                                            args.top_k if filtered else 0, args.top_p if filtered else 1.0)
+        base, margins = cpu_baseline(inputs, args.cpu_seconds, args.cpu_threads, args.rule,
+                                     args.top_k if filtered else 0, args.top_p if filtered else 1.0)
+        line["cpu_baseline"] = base
+        line["acceptance"]["oracle_set0"] = margins
     print(json.dumps(line), flush=True)
 
 

@@ -321,6 +321,15 @@ typedef struct {
 
 sv_status sv_compact_kv(const sv_compact_desc* desc /* [host] */, void* stream);
 
+/* Measurement aid, not part of verification: streams `bytes` (a multiple
+ * of 16, 16-byte aligned) from `src` with the row-statistics pass's access
+ * pattern (16-byte nontemporal loads, contiguous shares of `workgroups`
+ * workgroups of 256 threads) and XOR-folds them, writing one word per
+ * workgroup to sink[workgroups].  Its bandwidth is the attainable read
+ * ceiling that the verification kernels are quoted against.  Device
+ * pointers; SV_ERR_INVALID_ARGUMENT for bad sizes or alignment. */
+sv_status sv_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,5 +10,5 @@ from ._lib import (  # noqa: F401
     MAX_VOCAB, REQ_BAD_DRAFT_ID, REQ_BAD_TEMPERATURE, REQ_BAD_TREE, REQ_INTERNAL, REQ_NONFINITE, REQ_OK,
     LIB_PATH, PLAN_MAX_SLOTS, PreparedChain, SpecVerifyError, Workspace, abi_version, chain_workspace_bytes, compact_kv, default_workspace, lib, plan_budget,
     row_stats, row_stats_workspace_bytes, status_string, tree_workspace_bytes, verify_chain, verify_chain_noalloc,
-    verify_tree, SCRATCH_BYTES, SCRATCH_MAX_BATCH,
+    verify_tree, SCRATCH_BYTES, SCRATCH_MAX_BATCH, PreparedTree, stream_read,
 )

@@ -107,6 +107,8 @@ def lib():
                 L.sv_compact_kv.argtypes = [ctypes.POINTER(CompactDesc), _P]
                 L.sv_plan_budget.restype = ctypes.c_int
                 L.sv_plan_budget.argtypes = [ctypes.POINTER(PlanDesc), _P]
+                L.sv_stream_read.restype = ctypes.c_int
+                L.sv_stream_read.argtypes = [_P, _SZ, _P, _I32, _P]
                 L.sv_row_stats.restype = ctypes.c_int
                 L.sv_row_stats.argtypes = [_I32, _I32, ctypes.c_int, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
                 _lib = L
@@ -468,6 +470,69 @@ def row_stats(logits, temperature, *, workspace=None):
     if st != OK:
         raise SpecVerifyError(st, "sv_row_stats")
     return out
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None):
+    """Enqueue one sv_stream_read of the whole of `src` (a device tensor,
+    16-byte aligned, a multiple of 16 bytes) into `sink` (uint32, at least
+    `workgroups` entries): the read-bandwidth ceiling measurement."""
+    s = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(src.device).cuda_stream)
+    st = lib().sv_stream_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_size_t(src.numel() * src.element_size()),
+                              ctypes.c_void_p(sink.data_ptr()), int(workgroups), s)
+    if st != OK:
+        raise SpecVerifyError(st, "sv_stream_read")
+
+
+class PreparedTree:
+    """A tree verification with its descriptor built once, for calling
+    repeatedly on fixed device buffers.  launch() enqueues one sv_verify_tree
+    on the current stream; outputs are overwritten in place."""
+
+    def __init__(self, logits, node_tokens, parent, temperature, seeds, *, flags=0, workspace=None, top_k=None,
+                 top_p=None):
+        device = logits.device
+        bs, N, V = (int(x) for x in logits.shape)
+        code = _dtype_code(logits)
+        self.logits, lstride = _rows_view(logits, 2)
+        self.nt = _on(node_tokens.reshape(bs, N), device, torch.int32, "node_tokens")
+        self.par = _on(parent.reshape(bs, N), device, torch.int32, "parent")
+        self.temp = _on(temperature.reshape(bs), device, torch.float32, "temperature")
+        self.seeds = _seed_tensor(seeds, bs, device)
+        self.out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=device),
+                        accept_path=torch.empty(bs, N, dtype=torch.int32, device=device),
+                        tokens=torch.empty(bs, N, dtype=torch.int32, device=device),
+                        status=torch.empty(bs, dtype=torch.int32, device=device))
+        self.top_k = None if top_k is None else _on(top_k.reshape(bs), device, torch.int32, "top_k")
+        self.top_p = None if top_p is None else _on(top_p.reshape(bs), device, torch.float32, "top_p")
+        self.ws = workspace if workspace is not None else default_workspace(device)
+        self.ws.ensure(tree_workspace_bytes(bs, N, V, code))
+        self.device = device
+        self.desc = TreeDesc(bs, N, V, code, self.logits.data_ptr(), lstride, self.nt.data_ptr(), self.par.data_ptr(),
+                             self.temp.data_ptr(), self.seeds.data_ptr(), self.out["accept_len"].data_ptr(),
+                             self.out["accept_path"].data_ptr(), self.out["tokens"].data_ptr(),
+                             self.out["status"].data_ptr(), int(flags),
+                             self.top_k.data_ptr() if self.top_k is not None else None,
+                             self.top_p.data_ptr() if self.top_p is not None else None)
+        self._fn = lib().sv_verify_tree
+        self._phase_descs, self._phase_refs = [], {}
+
+    def launch(self, stream=None, phase_flag=0):
+        """Enqueue the call; phase_flag FLAG_STATS_ONLY or FLAG_DECIDE_ONLY
+        enqueues only that phase."""
+        s = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream)
+        d = self.desc
+        if phase_flag:
+            ref = self._phase_refs.get(phase_flag)
+            if ref is None:
+                d2 = TreeDesc.from_buffer_copy(self.desc)
+                d2.flags = int(self.desc.flags) | int(phase_flag)
+                self._phase_descs.append(d2)
+                ref = self._phase_refs[phase_flag] = ctypes.byref(d2)
+        else:
+            ref = ctypes.byref(d)
+        st = self._fn(ref, ctypes.c_void_p(self.ws.base), ctypes.c_size_t(self.ws.nbytes), s)
+        if st != OK:
+            raise SpecVerifyError(st, "sv_verify_tree")
 
 
 class PreparedChain:

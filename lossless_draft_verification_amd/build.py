@@ -8,7 +8,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "specverify.hip")
-SRCS = [SRC, os.path.join(PKG, "csrc", "planner.hip"), os.path.join(PKG, "csrc", "compact.hip")]
+SRCS = [SRC, os.path.join(PKG, "csrc", "planner.hip"), os.path.join(PKG, "csrc", "compact.hip"),
+        os.path.join(PKG, "csrc", "stream_read.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 

@@ -235,3 +235,13 @@ def test_noalloc_entry_point_rejects_before_any_hip_call():
     assert L.sv_verify_chain_noalloc(ctypes.byref(d), None) == _lib.ERR_WORKSPACE_TOO_SMALL
     d = _chain_desc(vocab=0)
     assert L.sv_verify_chain_noalloc(ctypes.byref(d), None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_stream_read_rejects_bad_arguments_before_any_hip_call():
+    L = sv.lib()
+    fake = ctypes.c_void_p(0x100000)
+    assert L.sv_stream_read(None, 1024, fake, 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sv_stream_read(fake, 1000 + 4, fake, 4, None) == _lib.ERR_INVALID_ARGUMENT   # not a multiple of 16
+    assert L.sv_stream_read(ctypes.c_void_p(0x100008), 1024, fake, 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sv_stream_read(fake, 1024, fake, 0, None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sv_stream_read(fake, 1024, None, 4, None) == _lib.ERR_INVALID_ARGUMENT

@@ -49,3 +49,23 @@ def test_filter_bytes_counts_the_filtered_rows_once():
     # stochastic requests 1 and 2 read rows 0..1 and 0..2: 5 rows
     assert bench.filter_bytes(inp, 3, 1.0) == 5 * (10 * 2 + 16)
     assert bench.filter_bytes(inp, 0, 0.9) == 5 * (10 * 2 + 16)
+
+
+def test_tree_algorithmic_bytes_by_hand():
+    bs, N, V = 2, 4, 10
+    logits = np.zeros((bs, N, V), np.float32)
+    tok = np.array([[0, 1, 2, 3], [0, 4, 5, 6]], np.int32)
+    par = np.array([[-1, 0, 0, 1], [-1, 0, 1, 2]], np.int32)
+    temp = np.array([1.0, 0.0], np.float32)                   # request 1 greedy
+    inp = workloads.TreeInputs(logits, tok, par, temp, np.arange(bs, dtype=np.uint64), "tiny tree")
+    stats, decide = bench.tree_algorithmic_bytes(inp, np.array([1, 3], np.int32))
+    bl = 4
+    assert stats == bs * (N * V * bl + (N - 1) * (bl + 8) + 4)
+    assert decide == bs * (4 + 8 + 8 * N) + V * bl + bs * (4 + 8 * N + 4)
+
+
+def test_positions_of_chains_and_trees():
+    inp = _inputs(bf16=False, onehot=True)
+    assert bench.positions_of(inp) == 2 + 1 + 2
+    t = workloads.tree_fp32(0, bs=3, N=5, V=64)
+    assert bench.positions_of(t) == 3 * 4
