@@ -68,14 +68,10 @@ constexpr int kWaves = kWG / 64;
 #ifndef SV_K1_ROUNDS
 #define SV_K1_ROUNDS 1
 #endif
-#ifndef SV_K1_DEPTH
-#define SV_K1_DEPTH 1
-#endif
 #ifndef SV_K1_OCC
 #define SV_K1_OCC 7
 #endif
 constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a K1 sub-chunk
-constexpr int kK1Depth = SV_K1_DEPTH;           // K1 sub-chunks in flight ahead of the one being folded
 #ifndef SV_KR_WORKGROUPS
 #define SV_KR_WORKGROUPS (256 * 7)
 #endif
@@ -142,6 +138,21 @@ struct K3Rec {
   int32_t pad[3];
 };
 
+// One share of a race chunk's sum in a row-statistics segment (the
+// chunk-sum path): the fp32 sum of the terms 2^(l c - off) of one row of 16
+// lanes, c = fp32(log2(e)/T), with off the row's running offset (fl(m c) of
+// its running max) when the chunk was folded.
+struct CSum {
+  float s;
+  float off;
+};
+constexpr int kCSumShares = kWG / 16;  // shares per race chunk: one per row of 16 lanes
+// Race chunks of one statistics segment whose shares are gathered in shared
+// memory and stored in one burst after the segment (stores issued between
+// the stream's loads would hold up its waits); longer segments store each
+// share as it is made.
+constexpr int kCSumLds = 80;
+
 // A filtered row's threshold and kept sum (written by the thresholds pass).
 struct FiltRec {
   double s;           // S' = sum over kept ids of exp((l - m)/T)
@@ -193,6 +204,9 @@ struct Params {
   const int32_t* top_k;  // per-request top-k (NULL: off)
   const float* top_p;    // per-request top-p (NULL: off)
   FiltRec* filt;         // [bs*R] thresholds and kept sums of filtered rows
+  CSum* csum;            // [bs*R][C3][kCSumShares] race-chunk sums of the rows' segments (csum calls)
+  int32_t csum_fold;     // stochastic rows fold with offsets shared by rows of 16 lanes (one-hot chains, trees)
+  int32_t csum_on;       // ... and publish their race-chunk sums (phased schedule, unfiltered)
   int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
   uint32_t flags;
@@ -218,6 +232,37 @@ __device__ __forceinline__ int wave_min_i(int v) {
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Reductions over each row of 16 lanes with DPP butterflies (quad swaps,
+// then the half-row and row mirrors): every lane of the row gets the result,
+// in a fixed order of operations.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// The max is v_max_f32 with the DPP operand (one instruction per step; the
+// s_nop gives the two wait states a DPP read of a just-written VGPR needs).
+// Its inputs are the entries' running maxima (never signalling NaNs), so no
+// canonicalisation is needed.
+__device__ __forceinline__ float row16_max(float v) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
   return v;
 }
 
@@ -501,6 +546,7 @@ __device__ __forceinline__ void k1_issue(const Params& P, int64_t elem0, int n, 
 struct K1Run {
   float m;       // running max
   float off;     // fl(m c): the running sum is relative to 2^off (-inf while m = -inf)
+  float offc;    // the offset the terms are computed with: off, or 0 while m = -inf
   int idx;       // first index (in the item) of the running max
   double s;      // sum of 2^(l c - off) (stochastic rows)
   bool nan;      // a NaN was seen (greedy rows; stochastic rows see it in s)
@@ -529,8 +575,13 @@ __device__ __forceinline__ void k1_unpack(const u32x4* v, float* x) {
 // Folds the NV entries x of one sub-chunk into the running statistics.
 // Entry i sits at item offset base + (i / EPV) * kWG * EPV + i % EPV, so the
 // thread's order is the row order and the first hit is the smallest index.
-template <int NV, int EPV, bool STOCH, bool NEED_AMAX>
-__device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K1Run& st) {
+// With CHUNKS (stochastic rows whose race chunks' sums are published) the
+// running offset is shared by each row of 16 lanes (their running max), so
+// that the lanes' terms add up per race chunk; cs[j] gets the thread's sum
+// over load j (bf16: one race chunk per load; fp32: the two loads form one
+// chunk, in cs[0]).
+template <int NV, int EPV, bool STOCH, bool NEED_AMAX, bool CHUNKS = false>
+__device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K1Run& st, float* cs = nullptr) {
 #pragma clang fp contract(off)
   float mx = x[0];
 #pragma unroll
@@ -551,32 +602,55 @@ __device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K
     st.nan |= nan_seen;
     st.m = fmaxf(st.m, mx);
   } else {
-    const float mn = fmaxf(st.m, mx);
-    const float off = (mn == -INFINITY) ? 0.f : mn * c;  // keeps l = -inf terms at 2^-inf = 0
-    // rescale factor: 0 until the first finite max (st.off = -inf; never
-    // inf * 0), exactly 1 while the max is unchanged, else at most 1
-    const float f = __builtin_amdgcn_exp2f(st.off - off);
+    // Only when some lane of the wave sees a new maximum do the offsets move
+    // (a wave-uniform branch); otherwise the rescale factor would be exactly
+    // 1 and is skipped, with the same result.
+    const bool grow = __ballot(mx > st.m) != 0;
+    float f = 1.f;
+    if (grow) {
+      const float mn = CHUNKS ? row16_max(fmaxf(st.m, mx)) : fmaxf(st.m, mx);
+      const float off = (mn == -INFINITY) ? 0.f : mn * c;  // keeps l = -inf terms at 2^-inf = 0
+      // rescale factor: 0 until the first finite max (st.off = -inf; never
+      // inf * 0), exactly 1 while the max is unchanged, else at most 1
+      f = __builtin_amdgcn_exp2f(st.off - off);
+      st.m = mn;
+      st.off = (mn == -INFINITY) ? -INFINITY : off;
+      st.offc = off;
+    }
+    const float off = st.offc;
     float e[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -off));
 #pragma unroll
-    for (int w = 1; w < NV; w *= 2)
+    for (int w = 1; w < NV; w *= 2) {
+      if (CHUNKS && w == NV / 2) {
+        // the two halves are the two loads
+        if (EPV == 8) {
+          cs[0] = e[0];
+          cs[1] = e[NV / 2];
+        } else {
+          cs[0] = e[0] + e[NV / 2];
+        }
+      }
 #pragma unroll
       for (int i = 0; i + w < NV; i += 2 * w) e[i] += e[i + w];
-    st.s = st.s * (double)f + (double)e[0];
-    st.m = mn;
-    st.off = (mn == -INFINITY) ? -INFINITY : off;
+    }
+    st.s = grow ? st.s * (double)f + (double)e[0] : st.s + (double)e[0];
   }
 }
 
 // Streams sub-chunks [s0, s1) of row `row` (the first already in flight in
-// raw0) and writes the segment's partial to slot `slot` of the row.
-template <bool BF16, bool STOCH, bool NEED_AMAX>
+// raw0) and writes the segment's partial to slot `slot` of the row.  With
+// CHUNKS, each row of 16 lanes also stores, per race chunk of the segment,
+// the sum of its lanes' terms and its offset (read by csum_race).
+template <bool BF16, bool STOCH, bool NEED_AMAX, bool CHUNKS = false>
 __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s0, int s1, int slot, float T,
-                                             u32x4* raw0, Smem& sm) {
+                                             u32x4* raw0, Smem& sm, CSum* cs_lds = nullptr) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NV = kVecPerThread * EPV;  // entries per thread per sub-chunk
   constexpr int SUB = NV * kWG;            // entries per sub-chunk
+  constexpr int NCH = BF16 ? 2 : 1;        // race chunks per sub-chunk
+  static_assert(SUB == NCH * kK3Chunk, "a sub-chunk is a whole number of race chunks");
   const int64_t start = (int64_t)s0 * SUB;
   const int n_seg = (int)(min((int64_t)s1 * SUB, (int64_t)P.V) - start);
   const int nsub = s1 - s0;
@@ -590,35 +664,10 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
   K1Run st;
   st.m = -INFINITY;
   st.off = -INFINITY;
+  st.offc = 0.f;
   st.idx = INT32_MAX;
   st.s = 0.0;
   st.nan = false;
-#if SV_K1_DEPTH > 1
-  // a ring of kK1Depth + 1 register buffers: kK1Depth sub-chunks are in
-  // flight ahead of the one being folded (the ring is unrolled, so every
-  // buffer index is static)
-  u32x4 buf[kK1Depth + 1][kVecPerThread];
-#pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j) buf[0][j] = raw0[j];
-#pragma unroll
-  for (int d = 1; d <= kK1Depth; ++d)
-    if (d < nsub) k1_issue<BF16>(P, elem0 + (int64_t)d * SUB, n_seg - d * SUB, buf[d]);
-#pragma unroll 1
-  for (int sub0 = 0; sub0 < nsub; sub0 += kK1Depth + 1) {
-#pragma unroll
-    for (int d = 0; d <= kK1Depth; ++d) {
-      const int sub = sub0 + d;
-      if (sub < nsub) {
-        float x[NV];
-        k1_unpack<BF16>(buf[d], x);
-        if (sub + kK1Depth < nsub)
-          k1_issue<BF16>(P, elem0 + (int64_t)(sub + kK1Depth) * SUB, n_seg - (sub + kK1Depth) * SUB,
-                         buf[(d + kK1Depth) % (kK1Depth + 1)]);
-        k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
-      }
-    }
-  }
-#else
   // two register buffers: the next sub-chunk is in flight while one is folded
   u32x4 cur[kVecPerThread], nxt[kVecPerThread];
 #pragma unroll
@@ -628,12 +677,36 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
     if (sub + 1 < nsub) k1_issue<BF16>(P, elem0 + (int64_t)(sub + 1) * SUB, n_seg - (sub + 1) * SUB, nxt);
     float x[NV];
     k1_unpack<BF16>(cur, x);
-    k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
+    if constexpr (CHUNKS) {
+      float cs[NCH];
+      k1_fold_sub<NV, EPV, STOCH, NEED_AMAX, true>(x, sub * SUB + threadIdx.x * EPV, cf, st, cs);
+      const int cl = sub * NCH;  // the segment's chunk index of load 0
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const float rs = row16_sum(cs[j]);
+        if ((threadIdx.x & 15) == 15 && P.csum_on) {
+          if (nsub * NCH <= kCSumLds) cs_lds[(cl + j) * kCSumShares + (threadIdx.x >> 4)] = CSum{rs, st.off};
+          else if (start / kK3Chunk + cl + j < P.C3)
+            P.csum[(row * P.C3 + start / kK3Chunk + cl + j) * kCSumShares + (threadIdx.x >> 4)] = CSum{rs, st.off};
+        }
+      }
+    } else {
+      k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
+    }
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) cur[j] = nxt[j];
   }
-#endif
-  const float mc = block_max(st.m, sm);
+  const float mc = block_max(st.m, sm);  // its barriers also order the shared-memory shares
+  if constexpr (CHUNKS) {
+    if (P.csum_on && nsub * NCH <= kCSumLds) {
+      // the segment's shares, one burst of whole chunks of kCSumShares
+      const int c0 = (int)(start / kK3Chunk);
+      const int n = min(nsub * NCH, P.C3 - c0) * kCSumShares;
+      uint64_t* dst = (uint64_t*)&P.csum[(row * P.C3 + c0) * kCSumShares];
+      const uint64_t* src = (const uint64_t*)cs_lds;
+      for (int i = threadIdx.x; i < n; i += kWG) dst[i] = src[i];
+    }
+  }
   double out_s = 0.0;
   int32_t out_amax = (int32_t)start;
   if (!STOCH || NEED_AMAX) {
@@ -1611,6 +1684,70 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, double lo, doub
   if (tid == 0) P.tokens[J.out_slot] = by;
 }
 
+// The race of a P or EXCL job (one-hot chains and trees, unfiltered) from
+// the race-chunk sums that the statistics pass published, by one
+// workgroup: certified bounds on every chunk's weight sum W_c without
+// reading the row, then the merge (candidate chunks, the winning chunk's id
+// race), which writes the sampled token.
+//
+// A published share s (fp32 sum of 2^t_i, t_i = fl(l_i c - off), c =
+// fp32(log2(e)/T)) stands for the exact sum of 2^(l_i c* - off), c* =
+// log2(e)/T, within  2^-23 (n + |off| s) + 2^-20 s + 2^-110  (units of
+// 2^off, n <= 128 ids): the argument's rounding and the rounding of c give
+// a relative error of each term of at most 2^-24 ln2 (2 |t_i| + |off|)
+// since |l_i c*| <= |t_i| + |off| + tiny, and sum_i 2^t_i |t_i| <= 0.531 n
+// for t_i <= 0; v_exp_f32 and the fp32 additions add at most 2^-20 s; terms
+// below the fp32 range add less than 2^-117.  Scaled by 2^(off - m c*) the
+// shares give W_c in units of the row's largest term (1/S is common to all
+// chunks and cancels in the race); an EXCL job subtracts the exact terms of
+// its removed ids.
+template <bool BF16, bool COH>
+__device__ __forceinline__ void csum_race(const Params& P, int b, Smem& sm) {
+  const Job& J = sm.job;
+  const int tid = threadIdx.x;
+  const double cd = 1.4426950408889634074 / J.t;
+  const double mref = (double)J.m * cd;
+  const uint64_t seed = P.seed[b];
+  double lo = 0.0, kh0 = -1.0;
+  for (int c = tid; c < P.C3; c += kWG) {
+    const CSum* cs = &P.csum[((int64_t)J.row * P.C3 + c) * kCSumShares];
+    double E = 0.0, err = 0.0;
+#pragma unroll 4
+    for (int w = 0; w < kCSumShares; ++w) {
+      const uint64_t bits = ld64<COH>(&cs[w]);
+      const float ws = __uint_as_float((uint32_t)bits), off = __uint_as_float((uint32_t)(bits >> 32));
+      if (off == -INFINITY) continue;  // the row of lanes saw only masked ids
+      // 2^(off - m c*) by v_exp_f32 (within 2^-22, and the argument's
+      // rounding 2^-24 |d|), counted in the bound below
+      const double d = (double)off - mref;
+      const double sc = (double)__builtin_amdgcn_exp2f((float)d);
+      E += (double)ws * sc;
+      err += (0x1p-23 * (128.0 + fabs((double)off) * (double)ws) + (0x1p-19 + 0x1p-23 * fabs(d)) * (double)ws +
+              0x1p-110) * sc;
+    }
+    double ex = 0.0;
+    if (J.kind == JOB_EXCL)
+      for (int i = 0; i < J.n_excl; ++i) {
+        const int x = J.excl[i];
+        if (x >= c * kK3Chunk && x < (c + 1) * kK3Chunk)
+          ex += exp(((double)load_logit<BF16>(P, J.row, x) - (double)J.m) / J.t);
+      }
+    const double whi = (E + err - ex * (1.0 - 0x1p-50)) * (1.0 + 0x1p-40);
+    const double wd = E - err - ex * (1.0 + 0x1p-50);
+    const double wlo = wd > 0.0 ? wd * (1.0 - 0x1p-40) : 0.0;
+    const double En = chunk_exp(seed, b, J.r, c);
+    K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
+    const double khi = whi / En * (1.0 + 0x1p-48), klo = wlo / En * (1.0 - 0x1p-48);
+    cst_f64(&rec->khi, khi);
+    cst_f64(&rec->klo, klo);
+    lo = fmax(lo, klo);
+    if (c == tid) kh0 = khi;
+  }
+  wait_mem();  // the records of chunks past the block are stored before k3_merge reads them
+  __syncthreads();
+  k3_merge<BF16>(P, b, lo, kh0, sm);
+}
+
 // ===================================================================== driver
 // K1 segment: sub-chunks [s0, s1) of row r of request b, written to the
 // row's partial slot `slot`.  Its first HBM loads are issued before
@@ -1621,8 +1758,9 @@ __device__ __forceinline__ void k3_merge(const Params& P, int b, double lo, doub
 // calls count each row's segments; the workgroup that completes a row
 // combines it.  The fused schedule counts each request's segments for its
 // sampling chunks to wait on.
-template <int MODE, bool BF16>
-__device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0, int s1, int slot, Smem& sm) {
+template <int MODE, bool BF16, bool CS = false>
+__device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0, int s1, int slot, Smem& sm,
+                                           CSum* cs_lds = nullptr) {
   const int64_t row = (int64_t)b * P.R + r;
   const int64_t start = (int64_t)s0 * P.SUB;
   const int n_seg = (int)(min((int64_t)s1 * P.SUB, (int64_t)P.V) - start);
@@ -1646,7 +1784,9 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
   }
   const bool stoch = uniform_i(is_stochastic(T));
   if (uniform_i(need)) {
-    if (stoch) k1_seg_stats<BF16, true, MODE == MODE_ROWS>(P, row, s0, s1, slot, T, raw0, sm);
+    if (CS && stoch && MODE != MODE_ROWS && P.csum_fold)
+      k1_seg_stats<BF16, true, false, CS>(P, row, s0, s1, slot, T, raw0, sm, cs_lds);
+    else if (stoch) k1_seg_stats<BF16, true, MODE == MODE_ROWS>(P, row, s0, s1, slot, T, raw0, sm);
     else k1_seg_stats<BF16, false, false>(P, row, s0, s1, slot, T, raw0, sm);
     if (MODE != MODE_ROWS && threadIdx.x < 64 && stoch) {
       const int lane = threadIdx.x;
@@ -1686,11 +1826,12 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
 }
 
 // K1 item o of request b: segment o % Q of row o / Q.
-template <int MODE, bool BF16>
-__device__ __forceinline__ void run_k1_item(const Params& P, int b, int o, Smem& sm) {
+template <int MODE, bool BF16, bool CS = false>
+__device__ __forceinline__ void run_k1_item(const Params& P, int b, int o, Smem& sm, CSum* cs_lds = nullptr) {
   const int q = P.Q;
   const int r = o / q, c = o - r * q;
-  run_k1_seg<MODE, BF16>(P, b, r, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c, sm);
+  run_k1_seg<MODE, BF16, CS>(P, b, r, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c, sm,
+                             cs_lds);
 }
 
 // Request order of the decision/sampling work: for batches of at most 64
@@ -1815,9 +1956,25 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int item, Smem& 
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, SV_K1_OCC) void k1_kernel(Params P) {
   __shared__ Smem sm;
+  __shared__ CSum cs_lds[MODE == MODE_ROWS ? 1 : kCSumLds * kCSumShares];  // race-chunk shares of the segment
   const int n1 = P.R * P.Q;
   const int b = (int)(blockIdx.x / (uint32_t)n1);
-  run_k1_item<MODE, BF16>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)n1), sm);
+  run_k1_item<MODE, BF16, MODE != MODE_ROWS>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)n1), sm, cs_lds);
+}
+
+// Decisions and sampling of a call whose statistics pass published the race
+// chunk sums (phased schedule): one workgroup per request decides and races
+// from the sums.  A kernel of its own, so that the fp64 bound arithmetic
+// has the registers it needs without taxing the other kernels'.
+template <int MODE, bool BF16>
+__global__ __launch_bounds__(kWG, 2) void k23c_kernel(Params P) {
+  __shared__ Smem sm;
+  if constexpr (MODE != MODE_ROWS) {
+    const int b = (int)blockIdx.x;
+    if (MODE == MODE_CHAIN) decide_chain<BF16, false>(P, b, true, sm);
+    else decide_tree<BF16, false>(P, b, true, sm);
+    if (uniform_i(sm.job.kind) != JOB_NONE) csum_race<BF16, false>(P, b, sm);
+  }
 }
 
 template <int MODE, bool BF16>
@@ -1849,6 +2006,7 @@ __global__ __launch_bounds__(kWG, 8) void k23_kernel(Params P) {
 template <int MODE, bool BF16>
 __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
   __shared__ Smem sm;
+  __shared__ CSum cs_lds[MODE == MODE_ROWS ? 1 : kCSumLds * kCSumShares];  // unused: no shares are published
   if constexpr (MODE != MODE_ROWS) {
     const uint32_t n1 = (uint32_t)(P.R * P.Q), n3 = (uint32_t)P.CI, L = (uint32_t)P.lag, bs = (uint32_t)P.bs;
     const uint32_t seg1 = L * n1, seg2 = (bs - L) * (n1 + n3);
@@ -1871,7 +2029,7 @@ __global__ __launch_bounds__(kWG, 7) void fused_kernel(Params P) {
       k1 = false;
     }
     const int b = uniform_i(request_at(P, (int)g));
-    if (k1) run_k1_item<MODE, BF16>(P, b, (int)o, sm);
+    if (k1) run_k1_item<MODE, BF16, true>(P, b, (int)o, sm, cs_lds);
     else run_k23<MODE, BF16, true>(P, b, (int)o, sm);
   } else {
     const int n1 = P.R * P.Q;
@@ -2578,7 +2736,7 @@ __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
 // ===================================================================== host
 struct Shape {
   int SUB, nsub, Q, Qp, G, CPR, C3, G3, CI, CHr;
-  size_t gat_off, part_off, k3_off, r_off, f_off, total;
+  size_t gat_off, part_off, k3_off, r_off, f_off, cs_off, total;
 };
 
 // Work split of a call (a function of the shape alone, so results never
@@ -2617,20 +2775,21 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races, s
   s.k3_off = s.part_off + align256(sizeof(Partial) * (size_t)(bs * R * s.CPR));
   s.r_off = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
   s.f_off = s.r_off + align256(sizeof(double) * (size_t)(bs * (R - 1) * s.CHr));
-  s.total = s.f_off + (races ? align256(sizeof(FiltRec) * (size_t)(bs * R)) : 0);
+  s.cs_off = s.f_off + (races ? align256(sizeof(FiltRec) * (size_t)(bs * R)) : 0);
+  s.total = s.cs_off + (races ? align256(sizeof(CSum) * kCSumShares * (size_t)(bs * R * s.C3)) : 0);
   return s;
 }
 
 typedef void (*KernelFn)(Params);
 
 struct Kernels {
-  KernelFn k1, k23, fused, kr, kf;
+  KernelFn k1, k23, fused, kr, kf, k23c;
 };
 
 template <int MODE, bool BF16>
 static Kernels kernels_for() {
   return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>, kr_kernel<BF16>,
-                 kf_kernel<BF16>};
+                 kf_kernel<BF16>,         k23c_kernel<MODE, BF16>};
 }
 
 static Kernels select_kernels(int mode, bool bf16) {
@@ -2671,6 +2830,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.k3 = (K3Rec*)(base + S.k3_off);
   P.rpart = (double*)(base + S.r_off);
   P.filt = (FiltRec*)(base + S.f_off);
+  P.csum = (CSum*)(base + S.cs_off);
   P.CHr = S.CHr;
   P.SUB = S.SUB;
   P.nsub = S.nsub;
@@ -2681,11 +2841,19 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.C3 = S.C3;
   P.G3 = S.G3;
   P.CI = S.CI;
+  const bool filtered = P.mode != MODE_ROWS && (P.top_k != nullptr || P.top_p != nullptr);
+  // Race-chunk sums: when every sampling job can only race over p (the
+  // bonus) or p with ids removed -- one-hot chains and trees -- and no
+  // filter changes p, the statistics pass publishes the chunk sums and one
+  // decision/sampling item per request races from them.
+  // (every schedule folds these calls' rows alike, so that they give the
+  // same results)
+  P.csum_fold = P.mode != MODE_ROWS && (P.mode == MODE_TREE || P.draft_kind == SV_DRAFT_ONEHOT);
+  P.csum_on = P.csum_fold && !filtered && !(P.flags & SV_FLAG_FUSED);
   const int64_t grid23 = (int64_t)P.bs * P.CI;
   if (grid23 + P.G > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
   const int64_t gridr = (int64_t)P.bs * (P.k >= 2 ? P.k - 1 : 0) * P.CHr;
   if (gridr > (int64_t)INT32_MAX) return SV_ERR_UNSUPPORTED;
-  const bool filtered = P.mode != MODE_ROWS && (P.top_k != nullptr || P.top_p != nullptr);
   const int64_t gridf = (int64_t)P.bs * P.R;  // thresholds: one workgroup per row
   // Schedule: phased unless fused is asked for (phased measures faster on
   // the shapes benchmarked so far).
@@ -2711,7 +2879,8 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
     if (!(P.flags & SV_FLAG_STATS_ONLY)) {
       if ((P.flags & SV_FLAG_BLOCK) && P.k >= 2 && P.draft_kind == SV_DRAFT_PROBS)
         hipLaunchKernelGGL(K.kr, dim3((unsigned)gridr), dim3(kWG), 0, stream, P);
-      hipLaunchKernelGGL(K.k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
+      if (P.csum_on) hipLaunchKernelGGL(K.k23c, dim3((unsigned)P.bs), dim3(kWG), 0, stream, P);
+      else hipLaunchKernelGGL(K.k23, dim3((unsigned)grid23), dim3(kWG), 0, stream, P);
     }
   } else {
     hipLaunchKernelGGL(K.fused, dim3((unsigned)(P.G + grid23)), dim3(kWG), 0, stream, P);

@@ -203,6 +203,40 @@ def test_all_schedules_are_bit_identical(dev):
             np.testing.assert_array_equal(out[k], ref[k])
 
 
+@pytest.mark.parametrize("kind", ["onehot", "tree"])
+def test_chunk_sum_path_equals_the_row_rereading_path(dev, kind):
+    """One-hot chains and trees race from the race-chunk sums the statistics
+    pass publishes (phased schedule); the fused schedule re-reads the sampled
+    row instead.  Both fold the rows alike, so every output is equal bit for
+    bit, p included; the fp64 race agrees too.  V = 70001 spans 35 chunks
+    with a partial last one."""
+    if kind == "onehot":
+        rng = np.random.default_rng(31)
+        bs, k, V = 40, 3, 70001
+        l = (rng.standard_normal((bs, k + 1, V)) * 2.5).astype(np.float32)
+        ids = rng.integers(0, V, (bs, k)).astype(np.int32)
+        ids[::3, 0] = np.argmax(l[::3, 0], axis=-1)
+        temp = np.where(np.arange(bs) % 5 == 0, 0.0, 0.9).astype(np.float32)
+        inp = workloads.ChainInputs(workloads.f32_to_bf16_bits(l), ids, None, temp,
+                                    np.arange(bs, dtype=np.uint64) * 7 + 1, True, "one-hot chunk sums")
+        ref, a = run_chain(inp, dev, flags=sv.FLAG_PHASED)
+        _compare(ref, a, inp.name, kind="chain")
+        _, b = run_chain(inp, dev, flags=sv.FLAG_FUSED)
+        _, c = run_chain(inp, dev, flags=sv.FLAG_PHASED | sv.FLAG_FP64_RACE)
+        keys = ("accept_len", "tokens", "status")
+        np.testing.assert_array_equal(a["p_draft"].view(np.int64), b["p_draft"].view(np.int64))
+    else:
+        inp = _random_tree_inputs(77, 24, 12, 70001, "f32")
+        ref, a = run_tree(inp, dev, flags=sv.FLAG_PHASED)
+        _compare(ref, a, inp.name, extra=("accept_path",), kind="tree")
+        _, b = run_tree(inp, dev, flags=sv.FLAG_FUSED)
+        _, c = run_tree(inp, dev, flags=sv.FLAG_PHASED | sv.FLAG_FP64_RACE)
+        keys = ("accept_len", "tokens", "status", "accept_path")
+    for key in keys:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+        np.testing.assert_array_equal(a[key], c[key], err_msg=key)
+
+
 def test_large_batch_groups_race_chunks(dev):
     """96 requests x 49 race chunks exceed two rounds of one-chunk items, so
     each decision/sampling item takes 3 chunks (the last item one): parity
