@@ -452,6 +452,8 @@ def main():
                     help="top-k filtering of every stochastic request's target (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="top-p filtering of every stochastic request's target (1: off)")
+    ap.add_argument("--kf-rows", action="store_true",
+                    help="top-k thresholds from passes over the rows instead of the statistics pass's candidates")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds of each oracle timing (one core, all)")
     ap.add_argument("--cpu-threads", type=int, default=16,
                     help="threads of the sharded oracle timing (capped by the host's cores and the batch)")
@@ -536,6 +538,8 @@ def main():
         if tree:
             raise SystemExit("the block rule is defined for chains only")
         flags |= sv.FLAG_BLOCK
+    if args.kf_rows:
+        flags |= sv.FLAG_KF_ROWS
     V0 = inputs[0].vocab
     filtered = (0 < args.top_k < V0) or (0.0 < args.top_p < 1.0)
     if filtered and args.schedule == "fused":

@@ -135,6 +135,12 @@ enum {
  * nor for trees (SV_ERR_UNSUPPORTED).  With STATS_ONLY / DECIDE_ONLY the
  * extra pass belongs to the DECIDE_ONLY call. */
 #define SV_FLAG_BLOCK 32u
+/* Top-k thresholds from passes over the whole rows.  Without it, for top-k
+ * values up to 128 the row-statistics pass also keeps the groups of logits
+ * the kept set can come from, and the thresholds come from those alone (one
+ * read of each row in all); rows where ties defeat that are read again.
+ * Both give bit-identical results; this bit is a test and measurement aid. */
+#define SV_FLAG_KF_ROWS 64u
 
 typedef struct {
   int32_t batch;              /* bs, 1..SV_MAX_BATCH */

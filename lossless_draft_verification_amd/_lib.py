@@ -26,7 +26,7 @@ DRAFT_PROBS, DRAFT_ONEHOT = 0, 1
 # per-request status
 REQ_OK, REQ_BAD_DRAFT_ID, REQ_BAD_TREE, REQ_NONFINITE, REQ_BAD_TEMPERATURE, REQ_INTERNAL = 0, 1, 2, 3, 4, 5
 # flags
-FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED, FLAG_STATS_ONLY, FLAG_DECIDE_ONLY, FLAG_BLOCK = 1, 2, 4, 8, 16, 32
+FLAG_PHASED, FLAG_FP64_RACE, FLAG_FUSED, FLAG_STATS_ONLY, FLAG_DECIDE_ONLY, FLAG_BLOCK, FLAG_KF_ROWS = 1, 2, 4, 8, 16, 32, 64
 
 MAX_BATCH, MAX_DRAFT, MAX_NODES, MAX_VOCAB = 65536, 63, 64, 1 << 24
 SCRATCH_BYTES, SCRATCH_MAX_BATCH = 8 << 20, 1024

@@ -51,6 +51,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "specverify.h"
@@ -95,6 +96,7 @@ static_assert(kK3Chunk % (4 * kWG) == 0 && kK3Chunk == 4 * kWG * kK3Groups,
 // items take several chunks, so that large batches decide once per item.
 constexpr int kK3Slots = 2048;
 constexpr int kCandMax = 64;                    // candidates a race level re-keys in fp64 (more: fp64 race)
+constexpr int kCandTopK = 128;                  // largest top-k whose thresholds come from candidates
 constexpr int kChunkE = 64;                     // chunk noise values an item computes up front
 constexpr uint32_t kSpinLimit = 1u << 20;       // bounded waits (about a second)
 
@@ -207,6 +209,8 @@ struct Params {
   CSum* csum;            // [bs*R][C3][kCSumShares] race-chunk sums of the rows' segments (csum calls)
   int32_t csum_fold;     // stochastic rows fold with offsets shared by rows of 16 lanes (one-hot chains, trees)
   int32_t csum_on;       // ... and publish their race-chunk sums (phased schedule, unfiltered)
+  u32x4* cand;           // [bs*R][Q][kWG] top-k candidates: per thread and segment, the keys and sub-chunks
+                         // of its two largest groups (key 0: none)
   int32_t lag;        // fused schedule: requests between a request's K1 items and its sampling chunks
   int32_t sched;
   uint32_t flags;
@@ -361,6 +365,20 @@ __device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) 
 // A value that is the same in every lane, made visibly uniform (an SGPR) so
 // that branches on it are scalar branches rather than divergent regions.
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// 32-bit keys that order like the logits they stand for (-0 as +0, so equal
+// logits share one key; NaNs above +inf), and back.
+__device__ __forceinline__ uint32_t kf_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float kf_val(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// Lanes of mask m below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 __device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 
 // A request's sampling job: the result of its decision step (in LDS).
@@ -572,6 +590,29 @@ __device__ __forceinline__ void k1_unpack(const u32x4* v, float* x) {
   }
 }
 
+// ---------------------------------------------------------- top-k candidates
+// Statistics segments of a top-k filtered row (page "投机解码", section
+// "接受规则为什么不改变分布": the target p is the one after top-k / top-p)
+// also publish what the thresholds pass needs to find the kept set without
+// reading the row again.  A group is one thread's entries of one sub-chunk
+// (its kVecPerThread loads), named by gid = sub-chunk * kWG + thread within
+// the row; its key is the key of its largest logit.  Every thread keeps, in
+// registers, the keys and sub-chunks of its two largest groups of the
+// segment, and publishes them (a "lane" record per thread and segment).
+// The thresholds pass then takes g', the k-th largest published key: the
+// published keys are keys of distinct groups, so g' is at most the row's
+// k-th largest group key, which is at most tau, the row's k-th largest logit
+// (k groups with keys above tau would hold k logits above tau).  Every logit
+// >= g' lies in a group whose key is >= g'.  Such a group is either one of
+// its lane's two published groups, or its lane's second key is >= g' too;
+// so the published groups >= g' together with every group of the lanes
+// whose second key is >= g' (rare lanes) hold all of the row's logits
+// >= g', a set that holds every logit >= tau.
+// Whether a stochastic row with top-k tk takes its thresholds from candidates.
+__device__ __forceinline__ bool kc_row(const Params& P, int tk) {
+  return tk > 0 && tk < P.V && tk <= kCandTopK && !(P.flags & SV_FLAG_KF_ROWS);
+}
+
 // Folds the NV entries x of one sub-chunk into the running statistics.
 // Entry i sits at item offset base + (i / EPV) * kWG * EPV + i % EPV, so the
 // thread's order is the row order and the first hit is the smallest index.
@@ -579,9 +620,9 @@ __device__ __forceinline__ void k1_unpack(const u32x4* v, float* x) {
 // running offset is shared by each row of 16 lanes (their running max), so
 // that the lanes' terms add up per race chunk; cs[j] gets the thread's sum
 // over load j (bf16: one race chunk per load; fp32: the two loads form one
-// chunk, in cs[0]).
+// chunk, in cs[0]).  Returns the thread's max of the entries.
 template <int NV, int EPV, bool STOCH, bool NEED_AMAX, bool CHUNKS = false>
-__device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K1Run& st, float* cs = nullptr) {
+__device__ __forceinline__ float k1_fold_sub(const float* x, int base, float c, K1Run& st, float* cs = nullptr) {
 #pragma clang fp contract(off)
   float mx = x[0];
 #pragma unroll
@@ -637,15 +678,19 @@ __device__ __forceinline__ void k1_fold_sub(const float* x, int base, float c, K
     }
     st.s = grow ? st.s * (double)f + (double)e[0] : st.s + (double)e[0];
   }
+  return mx;
 }
 
 // Streams sub-chunks [s0, s1) of row `row` (the first already in flight in
 // raw0) and writes the segment's partial to slot `slot` of the row.  With
 // CHUNKS, each row of 16 lanes also stores, per race chunk of the segment,
-// the sum of its lanes' terms and its offset (read by csum_race).
-template <bool BF16, bool STOCH, bool NEED_AMAX, bool CHUNKS = false>
+// the sum of its lanes' terms and its offset (read by csum_race).  With
+// CAND and top-k tk > 0, every thread publishes its two largest groups (the
+// top-k candidates; CHUNKS then only sets the fold, nothing of the race
+// chunks is published).
+template <bool BF16, bool STOCH, bool NEED_AMAX, bool CHUNKS = false, bool CAND = false>
 __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s0, int s1, int slot, float T,
-                                             u32x4* raw0, Smem& sm, CSum* cs_lds = nullptr) {
+                                             u32x4* raw0, Smem& sm, CSum* cs_lds = nullptr, int tk = 0) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NV = kVecPerThread * EPV;  // entries per thread per sub-chunk
   constexpr int SUB = NV * kWG;            // entries per sub-chunk
@@ -668,6 +713,10 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
   st.idx = INT32_MAX;
   st.s = 0.0;
   st.nan = false;
+  // the thread's two largest group maxima (top-k candidates; NaN: none yet,
+  // so that groups of -inf count too) and their sub-chunks in the segment
+  float c1 = __builtin_nanf(""), c2 = __builtin_nanf("");
+  int u1 = -1, u2 = -1;
   // two register buffers: the next sub-chunk is in flight while one is folded
   u32x4 cur[kVecPerThread], nxt[kVecPerThread];
 #pragma unroll
@@ -677,27 +726,43 @@ __device__ __forceinline__ void k1_seg_stats(const Params& P, int64_t row, int s
     if (sub + 1 < nsub) k1_issue<BF16>(P, elem0 + (int64_t)(sub + 1) * SUB, n_seg - (sub + 1) * SUB, nxt);
     float x[NV];
     k1_unpack<BF16>(cur, x);
+    float mx;
     if constexpr (CHUNKS) {
       float cs[NCH];
-      k1_fold_sub<NV, EPV, STOCH, NEED_AMAX, true>(x, sub * SUB + threadIdx.x * EPV, cf, st, cs);
-      const int cl = sub * NCH;  // the segment's chunk index of load 0
+      mx = k1_fold_sub<NV, EPV, STOCH, NEED_AMAX, true>(x, sub * SUB + threadIdx.x * EPV, cf, st, cs);
+      if constexpr (!CAND) {
+        const int c0 = sub * NCH;  // the segment's chunk index of load 0
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const float rs = row16_sum(cs[j]);
-        if ((threadIdx.x & 15) == 15 && P.csum_on) {
-          if (nsub * NCH <= kCSumLds) cs_lds[(cl + j) * kCSumShares + (threadIdx.x >> 4)] = CSum{rs, st.off};
-          else if (start / kK3Chunk + cl + j < P.C3)
-            P.csum[(row * P.C3 + start / kK3Chunk + cl + j) * kCSumShares + (threadIdx.x >> 4)] = CSum{rs, st.off};
+        for (int j = 0; j < NCH; ++j) {
+          const float rs = row16_sum(cs[j]);
+          if ((threadIdx.x & 15) == 15 && P.csum_on) {
+            if (nsub * NCH <= kCSumLds) cs_lds[(c0 + j) * kCSumShares + (threadIdx.x >> 4)] = CSum{rs, st.off};
+            else if (start / kK3Chunk + c0 + j < P.C3)
+              P.csum[(row * P.C3 + start / kK3Chunk + c0 + j) * kCSumShares + (threadIdx.x >> 4)] =
+                  CSum{rs, st.off};
+          }
         }
       }
     } else {
-      k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
+      mx = k1_fold_sub<NV, EPV, STOCH, NEED_AMAX>(x, sub * SUB + threadIdx.x * EPV, cf, st);
+    }
+    if constexpr (CAND) {
+      const bool a1 = !(mx <= c1), a2 = !(mx <= c2);  // strict, and true while empty
+      c2 = a1 ? c1 : (a2 ? mx : c2);
+      u2 = a1 ? u1 : (a2 ? sub : u2);
+      c1 = a1 ? mx : c1;
+      u1 = a1 ? sub : u1;
     }
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) cur[j] = nxt[j];
   }
+  if constexpr (CAND) {
+    if (tk > 0)
+      P.cand[(row * P.Q + slot) * kWG + threadIdx.x] =
+          u32x4{u1 >= 0 ? kf_key(c1) : 0u, (uint32_t)(s0 + u1), u2 >= 0 ? kf_key(c2) : 0u, (uint32_t)(s0 + u2)};
+  }
   const float mc = block_max(st.m, sm);  // its barriers also order the shared-memory shares
-  if constexpr (CHUNKS) {
+  if constexpr (CHUNKS && !CAND) {
     if (P.csum_on && nsub * NCH <= kCSumLds) {
       // the segment's shares, one burst of whole chunks of kCSumShares
       const int c0 = (int)(start / kK3Chunk);
@@ -1758,7 +1823,7 @@ __device__ __forceinline__ void csum_race(const Params& P, int b, Smem& sm) {
 // calls count each row's segments; the workgroup that completes a row
 // combines it.  The fused schedule counts each request's segments for its
 // sampling chunks to wait on.
-template <int MODE, bool BF16, bool CS = false>
+template <int MODE, bool BF16, bool CS = false, bool CAND = false>
 __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0, int s1, int slot, Smem& sm,
                                            CSum* cs_lds = nullptr) {
   const int64_t row = (int64_t)b * P.R + r;
@@ -1784,9 +1849,16 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
   }
   const bool stoch = uniform_i(is_stochastic(T));
   if (uniform_i(need)) {
+    // top-k rows whose thresholds come from candidate groups
+    int tk = 0;
+    if (CAND && stoch) {
+      const int k = P.top_k ? P.top_k[b] : 0;
+      if (kc_row(P, k)) tk = k;
+    }
     if (CS && stoch && MODE != MODE_ROWS && P.csum_fold)
-      k1_seg_stats<BF16, true, false, CS>(P, row, s0, s1, slot, T, raw0, sm, cs_lds);
-    else if (stoch) k1_seg_stats<BF16, true, MODE == MODE_ROWS>(P, row, s0, s1, slot, T, raw0, sm);
+      k1_seg_stats<BF16, true, false, CS, CAND>(P, row, s0, s1, slot, T, raw0, sm, cs_lds, tk);
+    else if (stoch)
+      k1_seg_stats<BF16, true, MODE == MODE_ROWS, false, CAND>(P, row, s0, s1, slot, T, raw0, sm, nullptr, tk);
     else k1_seg_stats<BF16, false, false>(P, row, s0, s1, slot, T, raw0, sm);
     if (MODE != MODE_ROWS && threadIdx.x < 64 && stoch) {
       const int lane = threadIdx.x;
@@ -1826,12 +1898,12 @@ __device__ __forceinline__ void run_k1_seg(const Params& P, int b, int r, int s0
 }
 
 // K1 item o of request b: segment o % Q of row o / Q.
-template <int MODE, bool BF16, bool CS = false>
+template <int MODE, bool BF16, bool CS = false, bool CAND = false>
 __device__ __forceinline__ void run_k1_item(const Params& P, int b, int o, Smem& sm, CSum* cs_lds = nullptr) {
   const int q = P.Q;
   const int r = o / q, c = o - r * q;
-  run_k1_seg<MODE, BF16, CS>(P, b, r, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c, sm,
-                             cs_lds);
+  run_k1_seg<MODE, BF16, CS, CAND>(P, b, r, (int)((int64_t)c * P.nsub / q), (int)((int64_t)(c + 1) * P.nsub / q), c,
+                                   sm, cs_lds);
 }
 
 // Request order of the decision/sampling work: for batches of at most 64
@@ -1960,6 +2032,16 @@ __global__ __launch_bounds__(kWG, SV_K1_OCC) void k1_kernel(Params P) {
   const int n1 = P.R * P.Q;
   const int b = (int)(blockIdx.x / (uint32_t)n1);
   run_k1_item<MODE, BF16, MODE != MODE_ROWS>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)n1), sm, cs_lds);
+}
+
+// The statistics pass of a top-k filtered call: K1 that also publishes the
+// filtered rows' top-k candidates.
+template <int MODE, bool BF16>
+__global__ __launch_bounds__(kWG, SV_K1_OCC) void k1f_kernel(Params P) {
+  __shared__ Smem sm;
+  const int n1 = P.R * P.Q;
+  const int b = (int)(blockIdx.x / (uint32_t)n1);
+  run_k1_item<MODE, BF16, true, true>(P, b, (int)(blockIdx.x - (uint32_t)b * (uint32_t)n1), sm);
 }
 
 // Decisions and sampling of a call whose statistics pass published the race
@@ -2270,7 +2352,7 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
 // ===================================================================== KF
 // Top-k / top-p thresholds (page "投机解码", section
 // "接受规则为什么不改变分布": the target p is the one after the top-k /
-// top-p sampling parameters).  One workgroup of 1024 threads per row
+// top-p sampling parameters).  One workgroup of kKF threads per row
 // r <= k_b of a chain request that is stochastic and has a filter on; it
 // writes the row's threshold tau (the kept ids are those with l >= tau) and
 // its kept sum S' = sum over them of exp((l - m)/T), m the row max from the
@@ -2294,20 +2376,12 @@ __global__ __launch_bounds__(kWG, 4) void kr_kernel(Params P) {
 // descent finishes there.  When those keys exceed the LDS list, every level
 // reads the row again.  The kept sum is the fixed-point mass at or above the
 // cut (exact up to the same truncation, whatever the order).
-constexpr int kKF = 1024;                // threads of a thresholds workgroup
+constexpr int kKF = 512;                 // threads of a thresholds workgroup
 constexpr int kKFWaves = kKF / 64;
 constexpr int kKFBins = 2048;
 constexpr int kKFList = 8192;            // keys the LDS list holds
 constexpr int kKFUnroll = 8;             // groups of 4 ids per step on unaligned rows
 
-__device__ __forceinline__ uint32_t kf_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float kf_val(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 // Digit levels: shift and width.
 __device__ __forceinline__ int kf_shift(int L) { return L == 0 ? 21 : (L == 1 ? 10 : 0); }
 __device__ __forceinline__ int kf_width(int L) { return L == 2 ? 10 : 11; }
@@ -2591,23 +2665,23 @@ __device__ __forceinline__ void kf_collect(const Params& P, int64_t row, KFShare
   __syncthreads();
 }
 
+struct KFRow {
+  KFShared s;
+  double tab[64];  // 2^(j/64)
+  float red_m[kKFWaves];
+  uint64_t red_h[kKFWaves], red_l[kKFWaves];
+};
+
+// The thresholds of filtered row `row` (temperature Tf, top-k tk, top-p tp)
+// from passes over the row.
 template <bool BF16>
-__global__ __launch_bounds__(kKF) void kf_kernel(Params P) {
-  __shared__ KFShared s;
-  __shared__ double tab[64];  // 2^(j/64)
-  __shared__ float red_m[kKFWaves];
-  __shared__ uint64_t red_h[kKFWaves], red_l[kKFWaves];
+__device__ __forceinline__ void kf_row(const Params& P, int64_t row, float Tf, int tk, float tp, KFRow& w) {
+  KFShared& s = w.s;
+  double* tab = w.tab;
+  float* red_m = w.red_m;
+  uint64_t *red_h = w.red_h, *red_l = w.red_l;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = (int)(blockIdx.x / (uint32_t)P.R);
-  const int r = (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.R);
-  const float Tf = temp_of(P, b);
-  if (!request_filtered(P, b, Tf)) return;
-  int xi;
-  if (P.mode == MODE_CHAIN && r > chain_kb(P, b, xi)) return;  // a tree reads all its rows
-  const int tk = P.top_k ? P.top_k[b] : 0;
-  const float tp = P.top_p ? P.top_p[b] : 1.f;
   const bool use_k = tk > 0 && tk < P.V, use_p = tp > 0.f && tp < 1.f;
-  const int64_t row = (int64_t)b * P.R + r;
   // the row max, from the statistics pass's partials
   float m = -INFINITY;
   if (tid < P.Q) m = __uint_as_float((uint32_t)P.part[row * P.CPR + tid].m_amax);
@@ -2725,6 +2799,543 @@ __global__ __launch_bounds__(kKF) void kf_kernel(Params P) {
   }
 }
 
+
+// ------------------------------------------------ thresholds from candidates
+// The top-k rows whose statistics segments published candidates: one
+// workgroup of 256 threads per row, in four steps.
+//  1. g', the k-th largest of the published keys (see the top-k candidates
+//     of the statistics pass; 0 when fewer than k are published).
+//  2. The groups to read: the published groups >= g', and every group of
+//     the lanes whose second key is >= g'.
+//  3. Their logits >= g': exactly the row's logits >= g', a set that holds
+//     every logit >= tau, so the k-th largest of the set is tau and the
+//     masses at or above tau are the row's.
+//  4. tau, the top-p cut (the first group of equal logits from the top at
+//     which the mass reaches top_p times the top-k set's mass) and the kept
+//     sum S' (the fixed-point mass at or above the cut).  These are integer
+//     sums, whatever the method or the order, so they equal the row passes'.
+//     Sets of up to kKC logits are settled by ranking each key against the
+//     others, a key per thread; larger ones by radix descents over 8-bit
+//     digits.
+// A row whose groups or logits exceed the LDS takes the row passes.
+constexpr int kKC = kKF;          // threads of a candidate-thresholds workgroup
+constexpr int kDig = 256;         // digits of a radix level (thread t < kDig owns digit t)
+constexpr int kKCList = 4096;     // logits >= g' the LDS holds
+constexpr int kKCGroups = 1024;   // groups to read the LDS holds
+constexpr int kKCBatch = 4;       // loads in flight per thread
+constexpr int kKCPub = 1024;      // lane records the LDS holds (more: read from memory at each use)
+struct KCShared {
+  u32x4 pub[kKCPub];              // the row's lane records
+  uint32_t list[kKCList + 4];     // logits' keys (then zeros past them for the ranking)
+  uint32_t grp[kKCGroups];        // ids of the groups to read
+  uint64_t hh[kKC + 4], hl[kKC + 4];  // per digit: mass (integer parts, fraction parts) or counts (hl);
+                                      // ranked selection: per key (zeros past the keys)
+  uint64_t wh[kKC / 64], wl[kKC / 64];
+  double tab[64];
+  uint64_t ah, al, bh, bl;        // found digit: sums of the digits above it, and its own
+  uint32_t cnt[kDig];             // per digit: counts (selection of g')
+  uint32_t cw[kKC / 64];
+  int above;                      // found digit: count of the digits above it
+  uint32_t tau, cut;              // ranked selection: tau and the cut (0: none)
+  uint64_t cut_h, cut_l;          // ... and the mass at or above the cut
+  int rg[kKC], re[kKC];           // ranked selection: partial counts per thread
+  uint64_t ps[6][kKC];            // ... and partial mass sums (total, at or above, above; two parts each)
+  int digit;
+  int nlist, ngrp;
+  float m;
+};
+
+// One level of a descent: the first digit from the top at which the sum of
+// the digits at or above it reaches (nh, nl) (with frac > 0: frac times the
+// histogram's total).  Thread t owns digit t.  Called by every thread after
+// the barrier that ends the histogram; ends with a barrier.
+template <bool MASS>
+__device__ __forceinline__ void kc_find(KCShared& s, uint64_t& nh, uint64_t& nl, float frac) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool owner = tid < kDig;
+  const uint64_t bh = (MASS && owner) ? s.hh[tid] : 0, bl = owner ? s.hl[tid] : 0;
+  uint64_t ih = bh, il = bl;  // sums over the wave's lanes >= lane
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t vh = __shfl_down(ih, o, 64), vl = __shfl_down(il, o, 64);
+    if (lane + o < 64) {
+      ih += vh;
+      il += vl;
+    }
+  }
+  if (lane == 0) {
+    s.wh[wave] = ih;
+    s.wl[wave] = il;
+  }
+  __syncthreads();
+  uint64_t ah = ih - bh, al = il - bl, th = 0, tl = 0;
+#pragma unroll
+  for (int w = 0; w < kKC / 64; ++w) {
+    th += s.wh[w];
+    tl += s.wl[w];
+    if (w > wave) {
+      ah += s.wh[w];
+      al += s.wl[w];
+    }
+  }
+  if (frac > 0.f) kf_fix((double)frac * kf_float(th, tl), nh, nl);
+  if (owner && !kf_ge(ah, al, nh, nl) && kf_ge(ah + bh, al + bl, nh, nl)) {
+    s.digit = tid;
+    s.ah = ah;
+    s.al = al;
+    s.bh = bh;
+    s.bl = bl;
+  }
+  __syncthreads();
+}
+
+// Radix descent over the listed keys >= kmin, 8 bits a level: the count
+// descent (MASS false) finds the key at which the count from the top reaches
+// (nh, nl); the mass descent finds the group at which the mass from the top
+// reaches its need (frac > 0: frac times the set's mass), adding the masses
+// of the keys above it and of the group itself to (ch, cl).  Returns the key
+// (0: not found).  bf16 logits' keys end in 16 bits that the upper 16 fix (0
+// for a sign bit of 1, else all ones), so two levels settle them.
+template <bool BF16, bool MASS>
+__device__ __forceinline__ uint32_t kc_descent(KCShared& s, int n, double md, double cd, uint32_t kmin, uint64_t nh,
+                                               uint64_t nl, float frac, uint64_t& ch, uint64_t& cl) {
+  const int tid = threadIdx.x;
+  constexpr int LV = BF16 ? 2 : 4;
+  uint32_t pre = 0;
+  for (int L = 0; L < LV; ++L) {
+    const int sh = 24 - 8 * L;
+    if (tid < kDig) {
+      s.hh[tid] = 0;
+      s.hl[tid] = 0;
+    }
+    if (tid == 0) s.digit = -1;
+    __syncthreads();
+    for (int i = tid; i < n; i += kKC) {
+      const uint32_t key = s.list[i];
+      if (key >= kmin && (L == 0 || (key >> (sh + 8)) == pre)) {
+        const int d = (int)((key >> sh) & 255u);
+        if (MASS) {
+          uint64_t h, lo;
+          kf_mass(kf_val(key), md, cd, s.tab, h, lo);
+          atomicAdd((unsigned long long*)&s.hh[d], (unsigned long long)h);
+          atomicAdd((unsigned long long*)&s.hl[d], (unsigned long long)lo);
+        } else {
+          atomicAdd((unsigned long long*)&s.hl[d], 1ull);
+        }
+      }
+    }
+    __syncthreads();
+    kc_find<MASS>(s, nh, nl, L == 0 ? frac : 0.f);
+    const int d = s.digit;
+    if (d < 0) return 0;  // only for rows the decision step reports as non-finite
+    kf_sub(nh, nl, s.ah, s.al);
+    ch += s.ah;
+    cl += s.al;
+    if (L == LV - 1) {
+      ch += s.bh;
+      cl += s.bl;
+    }
+    pre = (pre << 8) | (uint32_t)d;
+  }
+  if (BF16) pre = (pre << 16) | ((pre & 0x8000u) ? 0u : 0xFFFFu);
+  return pre;
+}
+
+// Lane record i of the row: from LDS when the records were cached there.
+__device__ __forceinline__ u32x4 kc_pub(const KCShared& s, const u32x4* pub, int npub, int i) {
+  if (i >= npub) return u32x4{0u, 0u, 0u, 0u};
+  return npub <= kKCPub ? s.pub[i] : pub[i];
+}
+
+// The k-th largest of the row's published keys with its lower 16 bits
+// cleared -- the key itself for bf16 logits, whose keys' lower 16 bits the
+// upper ones fix, and at most it for fp32 logits -- or 0 when fewer than k
+// keys are published: a radix descent over two 8-bit digits with 32-bit
+// counts.
+template <bool BF16>
+__device__ __forceinline__ uint32_t kc_kth_pub(KCShared& s, const u32x4* pub, int npub, int k) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int LV = 2;
+  uint32_t pre = 0;
+  int need = k;
+  for (int L = 0; L < LV; ++L) {
+    const int sh = 24 - 8 * L;
+    if (tid < kDig) s.cnt[tid] = 0;
+    if (tid == 0) s.digit = -1;
+    __syncthreads();
+    for (int i0 = 0; i0 < npub; i0 += kKC * kKCBatch) {
+      u32x4 e[kKCBatch];
+#pragma unroll
+      for (int u = 0; u < kKCBatch; ++u) e[u] = kc_pub(s, pub, npub, i0 + u * kKC + tid);
+#pragma unroll
+      for (int u = 0; u < kKCBatch; ++u) {
+        const uint32_t ks[2] = {e[u].x, e[u].z};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bool on = ks[q] != 0u && (L == 0 || (ks[q] >> (sh + 8)) == pre);
+          if (on) atomicAdd(&s.cnt[(ks[q] >> sh) & 255u], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t c = tid < kDig ? s.cnt[tid] : 0u;
+    uint32_t in = c;  // counts of the wave's digits >= this one
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_down((int)in, o, 64);
+      if (lane + o < 64) in += v;
+    }
+    if (lane == 0) s.cw[wave] = in;
+    __syncthreads();
+    uint32_t above = in - c;
+#pragma unroll
+    for (int w = 0; w < kKC / 64; ++w)
+      if (w > wave) above += s.cw[w];
+    if (tid < kDig && above < (uint32_t)need && above + c >= (uint32_t)need) {
+      s.digit = tid;
+      s.above = (int)above;
+    }
+    __syncthreads();
+    const int d = s.digit;
+    if (d < 0) return 0u;
+    need -= s.above;
+    pre = (pre << 8) | (uint32_t)d;
+  }
+  return BF16 ? (pre << 16) | ((pre & 0x8000u) ? 0u : 0xFFFFu) : pre << 16;
+}
+
+__device__ __forceinline__ void wave_sum_u64(uint64_t& h, uint64_t& l) {
+  for (int o = 32; o > 0; o >>= 1) {
+    h += __shfl_xor(h, o, 64);
+    l += __shfl_xor(l, o, 64);
+  }
+}
+
+// Step 4 for n <= kKC listed keys, by ranking: every key is compared with
+// every listed key, the comparisons split over all threads (thread t takes
+// key t % Kp and part t / Kp of the others, Kp = n rounded up to a multiple
+// of 64) and the parts summed in LDS.  tau is the key with fewer than k
+// keys above it and at least k at or above it; each key of the top-k set
+// sums the masses above it and at or above it, and the cut is the key whose
+// mass at or above reaches the need while the mass above does not.  kcut = 0
+// (and S a NaN under top-p) for a row without them, as the descents give.
+// The list must hold zeros in [n, n + 4).
+__device__ __forceinline__ void kc_rank(KCShared& s, int n, int tk, bool use_p, float tp, double md, double cd,
+                                        uint32_t& kcut, double& Sum) {
+  const int tid = threadIdx.x;
+  const int Kp = (n + 63) & ~63;
+  const int Pn = kKC / Kp;                 // parts of the comparisons per key
+  const int i = tid % Kp, part = tid / Kp;
+  const bool act = part < Pn;
+  const int n4 = (n + 3) >> 2;             // groups of 4 keys (zeros past n)
+  const int q0 = act ? part * n4 / Pn : 0, q1 = act ? (part + 1) * n4 / Pn : 0;
+  const uint32_t v = (act && i < n) ? s.list[i] : 0u;
+  int g = 0, e = 0;
+  for (int q = q0; q < q1; ++q) {
+    const u32x4 k4 = *(const u32x4*)&s.list[4 * q];  // zeros count nowhere (v >= 1)
+    g += (int)(k4.x > v) + (int)(k4.y > v) + (int)(k4.z > v) + (int)(k4.w > v);
+    e += (int)(k4.x >= v) + (int)(k4.y >= v) + (int)(k4.z >= v) + (int)(k4.w >= v);
+  }
+  s.rg[tid] = g;
+  s.re[tid] = e;
+  if (tid == 0) {
+    s.tau = 0u;
+    s.cut = 0u;
+  }
+  __syncthreads();
+  const bool own = part == 0 && i < n;  // the thread that settles key i
+  if (own) {
+    for (int p = 1; p < Pn; ++p) {
+      g += s.rg[p * Kp + i];
+      e += s.re[p * Kp + i];
+    }
+    if (g < tk && tk <= e) s.tau = v;  // every such thread holds the same key
+  }
+  __syncthreads();
+  const uint32_t tau = s.tau;
+  if (tau == 0u) {
+    kcut = 0;
+    Sum = use_p ? __builtin_nan("") : 0.0;
+    return;
+  }
+  if (tid < Kp + 4) {
+    uint64_t h = 0, l = 0;
+    if (tid < n && s.list[tid] >= tau) kf_mass(kf_val(s.list[tid]), md, cd, s.tab, h, l);
+    s.hh[tid] = h;  // zeros past n
+    s.hl[tid] = l;
+  }
+  __syncthreads();
+  uint64_t th = 0, tl = 0, ch = 0, cl = 0, ah = 0, al = 0;
+  for (int q = q0; q < q1; ++q) {
+    const u32x4 k4 = *(const u32x4*)&s.list[4 * q];
+    const uint32_t kq[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t hj = s.hh[4 * q + u], lj = s.hl[4 * q + u];
+      th += hj;
+      tl += lj;
+      if (kq[u] >= v) {
+        ch += hj;
+        cl += lj;
+      }
+      if (kq[u] > v) {
+        ah += hj;
+        al += lj;
+      }
+    }
+  }
+  s.ps[0][tid] = th;
+  s.ps[1][tid] = tl;
+  s.ps[2][tid] = ch;
+  s.ps[3][tid] = cl;
+  s.ps[4][tid] = ah;
+  s.ps[5][tid] = al;
+  __syncthreads();
+  if (own) {
+    for (int p = 1; p < Pn; ++p) {
+      th += s.ps[0][p * Kp + i];
+      tl += s.ps[1][p * Kp + i];
+      ch += s.ps[2][p * Kp + i];
+      cl += s.ps[3][p * Kp + i];
+      ah += s.ps[4][p * Kp + i];
+      al += s.ps[5][p * Kp + i];
+    }
+  }
+  if (!use_p) {
+    // the set's total, as summed by the thread of key 0
+    th = s.ps[0][0];
+    tl = s.ps[1][0];
+    for (int p = 1; p < Pn; ++p) {
+      th += s.ps[0][p * Kp];
+      tl += s.ps[1][p * Kp];
+    }
+    kcut = tau;
+    Sum = kf_float(th + (tl >> 32), tl & 0xFFFFFFFFull);
+    return;
+  }
+  uint64_t nh, nl;
+  kf_fix((double)tp * kf_float(th, tl), nh, nl);
+  if (own && v >= tau && kf_ge(ch, cl, nh, nl) && !kf_ge(ah, al, nh, nl)) {
+    s.cut = v;  // every such thread holds the same key and sums
+    s.cut_h = ch;
+    s.cut_l = cl;
+  }
+  __syncthreads();
+  kcut = s.cut;
+  Sum = kcut ? kf_float(s.cut_h + (s.cut_l >> 32), s.cut_l & 0xFFFFFFFFull) : __builtin_nan("");
+}
+
+// Appends x to arr for every lane of the wave with `take`, one atomic on the
+// count *n per wave (positions past cap are counted, not written, so that
+// the caller sees the overflow).  Every lane of the wave calls it.
+__device__ __forceinline__ void wave_append(uint32_t* arr, int* n, int cap, bool take, uint32_t x) {
+  const uint64_t m = __ballot(take);
+  if (m == 0) return;
+  const int leader = __builtin_ctzll(m);
+  int base = 0;
+  if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(n, __popcll(m));
+  base = __shfl(base, leader, 64);
+  if (take) {
+    const int p = base + lanes_below(m);
+    if (p < cap) arr[p] = x;
+  }
+}
+
+// The thresholds of top-k row `row` from its candidates; false (every
+// thread alike, nothing written) when they do not fit the LDS.  rec holds
+// the row's lane records when they fit the LDS cache (loaded by the caller
+// ahead of its checks), pm the row's partial maxima.
+template <bool BF16>
+__device__ __forceinline__ bool kc_try(const Params& P, int64_t row, float Tf, int tk, float tp, uint64_t pm,
+                                       const u32x4* rec, KCShared& s) {
+  const int tid = threadIdx.x;
+  const int Q = P.Q;
+  const bool use_p = tp > 0.f && tp < 1.f;
+  const u32x4* pub = P.cand + row * Q * kWG;
+  const int npub = Q * kWG;
+  if (npub <= kKCPub)
+#pragma unroll
+    for (int j = 0; j < kKCPub / kKC; ++j)
+      if (j * kKC + tid < npub) s.pub[j * kKC + tid] = rec[j];
+  // wave 0: the row max from the partials
+  if (tid < 64) {
+    float m = tid < Q ? __uint_as_float((uint32_t)pm) : -INFINITY;
+    m = wave_max(m);
+    s.tab[tid] = exp2((double)tid / 64.0);
+    if (tid == 0) {
+      s.m = m;
+      s.ngrp = 0;
+      s.nlist = 0;
+    }
+  }
+  // 1. g'
+  const uint32_t g = kc_kth_pub<BF16>(s, pub, npub, tk);
+  // 2. the groups to read
+  for (int i0 = 0; i0 < npub; i0 += kKC * kKCBatch) {
+    u32x4 e[kKCBatch];
+#pragma unroll
+    for (int u = 0; u < kKCBatch; ++u) e[u] = kc_pub(s, pub, npub, i0 + u * kKC + tid);
+#pragma unroll
+    for (int u = 0; u < kKCBatch; ++u) {
+      const int i = i0 + u * kKC + tid;
+      const int seg = i / kWG, t = i - seg * kWG;
+      const bool both = e[u].z != 0u && e[u].z >= g;
+      if (both) {
+        // both of the lane's groups are >= g': every group of the lane
+        const int s0 = (int)((int64_t)seg * P.nsub / Q), s1 = (int)((int64_t)(seg + 1) * P.nsub / Q);
+        const int p = atomicAdd(&s.ngrp, s1 - s0);
+        for (int sub = s0; sub < s1; ++sub)
+          if (p + sub - s0 < kKCGroups) s.grp[p + sub - s0] = (uint32_t)(sub * kWG + t);
+      }
+      wave_append(s.grp, &s.ngrp, kKCGroups, !both && e[u].x != 0u && e[u].x >= g, e[u].y * kWG + t);
+    }
+  }
+  __syncthreads();
+  if (s.ngrp > kKCGroups) return false;
+  {
+    // 3. their logits >= g', kKCBatch loads of 16 bytes in flight per thread
+    constexpr int EPV = BF16 ? 8 : 4;
+    const int ng = s.ngrp;
+    const int64_t off = row * P.lstride;
+    for (int i0 = 0; i0 < ng * kVecPerThread; i0 += kKC * kKCBatch) {
+      u32x4 v[kKCBatch];
+      int e0[kKCBatch];
+#pragma unroll
+      for (int u = 0; u < kKCBatch; ++u) {
+        const int i = i0 + u * kKC + tid;
+        e0[u] = P.V;
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (i < ng * kVecPerThread) {
+          const int gi = i / kVecPerThread, j = i - gi * kVecPerThread;
+          const uint32_t gid = s.grp[gi];
+          const int64_t e64 = (int64_t)(gid / kWG) * P.SUB + (int64_t)(j * kWG + (int)(gid % kWG)) * EPV;
+          if (e64 < P.V) {
+            e0[u] = (int)e64;
+            if (P.aligned && e0[u] + EPV <= P.V)
+              v[u] = BF16 ? *(const u32x4*)((const uint16_t*)P.logits + off + e0[u])
+                          : *(const u32x4*)((const float*)P.logits + off + e0[u]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kKCBatch; ++u) {
+        float l[EPV];
+        if (P.aligned && e0[u] + EPV <= P.V) {
+          const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            if (BF16) {
+              l[2 * h] = __uint_as_float(w[h] << 16);
+              l[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+            } else {
+              l[h] = __uint_as_float(w[h]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) l[e] = e0[u] + e < P.V ? load_logit<BF16>(P, row, e0[u] + e) : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const uint32_t key = kf_key(l[e]);
+          wave_append(s.list, &s.nlist, kKCList, e0[u] + e < P.V && key >= g, key);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (s.nlist > kKCList) return false;
+  // 4. tau, the cut and S'
+  const int n = s.nlist;
+  const double md = (double)s.m, cd = 1.4426950408889634074 / (double)Tf;
+  uint32_t kcut = 0;
+  double S = 0.0;
+  if (n <= kKC) {
+    if (tid < 4) s.list[n + tid] = 0u;
+    __syncthreads();
+    kc_rank(s, n, tk, use_p, tp, md, cd, kcut, S);
+  } else {
+    uint64_t ch = 0, cl = 0;
+    const uint32_t kmin = kc_descent<BF16, false>(s, n, md, cd, 0u, 0, (uint64_t)tk, 0.f, ch, cl);
+    ch = cl = 0;
+    kcut = kmin;
+    if (use_p) {
+      const uint32_t cut = kc_descent<BF16, true>(s, n, md, cd, kmin, 0, 0, tp, ch, cl);
+      kcut = cut;
+      S = cut ? kf_float(ch + (cl >> 32), cl & 0xFFFFFFFFull) : __builtin_nan("");
+    } else {
+      // top-k alone: the fixed-point mass of the keys >= kmin
+      const int lane = tid & 63, wave = tid >> 6;
+      uint64_t th = 0, tl = 0;
+      for (int i = tid; i < n; i += kKC) {
+        const uint32_t key = s.list[i];
+        if (key >= kmin) {
+          uint64_t h, lo;
+          kf_mass(kf_val(key), md, cd, s.tab, h, lo);
+          th += h;
+          tl += lo;
+        }
+      }
+      wave_sum_u64(th, tl);
+      if (lane == 0) {
+        s.wh[wave] = th;
+        s.wl[wave] = tl;
+      }
+      __syncthreads();
+      th = tl = 0;
+#pragma unroll
+      for (int w = 0; w < kKC / 64; ++w) {
+        th += s.wh[w];
+        tl += s.wl[w];
+      }
+      S = kf_float(th + (tl >> 32), tl & 0xFFFFFFFFull);
+    }
+  }
+  if (tid == 0) {
+    P.filt[row].s = S;
+    P.filt[row].tau = kcut ? kf_val(kcut) : -INFINITY;
+  }
+  return true;
+}
+
+// Thresholds of the filtered rows (stochastic, r <= k_b for chains): one
+// workgroup per row; top-k rows with candidates take them from those, the
+// rest (top-p alone, larger top-k, candidates that do not fit) from passes
+// over the row.
+union KFLds {
+  KCShared c;
+  KFRow f;
+};
+static_assert(kKC == kKF && kKC >= kDig && kKC % 64 == 0, "one workgroup shape for both thresholds paths");
+
+template <bool BF16>
+__global__ __launch_bounds__(kKF, 4) void kf_kernel(Params P) {
+  __shared__ KFLds u;
+  const int tid = threadIdx.x;
+  const int b = (int)(blockIdx.x / (uint32_t)P.R);
+  const int r = (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.R);
+  const int64_t row = (int64_t)b * P.R + r;
+  const int Q = P.Q;
+  // the row's partials and lane records are loaded ahead of the checks (in
+  // bounds for every row of a filtered call; used by candidate rows only)
+  uint64_t pm = 0;
+  if (tid < Q) pm = P.part[row * P.CPR + tid].m_amax;
+  u32x4 rec[kKCPub / kKC];
+  const int npub = Q * kWG;
+  const u32x4* pub = P.cand + row * Q * kWG;
+#pragma unroll
+  for (int j = 0; j < kKCPub / kKC; ++j)
+    rec[j] = (P.top_k && npub <= kKCPub && j * kKC + tid < npub) ? pub[j * kKC + tid] : u32x4{0u, 0u, 0u, 0u};
+  const float Tf = temp_of(P, b);
+  const int tk = P.top_k ? P.top_k[b] : 0;
+  const float tp = P.top_p ? P.top_p[b] : 1.f;
+  int xi;
+  const int kb = P.mode == MODE_CHAIN ? chain_kb(P, b, xi) : P.R;
+  if (!request_filtered(P, b, Tf)) return;
+  if (P.mode == MODE_CHAIN && r > kb) return;  // a tree reads all its rows
+  if (kc_row(P, tk) && kc_try<BF16>(P, row, Tf, tk, tp, pm, rec, u.c)) return;
+  __syncthreads();  // the shared memory changes roles
+  kf_row<BF16>(P, row, Tf, tk, tp, u.f);
+}
+
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
   const size_t n16 = n / 16;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -2776,20 +3387,27 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races, s
   s.r_off = s.k3_off + align256(sizeof(K3Rec) * (size_t)(bs * s.C3));
   s.f_off = s.r_off + align256(sizeof(double) * (size_t)(bs * (R - 1) * s.CHr));
   s.cs_off = s.f_off + (races ? align256(sizeof(FiltRec) * (size_t)(bs * R)) : 0);
-  s.total = s.cs_off + (races ? align256(sizeof(CSum) * kCSumShares * (size_t)(bs * R * s.C3)) : 0);
+  // The race-chunk sums (unfiltered calls) and the top-k candidates
+  // (filtered calls: a record per thread of every statistics segment) share
+  // one area.
+  const size_t cs_bytes = align256(sizeof(CSum) * kCSumShares * (size_t)(bs * R * s.C3));
+  const size_t cand_bytes = align256(sizeof(u32x4) * kWG * (size_t)(bs * R * s.Q));
+  s.total = s.cs_off + (races ? std::max(cs_bytes, cand_bytes) : 0);
   return s;
 }
 
 typedef void (*KernelFn)(Params);
 
 struct Kernels {
-  KernelFn k1, k23, fused, kr, kf, k23c;
+  KernelFn k1, k23, fused, kr, kf, k23c, k1f;
 };
 
 template <int MODE, bool BF16>
 static Kernels kernels_for() {
-  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>, fused_kernel<MODE, BF16>, kr_kernel<BF16>,
-                 kf_kernel<BF16>,         k23c_kernel<MODE, BF16>};
+  KernelFn k1f = nullptr;  // row-statistics calls have no filters
+  if constexpr (MODE != MODE_ROWS) k1f = k1f_kernel<MODE, BF16>;
+  return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>,  fused_kernel<MODE, BF16>, kr_kernel<BF16>,
+                 kf_kernel<BF16>,         k23c_kernel<MODE, BF16>, k1f};
 }
 
 static Kernels select_kernels(int mode, bool bf16) {
@@ -2831,6 +3449,7 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
   P.rpart = (double*)(base + S.r_off);
   P.filt = (FiltRec*)(base + S.f_off);
   P.csum = (CSum*)(base + S.cs_off);
+  P.cand = (u32x4*)(base + S.cs_off);
   P.CHr = S.CHr;
   P.SUB = S.SUB;
   P.nsub = S.nsub;
@@ -2873,7 +3492,9 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
     hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
   } else if (P.sched == SCHED_PHASED) {
     if (!(P.flags & SV_FLAG_DECIDE_ONLY)) {
-      hipLaunchKernelGGL(K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
+      // top-k calls: the statistics pass also publishes candidate groups
+      const bool cand = filtered && P.top_k != nullptr && !(P.flags & SV_FLAG_KF_ROWS);
+      hipLaunchKernelGGL(cand ? K.k1f : K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
       if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kKF), 0, stream, P);
     }
     if (!(P.flags & SV_FLAG_STATS_ONLY)) {
@@ -2937,7 +3558,8 @@ const char* sv_status_string(sv_status s) {
 static bool dtype_ok(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
 
 static const uint32_t kKnownFlags =
-    SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY | SV_FLAG_BLOCK;
+    SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY | SV_FLAG_BLOCK |
+    SV_FLAG_KF_ROWS;
 // At most one of PHASED, FUSED, STATS_ONLY, DECIDE_ONLY, except PHASED with
 // one of the split-phase bits.
 static bool one_schedule(uint32_t flags) {

@@ -79,7 +79,7 @@ def _call_chain(desc, ws_bytes=1 << 30, ws=0x200000):
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, 1), ("batch", sv.MAX_BATCH + 1, 1), ("max_draft", -1, 1), ("max_draft", 64, 1),
-    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3), ("flags", 64, 3),
+    ("vocab", 0, 1), ("logits_dtype", 5, 3), ("draft_kind", 9, 3), ("flags", 1 << 7, 3), ("flags", 256, 3),
     ("logits", None, 1), ("temperature", None, 1), ("seed", None, 1), ("accept_len", None, 1),
     ("tokens", None, 1), ("draft_ids", None, 1), ("logits_row_stride", 99, 1), ("draft_probs", None, 1),
     ("q_row_stride", 50, 1),
@@ -143,7 +143,7 @@ def _tree_desc(**kw):
 
 @pytest.mark.parametrize("field,value,code", [
     ("num_nodes", 0, 1), ("num_nodes", 65, 1), ("parent", None, 1), ("node_tokens", None, 1),
-    ("accept_path", None, 1), ("logits_dtype", 3, 3), ("logits_row_stride", 10, 1), ("flags", 64, 3),
+    ("accept_path", None, 1), ("logits_dtype", 3, 3), ("logits_row_stride", 10, 1), ("flags", 128, 3),
 ])
 def test_tree_argument_validation(field, value, code):
     d = _tree_desc(**{field: value})

@@ -800,3 +800,114 @@ def test_filtered_with_one_array_only(dev):
     tk6, tp6 = _filters(np.random.default_rng(72), 6, 5000)
     check_tree(tree, dev, top_k=tk6)
     check_tree(tree, dev, top_p=tp6)
+
+
+# ------------------------------- top-k thresholds from candidate groups
+# For top-k up to 128 the statistics pass keeps the groups the kept set can
+# come from and the thresholds pass reads only those; FLAG_KF_ROWS makes it
+# read the rows instead.  The two give bit-identical results, and the
+# candidate path is compared with the oracle as well.
+def _same(a, b, name):
+    for key in ("accept_len", "tokens", "status", "accept_path"):
+        if key in a:
+            np.testing.assert_array_equal(a[key], b[key], err_msg=f"{name}: {key}")
+    if "p_draft" in a:
+        np.testing.assert_array_equal(a["p_draft"].view(np.uint64), b["p_draft"].view(np.uint64),
+                                      err_msg=f"{name}: p_draft bits")
+
+
+def _chain_both_paths(inp, dev, tk, tp, flags=0, logits=None):
+    outs = []
+    for f in (flags, flags | sv.FLAG_KF_ROWS):
+        print(f"[parity] top-k candidates {inp.name} flags={f}", flush=True)
+        out = sv.verify_chain(_t(inp.logits, dev) if logits is None else logits, _t(inp.draft_ids, dev),
+                              _t(inp.temperature, dev), _t(inp.seeds, dev),
+                              draft_probs=None if inp.onehot else _t(inp.draft_probs, dev), onehot=inp.onehot,
+                              flags=f, return_p_draft=True, top_k=_t(tk, dev), top_p=_t(tp, dev))
+        torch.cuda.synchronize()
+        outs.append(_np(out))
+    _same(outs[0], outs[1], inp.name)
+    return outs[0]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_candidates_equal_row_passes(dev, dtype):
+    """k from 1 to 129 (the candidate path serves k <= 128), alone and with
+    top-p, over rows of three and more statistics segments."""
+    s = 310 + (dtype == "f32")
+    inp = _random_chain(s, 24, 5, 50000, dtype, "probs")
+    rng = np.random.default_rng(s)
+    tk = rng.choice(np.array([1, 2, 7, 50, 64, 100, 127, 128, 129, 0], np.int32), size=24).astype(np.int32)
+    tp = rng.choice(np.array([1.0, 1.0, 0.9, 0.5, 0.99], np.float32), size=24).astype(np.float32)
+    _chain_both_paths(inp, dev, tk, tp)
+    check_chain(inp, dev, top_k=tk, top_p=tp)
+
+
+def test_topk_candidates_headline_shape(dev):
+    """bs 64, k 7, V 128256 bf16 with top-k 50 and top-p 0.9 on every request."""
+    inp = workloads.chain_bf16_mixed(4)
+    tk = np.full(inp.batch, 50, np.int32)
+    tp = np.full(inp.batch, 0.9, np.float32)
+    _chain_both_paths(inp, dev, tk, tp)
+    check_chain(inp, dev, top_k=tk, top_p=tp)
+
+
+def test_topk_candidates_ties_and_short_rows(dev):
+    """Ties at the k-th logit (few distinct values, some rows all equal, so
+    lists overflow and rows are read instead), mostly -inf rows, rows shorter
+    than one sub-chunk, and rows that end inside a group."""
+    rng = np.random.default_rng(333)
+    for V, name in ((5000, "ties"), (300, "short"), (4099, "ragged")):
+        bs, k = 10, 3
+        l = (rng.standard_normal((bs, k + 1, V)) * 2).astype(np.float32)
+        l[0] = np.round(l[0])                       # a handful of values
+        l[1] = 0.25                                 # every logit equal
+        l[2, :, 40:] = -np.inf                      # 40 finite entries
+        l[3, :, : V // 2] = np.round(l[3, :, : V // 2] * 4) / 4
+        q = workloads._softmax_rows(l[:, :k].reshape(-1, V) * 0.7).reshape(bs, k, V).astype(np.float32)
+        ids = workloads._sample_rows(rng, q.reshape(-1, V)).reshape(bs, k).astype(np.int32)
+        temp = np.full(bs, 0.8, np.float32)
+        temp[7] = 0.0
+        tk = np.array([5, 50, 60, 128, 1, 3, 20, 9, 100, 64], np.int32)
+        tp = np.array([1.0, 0.9, 1.0, 0.7, 1.0, 0.95, 1.0, 0.5, 0.8, 1.0], np.float32)
+        for dtype in ("f32", "bf16"):
+            lg = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(l)) if dtype == "bf16" else l
+            ll = workloads.f32_to_bf16_bits(l) if dtype == "bf16" else l
+            inp = workloads.ChainInputs(ll, ids, q, temp, rng.integers(0, 2**63, size=bs).astype(np.uint64), False,
+                                        f"candidates {name} {dtype}")
+            assert np.isfinite(lg).any()
+            _chain_both_paths(inp, dev, tk, tp)
+            check_chain(inp, dev, top_k=tk, top_p=tp)
+
+
+def test_topk_candidates_unaligned_rows(dev):
+    """A strided view whose rows are not 16-byte aligned: the statistics pass
+    and the thresholds pass both take scalar loads."""
+    base = _random_chain(334, 6, 3, 9010, "f32", "probs")
+    V = 9001
+    lg = torch.from_numpy(base.logits).to(dev)[:, :, :V]
+    l = np.ascontiguousarray(base.logits[:, :, :V])
+    q = workloads._softmax_rows(l[:, :3].reshape(-1, V)).reshape(6, 3, V).astype(np.float32)
+    ids = np.minimum(base.draft_ids, V - 1).astype(np.int32)
+    inp = workloads.ChainInputs(l, ids, q, base.temperature, base.seeds, False, "candidates strided")
+    tk = np.array([10, 50, 128, 1, 77, 3], np.int32)
+    tp = np.array([1.0, 0.9, 0.6, 1.0, 0.95, 1.0], np.float32)
+    got = _chain_both_paths(inp, dev, tk, tp, logits=lg)
+    ref = oracle.verify_chain(l, ids, base.temperature, base.seeds, draft_probs=q, top_k=tk, top_p=tp)
+    _compare(ref, got, "candidates strided", kind="filtered chain")
+
+
+def test_topk_candidates_trees(dev):
+    inp = _random_tree_inputs(335, 9, 8, 33000, "bf16")
+    rng = np.random.default_rng(335)
+    tk = rng.choice(np.array([1, 20, 50, 128, 200], np.int32), size=9).astype(np.int32)
+    tp = rng.choice(np.array([1.0, 0.9], np.float32), size=9).astype(np.float32)
+    outs = []
+    for f in (0, sv.FLAG_KF_ROWS):
+        out = sv.verify_tree(_t(inp.logits, dev), _t(inp.node_tokens, dev), _t(inp.parent, dev),
+                             _t(inp.temperature, dev), _t(inp.seeds, dev), flags=f, top_k=_t(tk, dev),
+                             top_p=_t(tp, dev))
+        torch.cuda.synchronize()
+        outs.append(_np(out))
+    _same(outs[0], outs[1], "candidate trees")
+    check_tree(inp, dev, top_k=tk, top_p=tp)
