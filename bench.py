@@ -357,7 +357,8 @@ def bench_compact(args, sv, torch, dev, workloads):
 
 
 def bench_plan(args, sv, torch, dev):
-    """Latency of one survival top-k plan (a single-workgroup kernel): the
+    """Latency of one survival top-k plan (one launch: slot ranks over many
+    workgroups, the rest in the last to finish): the
     page's adaptive-verification shape (512 requests x 7 positions, half
     with accurate drafts) and the largest supported one (1024 x 8)."""
     rng = np.random.default_rng(11)
@@ -386,7 +387,7 @@ def bench_plan(args, sv, torch, dev):
                       "unit": "us/plan", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "higher_is_better": False, "data": "synthetic",
                       "config": {"workload": "plan 512 requests x 7 positions (and 1024 x 8)", "cases": lines},
-                      "roofline": {"bound": "latency", "note": "one workgroup; a few thousand slots"}}), flush=True)
+                      "roofline": {"bound": "latency", "note": "a few thousand slots ranked over many workgroups"}}), flush=True)
 
 
 def read_ceiling(sv, torch, dev, buffers, steps):

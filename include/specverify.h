@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 2
+#define SV_ABI_VERSION 3
 
 /* Limits of one call. */
 #define SV_MAX_BATCH 65536   /* requests per call */
@@ -273,8 +273,15 @@ int32_t sv_abi_version(void);
  * rate (sums in fp64; a NaN rate never wins; none that beats -inf: B* = 0).
  * Outputs: budget[0] = B*, draft_len[b] = admitted positions of request b
  * (pad its draft ids after that with -1 for sv_verify_chain), rate[0] =
- * rate(B*).  One workgroup does the whole plan; no workspace.  bs * K must
- * not exceed SV_PLAN_MAX_SLOTS (else SV_ERR_UNSUPPORTED). */
+ * rate(B*).  bs * K must not exceed SV_PLAN_MAX_SLOTS (else
+ * SV_ERR_UNSUPPORTED).
+ *
+ * workspace: device memory of at least sv_plan_workspace_bytes(bs, K) bytes
+ * (the same for every shape), 256-byte aligned (else SV_ERR_INVALID_ARGUMENT /
+ * SV_ERR_WORKSPACE_TOO_SMALL), all zero before its first use; every call
+ * leaves its counters at zero again, so it can be reused by calls of any
+ * shape that do not overlap (calls that overlap need their own).  The caller
+ * owns it. */
 #define SV_PLAN_MAX_SLOTS 8192
 
 typedef struct {
@@ -288,8 +295,13 @@ typedef struct {
   int32_t* budget;            /* [1] out: B* */
   int32_t* draft_len;         /* [bs] out */
   double* rate;               /* [1] out, may be NULL */
+  void* workspace;            /* device, see above */
+  size_t workspace_bytes;
 } sv_plan_desc;
 
+/* Workspace bytes of a plan of bs requests and K positions (0 for shapes
+ * sv_plan_budget rejects). */
+size_t sv_plan_workspace_bytes(int32_t batch, int32_t max_steps);
 sv_status sv_plan_budget(const sv_plan_desc* desc /* [host] */, void* stream);
 
 /* Accepted-path KV compaction after tree verification (page "投机解码", section

@@ -57,7 +57,7 @@ class TreeDesc(ctypes.Structure):
 class PlanDesc(ctypes.Structure):
     _fields_ = [("batch", _I32), ("max_steps", _I32), ("confidence", _P), ("num_steps", _P),
                 ("max_budget", _I32), ("cost", _P), ("base_tokens", ctypes.c_double),
-                ("budget", _P), ("draft_len", _P), ("rate", _P)]
+                ("budget", _P), ("draft_len", _P), ("rate", _P), ("workspace", _P), ("workspace_bytes", _SZ)]
 
 
 class CompactDesc(ctypes.Structure):
@@ -107,6 +107,8 @@ def lib():
                 L.sv_compact_kv.argtypes = [ctypes.POINTER(CompactDesc), _P]
                 L.sv_plan_budget.restype = ctypes.c_int
                 L.sv_plan_budget.argtypes = [ctypes.POINTER(PlanDesc), _P]
+                L.sv_plan_workspace_bytes.restype = _SZ
+                L.sv_plan_workspace_bytes.argtypes = [_I32, _I32]
                 L.sv_stream_read.restype = ctypes.c_int
                 L.sv_stream_read.argtypes = [_P, _SZ, _P, _I32, _P]
                 L.sv_row_stats.restype = ctypes.c_int
@@ -191,6 +193,24 @@ def default_workspace(device) -> Workspace:
         if ws is None:
             ws = Workspace(1 << 20, torch.device("cuda", index))
             _workspaces[key] = ws
+    return ws
+
+
+_plan_workspaces = {}
+
+
+def plan_workspace(device, nbytes: int) -> torch.Tensor:
+    """The planner's workspace when a call passes none: one zero-filled
+    buffer per (device, current stream), grown to the largest call so far
+    (a new buffer is zero-filled; a call leaves its counters at zero)."""
+    device = torch.device(device)
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
+    with _workspaces_lock:
+        ws = _plan_workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=torch.device("cuda", index))
+            _plan_workspaces[key] = ws
     return ws
 
 
@@ -405,13 +425,15 @@ def compact_kv(kv, accept_len, accept_path, node_slot):
     return moved
 
 
-def plan_budget(confidence, cost, base_tokens, num_steps=None):
+def plan_budget(confidence, cost, base_tokens, num_steps=None, workspace=None):
     """Survival top-k draft budget on the current stream (asynchronous).
 
     confidence [bs, K] float32; cost [max_budget + 1] float64 (step cost when
     B draft positions are verified); base_tokens: tokens a step yields with
-    none; num_steps [bs] int32 or None.  Returns device tensors: budget [1]
-    int32, draft_len [bs] int32, rate [1] float64.
+    none; num_steps [bs] int32 or None; workspace: a zero-filled uint8 device
+    tensor of at least plan_workspace_bytes(bs, K) bytes (None: one kept per
+    device and stream).  Returns device tensors: budget [1] int32, draft_len
+    [bs] int32, rate [1] float64.
     """
     if confidence.dim() != 2 or confidence.dtype != torch.float32:
         raise ValueError("confidence must be a [batch, K] float32 tensor")
@@ -429,12 +451,19 @@ def plan_budget(confidence, cost, base_tokens, num_steps=None):
     out = dict(budget=torch.empty(1, dtype=torch.int32, device=dev),
                draft_len=torch.empty(bs, dtype=torch.int32, device=dev),
                rate=torch.empty(1, dtype=torch.float64, device=dev))
+    need = int(lib().sv_plan_workspace_bytes(bs, K))
+    ws = plan_workspace(dev, need) if workspace is None else workspace
     d = PlanDesc(bs, K, conf.data_ptr(), ns.data_ptr() if ns is not None else None, c.numel() - 1, c.data_ptr(),
-                 float(base_tokens), out["budget"].data_ptr(), out["draft_len"].data_ptr(), out["rate"].data_ptr())
+                 float(base_tokens), out["budget"].data_ptr(), out["draft_len"].data_ptr(), out["rate"].data_ptr(),
+                 ws.data_ptr(), ws.numel() * ws.element_size())
     st = lib().sv_plan_budget(ctypes.byref(d), _stream(dev))
     if st != OK:
         raise SpecVerifyError(st, "sv_plan_budget")
     return out
+
+
+def plan_workspace_bytes(batch: int, max_steps: int) -> int:
+    return int(lib().sv_plan_workspace_bytes(int(batch), int(max_steps)))
 
 
 def row_stats(logits, temperature, *, workspace=None):

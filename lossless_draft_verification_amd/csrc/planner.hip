@@ -6,26 +6,27 @@
 //
 // A (request, position) slot's score is the chance that all of the
 // request's drafts up to that position are accepted: the fp32 product of its
-// confidences so far (each clamped to [0, 1], NaN as 0).  Slots are ranked by score, higher first, ties to the earlier
-// position and then to the smaller request index, so each request's admitted
-// slots form a prefix.  Admitting the top B slots is worth
-// (base + sum of their scores) / cost[B] expected tokens per unit of cost;
-// the budget is the first B in 0..min(max_budget, slots) that maximises it.
+// confidences so far (each clamped to [0, 1], NaN as 0).  Slots are ranked
+// by score, higher first, ties to the earlier position and then to the
+// smaller request index, so each request's admitted slots form a prefix.
+// Admitting the top B slots is worth (base + sum of their scores) / cost[B]
+// expected tokens per unit of cost; the budget is the first B in
+// 0..min(max_budget, slots) that maximises it.
 //
-// One workgroup of 1024 threads does the whole plan in LDS (a batch has at
-// most SV_PLAN_MAX_SLOTS slots): the slot keys
+// The slot keys
 //   (~bits(score)) << 32 | position << 20 | request
-// sort ascending in the required order (scores are >= 0, so their fp32 bit
-// patterns order like their values; unused slots are all-ones and sort
-// last).  A request's keys are already ascending along its positions, so
-// the slots start as bs sorted runs of K and a bottom-up merge sorts them in
-// ceil(log2 bs) rounds: each key finds its place in the partner run by a
-// binary search (keys of the left run go before equal keys of the right
-// one) and moves to the other LDS buffer.  Then fp64 prefix sums of the
-// sorted scores by contiguous chunks and one block scan; the first maximum
-// of the ratio by a block reduction; the admitted count of each request by
-// an atomic max of position + 1.  The work is a few thousand slots:
-// latency, not bandwidth, bounds it.
+// order ascending in the required order (scores are >= 0, so their fp32 bit
+// patterns order like their values; unused slots are all-ones and come
+// last), and they are distinct, so a slot's rank is the number of keys below
+// its own.  One launch of a grid of workgroups: each computes every key into
+// LDS and ranks its kSlots slots against them -- thread t compares the kReg
+// slots of group t / kParts with the keys t % kParts + m kParts, and the
+// counts are summed over the parts (a wave holds 64 parts of one group) --
+// then stores the slots' ranks and their scores in rank order.  The last workgroup to
+// finish takes fp64 prefix sums of the sorted scores (by contiguous chunks
+// and one block scan), the first maximum of the ratio, and each request's
+// admitted count (its slots ranked below the budget), and leaves its counter
+// at zero for the next call.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +36,17 @@ namespace svp {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kParts = 128;                  // threads that share one slot's comparisons
+constexpr int kReg = 4;                      // slots a thread compares every key it reads with
+constexpr int kSlots = kThreads / kParts * kReg;  // slots a workgroup ranks
+constexpr int kPer = SV_PLAN_MAX_SLOTS / kThreads;  // entries per thread of the last workgroup, at most
+
+// Workspace: the completion counter, then per slot its rank, then the
+// scores in rank order (arrays sized for SV_PLAN_MAX_SLOTS: one layout for
+// every shape).
+constexpr size_t kWsRank = 256;
+constexpr size_t kWsScore = kWsRank + 4 * (size_t)SV_PLAN_MAX_SLOTS;
+constexpr size_t kWsBytes = kWsScore + 4 * (size_t)SV_PLAN_MAX_SLOTS;
 
 struct PlanParams {
   int32_t bs, K, bmax_table;
@@ -45,6 +57,9 @@ struct PlanParams {
   int32_t* budget;
   int32_t* draft_len;
   double* rate;
+  uint32_t* counter;
+  uint32_t* rank;
+  float* sscore;
 };
 
 // Better (rate, B): a larger rate, or the same rate at a smaller B.  A NaN
@@ -53,90 +68,187 @@ __device__ __forceinline__ bool better(double r, int b, double br, int bb) {
   return r > br || (r == br && b < bb);
 }
 
-// Number of keys of the sorted range [lo, hi) of k below x (or, with
-// `upper`, not above x).
-__device__ __forceinline__ int count_before(const uint64_t* k, int lo, int hi, uint64_t x, bool upper) {
-  int n = hi - lo;
-  int base = lo;
-  while (n > 0) {
-    const int half = n >> 1;
-    const uint64_t v = k[base + half];
-    if (v < x || (upper && v == x)) {
-      base += half + 1;
-      n -= half + 1;
-    } else {
-      n = half;
+__device__ __forceinline__ int steps_of(const PlanParams& P, int b) {
+  const int len = P.num_steps ? P.num_steps[b] : P.K;
+  return len < 0 ? 0 : (len > P.K ? P.K : len);
+}
+
+// Keys of the slots [lo, hi) (slot s = b K + j; all-ones past a request's
+// drafted positions) into out[s - lo]: one thread per request, its
+// confidences loaded eight at a time ahead of the running product.
+__device__ __forceinline__ void slot_keys(const PlanParams& P, int lo, int hi, uint64_t* out) {
+  const int K = P.K;
+  const int b0 = lo / K, b1 = (hi + K - 1) / K;
+  for (int b = b0 + (int)threadIdx.x; b < b1; b += kThreads) {
+    const int len = steps_of(P, b);
+    float sc = 1.0f;
+    for (int j0 = 0; j0 < K; j0 += 8) {
+      float c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = j0 + u < K ? P.conf[(int64_t)b * K + j0 + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u, s = b * K + j;
+        if (j >= K) break;
+        float x = c[u];
+        if (!(x > 0.0f)) x = 0.0f;
+        if (x > 1.0f) x = 1.0f;
+        sc = __fmul_rn(sc, x);
+        if (s >= lo && s < hi)
+          out[s - lo] = j < len ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(sc)) << 32) | ((uint64_t)j << 20) |
+                                      (uint64_t)b
+                                : ~0ull;
+      }
     }
   }
-  return base - lo;
+}
+
+__device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(0xFFFFFFFFu - (uint32_t)(k >> 32)); }
+
+// Stores and loads of data that other workgroups of the launch write or read
+// (agent-scope relaxed atomics: they bypass the caches that are not
+// coherent across the device), and a wait for this wave's memory operations.
+__device__ __forceinline__ void cst32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t cld32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// For each of the kReg keys x[r], the keys keys[p], keys[p + kParts], ...
+// (below n) below it: the lanes of a wave, taking consecutive parts, read
+// consecutive keys.
+__device__ __forceinline__ void count_below(const uint64_t* keys, int p, int n, const uint64_t* x, uint32_t* c) {
+#pragma unroll
+  for (int r = 0; r < kReg; ++r) c[r] = 0;
+  int q = p;
+  for (; q + 3 * kParts < n; q += 4 * kParts) {
+    uint64_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = keys[q + u * kParts];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < kReg; ++r) c[r] += k[u] < x[r] ? 1u : 0u;
+  }
+  for (; q < n; q += kParts) {
+    const uint64_t k = keys[q];
+#pragma unroll
+    for (int r = 0; r < kReg; ++r) c[r] += k < x[r] ? 1u : 0u;
+  }
+}
+
+// Exclusive prefix over the workgroup of one double per thread, in a fixed
+// order (a wave scan, then the waves' totals).
+__device__ __forceinline__ double block_exclusive(double v, double* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double in = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double u = __shfl_up(in, o, 64);
+    if (lane >= o) in += u;
+  }
+  if (lane == 63) wsum[wave] = in;
+  __syncthreads();
+  double before = 0.0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  return before + in - v;
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
-  __shared__ uint64_t buf[2][SV_PLAN_MAX_SLOTS];
-  __shared__ double scan[kThreads];
+  __shared__ uint64_t keys[SV_PLAN_MAX_SLOTS];
+  __shared__ uint32_t part[kWaves][kReg / 2];
+  __shared__ double wsum[kWaves];
   __shared__ double red_r[kWaves];
   __shared__ int red_b[kWaves];
-  __shared__ int n_slots;
+  __shared__ int red_n[kWaves];
+  __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = P.K, N = P.bs * P.K;
-  uint64_t* keys = buf[0];
-  if (tid == 0) n_slots = 0;
-  for (int i = tid; i < N; i += kThreads) keys[i] = ~0ull;
+  const int N = P.bs * P.K;
+  // every key; this workgroup's slots [s0, s1)
+  slot_keys(P, 0, N, keys);
   __syncthreads();
-  // scores: one thread per request walks its positions in order
+  const int s0 = blockIdx.x * kSlots, s1 = min(s0 + kSlots, N);
+  const int g = tid / kParts, p = tid % kParts;  // slot group, part of the keys
+  uint64_t x[kReg];
+#pragma unroll
+  for (int r = 0; r < kReg; ++r) {
+    const int s = s0 + g * kReg + r;
+    x[r] = s < s1 ? keys[s] : ~0ull;
+  }
+  uint32_t c[kReg];
+  count_below(keys, p, N, x, c);
+  // sum over the parts: within the wave (two counts packed per word, each
+  // at most SV_PLAN_MAX_SLOTS < 2^16), then the group's two waves
+  uint32_t c2[kReg / 2];
+#pragma unroll
+  for (int r = 0; r < kReg / 2; ++r) c2[r] = c[2 * r] | (c[2 * r + 1] << 16);
+#pragma unroll
+  for (int r = 0; r < kReg / 2; ++r)
+    for (int o = 32; o > 0; o >>= 1) c2[r] += (uint32_t)__shfl_xor((int)c2[r], o, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < kReg / 2; ++r) part[wave][r] = c2[r];
+  __syncthreads();
+  static_assert(kParts == 128, "two waves per slot group");
+  if (tid < kSlots) {
+    const int gg = tid / kReg, r = tid % kReg;
+    const uint32_t w2 = part[2 * gg][r >> 1] + part[2 * gg + 1][r >> 1];
+    const uint32_t rk = (w2 >> (16 * (r & 1))) & 0xFFFFu;
+    const int s = s0 + tid;
+    if (s < s1) {
+      const uint64_t xs = keys[s];
+      cst32(&P.rank[s], rk);
+      if (xs != ~0ull) cst32((uint32_t*)&P.sscore[rk], __float_as_uint(key_score(xs)));
+    }
+  }
+  // the last workgroup to finish does the rest: every wave's stores are
+  // complete before the count
+  wait_mem();
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(P.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
+  __syncthreads();
+  if (!last) return;
+  // every load up front: drafted positions, the sorted scores and the costs
+  // that can be needed, and the ranks (into LDS, over the keys)
+  const int bmax0 = min(P.bmax_table, N);
+  const int C0 = (bmax0 + kThreads - 1) / kThreads;  // <= kPer
+  const int r0 = tid * C0;
+  int nst[kPer];
+  float sc[kPer];
+  double cs[kPer];
+  uint32_t rk[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int b = u * kThreads + tid;
+    nst[u] = b < P.bs ? steps_of(P, b) : 0;
+    sc[u] = (u < C0 && r0 + u < bmax0) ? __uint_as_float(cld32((const uint32_t*)&P.sscore[r0 + u])) : 0.0f;
+    cs[u] = (u < C0 && r0 + u < bmax0) ? P.cost[r0 + u + 1] : 1.0;
+    rk[u] = b < N ? cld32(&P.rank[b]) : 0u;
+  }
+  uint32_t* rank_lds = (uint32_t*)keys;  // the keys are no longer needed
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (u * kThreads + tid < N) rank_lds[u * kThreads + tid] = rk[u];
   int mine = 0;
-  for (int b = tid; b < P.bs; b += kThreads) {
-    int len = P.num_steps ? P.num_steps[b] : K;
-    len = len < 0 ? 0 : (len > K ? K : len);
-    float s = 1.0f;
-    for (int j = 0; j < len; ++j) {
-      float c = P.conf[(int64_t)b * K + j];
-      if (!(c > 0.0f)) c = 0.0f;
-      if (c > 1.0f) c = 1.0f;
-      s = __fmul_rn(s, c);
-      keys[b * K + j] = ((uint64_t)(0xFFFFFFFFu - __float_as_uint(s)) << 32) | ((uint64_t)j << 20) | (uint64_t)b;
-    }
-    mine += len;
-  }
-  if (mine) atomicAdd(&n_slots, mine);
-  // bottom-up merge of the sorted runs
-  int cur = 0;
-  for (int L = K; L < N; L <<= 1) {
-    __syncthreads();
-    const uint64_t* src = buf[cur];
-    uint64_t* dst = buf[cur ^ 1];
-    for (int p = tid; p < N; p += kThreads) {
-      const int run = p / L;
-      const int a0 = (run & ~1) * L, b0 = a0 + L, b1 = min(b0 + L, N);
-      const uint64_t x = src[p];
-      int pos;
-      if (b0 >= N) pos = p;  // the last run has no partner this round
-      else if (run & 1) pos = a0 + (p - b0) + count_before(src, a0, b0, x, true);
-      else pos = a0 + (p - a0) + count_before(src, b0, b1, x, false);
-      dst[pos] = x;
-    }
-    cur ^= 1;
-  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) mine += nst[u];
+  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) red_n[wave] = mine;
   __syncthreads();
-  keys = buf[cur];
-  const int n = n_slots;
+  int n = 0;
+  for (int w = 0; w < kWaves; ++w) n += red_n[w];
   const int bmax = P.bmax_table < n ? P.bmax_table : n;
   // gain(B) = sum of the first B sorted scores.  Thread t owns positions
-  // [t*C, (t+1)*C) of the sorted list (C = ceil(bmax / 1024)): its chunk
-  // total, an exclusive block scan of the totals, then its own B values.
-  const int C = (bmax + kThreads - 1) / kThreads;
-  const int r0 = tid * C, r1 = min(r0 + C, bmax);
-  double part = 0.0;
-  for (int r = r0; r < r1; ++r) part += (double)__uint_as_float(0xFFFFFFFFu - (uint32_t)(keys[r] >> 32));
-  scan[tid] = part;
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {  // inclusive Hillis-Steele scan, fixed order
-    const double v = tid >= o ? scan[tid - o] : 0.0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  double gain = scan[tid] - part;  // exclusive prefix: gain at B = r0
+  // [t C0, (t + 1) C0) of the sorted list, below bmax: its chunk total, an
+  // exclusive block scan of the totals, then its own B.
+  double part_sum = 0.0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (u < C0 && r0 + u < bmax) part_sum += (double)sc[u];
+  double gain = block_exclusive(part_sum, wsum);  // gain at B = r0
   double best_r = -INFINITY;
   int best_b = INT32_MAX;
   if (tid == 0) {  // B = 0
@@ -144,13 +256,16 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
     if (!(best_r > -INFINITY)) best_r = -INFINITY, best_b = INT32_MAX;
     else best_b = 0;
   }
-  for (int r = r0; r < r1; ++r) {
-    gain += (double)__uint_as_float(0xFFFFFFFFu - (uint32_t)(keys[r] >> 32));
-    const int B = r + 1;
-    const double rt = (P.base + gain) / P.cost[B];
-    if (better(rt, B, best_r, best_b)) {
-      best_r = rt;
-      best_b = B;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (u < C0 && r0 + u < bmax) {
+      gain += (double)sc[u];
+      const int B = r0 + u + 1;
+      const double rt = (P.base + gain) / cs[u];
+      if (better(rt, B, best_r, best_b)) {
+        best_r = rt;
+        best_b = B;
+      }
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -174,19 +289,26 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
       best_b = red_b[w];
     }
   const int bstar = best_b == INT32_MAX ? 0 : best_b;
-  for (int b = tid; b < P.bs; b += kThreads) P.draft_len[b] = 0;
-  __syncthreads();
-  for (int r = tid; r < bstar; r += kThreads) {
-    const uint64_t key = keys[r];
-    atomicMax(&P.draft_len[(int)(key & 0xFFFFFu)], (int)((key >> 20) & 63u) + 1);
+  // a request's admitted count: its slots ranked below the budget (a prefix
+  // of its positions)
+  for (int b = tid; b < P.bs; b += kThreads) {
+    int len = 0;
+    for (int j = 0; j < P.K; ++j) len += rank_lds[b * P.K + j] < (uint32_t)bstar ? 1 : 0;
+    P.draft_len[b] = len;
   }
   if (tid == 0) {
     *P.budget = bstar;
     if (P.rate) *P.rate = best_r;
+    cst32(P.counter, 0u);
   }
 }
 
 }  // namespace svp
+
+extern "C" size_t sv_plan_workspace_bytes(int32_t batch, int32_t max_steps) {
+  if (batch < 1 || max_steps < 1 || max_steps > 64 || (int64_t)batch * max_steps > SV_PLAN_MAX_SLOTS) return 0;
+  return svp::kWsBytes;
+}
 
 extern "C" sv_status sv_plan_budget(const sv_plan_desc* d, void* stream) {
   if (d == nullptr) return SV_ERR_INVALID_ARGUMENT;
@@ -194,6 +316,9 @@ extern "C" sv_status sv_plan_budget(const sv_plan_desc* d, void* stream) {
   if ((int64_t)d->batch * d->max_steps > SV_PLAN_MAX_SLOTS) return SV_ERR_UNSUPPORTED;
   if (d->confidence == nullptr || d->cost == nullptr || d->budget == nullptr || d->draft_len == nullptr)
     return SV_ERR_INVALID_ARGUMENT;
+  const int64_t n = (int64_t)d->batch * d->max_steps;
+  if (d->workspace == nullptr || ((uintptr_t)d->workspace & 255u) != 0) return SV_ERR_INVALID_ARGUMENT;
+  if (d->workspace_bytes < svp::kWsBytes) return SV_ERR_WORKSPACE_TOO_SMALL;
   svp::PlanParams P;
   P.bs = d->batch;
   P.K = d->max_steps;
@@ -205,6 +330,11 @@ extern "C" sv_status sv_plan_budget(const sv_plan_desc* d, void* stream) {
   P.budget = d->budget;
   P.draft_len = d->draft_len;
   P.rate = d->rate;
-  hipLaunchKernelGGL(svp::plan_kernel, dim3(1), dim3(svp::kThreads), 0, (hipStream_t)stream, P);
+  uint8_t* ws = (uint8_t*)d->workspace;
+  P.counter = (uint32_t*)ws;
+  P.rank = (uint32_t*)(ws + svp::kWsRank);
+  P.sscore = (float*)(ws + svp::kWsScore);
+  const int grid = (int)((n + svp::kSlots - 1) / svp::kSlots);
+  hipLaunchKernelGGL(svp::plan_kernel, dim3((unsigned)grid), dim3(svp::kThreads), 0, (hipStream_t)stream, P);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

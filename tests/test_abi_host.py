@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for expected in ("sv_verify_chain", "sv_verify_tree", "sv_row_stats", "sv_chain_workspace_bytes",
                      "sv_tree_workspace_bytes", "sv_row_stats_workspace_bytes", "sv_workspace_init",
-                     "sv_status_string", "sv_abi_version", "sv_plan_budget", "sv_compact_kv"):
+                     "sv_status_string", "sv_abi_version", "sv_plan_budget", "sv_plan_workspace_bytes", "sv_compact_kv"):
         assert expected in names
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.abi_version() == 2
+    assert sv.abi_version() == 3
     assert sv.status_string(0) == "ok"
     assert "workspace" in sv.status_string(2)
     assert sv.status_string(99) == "unknown status"
@@ -188,19 +188,30 @@ def test_product_path_does_not_touch_the_oracle():
 def _plan_desc(**kw):
     fake = 0x100000
     d = dict(batch=4, max_steps=7, confidence=fake, num_steps=None, max_budget=28, cost=fake, base_tokens=4.0,
-             budget=fake, draft_len=fake, rate=None)
+             budget=fake, draft_len=fake, rate=None, workspace=fake, workspace_bytes=1 << 20)
     d.update(kw)
     return _lib.PlanDesc(**d)
 
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, 1), ("max_steps", 0, 1), ("max_steps", 65, 1), ("max_budget", -1, 1), ("confidence", None, 1),
-    ("cost", None, 1), ("budget", None, 1), ("draft_len", None, 1), ("batch", 1171, 3),
+    ("cost", None, 1), ("budget", None, 1), ("draft_len", None, 1), ("batch", 1171, 3), ("workspace", None, 1),
+    ("workspace", 0x100010, 1), ("workspace_bytes", 1024, 2),
 ])
 def test_plan_argument_validation(field, value, code):
     d = _plan_desc(**{field: value})
     assert sv.lib().sv_plan_budget(ctypes.byref(d), None) == code
     assert sv.lib().sv_plan_budget(None, None) == 1
+
+
+def test_plan_workspace_bytes():
+    """One layout for every shape (a workspace serves calls of any shape)."""
+    n = sv.plan_workspace_bytes(512, 7)
+    assert n >= sv.PLAN_MAX_SLOTS * 8 and n % 256 == 0
+    for shape in ((1, 1), (8192, 1), (1024, 8), (3, 64)):
+        assert sv.plan_workspace_bytes(*shape) == n
+    for bad in ((0, 7), (4, 0), (4, 65), (1171, 7)):
+        assert sv.plan_workspace_bytes(*bad) == 0
 
 
 def _compact_desc(**kw):

@@ -92,3 +92,21 @@ def test_plan_is_deterministic(dev):
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_workspace_reuse_across_shapes(dev):
+    """One caller workspace serves plans of every shape in turn; each call
+    leaves its completion counter at zero."""
+    ws = torch.zeros(sv.plan_workspace_bytes(1024, 8), dtype=torch.uint8, device=dev)
+    for seed, bs, K in ((31, 1024, 8), (32, 3, 5), (33, 512, 7), (34, 1, 1), (35, 1024, 8)):
+        rng = np.random.default_rng(seed)
+        conf = rng.beta(4, 1.2, size=(bs, K)).astype(np.float32)
+        cost = 1.0 + np.arange(bs * K + 1) * rng.random() * 5.0 / (bs * K)
+        print(f"[plan] workspace reuse bs={bs} K={K}", flush=True)
+        ref = oracle.plan_budget(conf, cost, float(bs))
+        out = sv.plan_budget(torch.from_numpy(conf).to(dev), torch.from_numpy(cost).to(dev), float(bs), workspace=ws)
+        torch.cuda.synchronize()
+        if ref["margin"] >= 1e-12:
+            assert int(out["budget"].item()) == ref["budget"]
+            np.testing.assert_array_equal(out["draft_len"].cpu().numpy(), ref["draft_len"])
+        assert int(ws[:4].view(torch.int32).item()) == 0, "completion counter left non-zero"
