@@ -34,8 +34,12 @@
 //       token.
 // Two optional passes sit between them in the phased schedule: KR, the
 // block rule's residual masses of draft rows 1..k_b-1 (SV_FLAG_BLOCK), and
-// KF, the top-k / top-p thresholds and kept sums of every filtered row read
-// (the descriptors' top_k / top_p).
+// KF, the top-k / top-p thresholds and kept sums of every filtered row (the
+// descriptors' top_k / top_p): for top-k up to kCandTopK from the
+// candidates that K1 publishes for such rows (every thread's two largest
+// 16-entry groups), else from passes over the row.  Unfiltered one-hot
+// chains and trees run K23C in place of K23: K1 also publishes every race
+// chunk's sum, and one workgroup per request decides and races from those.
 // The phased schedule is two stream-ordered launches (K1, then K23).  The
 // fused schedule is one launch: the K23 items come after every K1 item in
 // dispatch order and wait (bounded, about a second, then SV_REQ_INTERNAL)
@@ -3536,6 +3540,17 @@ static sv_status scratch_address(void*& out) {
   return SV_OK;
 }
 
+// An enum-typed value from a caller, read as the int it holds: a caller may
+// pass any value, and reading an enum outside its enumerators' range is
+// undefined in C++.
+template <typename E>
+static int enum_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 }  // namespace sv
 
 using namespace sv;
@@ -3545,7 +3560,7 @@ extern "C" {
 int32_t sv_abi_version(void) { return SV_ABI_VERSION; }
 
 const char* sv_status_string(sv_status s) {
-  switch (s) {
+  switch (enum_int(s)) {
     case SV_OK: return "ok";
     case SV_ERR_INVALID_ARGUMENT: return "invalid argument";
     case SV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
@@ -3555,7 +3570,7 @@ const char* sv_status_string(sv_status s) {
   return "unknown status";
 }
 
-static bool dtype_ok(sv_dtype d) { return d == SV_F32 || d == SV_BF16; }
+static bool dtype_ok(const sv_dtype& d) { return enum_int(d) == SV_F32 || enum_int(d) == SV_BF16; }
 
 static const uint32_t kKnownFlags =
     SV_FLAG_PHASED | SV_FLAG_FP64_RACE | SV_FLAG_FUSED | SV_FLAG_STATS_ONLY | SV_FLAG_DECIDE_ONLY | SV_FLAG_BLOCK |
@@ -3605,7 +3620,8 @@ static sv_status chain_params(const sv_chain_desc* d, Params& P) {
       d->vocab < 1 || d->vocab > SV_MAX_VOCAB)
     return SV_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(d->logits_dtype)) return SV_ERR_UNSUPPORTED;
-  if (d->draft_kind != SV_DRAFT_PROBS && d->draft_kind != SV_DRAFT_ONEHOT) return SV_ERR_UNSUPPORTED;
+  if (enum_int(d->draft_kind) != SV_DRAFT_PROBS && enum_int(d->draft_kind) != SV_DRAFT_ONEHOT)
+    return SV_ERR_UNSUPPORTED;
   if (d->flags & ~kKnownFlags) return SV_ERR_UNSUPPORTED;
   if (!one_schedule(d->flags)) return SV_ERR_INVALID_ARGUMENT;
   if ((d->flags & SV_FLAG_BLOCK) && (d->flags & SV_FLAG_FUSED)) return SV_ERR_UNSUPPORTED;
