@@ -10,8 +10,11 @@ region; the timed steps rotate over several input sets whose total size
 exceeds the 256 MB Infinity Cache, so the stream really comes from HBM.
 
 The call is two stream-ordered kernels: the row-statistics pass (streams
-every logit row once; the dominant kernel) and the decision/sampling pass.
-Three timed passes:
+every logit row once; the dominant kernel) and the decision/sampling pass;
+--top-k / --top-p add the thresholds pass between them (and, for top-k, the
+statistics pass also keeps the candidate groups), --rule block the residual
+pass.  The first phase is always the statistics pass alone; the second
+phase holds the rest.  Three timed passes:
   1. throughput: K plain calls between two events -> value, ms_per_step;
   2. kernels: the same K calls, split into their two phases
      (FLAG_STATS_ONLY, FLAG_DECIDE_ONLY) and grouped by input set: the
@@ -36,6 +39,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -64,18 +68,18 @@ def kernel_source_hash() -> str:
 
 
 def filter_bytes(inp, top_k, top_p):
-    """Bytes the top-k / top-p thresholds must move at least: one read of
-    every filtered row (rows 0..k_b of each stochastic request, when a filter
-    is on) and its 16-byte record."""
+    """Bytes the top-k / top-p thresholds must move beyond the statistics
+    pass: the logits of a filtered row are already counted there (one pass
+    can keep what the thresholds need), so only each filtered row's 16-byte
+    record (rows 0..k_b of each stochastic request, when a filter is on)."""
     bs, R, V = inp.logits.shape
     k = R - 1
     if not ((0 < top_k < V) or (0.0 < top_p < 1.0)):
         return 0
-    bl = inp.logits.dtype.itemsize
     ids = inp.draft_ids
     kb = np.where((ids == -1).any(axis=1), np.argmax(ids == -1, axis=1), k) if k else np.zeros(bs, np.int64)
     stoch = (inp.temperature > 0) & np.isfinite(inp.temperature)
-    return int(((kb + 1) * stoch).sum() * (V * bl + 16))
+    return int(((kb + 1) * stoch).sum() * 16)
 
 
 def algorithmic_bytes(inp, accept_len, block=False):
@@ -130,18 +134,25 @@ def tree_algorithmic_bytes(inp, accept_len):
     return int(stats), int(decide)
 
 
-def load_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` measured with rocprofv3 counters for
-    this kernel source (committed under profiles/), or None if there is no
-    record or the kernel changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def load_traffic(workload: str, kernels, top_k=0, top_p=1.0):
+    """HBM bytes per launch of `kernels` (one name, or several whose bytes
+    add) measured with rocprofv3 counters for this kernel source (committed
+    under profiles/), or None if there is no record or the kernels changed
+    since the counters were taken."""
+    path = traffic_name(workload, top_k, top_p)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
+    total = 0
+    for k in ([kernels] if isinstance(kernels, str) else kernels):
+        b = rec.get("kernels", {}).get(k, {}).get("bytes_per_launch")
+        if b is None:
+            return None
+        total += b
+    return total
 
 
 def _pmc_per_dispatch(db_path, counter):
@@ -165,11 +176,34 @@ def _pmc_per_dispatch(db_path, counter):
     return {k: tot[k] / len(disp[k]) for k in tot}
 
 
-def write_traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, kernels=("k1_kernel", "k23_kernel")):
-    """Write profiles/traffic_<workload>.json from four rocprofv3 --pmc runs:
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the benchmark, and of a
-    plain device copy of known size (bench.py --copy-calibration-mib 1024),
-    whose counts scale the kernel's to bytes."""
+def _library_kernel(name):
+    """Short name of a library kernel from a profiler's kernel name, mangled
+    (_ZN2sv9kf_kernel...) or not (void sv::kf_kernel<true>(sv::Params)); None
+    for other kernels."""
+    m = re.match(r"_ZN(?:2sv|3svp)(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        return name[m.end():m.end() + n]
+    if name.startswith("_ZN12_GLOBAL__N_118stream_read_kernel"):
+        return "stream_read_kernel"
+    m = re.match(r"(?:void )?(?:sv|svp)::(\w+)", name)
+    if m:
+        return m.group(1)
+    return "stream_read_kernel" if name.startswith("(anonymous namespace)::stream_read_kernel") else None
+
+
+def traffic_name(workload, top_k=0, top_p=1.0):
+    """profiles/ file of a workload's counter record (filtered calls apart)."""
+    tag = "" if not ((top_k and top_k > 0) or top_p < 1.0) else f"_topk{top_k}_topp{top_p:g}"
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
+
+
+def write_traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, top_k=0, top_p=1.0):
+    """Write profiles/traffic_<workload>[_topk.._topp..].json from four
+    rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+    benchmark, and of a plain device copy of known size (bench.py
+    --copy-calibration-mib 1024), whose counts scale the kernels' to bytes.
+    Every kernel of the library in the run is recorded."""
     copy_bytes = 1024 << 20
 
     def pick(d, name):
@@ -183,15 +217,20 @@ def write_traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, ke
     ff, wf = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
     fetch = _pmc_per_dispatch(fetch_db, "FETCH_SIZE")
     write = _pmc_per_dispatch(write_db, "WRITE_SIZE")
-    rec = {"workload": WORKLOADS[workload], "kernel_source_sha256_16": kernel_source_hash(),
+    rec = {"workload": WORKLOADS[workload], "top_k": top_k, "top_p": top_p,
+           "kernel_source_sha256_16": kernel_source_hash(),
            "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": cf, "write_size_kib": cw,
                            "fetch_factor": ff, "write_factor": wf},
            "kernels": {}}
-    for k in kernels:
-        fk, wk = pick(fetch, k), pick(write, k)
+    for full in sorted(fetch):
+        k = _library_kernel(full)
+        if k is None or k in rec["kernels"]:
+            continue
+        fk, wk = pick(fetch, full), pick(write, full)
         rec["kernels"][k] = {"fetch_size_kib_per_dispatch": round(fk, 1), "write_size_kib_per_dispatch": round(wk, 1),
+                             "fetch_bytes_per_launch": int(round(fk * 1024 * ff)),
                              "bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf))}
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = traffic_name(workload, top_k, top_p)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -371,18 +410,22 @@ def bench_plan(args, sv, torch, dev):
         step = np.maximum(16e9 / (3.35e12 * 0.8), (bs + np.arange(n + 1)) * 16e9 / (989e12 * 0.5))
         cost = torch.from_numpy(0.25e-3 + step).to(dev)
         c = torch.from_numpy(conf).to(dev)
+        # descriptor built once: the loop below enqueues launches only, so the
+        # events see back-to-back kernels, not Python's per-call set-up
+        plan = sv.PreparedPlan(c, cost, float(bs))
         for _ in range(args.warmup):
-            sv.plan_budget(c, cost, float(bs))
+            plan.launch()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         stream = torch.cuda.current_stream(dev)
         e0.record(stream)
         for _ in range(args.steps):
-            out = sv.plan_budget(c, cost, float(bs))
+            plan.launch()
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
-        lines.append({"batch": bs, "K": K, "slots": n, "us_per_plan": us, "budget": int(out["budget"].item())})
+        lines.append({"batch": bs, "K": K, "slots": n, "us_per_plan": us,
+                      "budget": int(plan.out["budget"].item())})
     print(json.dumps({"metric": "survival top-k draft budget latency, 1 MI355X", "value": lines[0]["us_per_plan"],
                       "unit": "us/plan", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "higher_is_better": False, "data": "synthetic",
@@ -480,7 +523,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.traffic_from:
-        write_traffic(args.workload, *args.traffic_from)
+        write_traffic(args.workload, *args.traffic_from, top_k=args.top_k, top_p=args.top_p)
         return
 
     import torch
@@ -545,7 +588,7 @@ def main():
     filtered = (0 < args.top_k < V0) or (0.0 < args.top_p < 1.0)
     if filtered and args.schedule == "fused":
         raise SystemExit("top-k / top-p filtering needs the phased schedule")
-    calls, plain_calls = [], []
+    calls = []
     for inp in inputs:
         fk = fp = None
         if filtered:
@@ -560,9 +603,6 @@ def main():
             di, dq = to_dev(inp.draft_ids), to_dev(inp.draft_probs)
             mk = lambda f, w, k=None, p=None: sv.PreparedChain(dl, di, dt, ds, draft_probs=dq, onehot=inp.onehot,
                                                                flags=f, workspace=w, top_k=k, top_p=p)
-        if filtered:
-            # the same call without the filter: its statistics pass alone, for timing
-            plain_calls.append(mk(flags, sv.Workspace(1 << 20, dev)))
         calls.append(mk(flags, sv.Workspace(1 << 20, dev), fk, fp))
     resident = sum(c.logits.numel() * c.logits.element_size()
                    + (c.q.numel() * 4 if getattr(c, "q", None) is not None else 0) for c in calls)
@@ -616,14 +656,9 @@ def main():
     split = args.schedule != "fused"
     S = len(calls)
     groups = max(1, K // S)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(groups)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(groups)]
     torch.cuda.synchronize()
     for g in range(groups):
-        if filtered:
-            # the statistics pass alone (the unfiltered call's first phase)
-            ev[g][3].record(stream)
-            for c in plain_calls:
-                c.launch(phase_flag=sv.FLAG_STATS_ONLY)
         ev[g][0].record(stream)
         if split:
             for c in calls:
@@ -638,21 +673,14 @@ def main():
         ev[g][2].record(stream)
     torch.cuda.synchronize()
     first_ms = np.array([e[0].elapsed_time(e[1]) for e in ev]) / S
-    k1_ms = np.array([e[3].elapsed_time(e[0]) for e in ev]) / S if filtered else None
     filt_bytes = np.array([a[2] for a in alg] * groups, dtype=np.float64)
     second_ms = np.array([e[1].elapsed_time(e[2]) for e in ev]) / S if split else None
     stats_bytes = np.array([a[0] for a in alg] * groups, dtype=np.float64)
     decide_bytes = np.array([a[1] for a in alg] * groups, dtype=np.float64)
-    kf_ms = None
-    if split and filtered:
-        # the first phase is the statistics pass then the thresholds pass;
-        # the roofline covers the statistics pass timed alone
-        kf_ms = first_ms - k1_ms
-        first_ms = k1_ms
-        kernel = "row statistics (k1_kernel)"
-        kbytes = stats_bytes
-    elif split:
-        kernel = "row statistics (k1_kernel)"
+    # top-k calls' statistics pass also keeps the candidate groups
+    cand = filtered and 0 < args.top_k <= 128 and args.top_k < V0 and not args.kf_rows
+    if split:
+        kernel = "row statistics with top-k candidates (k1f_kernel)" if cand else "row statistics (k1_kernel)"
         kbytes = stats_bytes
     else:
         kernel = "fused verify (fused_kernel)"
@@ -665,13 +693,14 @@ def main():
     # the whole call
     call_bytes = (stats_bytes + decide_bytes + filt_bytes).mean()
     call_us = total_ms * 1e3 / K
-    kernel_us = float(first_ms.mean() * 1e3 + (second_ms.mean() * 1e3 if split else 0.0)
-                      + (kf_ms.mean() * 1e3 if kf_ms is not None else 0.0))
-    k1_name = "k1_kernel" if split else "fused_kernel"
-    traffic = None if (block or filtered) else load_traffic(args.workload, k1_name)
-    traffic23 = None if (block or filtered or not split) else load_traffic(args.workload, "k23_kernel")
+    kernel_us = float(first_ms.mean() * 1e3 + (second_ms.mean() * 1e3 if split else 0.0))
+    k1_name = ("k1f_kernel" if cand else "k1_kernel") if split else "fused_kernel"
+    tk, tp = (args.top_k, args.top_p) if filtered else (0, 1.0)
+    traffic = None if block else load_traffic(args.workload, k1_name, tk, tp)
+    rest = (["kf_kernel"] if filtered else []) + ["k23_kernel"]
+    traffic23 = None if (block or not split) else load_traffic(args.workload, rest, tk, tp)
     call = {
-        "kernels": ("k1_kernel + k23_kernel" if split else "fused_kernel")
+        "kernels": (f"{k1_name} + k23_kernel" if split else "fused_kernel")
                    + (" + kf_kernel" if filtered else "") + (" + kr_kernel" if block else ""),
         "algorithmic_bytes": float(call_bytes),
         "us_per_call": call_us,
@@ -738,19 +767,12 @@ def main():
     if split:
         line["roofline"]["other_kernel"] = {
             "kernel": ("residual masses, decisions and sampling (kr_kernel + k23_kernel)" if block
+                       else "filter thresholds, decisions and sampling (kf_kernel + k23_kernel)" if filtered
                        else "decisions and sampling (k23_kernel)"),
-            "algorithmic_bytes_per_launch": float(decide_bytes.mean()),
+            "algorithmic_bytes_per_launch": float((decide_bytes + filt_bytes).mean()),
             "launch_us_mean": float(second_ms.mean() * 1e3),
-            "achieved": float(decide_bytes.sum() / (second_ms.sum() * S * 1e-3) / 1e9),
+            "achieved": float((decide_bytes + filt_bytes).sum() / (second_ms.sum() * S * 1e-3) / 1e9),
             "traffic": traffic23,
-        }
-    if split and filtered:
-        line["roofline"]["filter_kernel"] = {
-            "kernel": "top-k / top-p thresholds (kf_kernel)",
-            "algorithmic_bytes_per_launch": float(filt_bytes.mean()),
-            "launch_us_mean": float(kf_ms.mean() * 1e3),
-            "achieved": float(filt_bytes.sum() / (kf_ms.sum() * S * 1e-3) / 1e9),
-            "timing": "first phase minus the statistics pass timed alone",
         }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

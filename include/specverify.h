@@ -111,9 +111,11 @@ enum {
 #define SV_FLAG_FP64_RACE 2u /* evaluate every sampling race entirely in fp64 (slow; a test aid) */
 #define SV_FLAG_FUSED 4u     /* one launch: the decision/sampling workgroups wait for their rows' statistics */
 /* Split-phase use of the phased schedule: a call with STATS_ONLY runs only
- * the row-statistics pass (outputs untouched); a following call with
- * DECIDE_ONLY, the same descriptor and workspace, on the same stream, runs
- * the decisions and sampling and writes the outputs.  Together they equal
+ * the row-statistics pass, the one launch that reads every target logit
+ * (outputs untouched); a following call with DECIDE_ONLY, the same
+ * descriptor and workspace, on the same stream, runs the rest (filter
+ * thresholds, block residuals, decisions and sampling) and writes the
+ * outputs.  Together they equal
  * one plain call; other work may be queued between them.  Neither may be
  * combined with SV_FLAG_FUSED or with each other. */
 #define SV_FLAG_STATS_ONLY 8u
@@ -177,7 +179,7 @@ typedef struct {
    * more launch (the thresholds of every row read, one workgroup each)
    * between the statistics and the decisions; not available with
    * SV_FLAG_FUSED (SV_ERR_UNSUPPORTED).  With STATS_ONLY / DECIDE_ONLY the
-   * thresholds belong to the STATS_ONLY call, and both calls must pass the
+   * thresholds belong to the DECIDE_ONLY call, and both calls must pass the
    * same arrays.  The arrays are read on the device (device pointers). */
   const int32_t* top_k;       /* [bs] or NULL */
   const float* top_p;         /* [bs] or NULL */

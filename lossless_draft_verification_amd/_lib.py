@@ -435,31 +435,48 @@ def plan_budget(confidence, cost, base_tokens, num_steps=None, workspace=None):
     device and stream).  Returns device tensors: budget [1] int32, draft_len
     [bs] int32, rate [1] float64.
     """
-    if confidence.dim() != 2 or confidence.dtype != torch.float32:
-        raise ValueError("confidence must be a [batch, K] float32 tensor")
-    if cost.dim() != 1 or cost.dtype != torch.float64 or cost.numel() < 1:
-        raise ValueError("cost must be a non-empty 1-D float64 tensor")
-    dev = confidence.device
-    conf = confidence.contiguous()
-    c = cost.to(dev).contiguous()
-    bs, K = conf.shape
-    ns = None
-    if num_steps is not None:
-        ns = num_steps.to(device=dev, dtype=torch.int32).contiguous()
-        if ns.numel() != bs:
-            raise ValueError("need one num_steps entry per request")
-    out = dict(budget=torch.empty(1, dtype=torch.int32, device=dev),
-               draft_len=torch.empty(bs, dtype=torch.int32, device=dev),
-               rate=torch.empty(1, dtype=torch.float64, device=dev))
-    need = int(lib().sv_plan_workspace_bytes(bs, K))
-    ws = plan_workspace(dev, need) if workspace is None else workspace
-    d = PlanDesc(bs, K, conf.data_ptr(), ns.data_ptr() if ns is not None else None, c.numel() - 1, c.data_ptr(),
-                 float(base_tokens), out["budget"].data_ptr(), out["draft_len"].data_ptr(), out["rate"].data_ptr(),
-                 ws.data_ptr(), ws.numel() * ws.element_size())
-    st = lib().sv_plan_budget(ctypes.byref(d), _stream(dev))
-    if st != OK:
-        raise SpecVerifyError(st, "sv_plan_budget")
-    return out
+    p = PreparedPlan(confidence, cost, base_tokens, num_steps, workspace)
+    p.launch()
+    return p.out
+
+
+class PreparedPlan:
+    """A survival top-k plan with its descriptor built once, for calling
+    repeatedly on fixed device buffers.  launch() enqueues one sv_plan_budget
+    on the current stream; outputs (self.out) are overwritten in place."""
+
+    def __init__(self, confidence, cost, base_tokens, num_steps=None, workspace=None):
+        if confidence.dim() != 2 or confidence.dtype != torch.float32:
+            raise ValueError("confidence must be a [batch, K] float32 tensor")
+        if cost.dim() != 1 or cost.dtype != torch.float64 or cost.numel() < 1:
+            raise ValueError("cost must be a non-empty 1-D float64 tensor")
+        dev = confidence.device
+        self.conf = confidence.contiguous()
+        self.cost = cost.to(dev).contiguous()
+        bs, K = self.conf.shape
+        self.ns = None
+        if num_steps is not None:
+            self.ns = num_steps.to(device=dev, dtype=torch.int32).contiguous()
+            if self.ns.numel() != bs:
+                raise ValueError("need one num_steps entry per request")
+        self.out = dict(budget=torch.empty(1, dtype=torch.int32, device=dev),
+                        draft_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                        rate=torch.empty(1, dtype=torch.float64, device=dev))
+        need = int(lib().sv_plan_workspace_bytes(bs, K))
+        self.ws = plan_workspace(dev, need) if workspace is None else workspace
+        self.device = dev
+        self.desc = PlanDesc(bs, K, self.conf.data_ptr(), self.ns.data_ptr() if self.ns is not None else None,
+                             self.cost.numel() - 1, self.cost.data_ptr(), float(base_tokens),
+                             self.out["budget"].data_ptr(), self.out["draft_len"].data_ptr(),
+                             self.out["rate"].data_ptr(), self.ws.data_ptr(), self.ws.numel() * self.ws.element_size())
+        self._ref = ctypes.byref(self.desc)
+        self._fn = lib().sv_plan_budget
+
+    def launch(self, stream=None):
+        s = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream)
+        st = self._fn(self._ref, s)
+        if st != OK:
+            raise SpecVerifyError(st, "sv_plan_budget")
 
 
 def plan_workspace_bytes(batch: int, max_steps: int) -> int:

@@ -3499,9 +3499,9 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
       // top-k calls: the statistics pass also publishes candidate groups
       const bool cand = filtered && P.top_k != nullptr && !(P.flags & SV_FLAG_KF_ROWS);
       hipLaunchKernelGGL(cand ? K.k1f : K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
-      if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kKF), 0, stream, P);
     }
     if (!(P.flags & SV_FLAG_STATS_ONLY)) {
+      if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kKF), 0, stream, P);
       if ((P.flags & SV_FLAG_BLOCK) && P.k >= 2 && P.draft_kind == SV_DRAFT_PROBS)
         hipLaunchKernelGGL(K.kr, dim3((unsigned)gridr), dim3(kWG), 0, stream, P);
       if (P.csum_on) hipLaunchKernelGGL(K.k23c, dim3((unsigned)P.bs), dim3(kWG), 0, stream, P);

@@ -42,13 +42,14 @@ def test_algorithmic_bytes_onehot_reads_no_q():
     assert decide == 3 * (4 + 8 + 8) + 3 * (4 + 12 + 4) + 2 * V * bl
 
 
-def test_filter_bytes_counts_the_filtered_rows_once():
+def test_filter_bytes_counts_the_filtered_rows_records():
     inp = _inputs(bf16=True, onehot=False)
     assert bench.filter_bytes(inp, 0, 1.0) == 0               # no filter
     assert bench.filter_bytes(inp, 10, 1.0) == 0              # k >= V is off
     # stochastic requests 1 and 2 read rows 0..1 and 0..2: 5 rows
-    assert bench.filter_bytes(inp, 3, 1.0) == 5 * (10 * 2 + 16)
-    assert bench.filter_bytes(inp, 0, 0.9) == 5 * (10 * 2 + 16)
+    # the rows' logits belong to the statistics pass; only the records remain
+    assert bench.filter_bytes(inp, 3, 1.0) == 5 * 16
+    assert bench.filter_bytes(inp, 0, 0.9) == 5 * 16
 
 
 def test_tree_algorithmic_bytes_by_hand():
