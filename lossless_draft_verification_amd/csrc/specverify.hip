@@ -2806,7 +2806,7 @@ __device__ __forceinline__ void kf_row(const Params& P, int64_t row, float Tf, i
 
 // ------------------------------------------------ thresholds from candidates
 // The top-k rows whose statistics segments published candidates: one
-// workgroup of 256 threads per row, in four steps.
+// workgroup of kKC threads per row, in four steps.
 //  1. g', the k-th largest of the published keys (see the top-k candidates
 //     of the statistics pass; 0 when fewer than k are published).
 //  2. The groups to read: the published groups >= g', and every group of
