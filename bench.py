@@ -592,8 +592,11 @@ def main():
     for inp in inputs:
         fk = fp = None
         if filtered:
-            fk = torch.full((inp.batch,), args.top_k, dtype=torch.int32, device=dev)
-            fp = torch.full((inp.batch,), args.top_p, dtype=torch.float32, device=dev)
+            # a filter that is off for every request is not passed at all
+            if 0 < args.top_k < inp.vocab:
+                fk = torch.full((inp.batch,), args.top_k, dtype=torch.int32, device=dev)
+            if 0.0 < args.top_p < 1.0:
+                fp = torch.full((inp.batch,), args.top_p, dtype=torch.float32, device=dev)
         dl, dt, ds = to_dev(inp.logits), to_dev(inp.temperature), to_dev(inp.seeds)
         if tree:
             dn, dp = to_dev(inp.node_tokens), to_dev(inp.parent)

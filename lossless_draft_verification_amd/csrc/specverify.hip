@@ -2444,26 +2444,26 @@ template <bool BF16>
 constexpr int kf_group() { return BF16 ? 8 : 4; }
 template <bool BF16>
 constexpr int kf_unroll() { return BF16 ? 4 : 8; }  // 64 or 128 bytes per thread per step
-template <bool BF16>
+template <bool BF16, int U = kf_unroll<BF16>()>
 struct KFRaw {
-  u32x4 v[kf_unroll<BF16>()];  // 8 bf16 or 4 fp32 logits per group
+  u32x4 v[U];  // 8 bf16 or 4 fp32 logits per group
 };
-template <bool BF16>
-__device__ __forceinline__ void kf_issue(const Params& P, int64_t off, int base, KFRaw<BF16>& r) {
+template <bool BF16, int U>
+__device__ __forceinline__ void kf_issue(const Params& P, int64_t off, int base, KFRaw<BF16, U>& r) {
   constexpr int E = kf_group<BF16>();
 #pragma unroll
-  for (int g = 0; g < kf_unroll<BF16>(); ++g) {
+  for (int g = 0; g < U; ++g) {
     int y0 = base + E * (g * kKF + (int)threadIdx.x);
     y0 = y0 < P.V ? y0 : 0;
     if constexpr (BF16) r.v[g] = *(const u32x4*)((const uint16_t*)P.logits + off + y0);
     else r.v[g] = *(const u32x4*)((const float*)P.logits + off + y0);
   }
 }
-template <bool BF16, typename F>
-__device__ __forceinline__ void kf_fold(const KFRaw<BF16>& r, int base, int V, F&& f) {
+template <bool BF16, int U, typename F>
+__device__ __forceinline__ void kf_fold(const KFRaw<BF16, U>& r, int base, int V, F&& f) {
   constexpr int E = kf_group<BF16>();
 #pragma unroll
-  for (int g = 0; g < kf_unroll<BF16>(); ++g) {
+  for (int g = 0; g < U; ++g) {
     const int y0 = base + E * (g * kKF + (int)threadIdx.x);
     if (y0 < V) {
       const uint32_t w[4] = {r.v[g].x, r.v[g].y, r.v[g].z, r.v[g].w};
@@ -2479,29 +2479,25 @@ __device__ __forceinline__ void kf_fold(const KFRaw<BF16>& r, int base, int V, F
     }
   }
 }
-template <bool BF16, bool LIST, typename F>
-__device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFShared& s, F&& f) {
+// U: groups per thread per step (loads in flight).
+template <bool BF16, int U = kf_unroll<BF16>(), typename F>
+__device__ __forceinline__ void kf_pass_mem(const Params& P, int64_t row, F&& f) {
   const int tid = threadIdx.x;
-  if (LIST) {
-    const int n = min(s.nlist, kKFList);
-    for (int i = tid; i < n; i += kKF) f(kf_val(s.list[i]));
-    return;
-  }
   const int V = P.V;
   const int64_t off = row * P.lstride;
   constexpr int E = kf_group<BF16>();
-  constexpr int step = E * kKF * kf_unroll<BF16>();
+  constexpr int step = E * kKF * U;
   if (P.aligned && (V % E) == 0) {
-    KFRaw<BF16> a, b;
-    kf_issue<BF16>(P, off, 0, a);
+    KFRaw<BF16, U> a, b;
+    kf_issue<BF16, U>(P, off, 0, a);
 #pragma unroll 1
     for (int base = 0;;) {
-      kf_issue<BF16>(P, off, base + step, b);
-      kf_fold<BF16>(a, base, V, f);
+      kf_issue<BF16, U>(P, off, base + step, b);
+      kf_fold<BF16, U>(a, base, V, f);
       base += step;
       if (base >= V) break;
-      kf_issue<BF16>(P, off, base + step, a);
-      kf_fold<BF16>(b, base, V, f);
+      kf_issue<BF16, U>(P, off, base + step, a);
+      kf_fold<BF16, U>(b, base, V, f);
       base += step;
       if (base >= V) break;
     }
@@ -2524,6 +2520,15 @@ __device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFSh
         if (base + 4 * (g * kKF + tid) + i < V) f(l[g][i]);
   }
 }
+template <bool BF16, bool LIST, typename F>
+__device__ __forceinline__ void kf_pass(const Params& P, int64_t row, const KFShared& s, F&& f) {
+  if (LIST) {
+    const int n = min(s.nlist, kKFList);
+    for (int i = (int)threadIdx.x; i < n; i += kKF) f(kf_val(s.list[i]));
+    return;
+  }
+  kf_pass_mem<BF16>(P, row, f);
+}
 
 __device__ __forceinline__ void kf_clear(KFShared& s) {
   for (int i = threadIdx.x; i < kKFBins; i += kKF) {
@@ -2536,13 +2541,15 @@ __device__ __forceinline__ void kf_clear(KFShared& s) {
 // The first bin from the top of a complete histogram of `nbins` bins at
 // which the sum of the bins at or above it reaches (nh, nl) (a normalised
 // fixed-point value, or a count in nl; with frac > 0 the need is frac times
-// the histogram's total instead): s.digit, s.ah/al (bins above), s.bh/bl
-// (the bin) and s.toth/totl.  Every thread calls it after the barrier that
+// the histogram's total plus (xh, xl), the mass of the ids left out of the
+// histogram, instead): s.digit, s.ah/al (bins above), s.bh/bl (the bin) and
+// s.toth/totl.  Every thread calls it after the barrier that
 // ends the histogram's pass; it ends with a barrier.  Thread t owns bins
 // [t per, (t + 1) per); the sums of the bins above a thread's come from a
 // suffix scan within its wave and the totals of the waves above.
 template <bool MASS>
-__device__ __forceinline__ void kf_find(KFShared& s, int nbins, uint64_t& nh, uint64_t& nl, float frac) {
+__device__ __forceinline__ void kf_find(KFShared& s, int nbins, uint64_t& nh, uint64_t& nl, float frac,
+                                        uint64_t xh = 0, uint64_t xl = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = nbins / kKF;
   uint64_t sh = 0, sl = 0;
@@ -2574,7 +2581,7 @@ __device__ __forceinline__ void kf_find(KFShared& s, int nbins, uint64_t& nh, ui
       rl += b;
     }
   }
-  if (frac > 0.f) kf_fix((double)frac * kf_float(th, tl), nh, nl);
+  if (frac > 0.f) kf_fix((double)frac * kf_float(th + xh, tl + xl), nh, nl);
   for (int j = per - 1; j >= 0; --j) {
     const uint64_t ph = rh, pl = rl;
     const uint64_t bh = MASS ? s.hh[tid * per + j] : 0, bl = s.hl[tid * per + j];
@@ -2606,11 +2613,15 @@ __device__ __forceinline__ void kf_mass(float l, double md, double cd, const dou
 // descent finds the group at which the mass from the top reaches its need
 // (frac > 0: frac times the set's mass), adding the masses above the found
 // group, and the group's own, to (ch, cl).  Returns the key (0: not found).
+// It starts at level L0 under the prefix pre0 of the levels above (keys all
+// under it).  A widened bf16 logit's key has its low 16 bits set by its
+// sign, so for bf16 the second level's prefix is already one logit.
 template <bool BF16, bool LIST, bool MASS>
 __device__ __forceinline__ uint32_t kf_descent(const Params& P, int64_t row, KFShared& s, const double* tab, double md, double cd,
-                               uint32_t kmin, uint64_t nh, uint64_t nl, float frac, uint64_t& ch, uint64_t& cl) {
-  uint32_t pre = 0;
-  for (int L = 0; L < 3; ++L) {
+                               uint32_t kmin, uint64_t nh, uint64_t nl, float frac, uint64_t& ch, uint64_t& cl,
+                               int L0 = 0, uint32_t pre0 = 0) {
+  uint32_t pre = pre0;
+  for (int L = L0; L < 3; ++L) {
     kf_clear(s);
     const int sh = kf_shift(L);
     const uint32_t mask = (1u << kf_width(L)) - 1u;
@@ -2635,11 +2646,12 @@ __device__ __forceinline__ uint32_t kf_descent(const Params& P, int64_t row, KFS
     kf_sub(nh, nl, s.ah, s.al);
     ch += s.ah;
     cl += s.al;
-    if (L == 2) {
+    pre = (pre << kf_width(L)) | (uint32_t)d;
+    if (L == 2 || (BF16 && L == 1)) {
       ch += s.bh;
       cl += s.bl;
+      if (L == 1) return (pre << 10) | (((pre >> 21) & 1u) ? 0u : 0x3FFu);
     }
-    pre = (pre << kf_width(L)) | (uint32_t)d;
   }
   return pre;
 }
@@ -2674,7 +2686,147 @@ struct KFRow {
   double tab[64];  // 2^(j/64)
   float red_m[kKFWaves];
   uint64_t red_h[kKFWaves], red_l[kKFWaves];
+  uint32_t kx0;    // top-p alone: key of the lower bound on the cut (0: none)
 };
+
+// Block sums of per-thread fixed-point parts; every thread gets them.
+__device__ __forceinline__ void kf_block_sum(uint64_t& h, uint64_t& l, uint64_t* red_h, uint64_t* red_l) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    h += __shfl_xor(h, o, 64);
+    l += __shfl_xor(l, o, 64);
+  }
+  if (lane == 0) {
+    red_h[wave] = h;
+    red_l[wave] = l;
+  }
+  __syncthreads();
+  h = l = 0;
+  for (int i = 0; i < kKFWaves; ++i) {
+    h += red_h[i];
+    l += red_l[i];
+  }
+  __syncthreads();  // the per-wave sums may be reused
+}
+
+// Full key of the 16-bit key k of a widened bf16 logit (its low 16 bits
+// follow from its sign).
+__device__ __forceinline__ uint32_t kf_key16_full(uint32_t k) { return (k << 16) | ((k & 0x8000u) ? 0u : 0xFFFFu); }
+
+// Top-p alone: the cut of row `row` and the mass at or above it (ch, cl);
+// 0 for a row with no finite cut (non-finite rows).
+// A lower bound on the cut from the statistics pass: the ids below x0 carry
+// at most V 2^((x0 - m) cd) = (1 - tp) S / 4 of the mass, S the row's sum
+// from the partials (within 1e-6 of the total), so the cut lies at or
+// above x0.  Those ids only add to the total whose top_p fraction is the
+// need: their masses are summed in registers and only the others are
+// histogrammed.  bf16 rows whose keys from the bound to the max span at most
+// kKFBins logit values count each value instead (a value's mass is its
+// count times the mass of one) and find the cut in that table, with no
+// second pass over the row.  Every way sums the same integers as the plain
+// descent (the need comes from the same total), so it finds the same cut
+// and kept mass; when the histogrammed mass cannot reach the need, the row
+// is taken again with every id in the histogram.
+template <bool BF16>
+__device__ __forceinline__ uint32_t kf_top_p(const Params& P, int64_t row, KFRow& w, double md, double cd, float tp,
+                                             uint64_t& ch, uint64_t& cl) {
+  KFShared& s = w.s;
+  const double* tab = w.tab;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    double sd = 0.0;
+    if (tid < P.Q) {
+      const Partial& pt = P.part[row * P.CPR + tid];
+      const double ps = __longlong_as_double((long long)pt.s);
+      const float pm = __uint_as_float((uint32_t)pt.m_amax);
+      if (pm != -INFINITY) sd = ps * exp2_f64_nonpos(((double)pm - md) * cd, tab);
+    }
+    sd = wave_sum_d(sd);
+    if (tid == 0) {
+      const double x0 = md + log2(0.25 * (1.0 - (double)tp) * sd / (double)P.V) / cd;
+      const float xf = (float)(x0 - fabs(x0) * 0x1p-20 - 0x1p-100);  // at or below x0
+      w.kx0 = (sd > 0.0 && fabs(x0) < 1e30 && fabsf(xf) < 1e30f) ? kf_key(xf) : 0u;
+    }
+  }
+  __syncthreads();
+  uint32_t kx = w.kx0;
+  uint64_t xh = 0, xl = 0;  // mass of the ids left out of the histogram
+  uint64_t nh = 0, nl = 0;
+  if constexpr (BF16) {
+    const uint32_t k16hi = kf_key((float)md) >> 16;
+    const uint32_t span = (uint32_t)kKFBins - 1u;
+    const uint32_t k16lo = max(kx >> 16, k16hi >= span ? k16hi - span : 0u);
+    if (kx != 0u) {
+      uint32_t* cnt = s.list;  // counts of the values k16lo + i
+      for (int i = tid; i < kKFBins; i += kKF) cnt[i] = 0u;
+      __syncthreads();
+      kf_pass<BF16, false>(P, row, s, [&](float l) {
+        const uint32_t k = (kf_key(l) >> 16) - k16lo;  // wraps for keys below the table
+        if (k < (uint32_t)kKFBins) {
+          atomicAdd(&cnt[k], 1u);
+        } else {
+          uint64_t h, lo;
+          kf_mass(l, md, cd, tab, h, lo);
+          xh += h;
+          xl += lo;
+        }
+      });
+      __syncthreads();
+      for (int i = tid; i < kKFBins; i += kKF) {
+        const uint32_t c = cnt[i];
+        uint64_t h = 0, lo = 0;
+        if (c) kf_mass(kf_val(kf_key16_full(k16lo + (uint32_t)i)), md, cd, tab, h, lo);
+        s.hh[i] = h * c;
+        s.hl[i] = lo * c;
+      }
+      kf_block_sum(xh, xl, w.red_h, w.red_l);  // its barriers also complete the table
+      kf_find<true>(s, kKFBins, nh, nl, tp, xh, xl);
+      if (s.digit >= 0) {
+        ch = s.ah + s.bh;
+        cl = s.al + s.bl;
+        return kf_key16_full(k16lo + (uint32_t)s.digit);
+      }
+      xh = xl = 0;
+      nh = nl = 0;
+    }
+  }
+  // first level of the masses from memory, the ids below the bound apart
+  for (;;) {
+    kf_clear(s);
+    kf_pass<BF16, false>(P, row, s, [&](float l) {
+      const uint32_t key = kf_key(l);
+      uint64_t h, lo;
+      kf_mass(l, md, cd, tab, h, lo);
+      if (key >= kx) {
+        atomicAdd((unsigned long long*)&s.hh[key >> 21], (unsigned long long)h);
+        atomicAdd((unsigned long long*)&s.hl[key >> 21], (unsigned long long)lo);
+      } else {
+        xh += h;
+        xl += lo;
+      }
+    });
+    kf_block_sum(xh, xl, w.red_h, w.red_l);  // its barriers also complete the histogram
+    kf_find<true>(s, kKFBins, nh, nl, tp, xh, xl);
+    if (s.digit >= 0 || kx == 0u) break;
+    kx = 0u;  // the bound did not hold: again with every id in the histogram
+    xh = xl = 0;
+    nh = nl = 0;
+  }
+  const int d = s.digit;
+  if (d < 0) return 0u;
+  kf_sub(nh, nl, s.ah, s.al);
+  const uint64_t ah = s.ah, al = s.al;
+  // the bin's keys to the list; the list's counter tells whether they fit
+  kf_collect<BF16>(P, row, s, (uint32_t)d << 21, ((uint32_t)d << 21) | 0x1FFFFFu);
+  if (s.nlist <= kKFList) {
+    ch = ah;
+    cl = al;
+    // the need left within the bin, from the second level
+    return kf_descent<BF16, true, true>(P, row, s, tab, md, cd, 0u, nh, nl, 0.f, ch, cl, 1, (uint32_t)d);
+  }
+  ch = cl = 0;
+  return kf_descent<BF16, false, true>(P, row, s, tab, md, cd, 0u, 0, 0, tp, ch, cl);
+}
 
 // The thresholds of filtered row `row` (temperature Tf, top-k tk, top-p tp)
 // from passes over the row.
@@ -2731,36 +2883,7 @@ __device__ __forceinline__ void kf_row(const Params& P, int64_t row, float Tf, i
       cut = listed ? kf_descent<BF16, true, true>(P, row, s, tab, md, cd, kmin, 0, 0, tp, ch, cl)
                    : kf_descent<BF16, false, true>(P, row, s, tab, md, cd, kmin, 0, 0, tp, ch, cl);
     } else {
-      // first level of the masses from memory
-      nh = nl = 0;
-      kf_clear(s);
-      kf_pass<BF16, false>(P, row, s, [&](float l) {
-        const uint32_t key = kf_key(l);
-        uint64_t h, lo;
-        kf_mass(l, md, cd, tab, h, lo);
-        atomicAdd((unsigned long long*)&s.hh[key >> 21], (unsigned long long)h);
-        atomicAdd((unsigned long long*)&s.hl[key >> 21], (unsigned long long)lo);
-      });
-      __syncthreads();
-      kf_find<true>(s, kKFBins, nh, nl, tp);
-      const int d = s.digit;
-      if (d < 0) {
-        cut = 0;
-      } else {
-        kf_sub(nh, nl, s.ah, s.al);
-        const uint64_t ah = s.ah, al = s.al;
-        // the bin's keys to the list; the list's counter tells whether they fit
-        kf_collect<BF16>(P, row, s, (uint32_t)d << 21, ((uint32_t)d << 21) | 0x1FFFFFu);
-        if (s.nlist <= kKFList) {
-          ch = ah;
-          cl = al;
-          // the need left within the bin, as a plain need (frac 0)
-          cut = kf_descent<BF16, true, true>(P, row, s, tab, md, cd, 0u, nh, nl, 0.f, ch, cl);
-        } else {
-          ch = cl = 0;
-          cut = kf_descent<BF16, false, true>(P, row, s, tab, md, cd, 0u, 0, 0, tp, ch, cl);
-        }
-      }
+      cut = kf_top_p<BF16>(P, row, w, md, cd, tp, ch, cl);
     }
     if (cut) {
       kcut = cut;
@@ -3300,12 +3423,202 @@ __device__ __forceinline__ bool kc_try(const Params& P, int64_t row, float Tf, i
   return true;
 }
 
+// ------------------------------------------------ top-p from value counts
+// bf16 rows filtered by top-p alone, in calls without top-k: a bf16 logit
+// is one of 65536 bit patterns and equal logits have equal masses, so one
+// pass counts each pattern (16-bit counters, two to a word: 128 KB of LDS)
+// and the masses come from the counts: a value's mass is its count times
+// the mass of one, the same integers as the sums id by id.  The total, the
+// need and the cut then come from the table alone: the masses of chunks of
+// 128 values in key order (16 lanes a chunk), the chunk of the cut by a scan
+// over the chunks (one per thread), the value by a scan within it.  -0 is
+// counted with +0 (one group of equal logits).  A count past 65535 carries
+// into its neighbour; the counts then no longer add up to V and the row
+// takes the passes over the row instead.
+constexpr int kKTVals = 65536;
+constexpr int kKTWords = kKTVals / 2;
+constexpr int kKTChunk = kKTVals / kKF;  // values per chunk: one chunk per thread
+static_assert(kKTChunk == 128 && kKF == 512, "a chunk is 16 lanes of 8 values; 4 chunks a wave");
+struct KTShared {
+  alignas(16) uint32_t tbl[kKTWords];    // counts of bit patterns 2i (low half) and 2i + 1
+  uint64_t ph[kKF], pl[kKF];             // per chunk: mass (integer, fraction parts)
+  uint64_t red_h[kKFWaves], red_l[kKFWaves];
+  uint32_t red_c[kKFWaves];
+  double tab[64];
+  uint64_t ah, al;                       // chunk of the cut: mass of the chunks above it
+  float m;
+  int chunk;                             // chunk of the cut (-1: none)
+};
+// Bit pattern of the bf16 logit whose 16-bit key is k (keys order like the
+// values: positive patterns follow the negative ones, which run backwards).
+__device__ __forceinline__ uint32_t kt_raw(uint32_t k) { return k >= 0x8000u ? k - 0x8000u : 0xFFFFu - k; }
+__device__ __forceinline__ uint32_t kt_count(const KTShared& t, uint32_t raw) {
+  return (t.tbl[raw >> 1] >> ((raw & 1u) << 4)) & 0xFFFFu;
+}
+
+// Thresholds of bf16 row `row` under top-p tp alone from its value counts;
+// false (nothing written) when a count overflowed.
+__device__ __forceinline__ bool kt_row(const Params& P, int64_t row, float Tf, float tp, KTShared& t) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float m = -INFINITY;
+  if (tid < P.Q) m = __uint_as_float((uint32_t)P.part[row * P.CPR + tid].m_amax);
+  if (tid < 64) {
+    m = wave_max(m);
+    if (tid == 0) {
+      t.m = m;
+      t.chunk = -1;
+    }
+    t.tab[tid] = exp2((double)tid / 64.0);
+  }
+  for (int i = tid; i < kKTWords / 4; i += kKF) ((u32x4*)t.tbl)[i] = u32x4{0u, 0u, 0u, 0u};
+  t.ph[tid] = 0;
+  t.pl[tid] = 0;
+  __syncthreads();
+  const double md = (double)t.m, cd = 1.4426950408889634074 / (double)Tf;
+  kf_pass_mem<true>(P, row, [&](float l) {
+    const uint32_t raw = __float_as_uint(l) >> 16;
+    atomicAdd(&t.tbl[raw >> 1], 1u << ((raw & 1u) << 4));
+  });
+  __syncthreads();
+  if (tid == 0) {
+    // -0 (pattern 0x8000, low half of word 0x4000) joins +0 (pattern 0)
+    const uint32_t c = t.tbl[0x4000] & 0xFFFFu;
+    t.tbl[0x4000] -= c;
+    t.tbl[0] += c;
+  }
+  __syncthreads();
+  // chunk masses: in pass j wave w takes the chunks 32 j + w + 8 g (g = 0..3,
+  // so a band of populated chunks spreads over the waves), a group of 16
+  // lanes per chunk, 8 consecutive values (one 16-byte word of counts) per
+  // lane; a negative chunk's patterns run backwards, which a sum does not
+  // see.  A wave with a populated value computes all its eight masses
+  // without branches, so that their latencies overlap.
+  uint32_t cnt = 0;
+  for (int j = 0; j < kKF / (4 * kKFWaves); ++j) {
+    const int kc = 4 * kKFWaves * j + wave + kKFWaves * (lane >> 4), part = lane & 15;
+    const uint32_t k0 = (uint32_t)(kc * kKTChunk + 8 * part);  // keys k0 .. k0 + 7
+    const uint32_t r0 = k0 >= 0x8000u ? k0 - 0x8000u : 0xFFF8u - k0;  // lowest pattern of the eight
+    const u32x4 q = *(const u32x4*)&t.tbl[r0 >> 1];
+    if (__ballot((q.x | q.y | q.z | q.w) != 0u) == 0ull) continue;
+    const uint32_t wq[4] = {q.x, q.y, q.z, q.w};
+    uint64_t sh = 0, sl = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = (wq[i >> 1] >> ((i & 1) << 4)) & 0xFFFFu;
+      uint64_t h, lo;
+      kf_mass(__uint_as_float((r0 + (uint32_t)i) << 16), md, cd, t.tab, h, lo);
+      sh += h * c;
+      sl += lo * c;
+      cnt += c;
+    }
+    for (int o = 8; o > 0; o >>= 1) {
+      sh += __shfl_xor(sh, o, 64);
+      sl += __shfl_xor(sl, o, 64);
+    }
+    if (part == 0) {
+      t.ph[kc] = sh;
+      t.pl[kc] = sl;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) t.red_c[wave] = cnt;
+  __syncthreads();  // also completes the chunks' masses
+  cnt = 0;
+  for (int w = 0; w < kKFWaves; ++w) cnt += t.red_c[w];
+  if (cnt != (uint32_t)P.V) return false;  // every thread alike
+  // the chunk of the cut: the first from the top at which the mass at or
+  // above it reaches the need (chunk tid; the chunks above are tid + 1..)
+  const uint64_t bh = t.ph[tid], bl = t.pl[tid];
+  uint64_t ih = bh, il = bl;  // sums over the wave's lanes >= lane
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t vh = __shfl_down(ih, o, 64), vl = __shfl_down(il, o, 64);
+    if (lane + o < 64) {
+      ih += vh;
+      il += vl;
+    }
+  }
+  if (lane == 0) {
+    t.red_h[wave] = ih;
+    t.red_l[wave] = il;
+  }
+  __syncthreads();
+  uint64_t rh = ih - bh, rl = il - bl, th = 0, tl = 0;
+  for (int w = 0; w < kKFWaves; ++w) {
+    th += t.red_h[w];
+    tl += t.red_l[w];
+    if (w > wave) {
+      rh += t.red_h[w];
+      rl += t.red_l[w];
+    }
+  }
+  uint64_t nh, nl;
+  kf_fix((double)tp * kf_float(th, tl), nh, nl);
+  if (!kf_ge(rh, rl, nh, nl) && kf_ge(rh + bh, rl + bl, nh, nl)) {
+    t.chunk = tid;
+    t.ah = rh;
+    t.al = rl;
+  }
+  __syncthreads();
+  const int c = t.chunk;
+  if (wave == 0) {
+    uint32_t cut = 0;
+    uint64_t ch = 0, cl = 0;
+    if (c >= 0) {
+      // lane j: keys 128 c + 2 j and 128 c + 2 j + 1 (the higher one first)
+      const uint32_t k0 = (uint32_t)(c * kKTChunk + 2 * lane);
+      const uint32_t p0 = kt_raw(k0), p1 = kt_raw(k0 + 1u);
+      const uint32_t c0 = kt_count(t, p0), c1 = kt_count(t, p1);
+      uint64_t h0 = 0, l0 = 0, h1 = 0, l1 = 0;
+      if (c0) {
+        kf_mass(__uint_as_float(p0 << 16), md, cd, t.tab, h0, l0);
+        h0 *= c0;
+        l0 *= c0;
+      }
+      if (c1) {
+        kf_mass(__uint_as_float(p1 << 16), md, cd, t.tab, h1, l1);
+        h1 *= c1;
+        l1 *= c1;
+      }
+      uint64_t sh = h0 + h1, sl = l0 + l1;  // then: sums over lanes >= lane
+      const uint64_t oh = sh, ol = sl;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t vh = __shfl_down(sh, o, 64), vl = __shfl_down(sl, o, 64);
+        if (lane + o < 64) {
+          sh += vh;
+          sl += vl;
+        }
+      }
+      const uint64_t ah = t.ah + (sh - oh), al = t.al + (sl - ol);  // mass above this lane's keys
+      int hit = -1;
+      if (!kf_ge(ah, al, nh, nl) && kf_ge(ah + h1, al + l1, nh, nl)) hit = 1;
+      else if (!kf_ge(ah + h1, al + l1, nh, nl) && kf_ge(ah + h1 + h0, al + l1 + l0, nh, nl)) hit = 0;
+      const uint64_t hm = __ballot(hit >= 0);
+      if (hm) {
+        const int src = __builtin_ctzll(hm);
+        const uint64_t xh = hit == 1 ? ah + h1 : ah + h1 + h0, xl = hit == 1 ? al + l1 : al + l1 + l0;
+        cut = __shfl(kf_key16_full(k0 + (hit == 1 ? 1u : 0u)), src, 64);
+        ch = __shfl(xh, src, 64);
+        cl = __shfl(xl, src, 64);
+      }
+    }
+    if (lane == 0) {
+      P.filt[row].s = cut ? kf_float(ch + (cl >> 32), cl & 0xFFFFFFFFull) : __builtin_nan("");
+      P.filt[row].tau = cut ? kf_val(cut) : -INFINITY;
+    }
+  }
+  return true;
+}
+
 // Thresholds of the filtered rows (stochastic, r <= k_b for chains): one
 // workgroup per row; top-k rows with candidates take them from those, the
 // rest (top-p alone, larger top-k, candidates that do not fit) from passes
-// over the row.
+// over the row, or (TABLE: bf16 calls without top-k) from value counts.
 union KFLds {
   KCShared c;
+  KFRow f;
+};
+union KFTLds {
+  KTShared t;
   KFRow f;
 };
 static_assert(kKC == kKF && kKC >= kDig && kKC % 64 == 0, "one workgroup shape for both thresholds paths");
@@ -3338,6 +3651,24 @@ __global__ __launch_bounds__(kKF, 4) void kf_kernel(Params P) {
   if (kc_row(P, tk) && kc_try<BF16>(P, row, Tf, tk, tp, pm, rec, u.c)) return;
   __syncthreads();  // the shared memory changes roles
   kf_row<BF16>(P, row, Tf, tk, tp, u.f);
+}
+
+// The thresholds pass of a bf16 call with top-p and no top-k: value counts
+// (one workgroup per CU: the table takes 128 KB of LDS).
+__global__ __launch_bounds__(kKF, 2) void kft_kernel(Params P) {
+  __shared__ KFTLds u;
+  const int b = (int)(blockIdx.x / (uint32_t)P.R);
+  const int r = (int)(blockIdx.x - (uint32_t)b * (uint32_t)P.R);
+  const int64_t row = (int64_t)b * P.R + r;
+  const float Tf = temp_of(P, b);
+  const float tp = P.top_p[b];
+  int xi;
+  const int kb = P.mode == MODE_CHAIN ? chain_kb(P, b, xi) : P.R;
+  if (!request_filtered(P, b, Tf)) return;
+  if (P.mode == MODE_CHAIN && r > kb) return;  // a tree reads all its rows
+  if (kt_row(P, row, Tf, tp, u.t)) return;
+  __syncthreads();  // the shared memory changes roles
+  kf_row<true>(P, row, Tf, 0, tp, u.f);
 }
 
 __global__ void fill_zero_kernel(uint8_t* p, size_t n) {
@@ -3403,15 +3734,17 @@ static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races, s
 typedef void (*KernelFn)(Params);
 
 struct Kernels {
-  KernelFn k1, k23, fused, kr, kf, k23c, k1f;
+  KernelFn k1, k23, fused, kr, kf, k23c, k1f, kft;
 };
 
 template <int MODE, bool BF16>
 static Kernels kernels_for() {
   KernelFn k1f = nullptr;  // row-statistics calls have no filters
   if constexpr (MODE != MODE_ROWS) k1f = k1f_kernel<MODE, BF16>;
+  KernelFn kft = nullptr;  // value counts: bf16 only
+  if constexpr (BF16) kft = kft_kernel;
   return Kernels{k1_kernel<MODE, BF16>, k23_kernel<MODE, BF16>,  fused_kernel<MODE, BF16>, kr_kernel<BF16>,
-                 kf_kernel<BF16>,         k23c_kernel<MODE, BF16>, k1f};
+                 kf_kernel<BF16>,         k23c_kernel<MODE, BF16>, k1f, kft};
 }
 
 static Kernels select_kernels(int mode, bool bf16) {
@@ -3501,7 +3834,10 @@ static sv_status launch(Params& P, const Shape& S, void* ws, size_t ws_bytes, hi
       hipLaunchKernelGGL(cand ? K.k1f : K.k1, dim3((unsigned)P.G), dim3(kWG), 0, stream, P);
     }
     if (!(P.flags & SV_FLAG_STATS_ONLY)) {
-      if (filtered) hipLaunchKernelGGL(K.kf, dim3((unsigned)gridf), dim3(kKF), 0, stream, P);
+      // bf16 calls with top-p and no top-k: thresholds from value counts
+      if (filtered)
+        hipLaunchKernelGGL((K.kft && P.top_k == nullptr) ? K.kft : K.kf, dim3((unsigned)gridf), dim3(kKF), 0, stream,
+                           P);
       if ((P.flags & SV_FLAG_BLOCK) && P.k >= 2 && P.draft_kind == SV_DRAFT_PROBS)
         hipLaunchKernelGGL(K.kr, dim3((unsigned)gridr), dim3(kWG), 0, stream, P);
       if (P.csum_on) hipLaunchKernelGGL(K.k23c, dim3((unsigned)P.bs), dim3(kWG), 0, stream, P);

@@ -789,6 +789,52 @@ def test_filtered_calls_are_deterministic(dev):
         np.testing.assert_array_equal(o["p_draft"].view(np.uint64), outs[0]["p_draft"].view(np.uint64))
 
 
+@pytest.mark.parametrize("case", ["bf16_headline", "bf16_flat", "f32", "bf16_wide_temps", "bf16_overflow"])
+def test_top_p_alone_paths(dev, case):
+    """Top-p without top-k, every request.  bf16 calls without a top-k array
+    take the thresholds from value counts; with an all-zero top-k array the
+    same rows take the passes over the row (with the cut's lower bound and a
+    table of up to 2048 values, or the histogram), and both must agree bit
+    for bit.  Cases: the headline shape, flat bf16 rows whose range spans
+    zero, fp32 rows, bf16 rows at several temperatures and top-p values, and
+    bf16 rows where one value repeats more than 65535 times (a counter
+    overflows and the row falls back)."""
+    rng = np.random.default_rng(340)
+    if case == "bf16_headline":
+        inp = workloads.chain_bf16_mixed(5)
+        tp = np.full(inp.batch, 0.9, np.float32)
+    elif case == "bf16_flat":
+        inp = _random_chain(341, 16, 4, 40000, "bf16", "probs", greedy_frac=0.0, scale=0.5)
+        tp = np.full(inp.batch, 0.8, np.float32)
+    elif case == "f32":
+        inp = _random_chain(342, 16, 4, 40000, "f32", "probs", greedy_frac=0.0)
+        tp = np.full(inp.batch, 0.9, np.float32)
+    elif case == "bf16_wide_temps":
+        inp = _random_chain(343, 24, 3, 70000, "bf16", "probs", greedy_frac=0.1)
+        tp = rng.choice(np.array([0.3, 0.6, 0.9, 0.99, 0.999], np.float32), size=24)
+    else:
+        bs, k, V = 4, 2, 70000
+        l = np.full((bs, k + 1, V), 0.25, np.float32)
+        l[:, :, : V // 8] = (rng.standard_normal((bs, k + 1, V // 8)) * 2).astype(np.float32)
+        l[1] = 0.25                                   # every logit equal
+        q = workloads._softmax_rows(l[:, :k].reshape(-1, V) * 0.9).reshape(bs, k, V).astype(np.float32)
+        ids = workloads._sample_rows(rng, q.reshape(-1, V)).reshape(bs, k).astype(np.int32)
+        inp = workloads.ChainInputs(workloads.f32_to_bf16_bits(l), ids, q, np.full(bs, 0.9, np.float32),
+                                    rng.integers(0, 2**63, size=bs).astype(np.uint64), False, "top-p overflow")
+        tp = np.array([0.5, 0.7, 0.95, 0.2], np.float32)
+    tp = tp.astype(np.float32)
+    check_chain(inp, dev, top_p=tp)
+    if inp.logits.dtype == np.uint16:
+        outs = []
+        for tk in (None, np.zeros(inp.batch, np.int32)):
+            out = sv.verify_chain(_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev),
+                                  _t(inp.seeds, dev), draft_probs=_t(inp.draft_probs, dev), return_p_draft=True,
+                                  top_k=_t(tk, dev), top_p=_t(tp, dev))
+            torch.cuda.synchronize()
+            outs.append(_np(out))
+        _same(outs[0], outs[1], f"top-p alone {case}: value counts vs passes over the row")
+
+
 def test_filtered_with_one_array_only(dev):
     """top_k alone and top_p alone (the other pointer NULL), chain and tree."""
     inp = _random_chain(71, 10, 4, 7000, "bf16", "probs")
