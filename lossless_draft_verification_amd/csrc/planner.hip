@@ -19,14 +19,16 @@
 // patterns order like their values; unused slots are all-ones and come
 // last), and they are distinct, so a slot's rank is the number of keys below
 // its own.  One launch of a grid of workgroups: each computes every key into
-// LDS and ranks its kSlots slots against them -- thread t compares the kReg
+// LDS (position-major, so that the lanes of a wave write consecutive words)
+// and ranks its kSlots slots against them -- thread t compares the kReg
 // slots of group t / kParts with the keys t % kParts + m kParts, and the
 // counts are summed over the parts (a wave holds 64 parts of one group) --
-// then stores the slots' ranks and their scores in rank order.  The last workgroup to
-// finish takes fp64 prefix sums of the sorted scores (by contiguous chunks
-// and one block scan), the first maximum of the ratio, and each request's
-// admitted count (its slots ranked below the budget), and leaves its counter
-// at zero for the next call.
+// then stores each slot's key at its rank: the sorted list of keys.  The
+// last workgroup to finish takes fp64 prefix sums of the sorted scores (by
+// contiguous chunks and one block scan), the first maximum of the ratio,
+// and each request's admitted count (one more than the largest position of
+// its keys ranked below the budget: a request's admitted slots are a
+// prefix), and leaves its counter at zero for the next call.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,12 +43,10 @@ constexpr int kReg = 4;                      // slots a thread compares every ke
 constexpr int kSlots = kThreads / kParts * kReg;  // slots a workgroup ranks
 constexpr int kPer = SV_PLAN_MAX_SLOTS / kThreads;  // entries per thread of the last workgroup, at most
 
-// Workspace: the completion counter, then per slot its rank, then the
-// scores in rank order (arrays sized for SV_PLAN_MAX_SLOTS: one layout for
-// every shape).
-constexpr size_t kWsRank = 256;
-constexpr size_t kWsScore = kWsRank + 4 * (size_t)SV_PLAN_MAX_SLOTS;
-constexpr size_t kWsBytes = kWsScore + 4 * (size_t)SV_PLAN_MAX_SLOTS;
+// Workspace: the completion counter, then the keys in rank order (sized for
+// SV_PLAN_MAX_SLOTS: one layout for every shape).
+constexpr size_t kWsKeys = 256;
+constexpr size_t kWsBytes = kWsKeys + 8 * (size_t)SV_PLAN_MAX_SLOTS;
 
 struct PlanParams {
   int32_t bs, K, bmax_table;
@@ -58,8 +58,7 @@ struct PlanParams {
   int32_t* draft_len;
   double* rate;
   uint32_t* counter;
-  uint32_t* rank;
-  float* sscore;
+  uint64_t* skey;
 };
 
 // Better (rate, B): a larger rate, or the same rate at a smaller B.  A NaN
@@ -73,13 +72,12 @@ __device__ __forceinline__ int steps_of(const PlanParams& P, int b) {
   return len < 0 ? 0 : (len > P.K ? P.K : len);
 }
 
-// Keys of the slots [lo, hi) (slot s = b K + j; all-ones past a request's
-// drafted positions) into out[s - lo]: one thread per request, its
-// confidences loaded eight at a time ahead of the running product.
-__device__ __forceinline__ void slot_keys(const PlanParams& P, int lo, int hi, uint64_t* out) {
-  const int K = P.K;
-  const int b0 = lo / K, b1 = (hi + K - 1) / K;
-  for (int b = b0 + (int)threadIdx.x; b < b1; b += kThreads) {
+// Keys of every slot (slot s = b K + j; all-ones past a request's drafted
+// positions) into out[j bs + b]: one thread per request, its confidences
+// loaded eight at a time ahead of the running product.
+__device__ __forceinline__ void slot_keys(const PlanParams& P, uint64_t* out) {
+  const int K = P.K, bs = P.bs;
+  for (int b = (int)threadIdx.x; b < bs; b += kThreads) {
     const int len = steps_of(P, b);
     float sc = 1.0f;
     for (int j0 = 0; j0 < K; j0 += 8) {
@@ -88,16 +86,15 @@ __device__ __forceinline__ void slot_keys(const PlanParams& P, int lo, int hi, u
       for (int u = 0; u < 8; ++u) c[u] = j0 + u < K ? P.conf[(int64_t)b * K + j0 + u] : 0.0f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u, s = b * K + j;
+        const int j = j0 + u;
         if (j >= K) break;
         float x = c[u];
         if (!(x > 0.0f)) x = 0.0f;
         if (x > 1.0f) x = 1.0f;
         sc = __fmul_rn(sc, x);
-        if (s >= lo && s < hi)
-          out[s - lo] = j < len ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(sc)) << 32) | ((uint64_t)j << 20) |
-                                      (uint64_t)b
-                                : ~0ull;
+        out[j * bs + b] = j < len ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(sc)) << 32) | ((uint64_t)j << 20) |
+                                        (uint64_t)b
+                                  : ~0ull;
       }
     }
   }
@@ -112,6 +109,12 @@ __device__ __forceinline__ void cst32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t cld32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cld64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = P.bs * P.K;
   // every key; this workgroup's slots [s0, s1)
-  slot_keys(P, 0, N, keys);
+  slot_keys(P, keys);
   __syncthreads();
   const int s0 = blockIdx.x * kSlots, s1 = min(s0 + kSlots, N);
   const int g = tid / kParts, p = tid % kParts;  // slot group, part of the keys
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
 #pragma unroll
   for (int r = 0; r < kReg; ++r) {
     const int s = s0 + g * kReg + r;
-    x[r] = s < s1 ? keys[s] : ~0ull;
+    x[r] = s < s1 ? keys[(s % P.K) * P.bs + s / P.K] : ~0ull;
   }
   uint32_t c[kReg];
   count_below(keys, p, N, x, c);
@@ -197,9 +200,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
     const uint32_t rk = (w2 >> (16 * (r & 1))) & 0xFFFFu;
     const int s = s0 + tid;
     if (s < s1) {
-      const uint64_t xs = keys[s];
-      cst32(&P.rank[s], rk);
-      if (xs != ~0ull) cst32((uint32_t*)&P.sscore[rk], __float_as_uint(key_score(xs)));
+      const uint64_t xs = keys[(s % P.K) * P.bs + s / P.K];
+      if (xs != ~0ull) cst64(&P.skey[rk], xs);
     }
   }
   // the last workgroup to finish does the rest: every wave's stores are
@@ -210,44 +212,36 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
     last = __hip_atomic_fetch_add(P.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
   __syncthreads();
   if (!last) return;
-  // every load up front: drafted positions, the sorted scores and the costs
-  // that can be needed, and the ranks (into LDS, over the keys)
+  // drafted positions: the keys in use (the sorted list's length)
+  int mine = 0;
+  for (int i = tid; i < N; i += kThreads) mine += keys[i] != ~0ull ? 1 : 0;
+  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) red_n[wave] = mine;
+  // every load up front: the sorted keys and the costs that can be needed
   const int bmax0 = min(P.bmax_table, N);
   const int C0 = (bmax0 + kThreads - 1) / kThreads;  // <= kPer
   const int r0 = tid * C0;
-  int nst[kPer];
-  float sc[kPer];
+  uint64_t sk[kPer];
   double cs[kPer];
-  uint32_t rk[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int b = u * kThreads + tid;
-    nst[u] = b < P.bs ? steps_of(P, b) : 0;
-    sc[u] = (u < C0 && r0 + u < bmax0) ? __uint_as_float(cld32((const uint32_t*)&P.sscore[r0 + u])) : 0.0f;
+    sk[u] = (u < C0 && r0 + u < bmax0) ? cld64(&P.skey[r0 + u]) : ~0ull;
     cs[u] = (u < C0 && r0 + u < bmax0) ? P.cost[r0 + u + 1] : 1.0;
-    rk[u] = b < N ? cld32(&P.rank[b]) : 0u;
   }
-  uint32_t* rank_lds = (uint32_t*)keys;  // the keys are no longer needed
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    if (u * kThreads + tid < N) rank_lds[u * kThreads + tid] = rk[u];
-  int mine = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) mine += nst[u];
-  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
-  if (lane == 0) red_n[wave] = mine;
   __syncthreads();
   int n = 0;
   for (int w = 0; w < kWaves; ++w) n += red_n[w];
   const int bmax = P.bmax_table < n ? P.bmax_table : n;
+  // each request's admitted count, in LDS over the keys (no longer needed)
+  int* adm = (int*)keys;
+  for (int b = tid; b < P.bs; b += kThreads) adm[b] = 0;
   // gain(B) = sum of the first B sorted scores.  Thread t owns positions
   // [t C0, (t + 1) C0) of the sorted list, below bmax: its chunk total, an
   // exclusive block scan of the totals, then its own B.
   double part_sum = 0.0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
-    if (u < C0 && r0 + u < bmax) part_sum += (double)sc[u];
+    if (u < C0 && r0 + u < bmax) part_sum += (double)key_score(sk[u]);
   double gain = block_exclusive(part_sum, wsum);  // gain at B = r0
   double best_r = -INFINITY;
   int best_b = INT32_MAX;
@@ -259,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     if (u < C0 && r0 + u < bmax) {
-      gain += (double)sc[u];
+      gain += (double)key_score(sk[u]);
       const int B = r0 + u + 1;
       const double rt = (P.base + gain) / cs[u];
       if (better(rt, B, best_r, best_b)) {
@@ -289,13 +283,14 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
       best_b = red_b[w];
     }
   const int bstar = best_b == INT32_MAX ? 0 : best_b;
-  // a request's admitted count: its slots ranked below the budget (a prefix
-  // of its positions)
-  for (int b = tid; b < P.bs; b += kThreads) {
-    int len = 0;
-    for (int j = 0; j < P.K; ++j) len += rank_lds[b * P.K + j] < (uint32_t)bstar ? 1 : 0;
-    P.draft_len[b] = len;
-  }
+  // a request's admitted count: one more than the largest position among
+  // its keys ranked below the budget
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (u < C0 && r0 + u < bstar)
+      atomicMax(&adm[(int)(sk[u] & 0xFFFFFu)], (int)((sk[u] >> 20) & 0xFFFu) + 1);
+  __syncthreads();
+  for (int b = tid; b < P.bs; b += kThreads) P.draft_len[b] = adm[b];
   if (tid == 0) {
     *P.budget = bstar;
     if (P.rate) *P.rate = best_r;
@@ -332,8 +327,7 @@ extern "C" sv_status sv_plan_budget(const sv_plan_desc* d, void* stream) {
   P.rate = d->rate;
   uint8_t* ws = (uint8_t*)d->workspace;
   P.counter = (uint32_t*)ws;
-  P.rank = (uint32_t*)(ws + svp::kWsRank);
-  P.sscore = (float*)(ws + svp::kWsScore);
+  P.skey = (uint64_t*)(ws + svp::kWsKeys);
   const int grid = (int)((n + svp::kSlots - 1) / svp::kSlots);
   hipLaunchKernelGGL(svp::plan_kernel, dim3((unsigned)grid), dim3(svp::kThreads), 0, (hipStream_t)stream, P);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
