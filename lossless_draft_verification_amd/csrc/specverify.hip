@@ -1778,12 +1778,26 @@ __device__ __forceinline__ void csum_race(const Params& P, int b, Smem& sm) {
   const double mref = (double)J.m * cd;
   const uint64_t seed = P.seed[b];
   double lo = 0.0, kh0 = -1.0;
+  static_assert(kCSumShares % 2 == 0, "shares are loaded two at a time");
   for (int c = tid; c < P.C3; c += kWG) {
     const CSum* cs = &P.csum[((int64_t)J.row * P.C3 + c) * kCSumShares];
+    // every share of the chunk in flight at once (128 contiguous bytes)
+    uint64_t sb[kCSumShares];
+    if constexpr (COH) {
+#pragma unroll
+      for (int w = 0; w < kCSumShares; ++w) sb[w] = ld64<COH>(&cs[w]);
+    } else {
+#pragma unroll
+      for (int w = 0; w < kCSumShares / 2; ++w) {
+        const u32x4 v = *(const u32x4*)&cs[2 * w];
+        sb[2 * w] = (uint64_t)v.x | ((uint64_t)v.y << 32);
+        sb[2 * w + 1] = (uint64_t)v.z | ((uint64_t)v.w << 32);
+      }
+    }
     double E = 0.0, err = 0.0;
-#pragma unroll 4
+#pragma unroll
     for (int w = 0; w < kCSumShares; ++w) {
-      const uint64_t bits = ld64<COH>(&cs[w]);
+      const uint64_t bits = sb[w];
       const float ws = __uint_as_float((uint32_t)bits), off = __uint_as_float((uint32_t)(bits >> 32));
       if (off == -INFINITY) continue;  // the row of lanes saw only masked ids
       // 2^(off - m c*) by v_exp_f32 (within 2^-22, and the argument's
@@ -1805,14 +1819,18 @@ __device__ __forceinline__ void csum_race(const Params& P, int b, Smem& sm) {
     const double wd = E - err - ex * (1.0 + 0x1p-50);
     const double wlo = wd > 0.0 ? wd * (1.0 - 0x1p-40) : 0.0;
     const double En = chunk_exp(seed, b, J.r, c);
-    K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
     const double khi = whi / En * (1.0 + 0x1p-48), klo = wlo / En * (1.0 - 0x1p-48);
-    cst_f64(&rec->khi, khi);
-    cst_f64(&rec->klo, klo);
+    if (P.C3 > kWG) {
+      // k3_merge reads the upper bounds of the chunks past the block from
+      // the records (its own thread's from kh0)
+      K3Rec* rec = &P.k3[(int64_t)b * P.C3 + c];
+      cst_f64(&rec->khi, khi);
+      cst_f64(&rec->klo, klo);
+    }
     lo = fmax(lo, klo);
     if (c == tid) kh0 = khi;
   }
-  wait_mem();  // the records of chunks past the block are stored before k3_merge reads them
+  if (P.C3 > kWG) wait_mem();  // those records are stored before k3_merge reads them
   __syncthreads();
   k3_merge<BF16>(P, b, lo, kh0, sm);
 }
