@@ -680,8 +680,11 @@ def main():
     second_ms = np.array([e[1].elapsed_time(e[2]) for e in ev]) / S if split else None
     stats_bytes = np.array([a[0] for a in alg] * groups, dtype=np.float64)
     decide_bytes = np.array([a[1] for a in alg] * groups, dtype=np.float64)
-    # top-k calls' statistics pass also keeps the candidate groups
+    # top-k calls' statistics pass also keeps the candidate groups; bf16
+    # calls with top-p and no top-k take the thresholds from value counts
     cand = filtered and 0 < args.top_k <= 128 and args.top_k < V0 and not args.kf_rows
+    bf16_logits = inputs[0].logits.dtype == np.uint16
+    thr_name = "kft_kernel" if (filtered and bf16_logits and not 0 < args.top_k < V0) else "kf_kernel"
     if split:
         kernel = "row statistics with top-k candidates (k1f_kernel)" if cand else "row statistics (k1_kernel)"
         kbytes = stats_bytes
@@ -700,11 +703,11 @@ def main():
     k1_name = ("k1f_kernel" if cand else "k1_kernel") if split else "fused_kernel"
     tk, tp = (args.top_k, args.top_p) if filtered else (0, 1.0)
     traffic = None if block else load_traffic(args.workload, k1_name, tk, tp)
-    rest = (["kf_kernel"] if filtered else []) + ["k23_kernel"]
+    rest = ([thr_name] if filtered else []) + ["k23_kernel"]
     traffic23 = None if (block or not split) else load_traffic(args.workload, rest, tk, tp)
     call = {
         "kernels": (f"{k1_name} + k23_kernel" if split else "fused_kernel")
-                   + (" + kf_kernel" if filtered else "") + (" + kr_kernel" if block else ""),
+                   + (f" + {thr_name}" if filtered else "") + (" + kr_kernel" if block else ""),
         "algorithmic_bytes": float(call_bytes),
         "us_per_call": call_us,
         "achieved_gbs_by_call_time": call_bytes / (call_us * 1e3),
@@ -770,7 +773,7 @@ def main():
     if split:
         line["roofline"]["other_kernel"] = {
             "kernel": ("residual masses, decisions and sampling (kr_kernel + k23_kernel)" if block
-                       else "filter thresholds, decisions and sampling (kf_kernel + k23_kernel)" if filtered
+                       else f"filter thresholds, decisions and sampling ({thr_name} + k23_kernel)" if filtered
                        else "decisions and sampling (k23_kernel)"),
             "algorithmic_bytes_per_launch": float((decide_bytes + filt_bytes).mean()),
             "launch_us_mean": float(second_ms.mean() * 1e3),
