@@ -1045,7 +1045,10 @@ __device__ void decide_chain(const Params& P, int b, bool writer, Smem& sm) {
   const int a = sm.a;
   if (tid == 0) {
     P.accept_len[b] = a;
-    if (P.status) P.status[b] = sm.status;
+    // a request with a race gets its status from the race's merge, after
+    // its token: a wait that gives up on the way writes REQ_INTERNAL, and no
+    // earlier OK may land after it
+    if (P.status && sm.job.kind == JOB_NONE) P.status[b] = sm.status;
   }
   for (int i = tid; i < R; i += kWG) {
     int t = -1;
@@ -1193,7 +1196,7 @@ __device__ void decide_tree(const Params& P, int b, bool writer, Smem& sm) {
   const int len = sm.len;
   if (tid == 0) {
     P.accept_len[b] = len;
-    if (P.status) P.status[b] = sm.status;
+    if (P.status && sm.job.kind == JOB_NONE) P.status[b] = sm.status;  // else written by the race's merge
   }
   for (int i = tid; i < N; i += kWG) {
     int node = -1, t = -1;
@@ -2043,7 +2046,10 @@ __device__ __forceinline__ void run_k23(const Params& P, int b, int item, Smem& 
     cst32(&P.ctrl->aborted, 1u);
     if (P.status) P.status[b] = SV_REQ_INTERNAL;
   }
-  if (done && sampled) k3_merge<BF16>(P, b, lo, kh0, sm);
+  if (done && sampled) {
+    k3_merge<BF16>(P, b, lo, kh0, sm);
+    if (tid == 0 && P.status) P.status[b] = SV_REQ_OK;  // the request's status, after its token
+  }
   if (tid == 0 && P.sched == SCHED_FUSED) cst32(&P.sync[b].k1_count, 0u);
 }
 
@@ -2077,7 +2083,10 @@ __global__ __launch_bounds__(kWG, 2) void k23c_kernel(Params P) {
     const int b = (int)blockIdx.x;
     if (MODE == MODE_CHAIN) decide_chain<BF16, false>(P, b, true, sm);
     else decide_tree<BF16, false>(P, b, true, sm);
-    if (uniform_i(sm.job.kind) != JOB_NONE) csum_race<BF16, false>(P, b, sm);
+    if (uniform_i(sm.job.kind) != JOB_NONE) {
+      csum_race<BF16, false>(P, b, sm);
+      if (threadIdx.x == 0 && P.status) P.status[b] = SV_REQ_OK;  // the request's status, after its token
+    }
   }
 }
 
