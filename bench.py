@@ -396,10 +396,11 @@ def bench_compact(args, sv, torch, dev, workloads):
 
 
 def bench_plan(args, sv, torch, dev):
-    """Latency of one survival top-k plan (one launch: slot ranks over many
-    workgroups, the rest in the last to finish): the
-    page's adaptive-verification shape (512 requests x 7 positions, half
-    with accurate drafts) and the largest supported one (1024 x 8)."""
+    """Latency of one survival top-k plan (two launches: slot ranks over
+    many workgroups, then the prefix sums, ratios and admitted counts in
+    one): the page's adaptive-verification shape (512 requests x 7
+    positions, half with accurate drafts) and the largest supported one
+    (1024 x 8)."""
     rng = np.random.default_rng(11)
     lines = []
     for bs, K in ((512, 7), (1024, 8)):
@@ -430,7 +431,7 @@ def bench_plan(args, sv, torch, dev):
                       "unit": "us/plan", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "higher_is_better": False, "data": "synthetic",
                       "config": {"workload": "plan 512 requests x 7 positions (and 1024 x 8)", "cases": lines},
-                      "roofline": {"bound": "latency", "note": "a few thousand slots ranked over many workgroups"}}), flush=True)
+                      "roofline": {"bound": "latency", "note": "a few thousand slots ranked over many workgroups, then one workgroup"}}), flush=True)
 
 
 def read_ceiling(sv, torch, dev, buffers, steps):

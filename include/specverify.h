@@ -280,10 +280,10 @@ int32_t sv_abi_version(void);
  *
  * workspace: device memory of at least sv_plan_workspace_bytes(bs, K) bytes
  * (the same for every shape), 256-byte aligned (else SV_ERR_INVALID_ARGUMENT /
- * SV_ERR_WORKSPACE_TOO_SMALL), all zero before its first use; every call
- * leaves its counters at zero again, so it can be reused by calls of any
- * shape that do not overlap (calls that overlap need their own).  The caller
- * owns it. */
+ * SV_ERR_WORKSPACE_TOO_SMALL), of any contents (it carries the ranked slots
+ * from one launch of the call to the next and needs no clearing); calls of
+ * any shape may reuse it as long as they do not overlap (calls that overlap
+ * need their own).  The caller owns it. */
 #define SV_PLAN_MAX_SLOTS 8192
 
 typedef struct {

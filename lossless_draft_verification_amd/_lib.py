@@ -200,16 +200,16 @@ _plan_workspaces = {}
 
 
 def plan_workspace(device, nbytes: int) -> torch.Tensor:
-    """The planner's workspace when a call passes none: one zero-filled
-    buffer per (device, current stream), grown to the largest call so far
-    (a new buffer is zero-filled; a call leaves its counters at zero)."""
+    """The planner's workspace when a call passes none: one buffer per
+    (device, current stream), grown to the largest call so far (its contents
+    do not matter: each call writes what it reads)."""
     device = torch.device(device)
     index = device.index if device.index is not None else torch.cuda.current_device()
     key = (index, torch.cuda.current_stream(index).cuda_stream)
     with _workspaces_lock:
         ws = _plan_workspaces.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=torch.device("cuda", index))
+            ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=torch.device("cuda", index))
             _plan_workspaces[key] = ws
     return ws
 
@@ -430,9 +430,9 @@ def plan_budget(confidence, cost, base_tokens, num_steps=None, workspace=None):
 
     confidence [bs, K] float32; cost [max_budget + 1] float64 (step cost when
     B draft positions are verified); base_tokens: tokens a step yields with
-    none; num_steps [bs] int32 or None; workspace: a zero-filled uint8 device
-    tensor of at least plan_workspace_bytes(bs, K) bytes (None: one kept per
-    device and stream).  Returns device tensors: budget [1] int32, draft_len
+    none; num_steps [bs] int32 or None; workspace: a uint8 device tensor of
+    at least plan_workspace_bytes(bs, K) bytes, any contents (None: one kept
+    per device and stream).  Returns device tensors: budget [1] int32, draft_len
     [bs] int32, rate [1] float64.
     """
     p = PreparedPlan(confidence, cost, base_tokens, num_steps, workspace)

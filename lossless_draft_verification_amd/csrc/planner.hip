@@ -18,19 +18,19 @@
 // order ascending in the required order (scores are >= 0, so their fp32 bit
 // patterns order like their values; unused slots are all-ones and come
 // last), and they are distinct, so a slot's rank is the number of keys below
-// its own.  One launch of a grid of workgroups: each computes every key into
-// LDS (position-major, so that the lanes of a wave write consecutive words)
-// and ranks its kSlots slots against them -- thread t compares the kReg
-// slots of group t / kParts with the keys t % kParts + m kParts, and the
-// counts are summed over the parts (a wave holds 64 parts of one group) --
-// then stores each slot's key at its rank: the sorted list of keys.  The
-// last workgroup to finish takes fp64 prefix sums of the sorted scores (by
-// contiguous chunks and one block scan), the first maximum of the ratio,
-// and each request's admitted count (one more than the largest position of
-// its keys ranked below the budget: a request's admitted slots are a
-// prefix), and leaves its counter at zero for the next call.
+// its own.  Two launches.  The first is a grid of workgroups, each building
+// every key in LDS (position-major, so that the lanes of a wave write
+// consecutive words) and ranking its own 16 or 32 slots against them by
+// counting; it stores each slot's key at its rank in the workspace: the
+// sorted list of keys.  The second, one workgroup, reads the sorted keys and
+// takes fp64 prefix sums of their scores (by contiguous chunks and one block
+// scan), the first maximum of the ratio, and each request's admitted count
+// (one more than the largest position of its keys ranked below the budget:
+// a request's admitted slots are a prefix).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "specverify.h"
 
@@ -38,18 +38,20 @@ namespace svp {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kParts = 128;                  // threads that share one slot's comparisons
-constexpr int kReg = 4;                      // slots a thread compares every key it reads with
-constexpr int kSlots = kThreads / kParts * kReg;  // slots a workgroup ranks
-constexpr int kPer = SV_PLAN_MAX_SLOTS / kThreads;  // entries per thread of the last workgroup, at most
+constexpr int kParts = 128;                  // threads that share one slot group's comparisons
+constexpr int kGroups = kThreads / kParts;   // slot groups of a workgroup
+constexpr int kPer = SV_PLAN_MAX_SLOTS / kThreads;  // entries per thread of the tail workgroup, at most
+// staged confidences: request b's row at b Kp, Kp = K rounded up to odd
+constexpr int kConfLds = SV_PLAN_MAX_SLOTS + SV_PLAN_MAX_SLOTS / 2;
 
-// Workspace: the completion counter, then the keys in rank order (sized for
-// SV_PLAN_MAX_SLOTS: one layout for every shape).
-constexpr size_t kWsKeys = 256;
-constexpr size_t kWsBytes = kWsKeys + 8 * (size_t)SV_PLAN_MAX_SLOTS;
+// Workspace: the keys in rank order, passed from the first launch to the
+// second (sized for SV_PLAN_MAX_SLOTS: one layout for every shape).
+constexpr size_t kWsBytes = 8 * (size_t)SV_PLAN_MAX_SLOTS;
 
 struct PlanParams {
   int32_t bs, K, bmax_table;
+  int32_t bmax0;  // min(bmax_table, bs K): sorted positions the second launch reads
+  int32_t lg;     // log2 of C0, the power of two >= bmax0 / kThreads: positions per thread
   const float* conf;
   const int32_t* num_steps;
   const double* cost;
@@ -57,7 +59,6 @@ struct PlanParams {
   int32_t* budget;
   int32_t* draft_len;
   double* rate;
-  uint32_t* counter;
   uint64_t* skey;
 };
 
@@ -73,77 +74,52 @@ __device__ __forceinline__ int steps_of(const PlanParams& P, int b) {
 }
 
 // Keys of every slot (slot s = b K + j; all-ones past a request's drafted
-// positions) into out[j bs + b]: one thread per request, its confidences
-// loaded eight at a time ahead of the running product.
-__device__ __forceinline__ void slot_keys(const PlanParams& P, uint64_t* out) {
-  const int K = P.K, bs = P.bs;
+// positions) into out[j bs + b], and those of slots s0 .. s0 + R - 1 also
+// into own[s - s0] (which the caller has set to all-ones).  The confidences are first staged in
+// shared memory by loads in which the lanes of a wave read consecutive
+// words, request b's at cs[b Kp] with an odd row stride Kp (so the lanes,
+// one request each, then read distinct banks); one thread per request takes
+// the running product.
+__device__ __forceinline__ void slot_keys(const PlanParams& P, uint64_t* out, float* cs, uint64_t* own, int s0,
+                                          int R) {
+  const int K = P.K, bs = P.bs, N = bs * K;
+  const bool pad = (K & 1) == 0;
+  const int Kp = K | 1;
+  const int n4 = ((uintptr_t)P.conf & 15u) == 0 ? N / 4 : 0;
+  for (int q = (int)threadIdx.x; q < n4; q += kThreads) {
+    const float4 v = ((const float4*)P.conf)[q];
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    int i = 4 * q, b = pad ? i / K : 0, j = i - b * K;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      cs[pad ? b * Kp + j : i + u] = e[u];
+      if (++j == K) j = 0, ++b;
+    }
+  }
+  for (int i = 4 * n4 + (int)threadIdx.x; i < N; i += kThreads) cs[pad ? i + i / K : i] = P.conf[i];
+  __syncthreads();
   for (int b = (int)threadIdx.x; b < bs; b += kThreads) {
     const int len = steps_of(P, b);
     float sc = 1.0f;
-    for (int j0 = 0; j0 < K; j0 += 8) {
-      float c[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = j0 + u < K ? P.conf[(int64_t)b * K + j0 + u] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        if (j >= K) break;
-        float x = c[u];
-        if (!(x > 0.0f)) x = 0.0f;
-        if (x > 1.0f) x = 1.0f;
-        sc = __fmul_rn(sc, x);
-        out[j * bs + b] = j < len ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(sc)) << 32) | ((uint64_t)j << 20) |
-                                        (uint64_t)b
-                                  : ~0ull;
-      }
+    for (int j = 0; j < K; ++j) {
+      float x = cs[b * Kp + j];
+      if (!(x > 0.0f)) x = 0.0f;
+      if (x > 1.0f) x = 1.0f;
+      sc = __fmul_rn(sc, x);
+      const uint64_t key =
+          j < len ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(sc)) << 32) | ((uint64_t)j << 20) | (uint64_t)b : ~0ull;
+      out[j * bs + b] = key;
+      if ((unsigned)(b * K + j - s0) < (unsigned)R) own[b * K + j - s0] = key;
     }
   }
 }
 
 __device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(0xFFFFFFFFu - (uint32_t)(k >> 32)); }
 
-// Stores and loads of data that other workgroups of the launch write or read
-// (agent-scope relaxed atomics: they bypass the caches that are not
-// coherent across the device), and a wait for this wave's memory operations.
-__device__ __forceinline__ void cst32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t cld32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void cst64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t cld64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// For each of the kReg keys x[r], the keys keys[p], keys[p + kParts], ...
-// (below n) below it: the lanes of a wave, taking consecutive parts, read
-// consecutive keys.
-__device__ __forceinline__ void count_below(const uint64_t* keys, int p, int n, const uint64_t* x, uint32_t* c) {
-#pragma unroll
-  for (int r = 0; r < kReg; ++r) c[r] = 0;
-  int q = p;
-  for (; q + 3 * kParts < n; q += 4 * kParts) {
-    uint64_t k[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) k[u] = keys[q + u * kParts];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < kReg; ++r) c[r] += k[u] < x[r] ? 1u : 0u;
-  }
-  for (; q < n; q += kParts) {
-    const uint64_t k = keys[q];
-#pragma unroll
-    for (int r = 0; r < kReg; ++r) c[r] += k < x[r] ? 1u : 0u;
-  }
-}
-
 // Exclusive prefix over the workgroup of one double per thread, in a fixed
-// order (a wave scan, then the waves' totals).
+// order (a wave scan, then the waves' totals).  A thread's result is formed
+// from the values of lower threads only (shifted, not by subtracting its
+// own), so a non-finite value reaches no thread below it.
 __device__ __forceinline__ double block_exclusive(double v, double* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double in = v;
@@ -152,113 +128,154 @@ __device__ __forceinline__ double block_exclusive(double v, double* wsum) {
     if (lane >= o) in += u;
   }
   if (lane == 63) wsum[wave] = in;
+  double ex = __shfl_up(in, 1, 64);
+  if (lane == 0) ex = 0.0;
   __syncthreads();
   double before = 0.0;
   for (int w = 0; w < wave; ++w) before += wsum[w];
-  return before + in - v;
+  return before + ex;
 }
 
-__global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
+// For each of the R keys x[r], the keys keys[p], keys[p + kParts], ...
+// (below n) below it: the lanes of a wave, taking consecutive parts, read
+// consecutive keys.
+template <int R>
+__device__ __forceinline__ void count_below(const uint64_t* keys, int p, int n, const uint64_t* x, uint32_t* c) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) c[r] = 0;
+  int q = p;
+  for (; q + 3 * kParts < n; q += 4 * kParts) {
+    uint64_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = keys[q + u * kParts];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) c[r] += k[u] < x[r] ? 1u : 0u;
+  }
+  for (; q < n; q += kParts) {
+    const uint64_t k = keys[q];
+#pragma unroll
+    for (int r = 0; r < R; ++r) c[r] += k < x[r] ? 1u : 0u;
+  }
+}
+
+// Ranks of the S slots [S blockIdx.x, S (blockIdx.x + 1)), S = R kGroups:
+// thread t compares the R slots of group t / kParts with the keys
+// t % kParts + m kParts, and the counts are summed over the parts (a wave
+// holds 64 parts of one group).  Each slot's key is then stored at its rank.
+template <int R>
+__global__ __launch_bounds__(kThreads) void rank_kernel(PlanParams P) {
+  static_assert(R % 2 == 0 && kParts == 128, "packed counts; two waves per slot group");
+  constexpr int S = R * kGroups;
   __shared__ uint64_t keys[SV_PLAN_MAX_SLOTS];
-  __shared__ uint32_t part[kWaves][kReg / 2];
+  __shared__ float confs[kConfLds];
+  __shared__ uint32_t part[kWaves][R / 2];
+  __shared__ uint64_t own[S];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = P.bs * P.K;
+  const int s0 = blockIdx.x * S;
+  if (tid < S) own[tid] = ~0ull;
+  slot_keys(P, keys, confs, own, s0, S);
+  __syncthreads();
+  const int g = tid / kParts, p = tid % kParts;  // slot group, part of the keys
+  uint64_t x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = own[g * R + r];
+  uint32_t c[R];
+  count_below<R>(keys, p, N, x, c);
+  // sum over the parts: within the wave (two counts packed per word, each
+  // at most SV_PLAN_MAX_SLOTS < 2^16), then the group's two waves
+  uint32_t c2[R / 2];
+#pragma unroll
+  for (int r = 0; r < R / 2; ++r) c2[r] = c[2 * r] | (c[2 * r + 1] << 16);
+#pragma unroll
+  for (int r = 0; r < R / 2; ++r)
+    for (int o = 32; o > 0; o >>= 1) c2[r] += (uint32_t)__shfl_xor((int)c2[r], o, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < R / 2; ++r) part[wave][r] = c2[r];
+  __syncthreads();
+  if (tid < S) {
+    const int gg = tid / R, r = tid % R;
+    const uint32_t w2 = part[2 * gg][r >> 1] + part[2 * gg + 1][r >> 1];
+    const uint32_t rk = (w2 >> (16 * (r & 1))) & 0xFFFFu;
+    if (s0 + tid < N) {
+      const uint64_t xs = own[tid];
+      // rank rk belongs to thread rk / C0 of the second launch, which reads
+      // its u-th entry at u kThreads + thread
+      if (xs != ~0ull && (int)rk < P.bmax0) P.skey[((int)rk & ((1 << P.lg) - 1)) * kThreads + ((int)rk >> P.lg)] = xs;
+    }
+  }
+}
+
+// The rest, by one workgroup once the ranks are stored (the launch
+// boundary makes them visible): fp64 prefix sums of the sorted scores, the
+// first maximum of the ratio, each request's admitted count.  Thread t owns
+// sorted positions [t C0, (t + 1) C0), stored so that its u-th entry is read
+// at u kThreads + t (the lanes of a wave read consecutive words).  Every
+// global load is issued first.  Entries at or past the drafted count n are
+// stale, but they only reach the sums at positions past n, and no budget
+// past n is taken, so the chunk sums need not wait for n: it is reduced
+// beside the scan.  The prefix sums then pass through LDS (rows of odd
+// stride C0 + 1) to the threads holding the costs: position u kThreads + t.
+__global__ __launch_bounds__(kThreads) void tail_kernel(PlanParams P) {
+  __shared__ double gsum[(kPer + 1) * kThreads];
+  __shared__ int adm[SV_PLAN_MAX_SLOTS];
   __shared__ double wsum[kWaves];
   __shared__ double red_r[kWaves];
   __shared__ int red_b[kWaves];
   __shared__ int red_n[kWaves];
-  __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = P.bs * P.K;
-  // every key; this workgroup's slots [s0, s1)
-  slot_keys(P, keys);
-  __syncthreads();
-  const int s0 = blockIdx.x * kSlots, s1 = min(s0 + kSlots, N);
-  const int g = tid / kParts, p = tid % kParts;  // slot group, part of the keys
-  uint64_t x[kReg];
-#pragma unroll
-  for (int r = 0; r < kReg; ++r) {
-    const int s = s0 + g * kReg + r;
-    x[r] = s < s1 ? keys[(s % P.K) * P.bs + s / P.K] : ~0ull;
-  }
-  uint32_t c[kReg];
-  count_below(keys, p, N, x, c);
-  // sum over the parts: within the wave (two counts packed per word, each
-  // at most SV_PLAN_MAX_SLOTS < 2^16), then the group's two waves
-  uint32_t c2[kReg / 2];
-#pragma unroll
-  for (int r = 0; r < kReg / 2; ++r) c2[r] = c[2 * r] | (c[2 * r + 1] << 16);
-#pragma unroll
-  for (int r = 0; r < kReg / 2; ++r)
-    for (int o = 32; o > 0; o >>= 1) c2[r] += (uint32_t)__shfl_xor((int)c2[r], o, 64);
-  if (lane == 0)
-#pragma unroll
-    for (int r = 0; r < kReg / 2; ++r) part[wave][r] = c2[r];
-  __syncthreads();
-  static_assert(kParts == 128, "two waves per slot group");
-  if (tid < kSlots) {
-    const int gg = tid / kReg, r = tid % kReg;
-    const uint32_t w2 = part[2 * gg][r >> 1] + part[2 * gg + 1][r >> 1];
-    const uint32_t rk = (w2 >> (16 * (r & 1))) & 0xFFFFu;
-    const int s = s0 + tid;
-    if (s < s1) {
-      const uint64_t xs = keys[(s % P.K) * P.bs + s / P.K];
-      if (xs != ~0ull) cst64(&P.skey[rk], xs);
-    }
-  }
-  // the last workgroup to finish does the rest: every wave's stores are
-  // complete before the count
-  wait_mem();
-  __syncthreads();
-  if (tid == 0)
-    last = __hip_atomic_fetch_add(P.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
-  __syncthreads();
-  if (!last) return;
-  // drafted positions: the keys in use (the sorted list's length)
-  int mine = 0;
-  for (int i = tid; i < N; i += kThreads) mine += keys[i] != ~0ull ? 1 : 0;
-  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
-  if (lane == 0) red_n[wave] = mine;
-  // every load up front: the sorted keys and the costs that can be needed
-  const int bmax0 = min(P.bmax_table, N);
-  const int C0 = (bmax0 + kThreads - 1) / kThreads;  // <= kPer
+  const int bmax0 = P.bmax0, lg = P.lg, C0 = 1 << lg, S = C0 + 1;
   const int r0 = tid * C0;
   uint64_t sk[kPer];
-  double cs[kPer];
+  double cc[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    sk[u] = (u < C0 && r0 + u < bmax0) ? cld64(&P.skey[r0 + u]) : ~0ull;
-    cs[u] = (u < C0 && r0 + u < bmax0) ? P.cost[r0 + u + 1] : 1.0;
+    const int i = u * kThreads + tid;
+    sk[u] = (u < C0 && r0 + u < bmax0) ? P.skey[i] : ~0ull;
+    cc[u] = (u < C0 && i < bmax0) ? P.cost[i + 1] : 1.0;
   }
-  __syncthreads();
-  int n = 0;
-  for (int w = 0; w < kWaves; ++w) n += red_n[w];
-  const int bmax = P.bmax_table < n ? P.bmax_table : n;
-  // each request's admitted count, in LDS over the keys (no longer needed)
-  int* adm = (int*)keys;
+  const double cost0 = tid == 0 ? P.cost[0] : 1.0;
+  int mine = 0;
+  for (int b = tid; b < P.bs; b += kThreads) mine += steps_of(P, b);
   for (int b = tid; b < P.bs; b += kThreads) adm[b] = 0;
-  // gain(B) = sum of the first B sorted scores.  Thread t owns positions
-  // [t C0, (t + 1) C0) of the sorted list, below bmax: its chunk total, an
-  // exclusive block scan of the totals, then its own B.
+  // drafted positions (the sorted list's length), reduced beside the scan
+  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) red_n[wave] = mine;
+  // gain(B) = sum of the first B sorted scores: the chunk totals, an
+  // exclusive block scan of them, then the thread's own prefix sums
   double part_sum = 0.0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
-    if (u < C0 && r0 + u < bmax) part_sum += (double)key_score(sk[u]);
+    if (u < C0 && r0 + u < bmax0) part_sum += (double)key_score(sk[u]);
   double gain = block_exclusive(part_sum, wsum);  // gain at B = r0
+  int n = 0;
+  for (int w = 0; w < kWaves; ++w) n += red_n[w];
+  const int bmax = P.bmax_table < n ? P.bmax_table : n;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (u < C0 && r0 + u < bmax) {
+      gain += (double)key_score(sk[u]);
+      gsum[tid * S + u] = gain;  // gain at B = r0 + u + 1
+    }
+  __syncthreads();
   double best_r = -INFINITY;
   int best_b = INT32_MAX;
   if (tid == 0) {  // B = 0
-    best_r = P.base / P.cost[0];
+    best_r = P.base / cost0;
     if (!(best_r > -INFINITY)) best_r = -INFINITY, best_b = INT32_MAX;
     else best_b = 0;
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    if (u < C0 && r0 + u < bmax) {
-      gain += (double)key_score(sk[u]);
-      const int B = r0 + u + 1;
-      const double rt = (P.base + gain) / cs[u];
-      if (better(rt, B, best_r, best_b)) {
+    const int i = u * kThreads + tid;
+    if (u < C0 && i < bmax) {
+      const double rt = (P.base + gsum[(i >> lg) * S + (i & (C0 - 1))]) / cc[u];
+      if (better(rt, i + 1, best_r, best_b)) {
         best_r = rt;
-        best_b = B;
+        best_b = i + 1;
       }
     }
   }
@@ -294,8 +311,22 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanParams P) {
   if (tid == 0) {
     *P.budget = bstar;
     if (P.rate) *P.rate = best_r;
-    cst32(P.counter, 0u);
   }
+}
+
+// The current device's compute units, looked up once per device.
+static int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 }  // namespace svp
@@ -325,10 +356,20 @@ extern "C" sv_status sv_plan_budget(const sv_plan_desc* d, void* stream) {
   P.budget = d->budget;
   P.draft_len = d->draft_len;
   P.rate = d->rate;
-  uint8_t* ws = (uint8_t*)d->workspace;
-  P.counter = (uint32_t*)ws;
-  P.skey = (uint64_t*)(ws + svp::kWsKeys);
-  const int grid = (int)((n + svp::kSlots - 1) / svp::kSlots);
-  hipLaunchKernelGGL(svp::plan_kernel, dim3((unsigned)grid), dim3(svp::kThreads), 0, (hipStream_t)stream, P);
+  P.skey = (uint64_t*)d->workspace;
+  P.bmax0 = (int32_t)(d->max_budget < n ? d->max_budget : n);
+  P.lg = 0;
+  while ((svp::kThreads << P.lg) < P.bmax0) ++P.lg;
+  // 16 slots a workgroup where that still needs no more workgroups than the
+  // device has compute units, else 32
+  const int cus = svp::compute_units();
+  if (cus <= 0) return SV_ERR_LAUNCH;
+  constexpr int s16 = 2 * svp::kGroups, s32 = 4 * svp::kGroups;
+  const hipStream_t st = (hipStream_t)stream;
+  if ((n + s16 - 1) / s16 <= cus)
+    hipLaunchKernelGGL(svp::rank_kernel<2>, dim3((unsigned)((n + s16 - 1) / s16)), dim3(svp::kThreads), 0, st, P);
+  else
+    hipLaunchKernelGGL(svp::rank_kernel<4>, dim3((unsigned)((n + s32 - 1) / s32)), dim3(svp::kThreads), 0, st, P);
+  hipLaunchKernelGGL(svp::tail_kernel, dim3(1u), dim3(svp::kThreads), 0, st, P);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }

@@ -789,6 +789,22 @@ def test_filtered_calls_are_deterministic(dev):
         np.testing.assert_array_equal(o["p_draft"].view(np.uint64), outs[0]["p_draft"].view(np.uint64))
 
 
+def test_top_p_alone_trees(dev):
+    """Top-p without top-k on bf16 trees: value counts (no top-k array)
+    against the passes over the row (an all-zero top-k array), bit for bit,
+    and both against the oracle."""
+    inp = _random_tree_inputs(344, 9, 8, 20000, "bf16")
+    tp = np.random.default_rng(344).choice(np.array([0.5, 0.9, 0.99], np.float32), size=9).astype(np.float32)
+    check_tree(inp, dev, top_p=tp)
+    outs = []
+    for tk in (None, np.zeros(9, np.int32)):
+        out = sv.verify_tree(_t(inp.logits, dev), _t(inp.node_tokens, dev), _t(inp.parent, dev),
+                             _t(inp.temperature, dev), _t(inp.seeds, dev), top_k=_t(tk, dev), top_p=_t(tp, dev))
+        torch.cuda.synchronize()
+        outs.append(_np(out))
+    _same(outs[0], outs[1], "top-p alone trees: value counts vs passes over the row")
+
+
 @pytest.mark.parametrize("case", ["bf16_headline", "bf16_flat", "f32", "bf16_wide_temps", "bf16_overflow"])
 def test_top_p_alone_paths(dev, case):
     """Top-p without top-k, every request.  bf16 calls without a top-k array

@@ -95,18 +95,50 @@ def test_plan_is_deterministic(dev):
 
 
 def test_workspace_reuse_across_shapes(dev):
-    """One caller workspace serves plans of every shape in turn; each call
-    leaves its completion counter at zero."""
+    """One caller workspace serves plans of every shape in turn, whatever an
+    earlier call or anything else left in it: before some calls it is filled
+    with random bytes (so entries of the sorted list past the drafted count
+    hold stale or non-finite keys), or with zeros (keys whose score bits are
+    NaN); num_steps leaves fewer drafted slots than the table covers."""
     ws = torch.zeros(sv.plan_workspace_bytes(1024, 8), dtype=torch.uint8, device=dev)
-    for seed, bs, K in ((31, 1024, 8), (32, 3, 5), (33, 512, 7), (34, 1, 1), (35, 1024, 8)):
+    cases = ((31, 1024, 8, None), (32, 3, 5, "random"), (33, 512, 7, None), (34, 1, 1, "zero"),
+             (35, 1024, 8, "random"), (36, 512, 7, "zero"), (37, 1000, 8, "random"))
+    for seed, bs, K, fill in cases:
         rng = np.random.default_rng(seed)
         conf = rng.beta(4, 1.2, size=(bs, K)).astype(np.float32)
         cost = 1.0 + np.arange(bs * K + 1) * rng.random() * 5.0 / (bs * K)
-        print(f"[plan] workspace reuse bs={bs} K={K}", flush=True)
+        num_steps = rng.integers(0, K + 1, size=bs).astype(np.int32) if fill else None
+        if fill == "random":
+            ws.copy_(torch.from_numpy(rng.integers(0, 256, size=ws.numel(), dtype=np.uint8)).to(dev))
+        elif fill == "zero":
+            ws.zero_()
+        print(f"[plan] workspace reuse bs={bs} K={K} fill={fill}", flush=True)
+        ref = oracle.plan_budget(conf, cost, float(bs), num_steps=num_steps)
+        out = sv.plan_budget(torch.from_numpy(conf).to(dev), torch.from_numpy(cost).to(dev), float(bs),
+                             num_steps=None if num_steps is None else torch.from_numpy(num_steps), workspace=ws)
+        torch.cuda.synchronize()
+        assert np.isfinite(float(out["rate"].item())) == np.isfinite(ref["rate"])
+        if ref["margin"] >= 1e-12:
+            assert int(out["budget"].item()) == ref["budget"]
+            np.testing.assert_array_equal(out["draft_len"].cpu().numpy(), ref["draft_len"])
+            assert float(out["rate"].item()) == pytest.approx(ref["rate"], rel=1e-12)
+
+
+def test_unaligned_confidences(dev):
+    """Confidences whose address is not 16-byte aligned (a view one float
+    into a larger buffer) take the word-by-word staging path."""
+    for seed, bs, K in ((41, 512, 7), (42, 1024, 8), (43, 33, 6)):
+        rng = np.random.default_rng(seed)
+        conf = rng.beta(4, 1.2, size=(bs, K)).astype(np.float32)
+        cost = 1.0 + np.arange(bs * K + 1) * rng.random() * 5.0 / (bs * K)
+        flat = torch.zeros(bs * K + 1, dtype=torch.float32, device=dev)
+        flat[1:] = torch.from_numpy(conf.ravel()).to(dev)
+        view = flat[1:].view(bs, K)
+        assert view.data_ptr() % 16 != 0
+        print(f"[plan] unaligned confidences bs={bs} K={K}", flush=True)
         ref = oracle.plan_budget(conf, cost, float(bs))
-        out = sv.plan_budget(torch.from_numpy(conf).to(dev), torch.from_numpy(cost).to(dev), float(bs), workspace=ws)
+        out = sv.plan_budget(view, torch.from_numpy(cost).to(dev), float(bs))
         torch.cuda.synchronize()
         if ref["margin"] >= 1e-12:
             assert int(out["budget"].item()) == ref["budget"]
             np.testing.assert_array_equal(out["draft_len"].cpu().numpy(), ref["draft_len"])
-        assert int(ws[:4].view(torch.int32).item()) == 0, "completion counter left non-zero"
