@@ -976,25 +976,29 @@ def test_topk_candidates_trees(dev):
 
 
 # ------------------------------------------------- the give-up path of waits
-def test_abort_flag_gives_internal_status_and_reset_recovers(dev):
+@pytest.mark.parametrize("drafts", ["probs", "onehot"])
+def test_abort_flag_gives_internal_status_and_reset_recovers(dev, drafts):
     """The workspace's abort flag, set from the host before a fused call:
     every bounded wait of the call gives up at its first poll (every kernel
     still ends), the requests whose work waited report REQ_INTERNAL and the
     others are still correct; re-initialising the workspace restores a call
-    that matches the oracle in full."""
+    that matches the oracle in full, with draft probabilities and with
+    one-hot drafts."""
     inp = workloads.chain_bf16_mixed(6, bs=32, k=5, V=20000)
+    probs = inp.draft_probs if drafts == "probs" else None
     ws = sv.Workspace(sv.chain_workspace_bytes(inp.batch, inp.max_draft, inp.vocab, sv.BF16), dev)
     off = ws.base - ws.buf.data_ptr()
     args = (_t(inp.logits, dev), _t(inp.draft_ids, dev), _t(inp.temperature, dev), _t(inp.seeds, dev))
-    ref = oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=inp.draft_probs)
+    onehot = probs is None
+    ref = oracle.verify_chain(inp.logits, inp.draft_ids, inp.temperature, inp.seeds, draft_probs=probs, onehot=onehot)
     # a request's status is written once its outputs are final (the race's
     # merge writes OK after the token), so a request that does not report
     # REQ_INTERNAL is complete however the give-ups interleave; three calls,
     # each on a re-initialised workspace
     for rep in range(3):
-        print(f"[parity] abort flag set before a fused call ({rep})", flush=True)
+        print(f"[parity] abort flag set before a fused call ({drafts}, {rep})", flush=True)
         ws.buf[off:off + 4].view(torch.int32).fill_(1)
-        out = _np(sv.verify_chain(*args, draft_probs=_t(inp.draft_probs, dev), flags=sv.FLAG_FUSED, workspace=ws))
+        out = _np(sv.verify_chain(*args, draft_probs=_t(probs, dev), onehot=onehot, flags=sv.FLAG_FUSED, workspace=ws))
         torch.cuda.synchronize()
         internal = out["status"] == sv.REQ_INTERNAL
         assert internal.any(), "no wait gave up"
@@ -1006,7 +1010,7 @@ def test_abort_flag_gives_internal_status_and_reset_recovers(dev):
         np.testing.assert_array_equal(out["tokens"][margin_ok], ref["tokens"][margin_ok])
         print(f"[parity]   {int(internal.sum())} of {inp.batch} requests reported REQ_INTERNAL; resetting", flush=True)
         ws.reset()
-    got = _np(sv.verify_chain(*args, draft_probs=_t(inp.draft_probs, dev), flags=sv.FLAG_FUSED, workspace=ws))
+    got = _np(sv.verify_chain(*args, draft_probs=_t(probs, dev), onehot=onehot, flags=sv.FLAG_FUSED, workspace=ws))
     torch.cuda.synchronize()
     assert int(ws.buf[off:off + 4].view(torch.int32).item()) == 0
     _compare(ref, got, "after reset", kind="chain")
