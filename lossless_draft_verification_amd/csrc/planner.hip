@@ -44,8 +44,9 @@ constexpr int kPer = SV_PLAN_MAX_SLOTS / kThreads;  // entries per thread of the
 // staged confidences: request b's row at b Kp, Kp = K rounded up to odd
 constexpr int kConfLds = SV_PLAN_MAX_SLOTS + SV_PLAN_MAX_SLOTS / 2;
 
-// Workspace: the keys in rank order, passed from the first launch to the
-// second (sized for SV_PLAN_MAX_SLOTS: one layout for every shape).
+// Workspace: the keys of the ranks below min(max_budget, slots), each where
+// the second launch reads it, passed from the first launch to the second
+// (sized for SV_PLAN_MAX_SLOTS: one layout for every shape).
 constexpr size_t kWsBytes = 8 * (size_t)SV_PLAN_MAX_SLOTS;
 
 struct PlanParams {
@@ -75,11 +76,11 @@ __device__ __forceinline__ int steps_of(const PlanParams& P, int b) {
 
 // Keys of every slot (slot s = b K + j; all-ones past a request's drafted
 // positions) into out[j bs + b], and those of slots s0 .. s0 + R - 1 also
-// into own[s - s0] (which the caller has set to all-ones).  The confidences are first staged in
-// shared memory by loads in which the lanes of a wave read consecutive
-// words, request b's at cs[b Kp] with an odd row stride Kp (so the lanes,
-// one request each, then read distinct banks); one thread per request takes
-// the running product.
+// into own[s - s0] (which the caller has set to all-ones).  The confidences
+// are first staged in shared memory by loads in which the lanes of a wave
+// read consecutive words, request b's at cs[b Kp] with an odd row stride Kp
+// (so the lanes, one request each, then read distinct banks); one thread per
+// request takes the running product.
 __device__ __forceinline__ void slot_keys(const PlanParams& P, uint64_t* out, float* cs, uint64_t* own, int s0,
                                           int R) {
   const int K = P.K, bs = P.bs, N = bs * K;
@@ -118,8 +119,9 @@ __device__ __forceinline__ float key_score(uint64_t k) { return __uint_as_float(
 
 // Exclusive prefix over the workgroup of one double per thread, in a fixed
 // order (a wave scan, then the waves' totals).  A thread's result is formed
-// from the values of lower threads only (shifted, not by subtracting its
-// own), so a non-finite value reaches no thread below it.
+// from the values of lower threads only (the inclusive scan shifted by one
+// lane, not minus the thread's own value), so a non-finite value reaches
+// only the threads above it.
 __device__ __forceinline__ double block_exclusive(double v, double* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double in = v;
