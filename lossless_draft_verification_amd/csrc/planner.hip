@@ -219,8 +219,9 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(PlanParams P) {
 // global load is issued first.  Entries at or past the drafted count n are
 // stale, but they only reach the sums at positions past n, and no budget
 // past n is taken, so the chunk sums need not wait for n: it is reduced
-// beside the scan.  The prefix sums then pass through LDS (rows of odd
-// stride C0 + 1) to the threads holding the costs: position u kThreads + t.
+// beside the scan.  With more than four positions per thread the prefix
+// sums then pass through LDS (rows of odd stride C0 + 1) to the threads
+// holding the costs, which are loaded for position u kThreads + t.
 __global__ __launch_bounds__(kThreads) void tail_kernel(PlanParams P) {
   __shared__ double gsum[(kPer + 1) * kThreads];
   __shared__ int adm[SV_PLAN_MAX_SLOTS];
@@ -231,13 +232,17 @@ __global__ __launch_bounds__(kThreads) void tail_kernel(PlanParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bmax0 = P.bmax0, lg = P.lg, C0 = 1 << lg, S = C0 + 1;
   const int r0 = tid * C0;
+  // up to four positions per thread: each thread loads its own positions'
+  // costs (a short stride) and takes their ratios where its prefix sums
+  // are; more: the costs of positions u kThreads + t, reached through LDS
+  const bool own = lg <= 2;
   uint64_t sk[kPer];
   double cc[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int i = u * kThreads + tid;
+    const int i = u * kThreads + tid, pos = own ? r0 + u : i;
     sk[u] = (u < C0 && r0 + u < bmax0) ? P.skey[i] : ~0ull;
-    cc[u] = (u < C0 && i < bmax0) ? P.cost[i + 1] : 1.0;
+    cc[u] = (u < C0 && pos < bmax0) ? P.cost[pos + 1] : 1.0;
   }
   const double cost0 = tid == 0 ? P.cost[0] : 1.0;
   int mine = 0;
@@ -256,13 +261,6 @@ __global__ __launch_bounds__(kThreads) void tail_kernel(PlanParams P) {
   int n = 0;
   for (int w = 0; w < kWaves; ++w) n += red_n[w];
   const int bmax = P.bmax_table < n ? P.bmax_table : n;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    if (u < C0 && r0 + u < bmax) {
-      gain += (double)key_score(sk[u]);
-      gsum[tid * S + u] = gain;  // gain at B = r0 + u + 1
-    }
-  __syncthreads();
   double best_r = -INFINITY;
   int best_b = INT32_MAX;
   if (tid == 0) {  // B = 0
@@ -270,14 +268,34 @@ __global__ __launch_bounds__(kThreads) void tail_kernel(PlanParams P) {
     if (!(best_r > -INFINITY)) best_r = -INFINITY, best_b = INT32_MAX;
     else best_b = 0;
   }
+  if (own) {
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = u * kThreads + tid;
-    if (u < C0 && i < bmax) {
-      const double rt = (P.base + gsum[(i >> lg) * S + (i & (C0 - 1))]) / cc[u];
-      if (better(rt, i + 1, best_r, best_b)) {
-        best_r = rt;
-        best_b = i + 1;
+    for (int u = 0; u < kPer; ++u)
+      if (u < C0 && r0 + u < bmax) {
+        gain += (double)key_score(sk[u]);  // gain at B = r0 + u + 1
+        const double rt = (P.base + gain) / cc[u];
+        if (better(rt, r0 + u + 1, best_r, best_b)) {
+          best_r = rt;
+          best_b = r0 + u + 1;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (u < C0 && r0 + u < bmax) {
+        gain += (double)key_score(sk[u]);
+        gsum[tid * S + u] = gain;  // gain at B = r0 + u + 1
+      }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (u < C0 && i < bmax) {
+        const double rt = (P.base + gsum[(i >> lg) * S + (i & (C0 - 1))]) / cc[u];
+        if (better(rt, i + 1, best_r, best_b)) {
+          best_r = rt;
+          best_b = i + 1;
+        }
       }
     }
   }
