@@ -68,7 +68,7 @@ constexpr int kWaves = kWG / 64;
 #define SV_K1_VEC 2
 #endif
 #ifndef SV_K1_SLOTS
-#define SV_K1_SLOTS (256 * 7)
+#define SV_K1_SLOTS (256 * 4)
 #endif
 #ifndef SV_K1_ROUNDS
 #define SV_K1_ROUNDS 1
@@ -84,9 +84,13 @@ constexpr int kVecPerThread = SV_K1_VEC;        // 16-byte loads per thread in a
 #define SV_KR_UNROLL 4
 #endif
 constexpr int kKRWorkgroups = SV_KR_WORKGROUPS;  // block rule's residual-mass pass: workgroups it aims at
-// K1 workgroups per call: an MI355X holds 256 CUs x 7 of them at once (71
-// VGPRs), so the stream is one round.
+// K1 workgroups per call: at least four per CU of an MI355X where the rows
+// allow, and no more than it holds at once (seven per CU at K1's 71 VGPRs),
+// so the stream is one round.  Longer segments stream as fast as shorter
+// ones on large batches, faster on small ones, and leave fewer partials for
+// the decision step to fold.
 constexpr int kK1Workgroups = SV_K1_SLOTS * SV_K1_ROUNDS;
+constexpr int kK1Resident = 256 * SV_K1_OCC * SV_K1_ROUNDS;
 // Ids per chunk of the sampling race: part of the sampler's definition (the
 // race picks a chunk, then an id inside it), fixed independently of any
 // workgroup shape; the kernels' tiles are sized to it.
@@ -3713,14 +3717,16 @@ struct Shape {
 };
 
 // Work split of a call (a function of the shape alone, so results never
-// depend on the device or the schedule): every row in Q segments, as many
-// as the K1 workgroups that are resident at once allow (at most 64 and at
-// most one per sub-chunk; one when there are more rows than that).
+// depend on the device or the schedule): every row in Q segments, the
+// fewest that give kK1Workgroups workgroups, but no more than are resident
+// at once (at most 64 and at most one per sub-chunk; one when there are
+// more rows than that).
 static Shape shape_of(int64_t bs, int64_t R, int64_t V, int dtype, bool races, size_t data_off = kDataOffset) {
   Shape s;
   s.SUB = (dtype == SV_BF16 ? 8 : 4) * kVecPerThread * kWG;
   s.nsub = (int)((V + s.SUB - 1) / s.SUB);
-  int64_t q = kK1Workgroups / (bs * R);
+  int64_t q = (kK1Workgroups + bs * R - 1) / (bs * R);
+  if (q > kK1Resident / (bs * R)) q = kK1Resident / (bs * R);
   if (q > s.nsub) q = s.nsub;
   if (q > 64) q = 64;
   if (q < 1) q = 1;
