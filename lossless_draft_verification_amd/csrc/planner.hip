@@ -38,7 +38,7 @@ namespace svp {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kParts = 128;                  // threads that share one slot group's comparisons
+constexpr int kParts = 256;                  // threads that share one slot group's comparisons
 constexpr int kGroups = kThreads / kParts;   // slot groups of a workgroup
 constexpr int kPer = SV_PLAN_MAX_SLOTS / kThreads;  // entries per thread of the tail workgroup, at most
 // staged confidences: request b's row at b Kp, Kp = K rounded up to odd
@@ -168,7 +168,7 @@ __device__ __forceinline__ void count_below(const uint64_t* keys, int p, int n, 
 // holds 64 parts of one group).  Each slot's key is then stored at its rank.
 template <int R>
 __global__ __launch_bounds__(kThreads) void rank_kernel(PlanParams P) {
-  static_assert(R % 2 == 0 && kParts == 128, "packed counts; two waves per slot group");
+  static_assert(R % 2 == 0 && kParts == 256, "packed counts; four waves per slot group");
   constexpr int S = R * kGroups;
   __shared__ uint64_t keys[SV_PLAN_MAX_SLOTS];
   __shared__ float confs[kConfLds];
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(PlanParams P) {
   uint32_t c[R];
   count_below<R>(keys, p, N, x, c);
   // sum over the parts: within the wave (two counts packed per word, each
-  // at most SV_PLAN_MAX_SLOTS < 2^16), then the group's two waves
+  // at most SV_PLAN_MAX_SLOTS < 2^16), then the group's four waves
   uint32_t c2[R / 2];
 #pragma unroll
   for (int r = 0; r < R / 2; ++r) c2[r] = c[2 * r] | (c[2 * r + 1] << 16);
@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(PlanParams P) {
   __syncthreads();
   if (tid < S) {
     const int gg = tid / R, r = tid % R;
-    const uint32_t w2 = part[2 * gg][r >> 1] + part[2 * gg + 1][r >> 1];
+    const uint32_t w2 = part[4 * gg][r >> 1] + part[4 * gg + 1][r >> 1] + part[4 * gg + 2][r >> 1] +
+                        part[4 * gg + 3][r >> 1];
     const uint32_t rk = (w2 >> (16 * (r & 1))) & 0xFFFFu;
     if (s0 + tid < N) {
       const uint64_t xs = own[tid];
@@ -384,12 +385,12 @@ extern "C" sv_status sv_plan_budget(const sv_plan_desc* d, void* stream) {
   // device has compute units, else 32
   const int cus = svp::compute_units();
   if (cus <= 0) return SV_ERR_LAUNCH;
-  constexpr int s16 = 2 * svp::kGroups, s32 = 4 * svp::kGroups;
+  constexpr int s16 = 4 * svp::kGroups, s32 = 8 * svp::kGroups;
   const hipStream_t st = (hipStream_t)stream;
   if ((n + s16 - 1) / s16 <= cus)
-    hipLaunchKernelGGL(svp::rank_kernel<2>, dim3((unsigned)((n + s16 - 1) / s16)), dim3(svp::kThreads), 0, st, P);
+    hipLaunchKernelGGL(svp::rank_kernel<4>, dim3((unsigned)((n + s16 - 1) / s16)), dim3(svp::kThreads), 0, st, P);
   else
-    hipLaunchKernelGGL(svp::rank_kernel<4>, dim3((unsigned)((n + s32 - 1) / s32)), dim3(svp::kThreads), 0, st, P);
+    hipLaunchKernelGGL(svp::rank_kernel<8>, dim3((unsigned)((n + s32 - 1) / s32)), dim3(svp::kThreads), 0, st, P);
   hipLaunchKernelGGL(svp::tail_kernel, dim3(1u), dim3(svp::kThreads), 0, st, P);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
